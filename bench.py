@@ -1,0 +1,393 @@
+"""Benchmark of the quantized-weight linear projection on one MI355X.
+
+One step runs every row of the hot path once on its workload, inputs already
+resident in HBM:
+  decode_mxfp8   MXFP8 256x512 decode (FP32 out)            + MXFP8 GEMV T=1
+  reencode       block-128 E4M3 -> per-row FP8, 5120x17408
+  gemv_fp8row    row-FP8 17408x5120, T = 1, 4, 16, 33 (BF16 out)   <- headline
+  gemv_down      re-encoded 5120x17408, T = 1, 33; BF16 gate 96x5120, T = 1, 33
+  gemv_q4g64 / gemv_q8g32   at 17408x5120 and 5120x17408, T = 1, 8, 33
+  head           row-FP8 152064x5120, T = 1..64
+  quant_int8     1792x5120 per-token-per-64 int8 quantization
+  gemm_w8a8      W8A8 GEMM M=1792, N=17408, K=5120
+  gemm_fp8       per-token E4M3 quantization + FP8 GEMM, same shape
+Weights of the decode GEMVs rotate over copies totalling more than 512 MB so
+that the 256 MB last-level cache cannot serve them.  Every launch is bracketed
+by HIP events on the stream it runs on; per-row averages come from those.
+
+`value` is the headline: decode GEMV HBM GB/s on row-FP8 17408x5120 over
+T = 1, 4, 16, 33 (algorithmic bytes / kernel time).  The prefill GEMMs are
+reported in `prefill` (TOPS and fraction of the MFMA peak).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+FP8_PEAK_TFLOPS = 5000.0
+ROTATE_BYTES = 512 << 20
+DEV = "cuda:0"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--rows", default="all", help="comma list of row groups to run (default: all)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--rows-json", default=None, help="also write per-row results to this file")
+    return p.parse_args()
+
+
+class Row:
+    def __init__(self, name, kernel, unit, work, fn):
+        self.name, self.kernel, self.unit, self.work, self.fn = name, kernel, unit, work, fn
+        self.ms = []
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def to_dev(a):
+    torch = _torch()
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    elif a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(a).to(DEV)
+
+
+def rotation(*tensors):
+    """Copies of a weight set (first tensor sets the count) totalling > ROTATE_BYTES;
+    returns a function that hands out the next copy on every call."""
+    first = tensors[0]
+    n = max(1, -(-ROTATE_BYTES // (first.numel() * first.element_size())))
+    sets = [tuple(tensors)] + [tuple(t.clone() for t in tensors) for _ in range(n - 1)]
+    state = [0]
+
+    def nxt():
+        v = sets[state[0] % len(sets)]
+        state[0] += 1
+        return v
+    return nxt
+
+
+def empty(shape, dtype):
+    return _torch().empty(shape, dtype=dtype, device=DEV)
+
+
+# Each section builds its rows in its own scope: the launch closures capture
+# only names that are never rebound.
+
+def rows_mxfp8(nq, W):
+    torch = _torch()
+    d = W.mxfp8_gemv()
+    words, e8, x = to_dev(d["words"]), to_dev(d["e8m0"]), to_dev(d["x"])
+    n, k = 256, 512
+    out = empty((n, k), torch.float32)
+    y = empty((1, n), torch.float32)
+    return [Row("decode_mxfp8", "decode_mxfp8", "GB/s", n * k + n * k // 32 + 4 * n * k,
+                lambda: nq.nq_decode_mxfp8(words, e8, n, k, out)),
+            Row("gemv_mxfp8_T1", "gemv_mxfp8", "GB/s", n * k + n * k // 32 + 2 * k + 4 * n,
+                lambda: nq.nq_gemv_qgroup(nq.NQ_W_MXFP8_G32, words, e8, x, 1, n, k, y))]
+
+
+def _fp8row_gemv_rows(nq, prefix, kernel, q, s, xs, ts, rotate=True):
+    torch = _torch()
+    n, k = q.shape
+    nxt = rotation(q, s) if rotate else (lambda: (q, s))
+    rows = []
+    for t, xt in zip(ts, xs):
+        y = empty((t, n), torch.int16)
+        ws = nq.alloc_gemv_workspace(-1, t, n, k, DEV)
+
+        def fn(t=t, xt=xt, y=y, ws=ws):
+            qq, ss = nxt()
+            nq.nq_gemv_fp8row(qq, ss, xt, t, n, k, y, ws)
+        rows.append(Row(f"{prefix}_T{t}", kernel, "GB/s", n * k + 2 * n + 2 * t * k + 2 * t * n, fn))
+    return rows
+
+
+def _encode_bf16_on_gpu(nq, w_bf16):
+    torch = _torch()
+    n, k = w_bf16.shape
+    wb = to_dev(w_bf16)
+    q, s = empty((n, k), torch.uint8), empty((n,), torch.int16)
+    nq.nq_encode_fp8row_bf16(wb, n, k, q, s)
+    del wb
+    return q, s
+
+
+def rows_gemv_fp8row(nq, W):
+    n, k = W.FFN, W.HIDDEN
+    q, s = _encode_bf16_on_gpu(nq, W.fp8row_weights_bf16(n, k))
+    x33 = to_dev(W.activations(33, k))
+    ts = (1, 4, 16, 33)
+    return _fp8row_gemv_rows(nq, "gemv_fp8row", "gemv_fp8row", q, s, [x33[:t].contiguous() for t in ts], ts)
+
+
+def rows_reencode_and_down(nq, W, want_reencode, want_down):
+    torch = _torch()
+    d = W.block128_codes()
+    n, k = d["codes"].shape
+    codes, wsi = to_dev(d["codes"]), to_dev(d["wsi"])
+    gr, gc = d["wsi"].shape
+    q, s = empty((n, k), torch.uint8), empty((n,), torch.int16)
+    nq.nq_reencode_block128_to_row(codes, wsi, n, k, 0, n, q, s)
+    rows = []
+    if want_reencode:
+        rows.append(Row("reencode", "reencode", "GB/s", 2 * n * k + 4 * gr * gc + 2 * n,
+                        lambda: nq.nq_reencode_block128_to_row(codes, wsi, n, k, 0, n, q, s)))
+    if want_down:
+        ts = (1, 33)
+        xs = [to_dev(W.activations(t, k, workload=3, tensor=3)) for t in ts]
+        rows += _fp8row_gemv_rows(nq, "gemv_down", "gemv_fp8row", q, s, xs, ts)
+        rows += rows_gate(nq, W)
+    return rows
+
+
+def rows_gate(nq, W):
+    torch = _torch()
+    gate = to_dev(W.gate_bf16())
+    n, k = W.GATE_ROWS, W.HIDDEN
+    rows = []
+    for t in (1, 33):
+        xg = to_dev(W.activations(t, k, workload=3, tensor=4))
+        yg = empty((t, n), torch.int16)
+        rows.append(Row(f"gemv_gate_T{t}", "gemv_bf16", "GB/s", 2 * n * k + 2 * t * k + 2 * t * n,
+                        lambda t=t, xg=xg, yg=yg: nq.nq_gemv_qgroup(nq.NQ_W_BF16, gate, None, xg, t, n, k, yg)))
+    return rows
+
+
+def rows_grouped(nq, W, name):
+    torch = _torch()
+    fmt = {"q4g64": nq.NQ_W_Q4G64_F16S, "q8g32": nq.NQ_W_Q8G32_F16S}[name]
+    gs = 64 if name == "q4g64" else 32
+    rows = []
+    for (n, k) in ((W.FFN, W.HIDDEN), (W.HIDDEN, W.FFN)):
+        rows += _grouped_shape_rows(nq, W, name, fmt, gs, n, k, torch)
+    return rows
+
+
+def _grouped_shape_rows(nq, W, name, fmt, gs, n, k, torch):
+    dd = W.grouped(name, n, k)
+    cd, sd = to_dev(dd["codes"]), to_dev(dd["scales"])
+    nxt = rotation(cd, sd)
+    cbytes = cd.numel()
+    rows = []
+    for t in (1, 8, 33):
+        y = empty((t, n), torch.int16)
+        xt = to_dev(W.activations(t, k, workload=4, tensor=50))
+        ws = nq.alloc_gemv_workspace(fmt, t, n, k, DEV)
+
+        def fn(t=t, xt=xt, y=y, ws=ws):
+            cc, ss = nxt()
+            nq.nq_gemv_qgroup(fmt, cc, ss, xt, t, n, k, y, ws)
+        rows.append(Row(f"gemv_{name}_{n}x{k}_T{t}", f"gemv_{name}", "GB/s",
+                        cbytes + 2 * n * (k // gs) + 2 * t * k + 2 * t * n, fn))
+    return rows
+
+
+def rows_head(nq, W):
+    n, k = W.HEAD_ROWS, W.HIDDEN
+    q, s = _encode_bf16_on_gpu(nq, W.head_weights_bf16())
+    x64 = to_dev(W.activations(64, k, workload=5, tensor=4))
+    ts = list(range(1, 65))
+    return _fp8row_gemv_rows(nq, "head", "gemv_head", q, s, [x64[:t].contiguous() for t in ts], ts,
+                             rotate=False)
+
+
+def rows_prefill(nq, W, want_quant, want_w8a8, want_fp8):
+    torch = _torch()
+    d = W.w8a8_prefill()
+    m, k = d["x"].shape
+    n = d["w"].shape[0]
+    x = to_dev(d["x"])
+    qa, sa = empty((m, k), torch.int8), empty((m, k // 64), torch.float32)
+    nq.nq_quantize_act_int8_g64(x, m, k, qa, sa)
+    rows = []
+    if want_quant:
+        rows.append(Row("quant_int8", "quant_int8", "GB/s", 2 * m * k + m * k + 4 * m * (k // 64),
+                        lambda: nq.nq_quantize_act_int8_g64(x, m, k, qa, sa)))
+    if want_w8a8:
+        w, ws = to_dev(d["w"]), to_dev(d["w_scale"])
+        y = empty((m, n), torch.float32)
+        rows.append(Row("gemm_w8a8", "gemm_w8a8", "TOPS", 2 * m * n * k,
+                        lambda: nq.nq_gemm_w8a8_g64(qa, sa, w, ws, m, n, k, y)))
+    if want_fp8:
+        rows.append(_fp8_gemm_row(nq, W, m, n, k))
+    return rows
+
+
+def _fp8_gemm_row(nq, W, m, n, k):
+    torch = _torch()
+    q, s = _encode_bf16_on_gpu(nq, W.fp8row_weights_bf16(n, k))
+    xf = to_dev(W.activations(m, k, workload=5, tensor=6))
+    ac, asc = empty((m, k), torch.uint8), empty((m,), torch.float32)
+    yf = empty((m, n), torch.float32)
+    return Row("gemm_fp8", "gemm_fp8", "TFLOP/s", 2 * m * n * k,
+               lambda: nq.nq_gemm_fp8row(xf, q, s, m, n, k, ac, asc, yf))
+
+
+def build_rows(selected):
+    from quantized_weight_linear_amd import nq
+    from quantized_weight_linear_amd import workloads as W
+
+    groups = None if selected == "all" else set(selected.split(","))
+
+    def want(name):
+        return groups is None or name in groups
+
+    rows = []
+    if want("decode_mxfp8"):
+        rows += rows_mxfp8(nq, W)
+    if want("gemv_fp8row"):
+        rows += rows_gemv_fp8row(nq, W)
+    if want("reencode") or want("gemv_down"):
+        rows += rows_reencode_and_down(nq, W, want("reencode"), want("gemv_down"))
+    for name in ("q4g64", "q8g32"):
+        if want(f"gemv_{name}"):
+            rows += rows_grouped(nq, W, name)
+    if want("head"):
+        rows += rows_head(nq, W)
+    if want("quant_int8") or want("gemm_w8a8") or want("gemm_fp8"):
+        rows += rows_prefill(nq, W, want("quant_int8"), want("gemm_w8a8"), want("gemm_fp8"))
+    _torch().cuda.synchronize()
+    return rows
+
+
+def cpu_baseline():
+    """The oracle (as it stands) on the headline workload: row-FP8 decode GEMV
+    17408x5120 at T = 1, 4, 16, 33, on the host cores."""
+    from oracle import method as M
+    from quantized_weight_linear_amd import workloads as W
+
+    n, k = W.FFN, W.HIDDEN
+    w = W.fp8row_weights_bf16(n, k)
+    wq, ws = M.encode_fp8row_bf16(w)
+    x33 = W.activations(33, k)
+    total_bytes, total_s = 0, 0.0
+    for t in (1, 4, 16, 33):
+        t0 = time.perf_counter()
+        M.gemv_fp8row(wq, ws, x33[:t])
+        total_s += time.perf_counter() - t0
+        total_bytes += n * k + 2 * n + 2 * t * k + 2 * t * n
+    try:
+        import threadpoolctl
+        threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    return {"value": round(total_bytes / total_s / 1e9, 3), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": "oracle decode GEMV (numpy float64) on the full row-FP8 17408x5120 weight, "
+                      "T = 1, 4, 16, 33 once each; the oracle's weight encode is not timed"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(how the path would shard is described in DESIGN.md)"}))
+        sys.exit(2)
+    torch = _torch()
+    from quantized_weight_linear_amd import nq
+    nq.lib()
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    t_setup = time.perf_counter()
+    rows = build_rows(args.rows)
+    log(f"setup {time.perf_counter() - t_setup:.1f}s, {len(rows)} launches per step")
+
+    for i in range(args.warmup):
+        for r in rows:
+            r.fn()
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+
+    stream = torch.cuda.current_stream()
+    events = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for r in rows:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            r.fn()
+            b.record(stream)
+            events.append((r, a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for r, a, b in events:
+        r.ms.append(a.elapsed_time(b))
+    log(f"timed {args.steps} steps in {wall:.3f}s")
+
+    results = {}
+    for r in rows:
+        ms = float(np.mean(r.ms))
+        if r.unit == "GB/s":
+            rate = r.work / (ms * 1e-3) / 1e9
+            frac = rate / HBM_PEAK_GBS
+        else:
+            rate = r.work / (ms * 1e-3) / 1e12
+            frac = rate / (INT8_PEAK_TOPS if r.unit == "TOPS" else FP8_PEAK_TFLOPS)
+        results[r.name] = {"kernel": r.kernel, "us": round(ms * 1e3, 3), "rate": round(rate, 2),
+                           "unit": r.unit, "frac": round(frac, 4), "work": r.work}
+
+    head = [r for r in rows if r.name.startswith("gemv_fp8row_T")]
+    line = {"metric": "decode GEMV HBM GB/s (% peak) at T=1..33; prefill GEMM TOPS (% MFMA peak) at T=1792",
+            "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(wall / args.steps * 1e3, 3), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "fp8(e4m3) weights x bf16 activations, fp32 accumulate",
+            "data": "synthetic",
+            "config": {"workload": "row-FP8 decode GEMV 17408x5120 (FFN up/gate), T=1,4,16,33, BF16 out; "
+                                   "one step = every hot-path row once",
+                       "T": [1, 4, 16, 33], "N": 17408, "K": 5120}}
+    if head:
+        byt = sum(r.work * len(r.ms) for r in head)
+        sec = sum(sum(r.ms) * 1e-3 for r in head)
+        gbs = byt / sec / 1e9
+        line["value"] = round(gbs, 2)
+        line["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                            "kernel": "gemv_mfma_kernel, row-FP8 17408x5120, launches T=1,4,16,33",
+                            "bytes_per_launch": {r.name: r.work for r in head},
+                            "us_per_launch": {r.name: results[r.name]["us"] for r in head}}
+    pre = {}
+    for name in ("gemm_w8a8", "gemm_fp8"):
+        if name in results:
+            pre[name] = {"us": results[name]["us"], "rate": results[name]["rate"], "unit": results[name]["unit"],
+                         "frac_of_peak": results[name]["frac"]}
+    if pre:
+        line["prefill"] = pre
+    line["rows"] = {k: {"us": v["us"], "rate": v["rate"], "unit": v["unit"], "frac": v["frac"]}
+                    for k, v in results.items()}
+    if not args.no_cpu_baseline and head:
+        log("cpu baseline (oracle) ...")
+        line["cpu_baseline"] = cpu_baseline()
+    if args.rows_json:
+        with open(args.rows_json, "w") as f:
+            json.dump(results, f, indent=1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,240 @@
+/*
+ * nq.h — quantized-weight linear projection for AMD MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  Packed low-bit weights are decoded
+ * on the fly against their stored scales and multiplied by BF16 activations:
+ * a bandwidth-bound GEMV / skinny GEMM for decode and verify steps (a few
+ * tokens) and MFMA GEMMs for prefill chunks.
+ *
+ * Sources (the web pages the method is described on), cited by title and
+ * section below:
+ *   [MXFP8 card]   "Qwen3.8-27B "MXFP8-CRACK" — NInfer artifact"
+ *   [FP8 card]     "Qwen3.8-27B EfficientThink-Uncensored FP8 for NInfer"
+ *   [NVFP4 card]   "Qwen3.8-27B-NVIDIA-NVFP4-NInferV3"
+ *   [RTX5080 card] "Qwen3.8-27B for NInfer — RTX 5080 16 GB, true 128K + Vision"
+ *   [int8 card]    "Qwen3.8-27B, NInfer int8-prefill artifact for the RTX 4090"
+ *
+ * Conventions for every entry point
+ *   - Matrices are dense and row-major.  A weight matrix is [N][K]: N output
+ *     rows, K input channels; activations are [T][K] (T tokens); outputs are
+ *     [T][N]; y[t][n] = sum_k x[t][k] * W[n][k].  Group and block axes run
+ *     along K.
+ *   - BF16 / FP16 values are passed as their 16-bit patterns (uint16_t), FP32
+ *     as float, E4M3 codes as uint8_t (OCP E4M3, "e4m3fn": bias 7, largest
+ *     finite 448, S.1111.111 is NaN).
+ *   - All data pointers are DEVICE pointers and must be 16-byte aligned.  The
+ *     caller owns every buffer; the library allocates nothing and keeps no
+ *     state between calls.  `stream` is a hipStream_t (NULL = the default
+ *     stream); every call only enqueues work on it and returns without
+ *     synchronizing.  Output buffers must not overlap inputs.
+ *   - A buffer whose size is zero may be NULL.  Calls with nothing to compute
+ *     (N == 0 or T == 0) return NQ_OK without launching.
+ *   - Every call validates all arguments before enqueuing anything and returns
+ *     the first failing check; on any error nothing is written.  No C++
+ *     exception crosses this interface.
+ */
+#ifndef NQ_H
+#define NQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NQ_ABI_VERSION 1
+
+typedef enum {
+    NQ_OK = 0,
+    NQ_ERR_NULL = 1,    /* a required pointer is NULL */
+    NQ_ERR_SHAPE = 2,   /* a size is negative, a divisibility rule fails, or a grid does not match */
+    NQ_ERR_ALIGN = 3,   /* a pointer is not 16-byte aligned */
+    NQ_ERR_FORMAT = 4,  /* an enum value is unknown */
+    NQ_ERR_RANGE = 5,   /* a row range is empty or outside [0, N] */
+    NQ_ERR_HIP = 6      /* the HIP runtime reported an error when enqueuing */
+} nq_status;
+
+typedef enum { NQ_OUT_F32 = 0, NQ_OUT_BF16 = 1 } nq_out;
+
+typedef enum {
+    NQ_W_Q4G64_F16S = 0,  /* 4-bit two's-complement codes, element 2j in the low nibble of byte j
+                             ([N][K/2] bytes), one FP16 scale per 64 elements ([N][K/64]) */
+    NQ_W_Q8G32_F16S = 1,  /* int8 codes [N][K], one FP16 scale per 32 elements [N][K/32] */
+    NQ_W_Q8G64_F16S = 2,  /* int8 codes [N][K], one FP16 scale per 64 elements [N][K/64] */
+    NQ_W_MXFP8_G32 = 3,   /* four E4M3 codes per little-endian u32 word ([N][K/4]), one UE8M0
+                             byte per 32 elements ([N][K/32]) worth 2^(b-127); b = 255 is NaN */
+    NQ_W_BF16 = 4         /* BF16 weights [N][K], no scales */
+} nq_wfmt;
+
+typedef enum { NQ_ROUTE_BF16 = 0, NQ_ROUTE_A8 = 1 } nq_route_kind;
+
+/* Version of this interface (NQ_ABI_VERSION). */
+int nq_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* nq_status_string(int status);
+
+/*
+ * MXFP8 decode.  [MXFP8 card, "How it was built", item 1]: four E4M3 codes
+ * per 32-bit word, one UE8M0 scale byte 2^(b-127) per 32-element group, decoded
+ * to BF16.
+ *   words  [N][K/4] u32, element 4j+i in bits 8i..8i+7 of word j
+ *   e8m0   [N][K/32] u8
+ *   w_out  [N][K] FP32 (out_dt = NQ_OUT_F32) or BF16 bits (NQ_OUT_BF16): the
+ *          exact value e4m3(code) * 2^(b-127) rounded once to nearest-even
+ *          (overflow to infinity; NaN codes or b = 255 give the quiet NaN
+ *          0x7FC00000 / 0x7FC0).
+ * Errors: K % 32 != 0 -> NQ_ERR_SHAPE.
+ */
+nq_status nq_decode_mxfp8(const uint32_t* words, const uint8_t* e8m0, int64_t N, int64_t K,
+                          int out_dt, void* w_out, void* stream);
+
+/*
+ * Block-128x128 E4M3 -> one BF16 scale per output row ("fp8_row_maxabs").
+ * [FP8 card, "Conversion and verification", "Block-wise to per-row,
+ * exactly"]: each code is decoded in FP32 as e4m3(code) times the scale of its
+ * 128x128 block (weight_scale_inv), the grid is checked against the code shape,
+ * the values are re-encoded with one BF16 scale per row, and a row range reads
+ * only the block rows it touches.
+ *   codes      [N][K] E4M3 codes
+ *   wsi        [gr][gc] FP32, gr = ceil(N/128), gc = ceil(K/128)
+ *   rows       [row_begin, row_end) of the N rows are re-encoded
+ *   out_codes  [row_end-row_begin][K]: e4m3_rne_sat(fp32(v / s)) where v is the
+ *              FP32 decoded value and s the row scale
+ *   out_scale  [row_end-row_begin] BF16 bits: s = bf16_rne(fp32(max|v| / 448))
+ * A row of zeros gets s = +0 and keeps its signed zero codes; a row holding a
+ * NaN code gets s = NaN (0x7FC0) and NaN codes (0x7F).
+ * Errors: gr/gc mismatch -> NQ_ERR_SHAPE; bad row range -> NQ_ERR_RANGE.
+ */
+nq_status nq_reencode_block128_to_row(const uint8_t* codes, const float* wsi, int64_t N, int64_t K,
+                                      int64_t gr, int64_t gc, int64_t row_begin, int64_t row_end,
+                                      uint8_t* out_codes, uint16_t* out_scale, void* stream);
+
+/*
+ * BF16 -> row-scaled FP8, the same per-row encoding as above applied to BF16
+ * values.  [NVFP4 card, "How it was created"]: the token embedding goes from
+ * its BF16 source to row-scale FP8.
+ *   w          [N][K] BF16 bits;  out_codes [N][K];  out_scale [N] BF16 bits
+ */
+nq_status nq_encode_fp8row_bf16(const uint16_t* w, int64_t N, int64_t K, uint8_t* out_codes,
+                                uint16_t* out_scale, void* stream);
+
+/*
+ * Int8 activation quantization for the W8A8 prefill route.  [int8 card, "What
+ * changes"]: per token and per 64 channels, scale = amax / 127.
+ *   x      [T][K] BF16 bits, K % 64 == 0
+ *   q      [T][K] int8: clamp(rne(fp32(x / s)), -127, 127); an all-zero group
+ *          (s = 0) gives 0, a NaN quotient gives 0
+ *   scale  [T][K/64] FP32: s = fp32(amax / 127) (IEEE division)
+ */
+nq_status nq_quantize_act_int8_g64(const uint16_t* x, int64_t T, int64_t K, int8_t* q, float* scale,
+                                   void* stream);
+
+/*
+ * Per-token E4M3 activation quantization for the FP8-activation GEMM.  The
+ * pages name FP8-activation routes ([FP8 card, "Conversion and verification",
+ * "Hardware fit"]) without describing their quantizer; this is the reading
+ * used here: s = fp32(amax_t / 448), codes e4m3_rne_sat(fp32(x / s)), an
+ * all-zero token gets s = 0 and keeps its signed zeros.
+ *   x [M][K] BF16 bits;  codes [M][K];  scale [M] FP32
+ */
+nq_status nq_quantize_act_fp8_row(const uint16_t* x, int64_t M, int64_t K, uint8_t* codes, float* scale,
+                                  void* stream);
+
+/*
+ * Decode GEMV on row-scaled FP8 weights, BF16 activations, FP32 accumulation.
+ * [FP8 card, introduction]: one BF16 scale per output row; [int8 card, "What
+ * changes"]: decode and verify steps use BF16 activations; [NVFP4 card, "How
+ * it was created"]: weights are dequantized on the fly against their scales.
+ *   w        [N][K] E4M3 codes;  w_scale [N] BF16 bits;  x [T][K] BF16 bits
+ *   y        [T][N] FP32 or BF16 bits: y = s[n] * sum_k x[t][k] * e4m3(w[n][k]);
+ *            a BF16 output is the RNE rounding of the FP32 result
+ *   workspace, workspace_bytes   optional device scratch (see
+ *            nq_gemv_workspace_bytes); NULL / 0 is always valid
+ * Any K >= 0 and any T >= 0 are accepted.
+ */
+nq_status nq_gemv_fp8row(const uint8_t* w, const uint16_t* w_scale, const uint16_t* x, int64_t T,
+                         int64_t N, int64_t K, int out_dt, void* y, void* workspace,
+                         int64_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of optional workspace that let the decode GEMVs split K across
+ * workgroups for a (format, T, N, K) call (0 when the call does not use one).
+ * With a workspace of at least this size the K range of each 64-row tile is
+ * divided among several workgroups; each writes an FP32 partial and the last
+ * one to finish (an atomic counter per tile) sums the partials in a fixed
+ * order, so results stay deterministic.  Without it (NULL, or smaller) one
+ * workgroup covers the whole K range of its tile; both are correct, the
+ * split is faster when N is small.  The workspace must be zero-filled once
+ * before its first use; every call leaves it zero-filled again.  Calls that
+ * share a workspace must be ordered (the same stream); the workspace holds
+ * no data between calls.  `fmt` is an nq_wfmt, or -1 for row-scaled FP8.
+ */
+int64_t nq_gemv_workspace_bytes(int fmt, int64_t T, int64_t N, int64_t K);
+
+/*
+ * Decode GEMV on grouped weights (see nq_wfmt for layouts), BF16 activations,
+ * FP32 accumulation: y[t][n] = sum_g sc[n][g] * sum_{k in g} x[t][k] * q[n][k].
+ * [NVFP4 card, "What is in the file"] (grouped Q4/Q5/Q6/Q8 with FP16 scales,
+ * BF16 projections); [RTX5080 card, "Quantization profile"] (Q4 group-64 with
+ * FP16 scales); [MXFP8 card, "How it was built"] (MXFP8).
+ *   w_codes, w_scales  per nq_wfmt (w_scales is ignored and may be NULL for BF16)
+ * Errors: K not a multiple of the group size -> NQ_ERR_SHAPE.
+ */
+nq_status nq_gemv_qgroup(int fmt, const void* w_codes, const void* w_scales, const uint16_t* x,
+                         int64_t T, int64_t N, int64_t K, int out_dt, void* y, void* workspace,
+                         int64_t workspace_bytes, void* stream);
+
+/*
+ * W8A8 prefill GEMM.  [int8 card, "What changes"]: int8 activation codes times
+ * int8 weight codes, summed exactly in int32 per 64-channel group; each group
+ * sum is scaled by weight_scale x activation_scale in FP32 and the scaled
+ * groups are summed.
+ *   a_q [M][K] int8, a_scale [M][K/64] FP32 (from nq_quantize_act_int8_g64)
+ *   w_q [N][K] int8, w_scale [N][K/64] FP16 bits (Q8 group-64 weights)
+ *   y   [M][N] FP32 or BF16 bits
+ *   group_sums  NULL, or [M][N][K/64] int32 receiving every exact group sum
+ *               (a check hook for small shapes)
+ * Errors: K % 64 != 0 -> NQ_ERR_SHAPE.
+ */
+nq_status nq_gemm_w8a8_g64(const int8_t* a_q, const float* a_scale, const int8_t* w_q,
+                           const uint16_t* w_scale, int64_t M, int64_t N, int64_t K, int out_dt,
+                           void* y, int32_t* group_sums, void* stream);
+
+/*
+ * FP8-activation prefill GEMM on row-scaled FP8 weights.  [FP8 card,
+ * "Conversion and verification", "Hardware fit"]: the row-scaled FP8 weights
+ * are multiplied on FP8 matrix units directly instead of being dequantized to
+ * BF16 first.  Activations are quantized as nq_quantize_act_fp8_row, into the
+ * caller-owned workspaces a_codes [M][K] and a_scale [M] (readable afterwards);
+ * y[m][n] = a_scale[m] * w_scale[n] * sum_k e4m3(a_codes[m][k]) * e4m3(w[n][k]).
+ * Errors: K % 16 != 0 -> NQ_ERR_SHAPE.
+ */
+nq_status nq_gemm_fp8row(const uint16_t* x, const uint8_t* w, const uint16_t* w_scale, int64_t M,
+                         int64_t N, int64_t K, uint8_t* a_codes, float* a_scale, int out_dt, void* y,
+                         void* stream);
+
+/*
+ * Route rule.  [int8 card, "What changes"]: a projection permitted to use
+ * int8 activations takes that route only in steps of 129 tokens or more;
+ * every other step keeps the BF16-activation route.  Host-only; returns an
+ * nq_route_kind.
+ */
+int nq_route(int64_t T, int allow_a8);
+
+/*
+ * The Q8 group-64 projection as an engine step runs it: routed by nq_route.
+ * BF16 route: nq_gemv_qgroup(NQ_W_Q8G64_F16S, ...).  A8 route:
+ * nq_quantize_act_int8_g64 into the caller-owned workspaces a_q_ws [T][K] and
+ * a_scale_ws [T][K/64] (needed only when the A8 route is taken), then
+ * nq_gemm_w8a8_g64.  `workspace` is the optional GEMV workspace.
+ */
+nq_status nq_linear_q8g64(const uint16_t* x, int64_t T, const int8_t* w_q, const uint16_t* w_scale,
+                          int64_t N, int64_t K, int allow_a8, int8_t* a_q_ws, float* a_scale_ws,
+                          int out_dt, void* y, void* workspace, int64_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NQ_H */

@@ -1,0 +1,40 @@
+// Host-side launchers for the HIP kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nq {
+
+// Weight formats, same values as nq_wfmt plus the row-scaled FP8 format.
+enum WFmt { W_Q4G64 = 0, W_Q8G32 = 1, W_Q8G64 = 2, W_MXFP8 = 3, W_BF16 = 4, W_FP8ROW = 5 };
+
+hipError_t launch_decode_mxfp8(const uint32_t* words, const uint8_t* e8, int64_t N, int64_t K, bool bf16_out,
+                               void* out, hipStream_t stream);
+hipError_t launch_reencode_block128(const uint8_t* codes, const float* wsi, int64_t N, int64_t K, int64_t gc,
+                                    int64_t r0, int64_t r1, uint8_t* out_codes, uint16_t* out_scale,
+                                    hipStream_t stream);
+hipError_t launch_encode_fp8row_bf16(const uint16_t* w, int64_t N, int64_t K, uint8_t* out_codes,
+                                     uint16_t* out_scale, hipStream_t stream);
+hipError_t launch_quantize_int8_g64(const uint16_t* x, int64_t T, int64_t K, int8_t* q, float* scale,
+                                    hipStream_t stream);
+hipError_t launch_quantize_fp8_row(const uint16_t* x, int64_t M, int64_t K, uint8_t* codes, float* scale,
+                                   hipStream_t stream);
+
+// Decode GEMV for every weight format.  `scales` is the per-format scale
+// array (row scales for W_FP8ROW).  `workspace` (may be NULL) enables split-K
+// across workgroups when it is large enough (gemv_workspace_bytes).
+int64_t gemv_workspace_bytes(int fmt, int64_t T, int64_t N, int64_t K);
+hipError_t launch_gemv(int fmt, const void* w, const void* scales, const uint16_t* x, int64_t T, int64_t N,
+                       int64_t K, bool bf16_out, void* y, void* workspace, int64_t workspace_bytes,
+                       hipStream_t stream);
+
+hipError_t launch_gemm_w8a8(const int8_t* a_q, const float* a_scale, const int8_t* w_q, const uint16_t* w_scale,
+                            int64_t M, int64_t N, int64_t K, bool bf16_out, void* y, int32_t* group_sums,
+                            hipStream_t stream);
+hipError_t launch_gemm_fp8(const uint8_t* a_codes, const float* a_scale, const uint8_t* w, const uint16_t* w_scale,
+                           int64_t M, int64_t N, int64_t K, bool bf16_out, void* y, hipStream_t stream);
+
+int device_cu_count();
+
+}  // namespace nq

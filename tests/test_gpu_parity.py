@@ -1,0 +1,503 @@
+"""HIP library vs the CPU oracle, through the C ABI (needs an MI355X).
+
+Integer and encoded results (decoded weights, re-encoded codes and scales,
+int8 codes and scales, int32 group sums, FP8 activation codes) must match the
+oracle bit for bit.  FP32 outputs must be within a relative Frobenius error of
+1e-5 of the float64 oracle; a BF16 output must be the round-to-nearest-even of
+the same kernel's FP32 output, bit for bit, and within 2^-8 of the oracle.
+Inputs come from the seeded generators; the oracle never sees a GPU result.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats as F
+from oracle import method as M
+from quantized_weight_linear_amd import nq
+from quantized_weight_linear_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+FP32_TOL = 1e-5
+BF16_TOL = 2.0 ** -8
+
+_NP2T = {np.uint8: torch.uint8, np.int8: torch.int8, np.uint16: torch.int16, np.int16: torch.int16,
+         np.uint32: torch.int32, np.int32: torch.int32, np.float32: torch.float32}
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    view = {np.dtype(np.uint16): np.int16, np.dtype(np.uint32): np.int32}.get(a.dtype)
+    if view is not None:
+        a = a.view(view)
+    return torch.from_numpy(a).to(DEV)
+
+
+def host(t, dtype):
+    torch.cuda.synchronize()
+    return t.cpu().numpy().view(dtype)
+
+
+def empty(shape, np_dtype):
+    return torch.empty(shape, dtype=_NP2T[np_dtype], device=DEV)
+
+
+def rel_fro(got, ref):
+    ref = np.asarray(ref, np.float64)
+    d = np.linalg.norm(np.asarray(got, np.float64) - ref)
+    n = np.linalg.norm(ref)
+    return d / n if n > 0 else d
+
+
+def bf16_of_f32_bits(f32):
+    return F.encode_bf16(np.asarray(f32, np.float32).astype(np.float64))
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    say(f"[gpu] {request.node.name}")
+    yield
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# a1: MXFP8 decode
+# ---------------------------------------------------------------------------
+
+def _all_code_words(rows):
+    c = np.arange(256, dtype=np.uint32)
+    words = (c[0::4] | (c[1::4] << 8) | (c[2::4] << 16) | (c[3::4] << 24)).reshape(1, 64)
+    return np.repeat(words, rows, axis=0)
+
+
+@pytest.mark.parametrize("bvals", [list(range(120, 131)), [0, 1, 2, 3, 127, 245, 246, 247, 250, 254, 255]])
+def test_decode_mxfp8_every_code(bvals):
+    words = _all_code_words(len(bvals))
+    e8 = np.repeat(np.array(bvals, np.uint8)[:, None], 8, axis=1)
+    n, k = words.shape[0], 256
+    for out in ("f32", "bf16"):
+        y = empty((n, k), np.float32 if out == "f32" else np.uint16)
+        nq.nq_decode_mxfp8(dev(words), dev(e8), n, k, y)
+        got = host(y, np.uint32 if out == "f32" else np.uint16)
+        ref = M.decode_mxfp8(words, e8, out=out)
+        assert np.array_equal(got, ref), out
+
+
+def test_decode_mxfp8_config1():
+    d = W.mxfp8_gemv()
+    n, k = d["words"].shape[0], d["words"].shape[1] * 4
+    for out in ("f32", "bf16"):
+        y = empty((n, k), np.float32 if out == "f32" else np.uint16)
+        nq.nq_decode_mxfp8(dev(d["words"]), dev(d["e8m0"]), n, k, y)
+        assert np.array_equal(host(y, np.uint32 if out == "f32" else np.uint16),
+                              M.decode_mxfp8(d["words"], d["e8m0"], out=out))
+
+
+# ---------------------------------------------------------------------------
+# a2: block-128 -> per-row re-encode, and BF16 -> per-row encode
+# ---------------------------------------------------------------------------
+
+def _block_inputs(n, k, seed, bf16_scales=True):
+    g = W.rng(90, seed)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    codes = finite[g.integers(0, finite.size, (n, k))]
+    shape = (-(-n // 128), -(-k // 128))
+    if bf16_scales:
+        wsi = W.bf16_log_uniform_as_f32(g, shape, -10, -4)
+    else:
+        wsi = np.exp2(g.uniform(-10, -4, shape)).astype(np.float32)    # full 24-bit significands
+    return codes, wsi
+
+
+def _gpu_reencode(codes, wsi, r0, r1):
+    n, k = codes.shape
+    oc = empty((r1 - r0, k), np.uint8)
+    osc = empty((r1 - r0,), np.uint16)
+    nq.nq_reencode_block128_to_row(dev(codes), dev(wsi), n, k, r0, r1, oc, osc)
+    return host(oc, np.uint8), host(osc, np.uint16)
+
+
+@pytest.mark.parametrize("n,k,bf16_scales", [(300, 520, True), (130, 200, False), (4, 8, True),
+                                             (256, 384, False), (129, 1000, True)])
+def test_reencode_small(n, k, bf16_scales):
+    codes, wsi = _block_inputs(n, k, n * 7 + k, bf16_scales)
+    codes[1] = 0x00                        # zero row: scale +0, codes unchanged
+    codes[2, ::3] = 0x80
+    codes[2, 1::3] = 0x00
+    codes[2, 2::3] = 0x80
+    if n > 5:
+        codes[5, 3] = 0x7F                 # NaN row
+    for r0, r1 in [(0, n), (1, min(n, 3)), (n // 2, n)]:
+        q, s = _gpu_reencode(codes, wsi, r0, r1)
+        qo, so = M.reencode_block128_to_row(codes, wsi, r0, r1)
+        assert np.array_equal(s, so), (r0, r1)
+        assert np.array_equal(q, qo), (r0, r1)
+
+
+def test_reencode_config3_full_sampled_rows():
+    d = W.block128_codes()
+    n, k = d["codes"].shape
+    q, s = _gpu_reencode(d["codes"], d["wsi"], 0, n)
+    rows = np.unique(np.concatenate([[0, 127, 128, n - 1], W.rng(91, 0).integers(0, n, 60)]))
+    for r in rows:
+        qo, so = M.reencode_block128_to_row(d["codes"][r:r + 1], np.ones((1, d["wsi"].shape[1]), np.float32)
+                                            * d["wsi"][r // 128][None, :])
+        assert so[0] == s[r] and np.array_equal(qo[0], q[r]), r
+    # a row range reads only its block rows and gives the same slice
+    q2, s2 = _gpu_reencode(d["codes"], d["wsi"], 1000, 1300)
+    assert np.array_equal(q2, q[1000:1300]) and np.array_equal(s2, s[1000:1300])
+
+
+@pytest.mark.parametrize("n,k", [(64, 5120), (33, 200), (4, 8), (17, 16)])
+def test_encode_fp8row_bf16_small(n, k):
+    w = W.bf16_normal(W.rng(92, n + k), (n, k), std=0.02)
+    w[0, :] = 0
+    oc, osc = empty((n, k), np.uint8), empty((n,), np.uint16)
+    nq.nq_encode_fp8row_bf16(dev(w), n, k, oc, osc)
+    qo, so = M.encode_fp8row_bf16(w)
+    assert np.array_equal(host(osc, np.uint16), so) and np.array_equal(host(oc, np.uint8), qo)
+
+
+# ---------------------------------------------------------------------------
+# a5: int8 activation quantization; a7 input: E4M3 per-token quantization
+# ---------------------------------------------------------------------------
+
+def _special_activations(t, k):
+    x = W.bf16_normal(W.rng(93, t * k), (t, k), outlier_p=0.01)
+    xf = (x.astype(np.uint32) << 16).view(np.float32).copy()
+    xf[0, :64] = 0.0                                       # zero group
+    xf[1, :64] = np.array([127.0, 2.5, 3.5, -2.5, 126.5, -126.5, 0.5, 1.5] * 8, np.float32)  # ties
+    xf[2, 64:128] = -3.0                                    # constant group
+    xf[3, 5] = np.nan                                       # NaN group
+    xf[3, 70] = np.inf                                      # inf group
+    xf[4, :] = -0.0
+    return W.to_bf16_bits(xf)
+
+
+@pytest.mark.parametrize("t,k", [(7, 256), (33, 5120), (1, 64)])
+def test_quantize_int8_small(t, k):
+    x = _special_activations(max(t, 5), k)[:t] if t >= 5 else W.bf16_normal(W.rng(94, k), (t, k))
+    q, s = empty((t, k), np.int8), empty((t, k // 64), np.float32)
+    nq.nq_quantize_act_int8_g64(dev(x), t, k, q, s)
+    qo, so = M.quantize_act_int8_g64(x)
+    assert np.array_equal(host(s, np.uint32), so)
+    assert np.array_equal(host(q, np.int8), qo)
+
+
+def test_quantize_int8_config5_full():
+    d = W.w8a8_prefill()
+    m, k = d["x"].shape
+    q, s = empty((m, k), np.int8), empty((m, k // 64), np.float32)
+    nq.nq_quantize_act_int8_g64(dev(d["x"]), m, k, q, s)
+    qo, so = M.quantize_act_int8_g64(d["x"])
+    assert np.array_equal(host(s, np.uint32), so)
+    assert np.array_equal(host(q, np.int8), qo)
+
+
+@pytest.mark.parametrize("m,k", [(7, 256), (70, 400), (3, 8)])
+def test_quantize_fp8_row(m, k):
+    x = _special_activations(max(m, 5), k)[:m] if m >= 5 else W.bf16_normal(W.rng(95, k), (m, k))
+    c, s = empty((m, k), np.uint8), empty((m,), np.float32)
+    nq.nq_quantize_act_fp8_row(dev(x), m, k, c, s)
+    co, so = M.quantize_act_fp8_row(x)
+    assert np.array_equal(host(s, np.uint32), so)
+    assert np.array_equal(host(c, np.uint8), co)
+
+
+# ---------------------------------------------------------------------------
+# a3 / a4: decode GEMVs
+# ---------------------------------------------------------------------------
+
+def _run_gemv_fp8row(wq, ws, x, workspace_mode, out):
+    t, k = x.shape
+    n = wq.shape[0]
+    y = empty((t, n), np.float32 if out == "f32" else np.uint16)
+    wsp = nq.alloc_gemv_workspace(-1, t, n, k, DEV) if workspace_mode else None
+    nq.nq_gemv_fp8row(dev(wq), dev(ws), dev(x), t, n, k, y, wsp)
+    return host(y, np.float32 if out == "f32" else np.uint16), wsp
+
+
+def _check_float_out(got_f32, got_bf16, ref):
+    assert rel_fro(got_f32, ref) <= FP32_TOL, rel_fro(got_f32, ref)
+    assert np.array_equal(got_bf16, bf16_of_f32_bits(got_f32))
+    assert rel_fro(F.bf16_decode(got_bf16), ref) <= BF16_TOL
+
+
+GEMV_SHAPES = [(1000, 1536), (200, 1408), (64, 256), (37, 200), (8, 8), (130, 100), (16, 0)]
+
+
+@pytest.mark.parametrize("n,k", GEMV_SHAPES)
+@pytest.mark.parametrize("t", [1, 4, 16, 17, 33, 64, 65])
+def test_gemv_fp8row(n, k, t):
+    w = W.bf16_normal(W.rng(96, n * 3 + k), (n, k), std=0.02)
+    wq, ws = M.encode_fp8row_bf16(w)
+    x = W.bf16_normal(W.rng(97, t + k), (t, k))
+    ref = M.gemv_fp8row(wq, ws, x)
+    for wmode in (False, True):
+        y32, wsp = _run_gemv_fp8row(wq, ws, x, wmode, "f32")
+        y16, _ = _run_gemv_fp8row(wq, ws, x, wmode, "bf16")
+        if k == 0:
+            assert np.all(y32 == 0)
+            continue
+        _check_float_out(y32, y16, ref)
+        if wsp is not None:
+            assert int(wsp.view(torch.int32)[:64].abs().sum().item()) == 0     # counters reset
+
+
+def test_gemv_fp8row_one_hot_is_exact():
+    n, k = 300, 512
+    w = W.bf16_normal(W.rng(98, 0), (n, k), std=0.02)
+    wq, ws = M.encode_fp8row_bf16(w)
+    cols = [0, 1, 100, 511]
+    x = np.zeros((len(cols), k), np.float32)
+    for i, c in enumerate(cols):
+        x[i, c] = 1.0
+    xb = W.to_bf16_bits(x)
+    y, _ = _run_gemv_fp8row(wq, ws, xb, True, "f32")
+    ref = M.gemv_fp8row(wq, ws, xb)
+    assert np.array_equal(y.astype(np.float64), F.round_f32(ref))
+
+
+GROUP_FMTS = [("q4g64", nq.NQ_W_Q4G64_F16S), ("q8g32", nq.NQ_W_Q8G32_F16S), ("q8g64", nq.NQ_W_Q8G64_F16S),
+              ("mxfp8", nq.NQ_W_MXFP8_G32), ("bf16", nq.NQ_W_BF16)]
+
+
+def _grouped_inputs(name, n, k, seed):
+    if name in ("q4g64", "q8g32", "q8g64"):
+        d = W.grouped(name, n, k, seed)
+        return d["codes"], d["scales"]
+    if name == "mxfp8":
+        g = W.rng(99, seed)
+        words = W.pack_bytes_to_words(W.e4m3_codes(g, (n, k)))
+        return words, g.integers(120, 131, (n, k // 32)).astype(np.uint8)
+    return W.bf16_normal(W.rng(99, seed), (n, k), std=0.02), None
+
+
+def _run_gemv_q(fmt, codes, scales, x, n, workspace_mode, out):
+    t, k = x.shape
+    y = empty((t, n), np.float32 if out == "f32" else np.uint16)
+    wsp = nq.alloc_gemv_workspace(fmt, t, n, k, DEV) if workspace_mode else None
+    nq.nq_gemv_qgroup(fmt, dev(codes), dev(scales) if scales is not None else None, dev(x), t, n, k, y, wsp)
+    return host(y, np.float32 if out == "f32" else np.uint16)
+
+
+@pytest.mark.parametrize("name,fmt", GROUP_FMTS)
+@pytest.mark.parametrize("n,k", [(1000, 1536), (200, 1408), (70, 192), (9, 64)])
+@pytest.mark.parametrize("t", [1, 8, 33, 64])
+def test_gemv_qgroup(name, fmt, n, k, t):
+    codes, scales = _grouped_inputs(name, n, k, n + k + t)
+    x = W.bf16_normal(W.rng(100, t + k), (t, k))
+    ref = M.gemv_qgroup(name, codes, scales, x)
+    for wmode in (False, True):
+        y32 = _run_gemv_q(fmt, codes, scales, x, n, wmode, "f32")
+        y16 = _run_gemv_q(fmt, codes, scales, x, n, wmode, "bf16")
+        _check_float_out(y32, y16, ref)
+
+
+def test_gemv_mxfp8_config1():
+    d = W.mxfp8_gemv()
+    n, k = d["words"].shape[0], d["words"].shape[1] * 4
+    y32 = _run_gemv_q(nq.NQ_W_MXFP8_G32, d["words"], d["e8m0"], d["x"], n, True, "f32")
+    y16 = _run_gemv_q(nq.NQ_W_MXFP8_G32, d["words"], d["e8m0"], d["x"], n, True, "bf16")
+    _check_float_out(y32, y16, M.gemv_qgroup("mxfp8", d["words"], d["e8m0"], d["x"]))
+
+
+def _sampled_rows(n, seed, count=96):
+    return np.unique(np.concatenate([[0, 63, 64, n - 1], W.rng(101, seed).integers(0, n, count)]))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("n,k,ts", [(W.FFN, W.HIDDEN, [1, 4, 16, 33]), (W.HIDDEN, W.FFN, [1, 33])])
+def test_gemv_fp8row_full_size(n, k, ts):
+    w = W.fp8row_weights_bf16(n, k)
+    wd = dev(w)
+    wq_d, ws_d = empty((n, k), np.uint8), empty((n,), np.uint16)
+    nq.nq_encode_fp8row_bf16(wd, n, k, wq_d, ws_d)
+    del wd
+    rows = _sampled_rows(n, n)
+    wq_o, ws_o = M.encode_fp8row_bf16(w[rows])
+    assert np.array_equal(host(wq_d, np.uint8)[rows], wq_o) and np.array_equal(host(ws_d, np.uint16)[rows], ws_o)
+    for t in ts:
+        x = W.activations(t, k)
+        y = empty((t, n), np.float32)
+        wsp = nq.alloc_gemv_workspace(-1, t, n, k, DEV)
+        nq.nq_gemv_fp8row(wq_d, ws_d, dev(x), t, n, k, y, wsp)
+        got = host(y, np.float32)[:, rows]
+        assert rel_fro(got, M.gemv_fp8row(wq_o, ws_o, x)) <= FP32_TOL, t
+
+
+@pytest.mark.slow
+def test_gemv_config3_reencode_then_gemv_and_gate():
+    d = W.block128_codes()
+    n, k = d["codes"].shape
+    q_d, s_d = empty((n, k), np.uint8), empty((n,), np.uint16)
+    nq.nq_reencode_block128_to_row(dev(d["codes"]), dev(d["wsi"]), n, k, 0, n, q_d, s_d)
+    rows = _sampled_rows(n, 3)
+    for t in (1, 33):
+        x = W.activations(t, k, workload=3, tensor=3)
+        y = empty((t, n), np.float32)
+        nq.nq_gemv_fp8row(q_d, s_d, dev(x), t, n, k, y, nq.alloc_gemv_workspace(-1, t, n, k, DEV))
+        got = host(y, np.float32)[:, rows]
+        ref = []
+        for r in rows:
+            qo, so = M.reencode_block128_to_row(d["codes"][r:r + 1],
+                                                d["wsi"][r // 128][None, :].copy())
+            ref.append(M.gemv_fp8row(qo, so, x)[:, 0])
+        assert rel_fro(got, np.stack(ref, axis=1)) <= FP32_TOL, t
+    gate = W.gate_bf16()
+    for t in (1, 33):
+        x = W.activations(t, W.HIDDEN, workload=3, tensor=4)
+        y32 = _run_gemv_q(nq.NQ_W_BF16, gate, None, x, gate.shape[0], True, "f32")
+        y16 = _run_gemv_q(nq.NQ_W_BF16, gate, None, x, gate.shape[0], True, "bf16")
+        _check_float_out(y32, y16, M.gemv_qgroup("bf16", gate, None, x))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,fmt", GROUP_FMTS[:2])
+@pytest.mark.parametrize("n,k", [(W.FFN, W.HIDDEN), (W.HIDDEN, W.FFN)])
+def test_gemv_qgroup_config4_full_size(name, fmt, n, k):
+    d = W.grouped(name, n, k)
+    cd, sd = dev(d["codes"]), dev(d["scales"])
+    rows = _sampled_rows(n, n + 1)
+    gs = 64 if name == "q4g64" else 32
+    for t in (1, 8, 33):
+        x = W.activations(t, k, workload=4, tensor=50)
+        y = empty((t, n), np.float32)
+        nq.nq_gemv_qgroup(fmt, cd, sd, dev(x), t, n, k, y, nq.alloc_gemv_workspace(fmt, t, n, k, DEV))
+        got = host(y, np.float32)[:, rows]
+        ref = M.gemv_qgroup(name, d["codes"][rows], d["scales"][rows], x)
+        assert rel_fro(got, ref) <= FP32_TOL, (name, t)
+        assert gs
+
+
+@pytest.mark.slow
+def test_gemv_head_full_size_sweep():
+    n, k = W.HEAD_ROWS, W.HIDDEN
+    w = W.head_weights_bf16()
+    wd = dev(w)
+    q_d, s_d = empty((n, k), np.uint8), empty((n,), np.uint16)
+    nq.nq_encode_fp8row_bf16(wd, n, k, q_d, s_d)
+    del wd
+    rows = _sampled_rows(n, 5)
+    qo, so = M.encode_fp8row_bf16(w[rows])
+    assert np.array_equal(host(q_d, np.uint8)[rows], qo) and np.array_equal(host(s_d, np.uint16)[rows], so)
+    for t in (1, 2, 7, 16, 33, 34, 48, 64):
+        x = W.activations(t, k, workload=5, tensor=4)
+        y = empty((t, n), np.float32)
+        nq.nq_gemv_fp8row(q_d, s_d, dev(x), t, n, k, y, nq.alloc_gemv_workspace(-1, t, n, k, DEV))
+        assert rel_fro(host(y, np.float32)[:, rows], M.gemv_fp8row(qo, so, x)) <= FP32_TOL, t
+
+
+# ---------------------------------------------------------------------------
+# a6: W8A8 GEMM; a7: FP8 GEMM; a8: route
+# ---------------------------------------------------------------------------
+
+def _w8a8_inputs(m, n, k, seed):
+    g = W.rng(102, seed)
+    x = W.bf16_normal(g, (m, k), outlier_p=0.01)
+    qa, sa = M.quantize_act_int8_g64(x)
+    w = W.int8_uniform(g, (n, k))
+    ws = W.f16_log_uniform(g, (n, k // 64), -9, -5)
+    return qa, sa, w, ws
+
+
+@pytest.mark.parametrize("m,n,k", [(64, 128, 5120), (70, 100, 640), (130, 257, 128), (1, 1, 64)])
+def test_w8a8_group_sums_and_output(m, n, k):
+    qa, sa, w, ws = _w8a8_inputs(m, n, k, m + n + k)
+    y32, y16 = empty((m, n), np.float32), empty((m, n), np.uint16)
+    gsum = empty((m, n, k // 64), np.int32)
+    nq.nq_gemm_w8a8_g64(dev(qa), dev(sa), dev(w), dev(ws), m, n, k, y32, gsum)
+    nq.nq_gemm_w8a8_g64(dev(qa), dev(sa), dev(w), dev(ws), m, n, k, y16)
+    ref, sums = M.gemm_w8a8_g64(qa, sa, w, ws, return_sums=True)
+    assert np.array_equal(host(gsum, np.int32).astype(np.int64), sums)
+    _check_float_out(host(y32, np.float32), host(y16, np.uint16), ref)
+
+
+def test_w8a8_power_of_two_scales_exact():
+    m, n, k = 40, 72, 64
+    g = W.rng(103, 0)
+    qa = W.int8_uniform(g, (m, k))
+    w = W.int8_uniform(g, (n, k))
+    sa = np.exp2(g.integers(-8, -2, (m, 1))).astype(np.float32)
+    ws = np.exp2(g.integers(-9, -5, (n, 1))).astype(np.float16).view(np.uint16)
+    y = empty((m, n), np.float32)
+    nq.nq_gemm_w8a8_g64(dev(qa), dev(sa.view(np.uint32)), dev(w), dev(ws), m, n, k, y)
+    ref = M.gemm_w8a8_g64(qa, sa.view(np.uint32), w, ws)
+    assert np.array_equal(host(y, np.float32).astype(np.float64), ref)
+
+
+@pytest.mark.slow
+def test_w8a8_config5_full_sampled():
+    d = W.w8a8_prefill()
+    m, k = d["x"].shape
+    n = d["w"].shape[0]
+    qa, sa = empty((m, k), np.int8), empty((m, k // 64), np.float32)
+    nq.nq_quantize_act_int8_g64(dev(d["x"]), m, k, qa, sa)
+    y = empty((m, n), np.float32)
+    nq.nq_gemm_w8a8_g64(qa, sa, dev(d["w"]), dev(d["w_scale"]), m, n, k, y)
+    qo, so = M.quantize_act_int8_g64(d["x"])
+    rows = W.rng(104, 0).choice(m, 48, replace=False)
+    cols = _sampled_rows(n, 6, 160)
+    got = host(y, np.float32)[np.ix_(rows, cols)]
+    ref = M.gemm_w8a8_g64(qo[rows], so[rows], d["w"][cols], d["w_scale"][cols])
+    assert rel_fro(got, ref) <= FP32_TOL
+
+
+@pytest.mark.parametrize("m,n,k", [(70, 100, 400), (128, 256, 5120), (1, 3, 16), (129, 130, 256)])
+def test_fp8_gemm(m, n, k):
+    x = W.bf16_normal(W.rng(105, m + n + k), (m, k), outlier_p=0.01)
+    w = W.bf16_normal(W.rng(106, m + n + k), (n, k), std=0.02)
+    wq, ws = M.encode_fp8row_bf16(w)
+    ac, asc = empty((m, k), np.uint8), empty((m,), np.float32)
+    y32, y16 = empty((m, n), np.float32), empty((m, n), np.uint16)
+    nq.nq_gemm_fp8row(dev(x), dev(wq), dev(ws), m, n, k, ac, asc, y32)
+    ref, qa, sa = M.gemm_fp8row(x, wq, ws)
+    assert np.array_equal(host(ac, np.uint8), qa) and np.array_equal(host(asc, np.uint32), sa)
+    nq.nq_gemm_fp8row(dev(x), dev(wq), dev(ws), m, n, k, ac, asc, y16)
+    _check_float_out(host(y32, np.float32), host(y16, np.uint16), ref)
+
+
+@pytest.mark.slow
+def test_fp8_gemm_full_sampled():
+    m, n, k = W.PREFILL_CHUNK, W.FFN, W.HIDDEN
+    w = W.fp8row_weights_bf16(n, k)
+    wq_d, ws_d = empty((n, k), np.uint8), empty((n,), np.uint16)
+    nq.nq_encode_fp8row_bf16(dev(w), n, k, wq_d, ws_d)
+    x = W.activations(m, k, workload=5, tensor=6)
+    ac, asc, y = empty((m, k), np.uint8), empty((m,), np.float32), empty((m, n), np.float32)
+    nq.nq_gemm_fp8row(dev(x), wq_d, ws_d, m, n, k, ac, asc, y)
+    rows = W.rng(107, 0).choice(m, 48, replace=False)
+    cols = _sampled_rows(n, 7, 160)
+    wq_o, ws_o = M.encode_fp8row_bf16(w[cols])
+    ref, qa, sa = M.gemm_fp8row(x[rows], wq_o, ws_o)
+    assert np.array_equal(host(ac, np.uint8)[rows], qa)
+    assert rel_fro(host(y, np.float32)[np.ix_(rows, cols)], ref) <= FP32_TOL
+
+
+@pytest.mark.parametrize("t", [1, 33, 128, 129, 300])
+def test_linear_route(t):
+    n, k = 200, 640
+    g = W.rng(108, t)
+    x = W.bf16_normal(g, (t, k))
+    w = W.int8_uniform(g, (n, k))
+    ws = W.f16_log_uniform(g, (n, k // 64), -9, -5)
+    xd, wd, wsd = dev(x), dev(w), dev(ws)
+    y = empty((t, n), np.float32)
+    aq, asc = empty((t, k), np.int8), empty((t, k // 64), np.float32)
+    wsp = nq.alloc_gemv_workspace(nq.NQ_W_Q8G64_F16S, t, n, k, DEV)
+    nq.nq_linear_q8g64(xd, t, wd, wsd, n, k, True, aq, asc, y, wsp)
+    got = host(y, np.float32)
+    ref = M.linear_w8g64(x, w, ws, True)
+    assert rel_fro(got, ref) <= FP32_TOL
+    direct = empty((t, n), np.float32)
+    if t >= 129:
+        nq.nq_gemm_w8a8_g64(aq, asc, wd, wsd, t, n, k, direct)
+    else:
+        nq.nq_gemv_qgroup(nq.NQ_W_Q8G64_F16S, wd, wsd, xd, t, n, k, direct, wsp)
+    assert np.array_equal(host(direct, np.uint32), got.view(np.uint32))
