@@ -173,6 +173,39 @@ nq_status nq_gemv_fp8row(const uint8_t* w, const uint16_t* w_scale, const uint16
 int64_t nq_gemv_workspace_bytes(int fmt, int64_t T, int64_t N, int64_t K);
 
 /*
+ * Packed weight layout for the decode GEMVs.  A one-time permutation of a
+ * row-major weight matrix (codes only; scales stay as they are) into the
+ * order in which the GEMV kernels stream it: rows in blocks of 16 (the last
+ * block zero-padded); chunk-major: for every chunk of KC columns (KC = 256
+ * when K % 256 == 0, else 128), for every row block, for every 8- or 16-byte
+ * piece of the chunk, the pieces of all 64 lanes of a wavefront stored
+ * contiguously (lane 16 g + i holds row i of the block, lane group g).  Every
+ * load instruction of the GEMV reads a contiguous 512 B or 1 KiB, and the
+ * grid, walking chunk by chunk, sweeps one contiguous window at a time.  The pages store weights in engine-specific tiled
+ * layouts too ([NVFP4 card, "How it was created"]: the NVFP4 storage layout
+ * works in 128-row tiles).
+ *   fmt       an nq_wfmt, or -1 for row-scaled FP8 codes
+ *   w         row-major codes as nq_gemv_fp8row / nq_gemv_qgroup take them
+ *   w_packed  nq_packed_weight_bytes(fmt, N, K) bytes, caller-owned
+ * Errors: K % 128 != 0 (or K == 0 with N > 0) -> NQ_ERR_SHAPE; unknown fmt ->
+ * NQ_ERR_FORMAT.
+ */
+int64_t nq_packed_weight_bytes(int fmt, int64_t N, int64_t K);
+nq_status nq_pack_weights(int fmt, const void* w, int64_t N, int64_t K, void* w_packed, void* stream);
+
+/*
+ * nq_gemv_fp8row / nq_gemv_qgroup on packed codes (from nq_pack_weights with
+ * the same fmt, N and K); every other argument as in the row-major calls, and
+ * the results are bit-identical to them.
+ */
+nq_status nq_gemv_fp8row_packed(const uint8_t* w_packed, const uint16_t* w_scale, const uint16_t* x,
+                                int64_t T, int64_t N, int64_t K, int out_dt, void* y, void* workspace,
+                                int64_t workspace_bytes, void* stream);
+nq_status nq_gemv_qgroup_packed(int fmt, const void* w_packed, const void* w_scales, const uint16_t* x,
+                                int64_t T, int64_t N, int64_t K, int out_dt, void* y, void* workspace,
+                                int64_t workspace_bytes, void* stream);
+
+/*
  * Decode GEMV on grouped weights (see nq_wfmt for layouts), BF16 activations,
  * FP32 accumulation: y[t][n] = sum_g sc[n][g] * sum_{k in g} x[t][k] * q[n][k].
  * [NVFP4 card, "What is in the file"] (grouped Q4/Q5/Q6/Q8 with FP16 scales,

@@ -159,9 +159,20 @@ int64_t nq_gemv_workspace_bytes(int fmt, int64_t T, int64_t N, int64_t K) {
     return nq::gemv_workspace_bytes(fmt, T, N, K);
 }
 
-nq_status nq_gemv_fp8row(const uint8_t* w, const uint16_t* w_scale, const uint16_t* x, int64_t T, int64_t N,
-                         int64_t K, int out_dt, void* y, void* workspace, int64_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The packed layout needs whole 128-column chunks and 32-bit buffer offsets.
+bool packed_shape_ok(int64_t N, int64_t K) {
+    return K % 128 == 0 && K > 0 && 64 * K * 2 < ((int64_t)1 << 31) && N * (K / 32) * 2 < ((int64_t)1 << 31);
+}
+
+nq_status gemv_fp8row_impl(const uint8_t* w, const uint16_t* w_scale, const uint16_t* x, int64_t T, int64_t N,
+                           int64_t K, int out_dt, void* y, void* workspace, int64_t workspace_bytes, void* stream,
+                           bool packed) {
     if (T < 0 || N < 0 || K < 0 || workspace_bytes < 0) return NQ_ERR_SHAPE;
+    if (packed && !packed_shape_ok(N, K)) return NQ_ERR_SHAPE;
     if (!out_ok(out_dt)) return NQ_ERR_FORMAT;
     NQ_TRY(need(w, N * K));
     NQ_TRY(need(w_scale, N));
@@ -174,16 +185,17 @@ nq_status nq_gemv_fp8row(const uint8_t* w, const uint16_t* w_scale, const uint16
     NQ_TRY(align_ok(workspace));
     if (T == 0 || N == 0) return NQ_OK;
     return from_hip(nq::launch_gemv(nq::W_FP8ROW, w, w_scale, x, T, N, K, out_dt == NQ_OUT_BF16, y, workspace,
-                                    workspace ? workspace_bytes : 0, as_stream(stream)));
+                                    workspace ? workspace_bytes : 0, as_stream(stream), packed));
 }
 
-nq_status nq_gemv_qgroup(int fmt, const void* w_codes, const void* w_scales, const uint16_t* x, int64_t T,
-                         int64_t N, int64_t K, int out_dt, void* y, void* workspace, int64_t workspace_bytes,
-                         void* stream) {
+nq_status gemv_qgroup_impl(int fmt, const void* w_codes, const void* w_scales, const uint16_t* x, int64_t T,
+                           int64_t N, int64_t K, int out_dt, void* y, void* workspace, int64_t workspace_bytes,
+                           void* stream, bool packed) {
     const int gs = group_of(fmt);
     if (gs == 0) return NQ_ERR_FORMAT;
     if (!out_ok(out_dt)) return NQ_ERR_FORMAT;
     if (T < 0 || N < 0 || K < 0 || workspace_bytes < 0 || K % gs != 0) return NQ_ERR_SHAPE;
+    if (packed && !packed_shape_ok(N, K)) return NQ_ERR_SHAPE;
     NQ_TRY(need(w_codes, N * K));
     if (fmt != NQ_W_BF16) NQ_TRY(need(w_scales, N * K));
     NQ_TRY(need(x, T * K));
@@ -196,7 +208,56 @@ nq_status nq_gemv_qgroup(int fmt, const void* w_codes, const void* w_scales, con
     if (T == 0 || N == 0) return NQ_OK;
     return from_hip(nq::launch_gemv(fmt, w_codes, fmt == NQ_W_BF16 ? nullptr : w_scales, x, T, N, K,
                                     out_dt == NQ_OUT_BF16, y, workspace, workspace ? workspace_bytes : 0,
-                                    as_stream(stream)));
+                                    as_stream(stream), packed));
+}
+
+// nq_wfmt, or -1 for row-scaled FP8, to the internal format code
+int internal_fmt(int fmt) { return fmt == -1 ? nq::W_FP8ROW : fmt; }
+
+}  // namespace
+
+extern "C" {
+
+nq_status nq_gemv_fp8row(const uint8_t* w, const uint16_t* w_scale, const uint16_t* x, int64_t T, int64_t N,
+                         int64_t K, int out_dt, void* y, void* workspace, int64_t workspace_bytes, void* stream) {
+    return gemv_fp8row_impl(w, w_scale, x, T, N, K, out_dt, y, workspace, workspace_bytes, stream, false);
+}
+
+nq_status nq_gemv_fp8row_packed(const uint8_t* w_packed, const uint16_t* w_scale, const uint16_t* x, int64_t T,
+                                int64_t N, int64_t K, int out_dt, void* y, void* workspace, int64_t workspace_bytes,
+                                void* stream) {
+    return gemv_fp8row_impl(w_packed, w_scale, x, T, N, K, out_dt, y, workspace, workspace_bytes, stream, true);
+}
+
+nq_status nq_gemv_qgroup(int fmt, const void* w_codes, const void* w_scales, const uint16_t* x, int64_t T,
+                         int64_t N, int64_t K, int out_dt, void* y, void* workspace, int64_t workspace_bytes,
+                         void* stream) {
+    return gemv_qgroup_impl(fmt, w_codes, w_scales, x, T, N, K, out_dt, y, workspace, workspace_bytes, stream,
+                            false);
+}
+
+nq_status nq_gemv_qgroup_packed(int fmt, const void* w_packed, const void* w_scales, const uint16_t* x, int64_t T,
+                                int64_t N, int64_t K, int out_dt, void* y, void* workspace, int64_t workspace_bytes,
+                                void* stream) {
+    return gemv_qgroup_impl(fmt, w_packed, w_scales, x, T, N, K, out_dt, y, workspace, workspace_bytes, stream,
+                            true);
+}
+
+int64_t nq_packed_weight_bytes(int fmt, int64_t N, int64_t K) {
+    if (N < 0 || K < 0 || (fmt != -1 && group_of(fmt) == 0)) return 0;
+    return nq::packed_weight_bytes(internal_fmt(fmt), N, K);
+}
+
+nq_status nq_pack_weights(int fmt, const void* w, int64_t N, int64_t K, void* w_packed, void* stream) {
+    if (fmt != -1 && group_of(fmt) == 0) return NQ_ERR_FORMAT;
+    if (N < 0 || K < 0) return NQ_ERR_SHAPE;
+    if (N > 0 && !packed_shape_ok(N, K)) return NQ_ERR_SHAPE;
+    NQ_TRY(need(w, N * K));
+    NQ_TRY(need(w_packed, N * K));
+    NQ_TRY(align_ok(w));
+    NQ_TRY(align_ok(w_packed));
+    if (N == 0) return NQ_OK;
+    return from_hip(nq::launch_pack_weights(internal_fmt(fmt), w, N, K, w_packed, as_stream(stream)));
 }
 
 nq_status nq_gemm_w8a8_g64(const int8_t* a_q, const float* a_scale, const int8_t* w_q, const uint16_t* w_scale,
@@ -270,7 +331,7 @@ nq_status nq_linear_q8g64(const uint16_t* x, int64_t T, const int8_t* w_q, const
     hipStream_t s = as_stream(stream);
     if (!a8)
         return from_hip(nq::launch_gemv(nq::W_Q8G64, w_q, w_scale, x, T, N, K, out_dt == NQ_OUT_BF16, y, workspace,
-                                        workspace ? workspace_bytes : 0, s));
+                                        workspace ? workspace_bytes : 0, s, false));
     hipError_t e = nq::launch_quantize_int8_g64(x, T, K, a_q_ws, a_scale_ws, s);
     if (e != hipSuccess) return NQ_ERR_HIP;
     return from_hip(nq::launch_gemm_w8a8(a_q_ws, a_scale_ws, w_q, w_scale, T, N, K, out_dt == NQ_OUT_BF16, y,

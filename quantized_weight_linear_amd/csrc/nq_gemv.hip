@@ -2,31 +2,49 @@
 // tokens (T <= 64 per pass), weights decoded on the fly in registers.
 //
 // Main path (K % 128 == 0): BF16 MFMA 16x16x32 on exactly decoded weights.
-//   - A workgroup (4 waves) owns 64 weight rows and a K range; waves are
-//     2 row-pairs (32 rows each) x 2 K-halves of every 256-wide K chunk.
-//   - Weights stream from HBM with 16-byte loads straight into registers (one
-//     chunk ahead) and are decoded there: E4M3 -> BF16 with the hardware
-//     scaled convert (exact), int8/int4 -> FP32 -> BF16 (exact for |q| <= 128).
-//   - The activation chunk [T_pad][256] is staged in LDS (zero-padded to a
-//     multiple of 16 tokens) and read as the MFMA B operand; each B fragment
-//     feeds two 16-row weight blocks.
-//   - Grouped formats run one MFMA chain per scale group and fold the group
-//     scale in FP32 (acc += sc * D); row-scaled FP8 applies its row scale once
-//     at the end; MXFP8 folds its power-of-two group scale into the exact
-//     convert.
-//   - The two K-halves are summed through LDS in a fixed order.  With a
-//     workspace, the K range is also split across workgroups; each split
+//   - A workgroup of 4 waves owns 64 weight rows and a K range; each wave owns
+//     16 rows over the whole range and streams them chunk by chunk (KC = 256
+//     or 128 columns, whichever divides K) sharing only the activation chunk.
+//   - Weights go from HBM straight into registers, depth<FMT>() chunks ahead
+//     of use, in a static register ring (the loop is unrolled by the depth).
+//     Each lane reads 16-byte pieces so that one load instruction covers 64
+//     contiguous bytes of 16 rows.
+//   - The hot loop has no branches: every chunk is full, prefetch indices are
+//     clamped to the last chunk (the repeated loads at the end hit in cache),
+//     and activations / scales come through buffer loads whose out-of-range
+//     offsets read as zero.  Branches inside the loop would make the compiler
+//     drain every outstanding load at each join.
+//   - The activation chunk [T_pad][KC] is double-buffered in LDS (rows past T
+//     read as zero); the next chunk's activations are requested before the
+//     next weights so that waiting for them never waits for weights.  One
+//     barrier per chunk.
+//   - Decode in registers: E4M3 -> BF16 by the hardware scaled convert
+//     (exact; MXFP8 passes its power-of-two group scale to the convert),
+//     int8 / int4 -> FP32 -> BF16 (exact for |q| <= 128), BF16 as stored.
+//   - Grouped formats run one MFMA chain per scale group and fold the FP16
+//     group scale in FP32 (acc += sc * D); row-scaled FP8 applies its BF16
+//     row scale once at the end.
+//   - With a workspace the K range is split across workgroups; each split
 //     writes an FP32 partial and the last workgroup of a row tile (atomic
-//     counter) sums the partials in split order, so results are deterministic.
+//     counter) sums the partials in split order: deterministic results.
 // Fallback (any K): one wave per (row, 8 tokens), scalar decode, FP32 sums.
 #include "nq_device.h"
 #include "nq_launch.h"
 
 namespace nq {
 
-constexpr int GV_ROWS = 64;
-constexpr int GV_KC = 256;
-constexpr int GV_XPITCH = GV_KC + 8;   // bf16 elements per LDS row (528 bytes: rows shift by 4 banks)
+constexpr int GV_ROWS = 64;   // rows per workgroup (4 waves x 16)
+constexpr unsigned BUF_FLAGS = 0x00020000u;
+
+template <int FMT>
+constexpr int group_size() {
+    return FMT == W_Q8G32 ? 32 : ((FMT == W_Q4G64 || FMT == W_Q8G64) ? 64 : 0);
+}
+
+template <int FMT>
+constexpr int depth() {
+    return FMT == W_BF16 ? 2 : (FMT == W_Q4G64 ? 4 : 3);
+}
 
 template <int FMT>
 __device__ __forceinline__ int64_t row_bytes(int64_t K) {
@@ -35,65 +53,87 @@ __device__ __forceinline__ int64_t row_bytes(int64_t K) {
     return K;
 }
 
-template <int FMT>
-constexpr int group_size() {
-    return FMT == W_Q8G32 ? 32 : ((FMT == W_Q4G64 || FMT == W_Q8G64) ? 64 : 0);
+// Pieces per lane per 16-row block and chunk, and their size.
+//   FP8ROW / MXFP8 / Q8G64: KC/64 x 16 B at byte 64q + 16g     (k = 64q + 16g + [0,16))
+//   Q4G64:                  KC/64 x  8 B at byte 32q + 8g      (k = 64q + 16g + [0,16))
+//   Q8G32:                  KC/32 x  8 B at byte 32s + 8g      (k = 32s + 8g + [0,8))
+//   BF16:                   KC/32 x 16 B at byte 64s + 16g     (k = 32s + 8g + [0,8))
+template <int FMT, int KC>
+struct WChunk {
+    static constexpr bool WIDE = (FMT == W_FP8ROW || FMT == W_MXFP8 || FMT == W_Q8G64 || FMT == W_BF16);
+    static constexpr int NP = (FMT == W_Q8G32 || FMT == W_BF16) ? KC / 32 : KC / 64;
+    typename std::conditional<WIDE, uint4, uint2>::type p[NP];
+    uint32_t e8[FMT == W_MXFP8 ? NP : 1];
+};
+
+// Where a wave's weights come from.  Row-major: the lane's row.  Packed (see
+// pack_weights_kernel): the lane's piece 0 of chunk 0 in its 16-row block;
+// pieces of one (chunk, block) are stored lane-major, so one load instruction
+// of the wave reads 64 x piece contiguous bytes, and the blocks of one chunk
+// are adjacent (cstride bytes from one chunk to the next).
+struct WSrc {
+    const uint8_t* w;       // row-major base, or packed base of (row block, lane)
+    const uint8_t* e8;      // MXFP8 scale bytes [N][K/32]
+    int64_t row;            // this lane's row (clamped to N - 1)
+    int64_t K;
+    int64_t cstride;        // packed: bytes between chunk c and c + 1 of a block
+};
+
+template <int FMT, int KC>
+constexpr int piece_bytes() {
+    return WChunk<FMT, KC>::WIDE ? 16 : 8;
 }
 
-// Per-lane raw weight bytes for one 16-row block and one 128-wide K half.
-template <int FMT>
-struct WRegs {
-    uint4 q[FMT == W_BF16 ? 4 : 2];
-    uint32_t e8;  // MXFP8 scale byte of the lane's 32-element group
-};
-template <>
-struct WRegs<W_Q4G64> {
-    uint2 q[2];
-    uint32_t e8;
-};
-template <>
-struct WRegs<W_Q8G32> {
-    uint2 q[4];
-    uint32_t e8;
-};
+// Byte offset, within a row-major row, of piece q of chunk c for lane group g.
+template <int FMT, int KC>
+__host__ __device__ __forceinline__ int64_t piece_offset(int64_t c, int q, int g) {
+    const int64_t kc0 = c * KC;
+    if (FMT == W_Q4G64) return (kc0 >> 1) + 32 * q + 8 * g;
+    if (FMT == W_Q8G32) return kc0 + 32 * q + 8 * g;
+    if (FMT == W_BF16) return 2 * kc0 + 64 * q + 16 * g;
+    return kc0 + 64 * q + 16 * g;
+}
 
-// Lane (i = row in block, g = lane group) loads its part of a K half starting
-// at absolute column kh0.  Layouts per format:
-//   FP8ROW / MXFP8 / BF16: g covers 32 contiguous columns kh0 + 32g ..
-//   Q8G64 / Q4G64:         g covers 16 columns in each 64-span: kh0 + 64s + 16g ..
-//   Q8G32:                 g covers 8 columns in each 32-span:  kh0 + 32s + 8g ..
-template <int FMT>
-__device__ __forceinline__ void load_wregs(WRegs<FMT>& r, const uint8_t* __restrict__ w,
-                                           const uint8_t* __restrict__ e8, int64_t row, int64_t K, int64_t kh0,
-                                           int g) {
-    const uint8_t* base = w + row * row_bytes<FMT>(K);
-    if constexpr (FMT == W_FP8ROW || FMT == W_MXFP8) {
-        const uint8_t* p = base + kh0 + 32 * g;
-        r.q[0] = ld_nt16(p);
-        r.q[1] = ld_nt16(p + 16);
-        if constexpr (FMT == W_MXFP8) r.e8 = e8[row * (K >> 5) + ((kh0 + 32 * g) >> 5)];
-    } else if constexpr (FMT == W_BF16) {
-        const uint8_t* p = base + 2 * (kh0 + 32 * g);
+template <int FMT, int KC, bool PK>
+__device__ __forceinline__ void load_chunk(WChunk<FMT, KC>& r, const WSrc& src, int64_t c, int g) {
+    constexpr int NP = WChunk<FMT, KC>::NP;
+    constexpr int PB = piece_bytes<FMT, KC>();
 #pragma unroll
-        for (int j = 0; j < 4; ++j) r.q[j] = ld_nt16(p + 16 * j);
-    } else if constexpr (FMT == W_Q8G64) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) r.q[s] = ld_nt16(base + kh0 + 64 * s + 16 * g);
-    } else if constexpr (FMT == W_Q4G64) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) r.q[s] = ld_nt8(base + ((kh0 + 64 * s + 16 * g) >> 1));
-    } else {  // W_Q8G32
-#pragma unroll
-        for (int s = 0; s < 4; ++s) r.q[s] = ld_nt8(base + kh0 + 32 * s + 8 * g);
+    for (int q = 0; q < NP; ++q) {
+        const uint8_t* p = PK ? src.w + c * src.cstride + q * (64 * PB)
+                              : src.w + src.row * row_bytes<FMT>(src.K) + piece_offset<FMT, KC>(c, q, g);
+        if constexpr (PB == 16) r.p[q] = *reinterpret_cast<const uint4*>(p);
+        else r.p[q] = *reinterpret_cast<const uint2*>(p);
+        if constexpr (FMT == W_MXFP8)
+            r.e8[q] = src.e8[src.row * (src.K >> 5) + (piece_offset<FMT, KC>(c, q, g) >> 5)];
     }
 }
 
-// LDS column offset (within the 256-wide chunk) of k-step ks for lane group g.
+// WSrc of a lane: rows past N are clamped (their outputs are never written).
+template <int FMT, int KC, bool PK>
+__device__ __forceinline__ WSrc make_wsrc(const uint8_t* w, const void* scales, int64_t row, int N, int64_t K,
+                                          int lane) {
+    WSrc s;
+    s.e8 = reinterpret_cast<const uint8_t*>(scales);
+    s.K = K;
+    s.row = row < N ? row : (int64_t)N - 1;
+    s.cstride = 0;
+    if (PK) {
+        constexpr int64_t BLOCK_CHUNK = (int64_t)WChunk<FMT, KC>::NP * 64 * piece_bytes<FMT, KC>();
+        const int64_t rb = s.row >> 4;                 // row block of the (clamped) row
+        s.cstride = ((int64_t)N + 15) / 16 * BLOCK_CHUNK;
+        s.w = w + rb * BLOCK_CHUNK + (int64_t)lane * piece_bytes<FMT, KC>();
+    } else {
+        s.w = w;
+    }
+    return s;
+}
+
+// LDS column (within the chunk) of k-step s for lane group g.
 template <int FMT>
-__device__ __forceinline__ int kstep_col(int kh, int ks, int g) {
-    if constexpr (FMT == W_Q8G64 || FMT == W_Q4G64) return kh * 128 + (ks >> 1) * 64 + 16 * g + (ks & 1) * 8;
-    else if constexpr (FMT == W_Q8G32) return kh * 128 + ks * 32 + 8 * g;
-    else return kh * 128 + 32 * g + ks * 8;
+__device__ __forceinline__ int kstep_col(int s, int g) {
+    if constexpr (FMT == W_Q8G32 || FMT == W_BF16) return 32 * s + 8 * g;
+    else return 64 * (s >> 1) + 16 * g + 8 * (s & 1);
 }
 
 __device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t d, int sh) {
@@ -108,245 +148,213 @@ __device__ __forceinline__ uint32_t i4x2_to_bf16x2(uint32_t d, int sh) {
     return f32x2_to_bf16x2(a, b);
 }
 
-// Decode the A fragment (8 BF16 weights) of k-step ks.
-template <int FMT>
-__device__ __forceinline__ v8bf decode_afrag(const WRegs<FMT>& r, int ks) {
+// The A fragment (8 BF16 weights) of k-step s.
+template <int FMT, int KC>
+__device__ __forceinline__ v8bf decode_afrag(const WChunk<FMT, KC>& r, int s) {
     uint32_t o[4];
     if constexpr (FMT == W_FP8ROW || FMT == W_MXFP8) {
-        const uint32_t* d = reinterpret_cast<const uint32_t*>(&r.q[0]);
-        const uint32_t d0 = d[2 * ks], d1 = d[2 * ks + 1];
-        const float sc = (FMT == W_MXFP8) ? ue8m0_to_f32(r.e8) : 1.0f;
+        const uint4 q = r.p[s >> 1];
+        const uint32_t d0 = (s & 1) ? q.z : q.x, d1 = (s & 1) ? q.w : q.y;
+        float sc = 1.0f;
+        if constexpr (FMT == W_MXFP8) sc = ue8m0_to_f32(r.e8[s >> 1]);
         o[0] = e4m3x2_to_bf16x2<false>(d0, sc);
         o[1] = e4m3x2_to_bf16x2<true>(d0, sc);
         o[2] = e4m3x2_to_bf16x2<false>(d1, sc);
         o[3] = e4m3x2_to_bf16x2<true>(d1, sc);
-    } else if constexpr (FMT == W_BF16) {
-        const uint4 q = r.q[ks];
-        o[0] = q.x; o[1] = q.y; o[2] = q.z; o[3] = q.w;
     } else if constexpr (FMT == W_Q8G64) {
-        const uint32_t* d = reinterpret_cast<const uint32_t*>(&r.q[ks >> 1]);
-        const uint32_t d0 = d[(ks & 1) * 2], d1 = d[(ks & 1) * 2 + 1];
+        const uint4 q = r.p[s >> 1];
+        const uint32_t d0 = (s & 1) ? q.z : q.x, d1 = (s & 1) ? q.w : q.y;
         o[0] = i8x2_to_bf16x2(d0, 0);
         o[1] = i8x2_to_bf16x2(d0, 16);
         o[2] = i8x2_to_bf16x2(d1, 0);
         o[3] = i8x2_to_bf16x2(d1, 16);
     } else if constexpr (FMT == W_Q4G64) {
-        const uint32_t* d = reinterpret_cast<const uint32_t*>(&r.q[ks >> 1]);
-        const uint32_t d0 = d[ks & 1];
+        const uint2 q = r.p[s >> 1];
+        const uint32_t d0 = (s & 1) ? q.y : q.x;
         o[0] = i4x2_to_bf16x2(d0, 0);
         o[1] = i4x2_to_bf16x2(d0, 8);
         o[2] = i4x2_to_bf16x2(d0, 16);
         o[3] = i4x2_to_bf16x2(d0, 24);
-    } else {  // W_Q8G32
-        const uint2 q = r.q[ks];
+    } else if constexpr (FMT == W_Q8G32) {
+        const uint2 q = r.p[s];
         o[0] = i8x2_to_bf16x2(q.x, 0);
         o[1] = i8x2_to_bf16x2(q.x, 16);
         o[2] = i8x2_to_bf16x2(q.y, 0);
         o[3] = i8x2_to_bf16x2(q.y, 16);
+    } else {  // W_BF16
+        const uint4 q = r.p[s];
+        o[0] = q.x; o[1] = q.y; o[2] = q.z; o[3] = q.w;
     }
     return __builtin_bit_cast(v8bf, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
-template <int FMT, int NCB>
+template <int FMT, int NCB, int KC, bool PK>
 __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint8_t* __restrict__ w,
                                                         const void* __restrict__ scales,
                                                         const uint16_t* __restrict__ x, int T, int N, int64_t K,
-                                                        int64_t k_per_split, int splits,
+                                                        int chunks_per_split, int splits,
                                                         float* __restrict__ partial,
                                                         unsigned* __restrict__ counters, int bf16_out,
                                                         void* __restrict__ y) {
     constexpr int TP = 16 * NCB;
+    constexpr int KS = KC / 32;                       // k-steps per chunk
+    constexpr int XPITCH = KC + 8;                    // bf16 per LDS row: rows shift by 4 banks
+    constexpr int XPR = KC / 8;                       // 16-byte activation pieces per row and chunk
+    constexpr int XP = TP * XPR / 256;                // ... per thread
     constexpr int GS = group_size<FMT>();
-    constexpr int NG = GS ? GV_KC / (GS ? GS : 1) : 1;  // scale groups per chunk
-    __shared__ __attribute__((aligned(16))) uint16_t xs[TP * GV_XPITCH];
-    __shared__ __attribute__((aligned(16))) uint16_t scs[GS ? NG * GV_ROWS : 1];
+    constexpr int NG = GS ? KC / (GS ? GS : 1) : 1;   // scale groups per chunk
+    constexpr int SP = GS ? (NG * GV_ROWS + 255) / 256 : 1;
+    constexpr int D = depth<FMT>();
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][TP * XPITCH];
+    __shared__ __attribute__((aligned(16))) uint16_t scs[2][GS ? NG * GV_ROWS : 1];
     __shared__ int s_last;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
-    const int rp = wv & 1;       // row pair: rows [32 rp, 32 rp + 32) of the tile
-    const int kh = wv >> 1;      // K half of each chunk
     const int li = lane & 15;
     const int lg = lane >> 4;
     const int tile = blockIdx.x;
     const int split = blockIdx.y;
     const int64_t row0 = (int64_t)tile * GV_ROWS;
-    const int64_t k_begin = (int64_t)split * k_per_split;
-    int64_t k_end = k_begin + k_per_split;
-    if (k_end > K) k_end = K;
-    const int nch = (int)((k_end - k_begin + GV_KC - 1) / GV_KC);
+    const int64_t total_chunks = K / KC;
+    const int64_t c_begin = (int64_t)split * chunks_per_split;
+    int nch = (int)(total_chunks - c_begin);
+    if (nch > chunks_per_split) nch = chunks_per_split;
+    const int64_t k_begin = c_begin * KC;
 
-    const uint8_t* e8 = reinterpret_cast<const uint8_t*>(scales);
-    const uint16_t* sc16 = reinterpret_cast<const uint16_t*>(scales);
+    const WSrc src = make_wsrc<FMT, KC, PK>(w, scales, row0 + wv * 16 + li, N, K, lane);
 
-    int64_t wrow[2];
+    // activations: rows >= T fall outside the buffer and read as zero
+    const __amdgpu_buffer_rsrc_t xrsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)((int64_t)T * K * 2), BUF_FLAGS);
+    __amdgpu_buffer_rsrc_t srsrc = xrsrc;
+    if constexpr (GS != 0)
+        srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)scales, (short)0, (int)((int64_t)N * (K / GS) * 2),
+                                                  BUF_FLAGS);
+
+    uint4 xreg[XP];
+    uint32_t sreg[SP];
+    auto load_x = [&](int c) {
+        const int64_t kc0 = k_begin + (int64_t)c * KC;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        int64_t r = row0 + rp * 32 + rb * 16 + li;
-        wrow[rb] = r < N ? r : (int64_t)N - 1;
-    }
-
-    v4f acc[2][NCB];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    // activation chunk staging: thread covers 16 bytes of 2*NCB token rows
-    const int xc = tid & 31;
-    const int xr = tid >> 5;
-    uint4 xreg[2 * NCB];
-    uint16_t sreg[GS ? (NG * GV_ROWS + 255) / 256 : 1];
-
-    auto load_x = [&](int64_t kc0) {
-#pragma unroll
-        for (int j = 0; j < 2 * NCB; ++j) {
-            const int t = xr + 8 * j;
-            const int64_t k = kc0 + 8 * xc;
-            if (t < T && k < k_end) xreg[j] = *reinterpret_cast<const uint4*>(x + (int64_t)t * K + k);
-            else xreg[j] = make_uint4(0, 0, 0, 0);
+        for (int j = 0; j < XP; ++j) {
+            const int idx = tid + 256 * j;
+            const int t = idx / XPR, pc = idx % XPR;
+            const int off = (int)(((int64_t)t * K + kc0 + 8 * pc) * 2);
+            xreg[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, off, 0, 0));
         }
         if constexpr (GS != 0) {
 #pragma unroll
-            for (int j = 0; j < (NG * GV_ROWS + 255) / 256; ++j) {
-                const int idx = tid + 256 * j;       // idx = row * NG + grp
+            for (int j = 0; j < SP; ++j) {
+                const int idx = tid + 256 * j;          // idx = row * NG + group
                 const int r = idx / NG, gi = idx % NG;
-                int64_t row = row0 + r;
-                if (row >= N) row = N - 1;
-                const int64_t grp = kc0 / GS + gi;
-                sreg[j] = (idx < NG * GV_ROWS && kc0 + (int64_t)gi * GS < k_end)
-                              ? sc16[row * (K / GS) + grp] : (uint16_t)0;
+                const int64_t row = row0 + r;           // rows >= N read as zero
+                const int off = (int)((row * (K / GS) + kc0 / GS + gi) * 2);
+                sreg[j] = __builtin_amdgcn_raw_buffer_load_b16(srsrc, off, 0, 0);
             }
         }
     };
-    auto store_x = [&]() {
+    auto store_x = [&](int buf) {
 #pragma unroll
-        for (int j = 0; j < 2 * NCB; ++j)
-            *reinterpret_cast<uint4*>(&xs[(xr + 8 * j) * GV_XPITCH + 8 * xc]) = xreg[j];
+        for (int j = 0; j < XP; ++j) {
+            const int idx = tid + 256 * j;
+            const int t = idx / XPR, pc = idx % XPR;
+            *reinterpret_cast<uint4*>(&xs[buf][t * XPITCH + 8 * pc]) = xreg[j];
+        }
         if constexpr (GS != 0) {
 #pragma unroll
-            for (int j = 0; j < (NG * GV_ROWS + 255) / 256; ++j) {
+            for (int j = 0; j < SP; ++j) {
                 const int idx = tid + 256 * j;
-                if (idx < NG * GV_ROWS) scs[(idx % NG) * GV_ROWS + idx / NG] = sreg[j];
+                if (SP * 256 == NG * GV_ROWS || idx < NG * GV_ROWS)
+                    scs[buf][(idx % NG) * GV_ROWS + idx / NG] = (uint16_t)sreg[j];
             }
         }
     };
 
-    WRegs<FMT> wc[2], wn[2];
-    auto load_w = [&](WRegs<FMT>* dst, int64_t kc0) {
-        const int64_t kh0 = kc0 + 128 * kh;
-        if (kh0 < k_end) {
+    v4f acc[NCB];
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) load_wregs<FMT>(dst[rb], w, e8, wrow[rb], K, kh0, lg);
+    for (int cb = 0; cb < NCB; ++cb) acc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const WChunk<FMT, KC>& wc, int buf) {
+        if constexpr (GS == 0) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const int col = kstep_col<FMT>(s, lg);
+                const v8bf a = decode_afrag<FMT, KC>(wc, s);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    const v8bf b = *reinterpret_cast<const v8bf*>(&xs[buf][(cb * 16 + li) * XPITCH + col]);
+                    acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[cb], 0, 0, 0);
+                }
+            }
+        } else {
+            constexpr int KPG = GS / 32;                 // k-steps per scale group
+#pragma unroll
+            for (int gq = 0; gq < KS / KPG; ++gq) {
+                v4f d[NCB];
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) d[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KPG; ++kk) {
+                    const int s = gq * KPG + kk;
+                    const int col = kstep_col<FMT>(s, lg);
+                    const v8bf a = decode_afrag<FMT, KC>(wc, s);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) {
+                        const v8bf b = *reinterpret_cast<const v8bf*>(&xs[buf][(cb * 16 + li) * XPITCH + col]);
+                        d[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, d[cb], 0, 0, 0);
+                    }
+                }
+                const uint2 s4 = *reinterpret_cast<const uint2*>(&scs[buf][gq * GV_ROWS + wv * 16 + 4 * lg]);
+                const float s0 = f16_bits_to_f32(s4.x & 0xFFFFu), s1 = f16_bits_to_f32(s4.x >> 16);
+                const float s2 = f16_bits_to_f32(s4.y & 0xFFFFu), s3 = f16_bits_to_f32(s4.y >> 16);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    acc[cb][0] = fmaf(d[cb][0], s0, acc[cb][0]);
+                    acc[cb][1] = fmaf(d[cb][1], s1, acc[cb][1]);
+                    acc[cb][2] = fmaf(d[cb][2], s2, acc[cb][2]);
+                    acc[cb][3] = fmaf(d[cb][3], s3, acc[cb][3]);
+                }
+            }
         }
+    };
+
+    // One chunk: compute from ring slot u, stage the next activation chunk,
+    // request the one after it, refill slot u with the chunk D ahead (indices
+    // clamped to the last chunk, so the body has no branch), barrier.
+    WChunk<FMT, KC> ring[D];
+    auto body = [&](int c, int u) {
+        compute(ring[u], c & 1);
+        store_x((c + 1) & 1);
+        load_x(min(c + 2, nch - 1));
+        load_chunk<FMT, KC, PK>(ring[u], src, c_begin + min(c + D, nch - 1), lg);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
     };
 
     if (nch > 0) {
-        load_w(wc, k_begin);
-        load_x(k_begin);
-    }
-    for (int c = 0; c < nch; ++c) {
-        const int64_t kc0 = k_begin + (int64_t)c * GV_KC;
+        load_x(0);
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            load_chunk<FMT, KC, PK>(ring[d], src, c_begin + min(d, nch - 1), lg);
+        store_x(0);
+        load_x(min(1, nch - 1));
         __syncthreads();
-        store_x();
-        __syncthreads();
-        if (c + 1 < nch) {
-            load_w(wn, kc0 + GV_KC);
-            load_x(kc0 + GV_KC);
+        int c = 0;
+        for (; c + D <= nch; c += D) {
+#pragma unroll
+            for (int u = 0; u < D; ++u) body(c + u, u);
         }
-        if (kc0 + 128 * kh < k_end) {
-            if constexpr (GS == 0) {
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const int col = kstep_col<FMT>(kh, ks, lg);
-                    v8bf b[NCB];
-#pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb)
-                        b[cb] = *reinterpret_cast<const v8bf*>(&xs[(cb * 16 + li) * GV_XPITCH + col]);
-#pragma unroll
-                    for (int rb = 0; rb < 2; ++rb) {
-                        const v8bf a = decode_afrag<FMT>(wc[rb], ks);
-#pragma unroll
-                        for (int cb = 0; cb < NCB; ++cb)
-                            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[cb], acc[rb][cb], 0, 0, 0);
-                    }
-                }
-            } else {
-                constexpr int KPG = GS / 32;             // k-steps per scale group
-#pragma unroll
-                for (int gq = 0; gq < 4 / KPG; ++gq) {
-                    v4f d[2][NCB];
-#pragma unroll
-                    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                        for (int cb = 0; cb < NCB; ++cb) d[rb][cb] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kk = 0; kk < KPG; ++kk) {
-                        const int ks = gq * KPG + kk;
-                        const int col = kstep_col<FMT>(kh, ks, lg);
-                        v8bf b[NCB];
-#pragma unroll
-                        for (int cb = 0; cb < NCB; ++cb)
-                            b[cb] = *reinterpret_cast<const v8bf*>(&xs[(cb * 16 + li) * GV_XPITCH + col]);
-#pragma unroll
-                        for (int rb = 0; rb < 2; ++rb) {
-                            const v8bf a = decode_afrag<FMT>(wc[rb], ks);
-#pragma unroll
-                            for (int cb = 0; cb < NCB; ++cb)
-                                d[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[cb], d[rb][cb], 0, 0, 0);
-                        }
-                    }
-                    // group index within the chunk of this k-step group
-                    const int gi = (kh * 128) / GS + gq;
-#pragma unroll
-                    for (int rb = 0; rb < 2; ++rb) {
-                        const uint2 s4 = *reinterpret_cast<const uint2*>(
-                            &scs[gi * GV_ROWS + rp * 32 + rb * 16 + 4 * lg]);
-                        const float s0 = f16_bits_to_f32(s4.x & 0xFFFFu), s1 = f16_bits_to_f32(s4.x >> 16);
-                        const float s2 = f16_bits_to_f32(s4.y & 0xFFFFu), s3 = f16_bits_to_f32(s4.y >> 16);
-#pragma unroll
-                        for (int cb = 0; cb < NCB; ++cb) {
-                            acc[rb][cb][0] = fmaf(d[rb][cb][0], s0, acc[rb][cb][0]);
-                            acc[rb][cb][1] = fmaf(d[rb][cb][1], s1, acc[rb][cb][1]);
-                            acc[rb][cb][2] = fmaf(d[rb][cb][2], s2, acc[rb][cb][2]);
-                            acc[rb][cb][3] = fmaf(d[rb][cb][3], s3, acc[rb][cb][3]);
-                        }
-                    }
-                }
-            }
-        }
-        if (c + 1 < nch) {
-            wc[0] = wn[0];
-            wc[1] = wn[1];
-        }
-    }
-
-    // Sum the two K halves through LDS (fixed order: half 0 + half 1).
-    __syncthreads();
-    float* red = reinterpret_cast<float*>(xs);
-    if (kh == 1) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-                *reinterpret_cast<v4f*>(&red[(((rp * 2 + rb) * NCB + cb) * 64 + lane) * 4]) = acc[rb][cb];
-    }
-    __syncthreads();
-    if (kh == 0) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-                const v4f o = *reinterpret_cast<const v4f*>(&red[(((rp * 2 + rb) * NCB + cb) * 64 + lane) * 4]);
-                acc[rb][cb] += o;
-            }
+        for (int u = 0; u < D - 1; ++u)
+            if (c + u < nch) body(c + u, u);
     }
 
     const int64_t npad = (int64_t)gridDim.x * GV_ROWS;
-    auto write_out = [&](int rb, int cb, v4f v) {
+    const int64_t n0 = row0 + wv * 16 + 4 * lg;           // this lane's 4 output rows
+    auto write_out = [&](int cb, v4f v) {
         const int t = cb * 16 + li;
-        const int64_t n0 = row0 + rp * 32 + rb * 16 + 4 * lg;
         if (t >= T) return;
         if constexpr (FMT == W_FP8ROW) {
             const uint16_t* rs = reinterpret_cast<const uint16_t*>(scales);
@@ -377,57 +385,269 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint8_t* __restric
     };
 
     if (splits == 1) {
-        if (kh == 0) {
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) write_out(rb, cb, acc[rb][cb]);
-        }
+        for (int cb = 0; cb < NCB; ++cb) write_out(cb, acc[cb]);
         return;
     }
 
-    // Split-K: publish this split's partial, the last workgroup of the tile sums.
-    if (kh == 0) {
+    // Split-K: publish this split's partial; the last workgroup of the tile sums.
+    // Partials move only through device-coherent (agent-scope) atomic stores
+    // and loads, which bypass the per-XCD L2; each wave waits for its stores to
+    // complete before the counter is bumped.  No device-scope fence: on this
+    // part it would write back and invalidate the whole L2.
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int t = cb * 16 + li;
+        if (t < T) {
+            uint32_t* p = reinterpret_cast<uint32_t*>(&partial[((int64_t)split * T + t) * npad + n0]);
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-                const int t = cb * 16 + li;
-                if (t < T) {
-                    const int64_t n0 = row0 + rp * 32 + rb * 16 + 4 * lg;
-                    *reinterpret_cast<v4f*>(&partial[((int64_t)split * T + t) * npad + n0]) = acc[rb][cb];
-                }
-            }
+            for (int r = 0; r < 4; ++r)
+                __hip_atomic_store(p + r, __float_as_uint(acc[cb][r]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
-    __threadfence();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0) {
-        const unsigned prev = atomicAdd(&counters[tile], 1u);
+        const unsigned prev = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == (unsigned)(splits - 1));
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
-    if (kh == 0) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int t = cb * 16 + li;
+        if (t >= T) continue;
+        v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < splits; ++s) {
+            const uint32_t* p = reinterpret_cast<const uint32_t*>(&partial[((int64_t)s * T + t) * npad + n0]);
+            v4f part;
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-                const int t = cb * 16 + li;
-                if (t >= T) continue;
-                const int64_t n0 = row0 + rp * 32 + rb * 16 + 4 * lg;
-                v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
-                for (int s = 0; s < splits; ++s) {
-                    const uint32_t* p =
-                        reinterpret_cast<const uint32_t*>(&partial[((int64_t)s * T + t) * npad + n0]);
-                    v4f part;
+            for (int r = 0; r < 4; ++r)
+                part[r] = __uint_as_float(__hip_atomic_load(p + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            sum += part;
+        }
+        write_out(cb, sum);
+    }
+    if (tid == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Resident-activation variant: when the workgroup's activation slice
+// [T][k range] (and its rows' group scales) fits in LDS, it is staged once and
+// the waves then stream weights with no barrier at all, each with its own
+// register ring (deeper than above: nothing else is in flight).  B fragments of
+// tokens t >= T read a zero row.
+// ---------------------------------------------------------------------------
+template <int FMT>
+constexpr int depth_resident() {
+    return FMT == W_BF16 ? 3 : (FMT == W_Q4G64 ? 8 : (FMT == W_MXFP8 ? 4 : 5));
+}
+
+template <int FMT, int NCB, int KC, bool PK>
+__global__ __launch_bounds__(256) void gemv_resident_kernel(const uint8_t* __restrict__ w,
+                                                            const void* __restrict__ scales,
+                                                            const uint16_t* __restrict__ x, int T, int N,
+                                                            int64_t K, int chunks_per_split, int splits,
+                                                            float* __restrict__ partial,
+                                                            unsigned* __restrict__ counters, int bf16_out,
+                                                            void* __restrict__ y) {
+    constexpr int KS = KC / 32;
+    constexpr int GS = group_size<FMT>();
+    constexpr int D = depth_resident<FMT>();
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    __shared__ int s_last;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    const int li = lane & 15;
+    const int lg = lane >> 4;
+    const int tile = blockIdx.x;
+    const int split = blockIdx.y;
+    const int64_t row0 = (int64_t)tile * GV_ROWS;
+    const int64_t total_chunks = K / KC;
+    const int64_t c_begin = (int64_t)split * chunks_per_split;
+    int nch = (int)(total_chunks - c_begin);
+    if (nch > chunks_per_split) nch = chunks_per_split;
+    const int64_t k_begin = c_begin * KC;
+    const int krange = nch * KC;
+    const int xpitch = chunks_per_split * KC + 8;         // bf16 per LDS row (rows shift by 4 banks)
+    const int ng_all = GS ? chunks_per_split * KC / (GS ? GS : 1) : 0;
+    uint16_t* xs = lds;                                    // [T + 1][xpitch], row T is zero
+    uint16_t* scs = lds + (T + 1) * xpitch;                // [ng_all][64 rows]
+
+    const WSrc src = make_wsrc<FMT, KC, PK>(w, scales, row0 + wv * 16 + li, N, K, lane);
+
+    // the first weight chunks are requested before the activations are staged
+    WChunk<FMT, KC> ring[D];
+    if (nch > 0) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        part[r] = __uint_as_float(__hip_atomic_load(p + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-                    sum += part;
-                }
-                write_out(rb, cb, sum);
+        for (int d = 0; d < D; ++d) load_chunk<FMT, KC, PK>(ring[d], src, c_begin + min(d, nch - 1), lg);
+    }
+
+    // stage activations (16-byte pieces), the zero row and the group scales
+    {
+        const int pieces = krange / 8;
+        for (int i = tid; i < (T + 1) * pieces; i += 256) {
+            const int t = i / pieces, pc = i - t * pieces;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (t < T) v = *reinterpret_cast<const uint4*>(x + (int64_t)t * K + k_begin + 8 * pc);
+            *reinterpret_cast<uint4*>(&xs[t * xpitch + 8 * pc]) = v;
+        }
+        if constexpr (GS != 0) {
+            const uint16_t* sc16 = reinterpret_cast<const uint16_t*>(scales);
+            const int ng = krange / GS;
+            for (int i = tid; i < ng * GV_ROWS; i += 256) {
+                const int r = i / ng, gi = i - r * ng;
+                int64_t row = row0 + r;
+                if (row >= N) row = N - 1;
+                scs[gi * GV_ROWS + r] = sc16[row * (K / GS) + k_begin / GS + gi];
             }
+        }
+        __syncthreads();
+    }
+    (void)ng_all;
+
+    v4f acc[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+    int brow[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) brow[cb] = min(cb * 16 + li, T) * xpitch;
+
+    auto compute = [&](const WChunk<FMT, KC>& wc, int c) {
+        const int kl = c * KC;                             // column of the chunk within the slice
+        if constexpr (GS == 0) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const int col = kl + kstep_col<FMT>(s, lg);
+                const v8bf a = decode_afrag<FMT, KC>(wc, s);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    const v8bf b = *reinterpret_cast<const v8bf*>(&xs[brow[cb] + col]);
+                    acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[cb], 0, 0, 0);
+                }
+            }
+        } else {
+            constexpr int KPG = GS / 32;
+#pragma unroll
+            for (int gq = 0; gq < KS / KPG; ++gq) {
+                v4f d[NCB];
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) d[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KPG; ++kk) {
+                    const int s = gq * KPG + kk;
+                    const int col = kl + kstep_col<FMT>(s, lg);
+                    const v8bf a = decode_afrag<FMT, KC>(wc, s);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) {
+                        const v8bf b = *reinterpret_cast<const v8bf*>(&xs[brow[cb] + col]);
+                        d[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, d[cb], 0, 0, 0);
+                    }
+                }
+                const int gi = kl / GS + gq;
+                const uint2 s4 = *reinterpret_cast<const uint2*>(&scs[gi * GV_ROWS + wv * 16 + 4 * lg]);
+                const float s0 = f16_bits_to_f32(s4.x & 0xFFFFu), s1 = f16_bits_to_f32(s4.x >> 16);
+                const float s2 = f16_bits_to_f32(s4.y & 0xFFFFu), s3 = f16_bits_to_f32(s4.y >> 16);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    acc[cb][0] = fmaf(d[cb][0], s0, acc[cb][0]);
+                    acc[cb][1] = fmaf(d[cb][1], s1, acc[cb][1]);
+                    acc[cb][2] = fmaf(d[cb][2], s2, acc[cb][2]);
+                    acc[cb][3] = fmaf(d[cb][3], s3, acc[cb][3]);
+                }
+            }
+        }
+    };
+
+    if (nch > 0) {
+        int c = 0;
+        for (; c + D <= nch; c += D) {
+#pragma unroll
+            for (int u = 0; u < D; ++u) {
+                compute(ring[u], c + u);
+                load_chunk<FMT, KC, PK>(ring[u], src, c_begin + min(c + u + D, nch - 1), lg);
+                // keep each refill right after the compute that frees its slot
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < D - 1; ++u)
+            if (c + u < nch) compute(ring[u], c + u);
+    }
+
+    const int64_t npad = (int64_t)gridDim.x * GV_ROWS;
+    const int64_t n0 = row0 + wv * 16 + 4 * lg;
+    auto write_out = [&](int cb, v4f v) {
+        const int t = cb * 16 + li;
+        if (t >= T) return;
+        if constexpr (FMT == W_FP8ROW) {
+            const uint16_t* rs = reinterpret_cast<const uint16_t*>(scales);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = (n0 + r < N) ? v[r] * bf16_bits_to_f32(rs[n0 + r]) : 0.f;
+        }
+        if (bf16_out) {
+            uint16_t* yo = reinterpret_cast<uint16_t*>(y) + (int64_t)t * N;
+            if (n0 + 3 < N && (N & 3) == 0) {
+                *reinterpret_cast<uint2*>(yo + n0) =
+                    make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                               f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (n0 + r < N) yo[n0 + r] = (uint16_t)f32_to_bf16_rne(v[r]);
+            }
+        } else {
+            float* yo = reinterpret_cast<float*>(y) + (int64_t)t * N;
+            if (n0 + 3 < N && (N & 3) == 0) {
+                *reinterpret_cast<v4f*>(yo + n0) = v;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (n0 + r < N) yo[n0 + r] = v[r];
+            }
+        }
+    };
+
+    if (splits == 1) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) write_out(cb, acc[cb]);
+        return;
+    }
+    // Split-K through device-coherent atomic stores / loads (see gemv_mfma_kernel).
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int t = cb * 16 + li;
+        if (t < T) {
+            uint32_t* p = reinterpret_cast<uint32_t*>(&partial[((int64_t)split * T + t) * npad + n0]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                __hip_atomic_store(p + r, __float_as_uint(acc[cb][r]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == (unsigned)(splits - 1));
+    }
+    __syncthreads();
+    if (!s_last) return;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int t = cb * 16 + li;
+        if (t >= T) continue;
+        v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < splits; ++s) {
+            const uint32_t* p = reinterpret_cast<const uint32_t*>(&partial[((int64_t)s * T + t) * npad + n0]);
+            v4f part;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                part[r] = __uint_as_float(__hip_atomic_load(p + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            sum += part;
+        }
+        write_out(cb, sum);
     }
     if (tid == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -496,62 +716,136 @@ __global__ __launch_bounds__(64) void gemv_generic_kernel(const uint8_t* __restr
 // ---------------------------------------------------------------------------
 struct GemvPlan {
     bool mfma;
+    bool resident;           // activation slice staged once in LDS (no barriers in the loop)
+    int kc;                  // chunk width (256 or 128)
     int64_t tiles;
     int splits;
-    int64_t k_per_split;
+    int chunks_per_split;
+    int64_t lds_bytes;       // dynamic LDS of the resident kernel
 };
 
-static GemvPlan plan_gemv(int64_t Tc, int64_t N, int64_t K) {
-    (void)Tc;
+constexpr int64_t RESIDENT_LDS_MAX = 64 << 10;
+
+static int fmt_group(int fmt) {
+    return fmt == W_Q8G32 ? 32 : ((fmt == W_Q4G64 || fmt == W_Q8G64) ? 64 : 0);
+}
+
+static double fmt_bytes_per_weight(int fmt) {
+    return fmt == W_Q4G64 ? 0.5 : (fmt == W_BF16 ? 2.0 : 1.0);
+}
+
+static int64_t resident_lds(int fmt, int64_t Tc, int64_t cps, int kc) {
+    const int gs = fmt_group(fmt);
+    const int64_t span = cps * kc;
+    return ((Tc + 1) * (span + 8) + (gs ? span / gs * GV_ROWS : 0)) * 2;
+}
+
+static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K) {
     GemvPlan p{};
-    p.mfma = (K > 0) && (K % 128 == 0);
+    // buffer offsets are 32-bit: the activation block must stay below 2 GiB
+    p.mfma = (K > 0) && (K % 128 == 0) && (Tc * K * 2 < ((int64_t)1 << 31)) &&
+             (N * (K / 32) * 2 < ((int64_t)1 << 31));
+    p.kc = (K % 256 == 0) ? 256 : 128;
     p.tiles = (N + GV_ROWS - 1) / GV_ROWS;
     p.splits = 1;
-    p.k_per_split = K;
+    p.chunks_per_split = p.mfma ? (int)(K / p.kc) : 0;
     if (!p.mfma) return p;
-    const int64_t chunks = (K + GV_KC - 1) / GV_KC;
-    const int64_t target = 2 * (int64_t)device_cu_count();
-    int64_t s = (target + p.tiles - 1) / p.tiles;
-    if (s > chunks / 2) s = chunks / 2;
-    if (s > 16) s = 16;
-    if (s < 1) s = 1;
-    const int64_t cps = (chunks + s - 1) / s;
-    p.k_per_split = cps * GV_KC;
+    const int64_t chunks = K / p.kc;
+    static const int per_cu = [] {
+        const char* e = getenv("NQ_GEMV_WGS_PER_CU");
+        const int v = e ? atoi(e) : 0;
+        return v > 0 ? v : 2;
+    }();
+    const int64_t target = per_cu * (int64_t)device_cu_count();
+    static const int min_chunks = [] {
+        const char* e = getenv("NQ_GEMV_MIN_CHUNKS");
+        const int v = e ? atoi(e) : 0;
+        return v > 0 ? v : 4;
+    }();
+    int64_t s0 = (target + p.tiles - 1) / p.tiles;
+    if (s0 > chunks / min_chunks) s0 = chunks / min_chunks;   // keep whole chunks per split
+    if (s0 > 32) s0 = 32;
+    if (s0 < 1) s0 = 1;
+    // resident variant: smallest split count >= s0 whose slice fits in LDS and
+    // whose FP32 partials stay within 12% of the weight bytes
+    const double wbytes = (double)N * (double)K * fmt_bytes_per_weight(fmt);
+    for (int64_t s = s0; s <= 32 && s <= chunks; ++s) {
+        const int64_t cps = (chunks + s - 1) / s;
+        const int64_t se = (chunks + cps - 1) / cps;
+        const double partial_bytes = se > 1 ? 8.0 * (double)se * (double)Tc * (double)N : 0.0;
+        const int64_t lds = resident_lds(fmt, Tc, cps, p.kc);
+        if (lds <= RESIDENT_LDS_MAX && partial_bytes <= 0.12 * wbytes) {
+            p.resident = true;
+            p.chunks_per_split = (int)cps;
+            p.splits = (int)se;
+            p.lds_bytes = lds;
+            return p;
+        }
+    }
+    const int64_t cps = (chunks + s0 - 1) / s0;
+    p.chunks_per_split = (int)cps;
     p.splits = (int)((chunks + cps - 1) / cps);
     return p;
 }
 
 static int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
 
-int64_t gemv_workspace_bytes(int fmt, int64_t T, int64_t N, int64_t K) {
-    (void)fmt;
-    const int64_t Tc = T < 64 ? T : 64;
-    const GemvPlan p = plan_gemv(Tc, N, K);
+static int64_t plan_workspace(const GemvPlan& p, int64_t Tc) {
     if (!p.mfma || p.splits == 1) return 0;
     return align256(p.tiles * 4) + (int64_t)p.splits * Tc * p.tiles * GV_ROWS * 4;
 }
 
-template <int FMT, int NCB>
+int64_t gemv_workspace_bytes(int fmt, int64_t T, int64_t N, int64_t K) {
+    if (fmt < 0) fmt = W_FP8ROW;
+    const int64_t Tc = T < 64 ? T : 64;
+    int64_t need = plan_workspace(plan_gemv(fmt, Tc, N, K), Tc);
+    if (T > 64) {                                   // the remainder pass may plan differently
+        const int64_t Tr = T % 64;
+        if (Tr) {
+            const int64_t r = plan_workspace(plan_gemv(fmt, Tr, N, K), Tr);
+            if (r > need) need = r;
+        }
+    }
+    return need;
+}
+
+template <int FMT, int NCB, int KC, bool PK>
 static void launch_mfma(const GemvPlan& p, const void* w, const void* scales, const uint16_t* x, int Tc, int64_t N,
                         int64_t K, bool bf16_out, void* y, float* partial, unsigned* counters,
                         hipStream_t stream) {
     dim3 grid((unsigned)p.tiles, (unsigned)p.splits);
-    gemv_mfma_kernel<FMT, NCB><<<grid, 256, 0, stream>>>(reinterpret_cast<const uint8_t*>(w), scales, x, Tc,
-                                                         (int)N, K, p.k_per_split, p.splits, partial, counters,
-                                                         bf16_out ? 1 : 0, y);
+    if (p.resident)
+        gemv_resident_kernel<FMT, NCB, KC, PK><<<grid, 256, (size_t)p.lds_bytes, stream>>>(
+            reinterpret_cast<const uint8_t*>(w), scales, x, Tc, (int)N, K, p.chunks_per_split, p.splits, partial,
+            counters, bf16_out ? 1 : 0, y);
+    else
+        gemv_mfma_kernel<FMT, NCB, KC, PK><<<grid, 256, 0, stream>>>(reinterpret_cast<const uint8_t*>(w), scales, x,
+                                                                     Tc, (int)N, K, p.chunks_per_split, p.splits,
+                                                                     partial, counters, bf16_out ? 1 : 0, y);
+}
+
+template <int FMT, int KC, bool PK>
+static void launch_ncb(const GemvPlan& p, const void* w, const void* scales, const uint16_t* x, int Tc, int64_t N,
+                       int64_t K, bool bf16_out, void* y, float* partial, unsigned* counters, hipStream_t stream) {
+    switch ((Tc + 15) / 16) {
+        case 1: launch_mfma<FMT, 1, KC, PK>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+        case 2: launch_mfma<FMT, 2, KC, PK>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+        case 3: launch_mfma<FMT, 3, KC, PK>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+        default: launch_mfma<FMT, 4, KC, PK>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+    }
 }
 
 template <int FMT>
-static void launch_fmt(const GemvPlan& p, const void* w, const void* scales, const uint16_t* x, int Tc, int64_t N,
-                       int64_t K, bool bf16_out, void* y, float* partial, unsigned* counters,
+static void launch_fmt(const GemvPlan& p, bool packed, const void* w, const void* scales, const uint16_t* x, int Tc,
+                       int64_t N, int64_t K, bool bf16_out, void* y, float* partial, unsigned* counters,
                        hipStream_t stream) {
     if (p.mfma) {
-        const int ncb = (Tc + 15) / 16;
-        switch (ncb) {
-            case 1: launch_mfma<FMT, 1>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
-            case 2: launch_mfma<FMT, 2>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
-            case 3: launch_mfma<FMT, 3>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
-            default: launch_mfma<FMT, 4>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+        if (packed) {
+            if (p.kc == 256) launch_ncb<FMT, 256, true>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream);
+            else launch_ncb<FMT, 128, true>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream);
+        } else {
+            if (p.kc == 256) launch_ncb<FMT, 256, false>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream);
+            else launch_ncb<FMT, 128, false>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream);
         }
     } else {
         dim3 grid((unsigned)N, (unsigned)((Tc + 7) / 8));
@@ -560,35 +854,114 @@ static void launch_fmt(const GemvPlan& p, const void* w, const void* scales, con
     }
 }
 
+// ---------------------------------------------------------------------------
+// Packed weight layout.  Rows are grouped in blocks of 16 (the last block
+// zero-padded).  Chunk-major: for every chunk c of KC columns, for every row
+// block, for every piece q of the chunk, the 64 lanes' pieces are stored one
+// after another in lane order (lane = 16 g + i holds row i, lane group g).  A
+// wave reading chunk c of its block reads NP runs of 64 x piece contiguous
+// bytes, and the waves of the whole grid, walking chunk by chunk, sweep one
+// contiguous window of memory at a time.  A pure permutation of the row-major
+// bytes; KC is 256 when K % 256 == 0, else 128.
+// ---------------------------------------------------------------------------
+template <int FMT, int KC>
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* __restrict__ src, int64_t N, int64_t K,
+                                                           uint8_t* __restrict__ dst, int64_t n_pieces) {
+    constexpr int NP = WChunk<FMT, KC>::NP;
+    constexpr int PB = piece_bytes<FMT, KC>();
+    const int64_t nrb = (N + 15) / 16;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_pieces; i += (int64_t)gridDim.x * 256) {
+        // i = ((c * nrb + rb) * NP + q) * 64 + lane
+        const int lane = (int)(i & 63);
+        const int64_t j = i >> 6;
+        const int q = (int)(j % NP);
+        const int64_t cr = j / NP;
+        const int64_t rb = cr % nrb, c = cr / nrb;
+        const int64_t row = rb * 16 + (lane & 15);
+        uint8_t* d = dst + i * PB;
+        if (row < N) {
+            const uint8_t* s = src + row * row_bytes<FMT>(K) + piece_offset<FMT, KC>(c, q, lane >> 4);
+            if constexpr (PB == 16) *reinterpret_cast<uint4*>(d) = *reinterpret_cast<const uint4*>(s);
+            else *reinterpret_cast<uint2*>(d) = *reinterpret_cast<const uint2*>(s);
+        } else {
+            if constexpr (PB == 16) *reinterpret_cast<uint4*>(d) = make_uint4(0, 0, 0, 0);
+            else *reinterpret_cast<uint2*>(d) = make_uint2(0, 0);
+        }
+    }
+}
+
+static int64_t row_bytes_host(int fmt, int64_t K) {
+    return fmt == W_Q4G64 ? K / 2 : (fmt == W_BF16 ? 2 * K : K);
+}
+
+int64_t packed_weight_bytes(int fmt, int64_t N, int64_t K) {
+    return (N + 15) / 16 * 16 * row_bytes_host(fmt, K);
+}
+
+template <int FMT, int KC>
+static void launch_pack(const void* src, int64_t N, int64_t K, void* dst, hipStream_t stream) {
+    constexpr int NP = WChunk<FMT, KC>::NP;
+    const int64_t n_pieces = (N + 15) / 16 * (K / KC) * NP * 64;
+    int64_t blocks = (n_pieces + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    pack_weights_kernel<FMT, KC><<<(unsigned)blocks, 256, 0, stream>>>(reinterpret_cast<const uint8_t*>(src), N, K,
+                                                                       reinterpret_cast<uint8_t*>(dst), n_pieces);
+}
+
+template <int FMT>
+static void launch_pack_fmt(const void* src, int64_t N, int64_t K, void* dst, hipStream_t stream) {
+    if (K % 256 == 0) launch_pack<FMT, 256>(src, N, K, dst, stream);
+    else launch_pack<FMT, 128>(src, N, K, dst, stream);
+}
+
+hipError_t launch_pack_weights(int fmt, const void* src, int64_t N, int64_t K, void* dst, hipStream_t stream) {
+    if (N == 0 || K == 0) return hipSuccess;
+    switch (fmt) {
+        case W_FP8ROW: launch_pack_fmt<W_FP8ROW>(src, N, K, dst, stream); break;
+        case W_MXFP8: launch_pack_fmt<W_MXFP8>(src, N, K, dst, stream); break;
+        case W_BF16: launch_pack_fmt<W_BF16>(src, N, K, dst, stream); break;
+        case W_Q8G64: launch_pack_fmt<W_Q8G64>(src, N, K, dst, stream); break;
+        case W_Q4G64: launch_pack_fmt<W_Q4G64>(src, N, K, dst, stream); break;
+        case W_Q8G32: launch_pack_fmt<W_Q8G32>(src, N, K, dst, stream); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_gemv(int fmt, const void* w, const void* scales, const uint16_t* x, int64_t T, int64_t N,
                        int64_t K, bool bf16_out, void* y, void* workspace, int64_t workspace_bytes,
-                       hipStream_t stream) {
+                       hipStream_t stream, bool packed) {
     if (T == 0 || N == 0) return hipSuccess;
     const size_t ybytes = bf16_out ? 2 : 4;
     for (int64_t t0 = 0; t0 < T; t0 += 64) {
         const int Tc = (int)((T - t0) < 64 ? (T - t0) : 64);
-        GemvPlan p = plan_gemv(Tc, N, K);
+        GemvPlan p = plan_gemv(fmt, Tc, N, K);
+        if (packed && !p.mfma) return hipErrorInvalidValue;    // only the MFMA kernels read packed weights
         float* partial = nullptr;
         unsigned* counters = nullptr;
         if (p.splits > 1) {
-            const int64_t need = align256(p.tiles * 4) + (int64_t)p.splits * Tc * p.tiles * GV_ROWS * 4;
+            const int64_t need = plan_workspace(p, Tc);
             if (workspace != nullptr && workspace_bytes >= need) {
                 counters = reinterpret_cast<unsigned*>(workspace);
                 partial = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + align256(p.tiles * 4));
             } else {
                 p.splits = 1;
-                p.k_per_split = K;
+                p.chunks_per_split = (int)(K / p.kc);
+                if (p.resident) {
+                    p.lds_bytes = resident_lds(fmt, Tc, p.chunks_per_split, p.kc);
+                    p.resident = p.lds_bytes <= RESIDENT_LDS_MAX;
+                }
             }
         }
         const uint16_t* xc = x + t0 * K;
         void* yc = reinterpret_cast<char*>(y) + t0 * N * ybytes;
         switch (fmt) {
-            case W_FP8ROW: launch_fmt<W_FP8ROW>(p, w, scales, xc, Tc, N, K, bf16_out, yc, partial, counters, stream); break;
-            case W_MXFP8: launch_fmt<W_MXFP8>(p, w, scales, xc, Tc, N, K, bf16_out, yc, partial, counters, stream); break;
-            case W_BF16: launch_fmt<W_BF16>(p, w, scales, xc, Tc, N, K, bf16_out, yc, partial, counters, stream); break;
-            case W_Q8G64: launch_fmt<W_Q8G64>(p, w, scales, xc, Tc, N, K, bf16_out, yc, partial, counters, stream); break;
-            case W_Q4G64: launch_fmt<W_Q4G64>(p, w, scales, xc, Tc, N, K, bf16_out, yc, partial, counters, stream); break;
-            case W_Q8G32: launch_fmt<W_Q8G32>(p, w, scales, xc, Tc, N, K, bf16_out, yc, partial, counters, stream); break;
+            case W_FP8ROW: launch_fmt<W_FP8ROW>(p, packed, w, scales, xc, Tc, N, K, bf16_out, yc, partial, counters, stream); break;
+            case W_MXFP8: launch_fmt<W_MXFP8>(p, packed, w, scales, xc, Tc, N, K, bf16_out, yc, partial, counters, stream); break;
+            case W_BF16: launch_fmt<W_BF16>(p, packed, w, scales, xc, Tc, N, K, bf16_out, yc, partial, counters, stream); break;
+            case W_Q8G64: launch_fmt<W_Q8G64>(p, packed, w, scales, xc, Tc, N, K, bf16_out, yc, partial, counters, stream); break;
+            case W_Q4G64: launch_fmt<W_Q4G64>(p, packed, w, scales, xc, Tc, N, K, bf16_out, yc, partial, counters, stream); break;
+            case W_Q8G32: launch_fmt<W_Q8G32>(p, packed, w, scales, xc, Tc, N, K, bf16_out, yc, partial, counters, stream); break;
             default: return hipErrorInvalidValue;
         }
         hipError_t e = hipGetLastError();

@@ -25,9 +25,12 @@ hipError_t launch_quantize_fp8_row(const uint16_t* x, int64_t M, int64_t K, uint
 // array (row scales for W_FP8ROW).  `workspace` (may be NULL) enables split-K
 // across workgroups when it is large enough (gemv_workspace_bytes).
 int64_t gemv_workspace_bytes(int fmt, int64_t T, int64_t N, int64_t K);
+// `packed`: weights in the layout written by launch_pack_weights (requires K % 128 == 0).
 hipError_t launch_gemv(int fmt, const void* w, const void* scales, const uint16_t* x, int64_t T, int64_t N,
                        int64_t K, bool bf16_out, void* y, void* workspace, int64_t workspace_bytes,
-                       hipStream_t stream);
+                       hipStream_t stream, bool packed);
+int64_t packed_weight_bytes(int fmt, int64_t N, int64_t K);
+hipError_t launch_pack_weights(int fmt, const void* src, int64_t N, int64_t K, void* dst, hipStream_t stream);
 
 hipError_t launch_gemm_w8a8(const int8_t* a_q, const float* a_scale, const int8_t* w_q, const uint16_t* w_scale,
                             int64_t M, int64_t N, int64_t K, bool bf16_out, void* y, int32_t* group_sums,

@@ -36,6 +36,10 @@ SIGNATURES = {
     "nq_gemm_w8a8_g64": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P]),
     "nq_gemm_fp8row": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _I, _P, _P]),
     "nq_route": (_I, [_I64, _I]),
+    "nq_packed_weight_bytes": (_I64, [_I, _I64, _I64]),
+    "nq_pack_weights": (_I, [_I, _P, _I64, _I64, _P, _P]),
+    "nq_gemv_fp8row_packed": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I64, _P]),
+    "nq_gemv_qgroup_packed": (_I, [_I, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I64, _P]),
     "nq_linear_q8g64": (_I, [_P, _I64, _P, _P, _I64, _I64, _I, _P, _P, _I, _P, _P, _I64, _P]),
 }
 
@@ -200,3 +204,35 @@ def nq_linear_q8g64(x, T, w_q, w_scale, N, K, allow_a8, a_q_ws, a_scale_ws, y, w
     _check(lib().nq_linear_q8g64(_ptr(x), T, _ptr(w_q), _ptr(w_scale), N, K, 1 if allow_a8 else 0,
                                  _ptr(a_q_ws), _ptr(a_scale_ws), _out_dt(y), _ptr(y), wp, wb,
                                  _stream(x, w_q)), "nq_linear_q8g64")
+
+
+NQ_FMT_FP8ROW = -1     # the format code the packing calls use for row-scaled FP8
+
+
+def nq_packed_weight_bytes(fmt, N, K):
+    return lib().nq_packed_weight_bytes(fmt, N, K)
+
+
+def nq_pack_weights(fmt, w, N, K, w_packed):
+    code_bytes = 1 if fmt == NQ_FMT_FP8ROW else _CODE_BYTES.get(fmt, 1)
+    _size(w, N * K * code_bytes, "w")
+    _size(w_packed, nq_packed_weight_bytes(fmt, N, K), "w_packed")
+    _check(lib().nq_pack_weights(fmt, _ptr(w), N, K, _ptr(w_packed), _stream(w)), "nq_pack_weights")
+
+
+def nq_gemv_fp8row_packed(w_packed, w_scale, x, T, N, K, y, workspace=None):
+    _size(w_packed, nq_packed_weight_bytes(NQ_FMT_FP8ROW, N, K), "w_packed")
+    _size(w_scale, 2 * N, "w_scale"); _size(x, 2 * T * K, "x"); _size(y, T * N * y.element_size(), "y")
+    wp, wb = _ws(workspace)
+    _check(lib().nq_gemv_fp8row_packed(_ptr(w_packed), _ptr(w_scale), _ptr(x), T, N, K, _out_dt(y), _ptr(y),
+                                       wp, wb, _stream(w_packed, x)), "nq_gemv_fp8row_packed")
+
+
+def nq_gemv_qgroup_packed(fmt, w_packed, w_scales, x, T, N, K, y, workspace=None):
+    if fmt in _CODE_BYTES:
+        _size(w_packed, nq_packed_weight_bytes(fmt, N, K), "w_packed")
+        _size(w_scales, N * K * _SCALE_BYTES[fmt], "w_scales")
+    _size(x, 2 * T * K, "x"); _size(y, T * N * y.element_size(), "y")
+    wp, wb = _ws(workspace)
+    _check(lib().nq_gemv_qgroup_packed(fmt, _ptr(w_packed), _ptr(w_scales), _ptr(x), T, N, K, _out_dt(y),
+                                       _ptr(y), wp, wb, _stream(w_packed, x)), "nq_gemv_qgroup_packed")

@@ -480,6 +480,78 @@ def test_fp8_gemm_full_sampled():
     assert rel_fro(host(y, np.float32)[np.ix_(rows, cols)], ref) <= FP32_TOL
 
 
+# ---------------------------------------------------------------------------
+# Packed weight layout: a permutation of the row-major codes, and packed GEMVs
+# equal the row-major ones bit for bit.
+# ---------------------------------------------------------------------------
+
+PACK_FMTS = [(-1, 1.0, 16), (nq.NQ_W_Q8G64_F16S, 1.0, 16), (nq.NQ_W_MXFP8_G32, 1.0, 16),
+             (nq.NQ_W_Q4G64_F16S, 0.5, 8), (nq.NQ_W_Q8G32_F16S, 1.0, 8), (nq.NQ_W_BF16, 2.0, 16)]
+
+
+def _unpack_reference(packed, fmt, n, k):
+    """Invert the documented layout with numpy: rows in blocks of 16; per chunk
+    of KC columns, per row block, per piece q, the 64 lanes' pieces in lane
+    order; lane 16 g + i holds row i of the block and piece q of lane group g."""
+    kc = 256 if k % 256 == 0 else 128
+    row_bytes = {0.5: k // 2, 1.0: k, 2.0: 2 * k}[dict((f, b) for f, b, _ in PACK_FMTS)[fmt]]
+    pb = dict((f, p) for f, _, p in PACK_FMTS)[fmt]
+    chunk_bytes = row_bytes * kc // k                       # bytes of one row per chunk
+    np_ = chunk_bytes // (4 * pb)                           # pieces per lane per chunk
+    nrb = -(-n // 16)
+    out = np.zeros((nrb * 16, row_bytes), np.uint8)
+    v = packed.reshape(k // kc, nrb, np_, 64, pb)
+    for g in range(4):
+        for q in range(np_):
+            off = 64 * q + 16 * g if pb == 16 else 32 * q + 8 * g
+            for c in range(k // kc):
+                base = c * chunk_bytes + off
+                out[:, base:base + pb] = v[c, :, q, 16 * g:16 * g + 16, :].reshape(nrb * 16, pb)
+    return out[:n]
+
+
+@pytest.mark.parametrize("fmt,bpe,pb", PACK_FMTS)
+@pytest.mark.parametrize("n,k", [(70, 384), (33, 512), (16, 128)])
+def test_pack_is_the_documented_permutation(fmt, bpe, pb, n, k):
+    nbytes = int(n * k * bpe)
+    src = W.rng(110, n + k).integers(0, 256, nbytes, dtype=np.int16).astype(np.uint8)
+    pk = empty((nq.nq_packed_weight_bytes(fmt, n, k),), np.uint8)
+    nq.nq_pack_weights(fmt, dev(src), n, k, pk)
+    back = _unpack_reference(host(pk, np.uint8), fmt, n, k)
+    assert np.array_equal(back.reshape(-1), src)
+    # padding rows of the last block are zero
+    assert nq.nq_packed_weight_bytes(fmt, n, k) == -(-n // 16) * 16 * int(k * bpe)
+
+
+@pytest.mark.parametrize("name,fmt", [("fp8row", -1)] + GROUP_FMTS)
+@pytest.mark.parametrize("n,k", [(1000, 1536), (200, 1408)])
+@pytest.mark.parametrize("t", [1, 16, 33])
+def test_gemv_packed_equals_row_major(name, fmt, n, k, t):
+    if name == "fp8row":
+        w = W.bf16_normal(W.rng(111, n + k), (n, k), std=0.02)
+        codes, scales = M.encode_fp8row_bf16(w)
+        ref = M.gemv_fp8row(codes, scales, W.bf16_normal(W.rng(112, t + k), (t, k)))
+    else:
+        codes, scales = _grouped_inputs(name, n, k, n + k + t)
+        ref = M.gemv_qgroup(name, codes, scales, W.bf16_normal(W.rng(112, t + k), (t, k)))
+    x = W.bf16_normal(W.rng(112, t + k), (t, k))
+    cd = dev(codes)
+    sd = dev(scales) if scales is not None else None
+    pk = empty((nq.nq_packed_weight_bytes(fmt, n, k),), np.uint8)
+    nq.nq_pack_weights(fmt, cd, n, k, pk)
+    wsp = nq.alloc_gemv_workspace(fmt, t, n, k, DEV)
+    y_row, y_pk = empty((t, n), np.float32), empty((t, n), np.float32)
+    if name == "fp8row":
+        nq.nq_gemv_fp8row(cd, sd, dev(x), t, n, k, y_row, wsp)
+        nq.nq_gemv_fp8row_packed(pk, sd, dev(x), t, n, k, y_pk, wsp)
+    else:
+        nq.nq_gemv_qgroup(fmt, cd, sd, dev(x), t, n, k, y_row, wsp)
+        nq.nq_gemv_qgroup_packed(fmt, pk, sd, dev(x), t, n, k, y_pk, wsp)
+    a, b = host(y_row, np.uint32), host(y_pk, np.uint32)
+    assert np.array_equal(a, b)
+    assert rel_fro(b.view(np.float32), ref) <= FP32_TOL
+
+
 @pytest.mark.parametrize("t", [1, 33, 128, 129, 300])
 def test_linear_route(t):
     n, k = 200, 640
