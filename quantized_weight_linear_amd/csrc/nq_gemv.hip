@@ -435,12 +435,14 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint8_t* __restric
 // Resident-activation variant: when the workgroup's activation slice
 // [T][k range] (and its rows' group scales) fits in LDS, it is staged once and
 // the waves then stream weights with no barrier at all, each with its own
-// register ring (deeper than above: nothing else is in flight).  B fragments of
-// tokens t >= T read a zero row.
+// register ring of 3 chunks (4 for MXFP8, whose scale loads are small).  Deeper
+// rings were measured slower: more bytes in flight per wave only lengthens the
+// memory queues and spreads the waves' finishing times.  B fragments of tokens
+// t >= T read a zero row.
 // ---------------------------------------------------------------------------
 template <int FMT>
 constexpr int depth_resident() {
-    return FMT == W_BF16 ? 3 : (FMT == W_Q4G64 ? 8 : (FMT == W_MXFP8 ? 4 : 5));
+    return FMT == W_MXFP8 ? 4 : 3;
 }
 
 template <int FMT, int NCB, int KC, bool PK>
@@ -782,6 +784,9 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K) {
             return p;
         }
     }
+    // streaming variant: once the row tiles alone cover every CU, splitting K
+    // only adds workgroups that compete for LDS bandwidth plus the partial exchange
+    if (p.tiles >= (int64_t)device_cu_count()) s0 = 1;
     const int64_t cps = (chunks + s0 - 1) / s0;
     p.chunks_per_split = (int)cps;
     p.splits = (int)((chunks + cps - 1) / cps);
