@@ -37,9 +37,14 @@ def hipcc():
     raise RuntimeError("hipcc not found (ROCm is required to build libnq.so)")
 
 
+# Per-source additions.  The GEMM keeps its MFMA results in ordinary VGPRs,
+# where the FP32 rescale reads them directly (no copy out of AGPRs per element).
+EXTRA = {"nq_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + FLAGS + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

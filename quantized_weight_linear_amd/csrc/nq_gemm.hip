@@ -1,109 +1,153 @@
 // Prefill GEMMs on CDNA4 MFMA: y[m][n] = sum_k A[m][k] * W[n][k] with
-// int8 x int8 (W8A8, per-64-group FP32 rescale) or E4M3 x E4M3 (row scales).
+// int8 x int8 codes (W8A8, FP32 rescale per 64-channel group) or E4M3 x E4M3
+// codes (one scale per token and one per weight row).
 //
-// Tiling: a workgroup of 4 waves computes a 128 (tokens) x 128 (weight rows)
-// block; each wave a 64 x 64 quadrant as 2 x 2 tiles of 32 x 32 MFMA output.
-// A and W panels of one K step are staged in LDS (rows padded by 16 bytes),
-// the next step's panels are prefetched into registers while the current
-// step computes.
+// Tiling.  A workgroup of 4 waves computes a 128 (tokens) x 128 (weight rows)
+// tile; each wave a 64 x 64 quadrant as 2 x 2 MFMA tiles of 32 x 32.
 //
-// W8A8 (one K step = one 64-channel scale group): two v_mfma_i32_32x32x32_i8
-// per tile sum the group exactly in int32.  The MFMA's C operand is the
+// Staging.  Codes go from memory straight into LDS with buffer loads in LDS
+// mode (no VGPR round trip, no VALU work): one load instruction of a wave
+// writes 1 KB of LDS in lane order, and each lane fetches the 16 bytes that
+// the MFMA fragment read of the same lane wants, so a fragment read is a
+// contiguous, conflict-free ds_read.  One stage holds 64 K-columns of both
+// panels (plus, for W8A8, the group's activation and weight scales); a ring of
+// 4 stages keeps 3 stages in flight while one is consumed, with one barrier
+// per stage.  Rows past M / N and columns past K are out of the buffer range
+// and read as zero.
+//
+// W8A8 (one stage = one 64-channel group): two v_mfma_i32_32x32x32_i8 per
+// tile sum the group exactly in int32.  The first MFMA's C operand is the
 // constant 0x4B400000 (the float 1.5 * 2^23), so the int32 result D = C + P
 // read as a float is exactly 12582912 + P for |P| < 2^22 (here |P| <= 64 *
-// 127^2).  The rescale is then two FP32 FMAs per element:
+// 128^2).  The rescale is then two FP32 FMAs per element:
 //     X   = fma(float(D), ws, -12582912 * ws)   -> P * ws rounded once
 //     acc = fma(X, as, acc)
-// (-12582912 * ws is exact: ws is FP16, 11 significant bits).
+// (-12582912 * ws is exact: ws is FP16, 11 significant bits).  Those two
+// FMAs per output element and group are the kernel's floor on this part:
+// 2 * M * N * K / 64 FP32 FMAs on the vector ALUs, about twice the int8 MFMA
+// time, so the MFMAs of one wave overlap the rescale of another.
 //
-// FP8 (one K step = 128 channels): v_mfma_f32_32x32x64_f8f6f4 on E4M3 codes,
-// FP32 accumulation over all K; y = acc * a_scale[m] * w_scale[n] at the end.
+// FP8: E4M3 codes are decoded exactly to BF16 (the hardware convert, scale 1)
+// after the fragment read and multiplied with v_mfma_f32_32x32x16_bf16: every
+// product of two E4M3 values is exact and the sums are FP32.  The native FP8
+// MFMA is not used: its dot products are not FP32-accurate (relative errors of
+// a few 1e-5 were measured on one instruction), outside this path's 1e-5
+// bound.  y = (acc * a_scale[m]) * w_scale[n] at the end.
 #include "nq_device.h"
 #include "nq_launch.h"
 
+// m0 is written by the LDS-mode loads below; nothing else in this file uses it.
+#pragma clang diagnostic ignored "-Winline-asm"
+
 namespace nq {
 
-constexpr int GM_BM = 128;
-constexpr int GM_BN = 128;
+constexpr int GB_M = 128;    // tokens per workgroup tile
+constexpr int GB_N = 128;    // weight rows per workgroup tile
+constexpr int GB_K = 64;     // K columns (bytes) per stage
+constexpr int GB_S = 4;      // stages in the LDS ring
 
-template <int BK>
-struct GemmSmem {
-    static constexpr int PITCH = BK + 16;   // bytes per LDS row
-    uint8_t a[GM_BM * PITCH];
-    uint8_t b[GM_BN * PITCH];
+struct GemmStage {
+    uint8_t a[GB_M * GB_K];  // 8 fragment blocks of 1 KB: block (row tile i4, pair p)
+    uint8_t b[GB_N * GB_K];
+    float as[GB_M];          // W8A8: activation scales of the stage's group
+    uint32_t ws[GB_N];       // W8A8: weight scales of the stage's group (FP16 bits, zero-extended:
+                             // a 2-byte load in LDS mode still writes 4 bytes per lane)
 };
+
+constexpr unsigned GB_FLAGS = 0x00020000u;
+constexpr int GB_OOB = 0x40000000;   // a buffer offset past every range used here
 
 // 32x32 MFMA output layout: lane l holds column (l % 32) and rows
 // 8 j + 4 (l / 32) + r for j, r in 0..3 (element 4 j + r).
 __device__ __forceinline__ int d_row(int lane, int e) { return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
 
-template <bool W8A8>
+// Buffer descriptor (base, no stride, num_records bytes): offsets at or past
+// num_records read as zero.
+__device__ __forceinline__ v4u buffer_desc(const void* base, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    v4u d;
+    d.x = (uint32_t)b;
+    d.y = (uint32_t)(b >> 32) & 0xFFFFu;
+    d.z = bytes;
+    d.w = GB_FLAGS;
+    return d;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// One buffer load in LDS mode: lane i's SIZE bytes from desc + voff land at
+// LDS address m0 + max(SIZE, 4) * i (sub-dword loads write a zero-extended
+// dword per lane).  Written as inline assembly so that the compiler
+// does not pair these loads with the LDS reads that follow them (it would
+// wait for every one still in flight); the ring below waits for exactly the
+// stage it consumes.  The instruction has no register result.
+template <int SIZE>
+__device__ __forceinline__ void lds_dma(v4u desc, uint32_t lds, int voff) {
+    if constexpr (SIZE == 16)
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :: "v"(voff), "s"(desc), "s"(lds) : "memory", "m0");
+    else if constexpr (SIZE == 4)
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                     :: "v"(voff), "s"(desc), "s"(lds) : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_ushort %0, %1, 0 offen lds"
+                     :: "v"(voff), "s"(desc), "s"(lds) : "memory", "m0");
+}
+
+template <bool W8A8, bool SUMS, bool KTAIL>
 __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A, const float* __restrict__ a_scale,
                                                    const uint8_t* __restrict__ W,
-                                                   const uint16_t* __restrict__ w_scale, int M, int N, int64_t K,
+                                                   const uint16_t* __restrict__ w_scale, int M, int N, int K,
                                                    int bf16_out, void* __restrict__ y,
                                                    int32_t* __restrict__ group_sums) {
-    constexpr int BK = W8A8 ? 64 : 128;
-    constexpr int PITCH = GemmSmem<BK>::PITCH;
-    constexpr int CHUNKS = BK / 16;                    // 16-byte pieces per panel row
-    constexpr int LOADS = GM_BM * CHUNKS / 256;        // 16-byte loads per thread per panel
-    __shared__ __attribute__((aligned(16))) GemmSmem<BK> sm;
-    __shared__ __attribute__((aligned(16))) float s_as[W8A8 ? GM_BM : 1];
-    __shared__ __attribute__((aligned(16))) float s_ws[W8A8 ? 2 * GM_BN : 1];
+    constexpr int DMA_PER_STAGE = W8A8 ? 5 : 4;   // load instructions per wave and stage
+    __shared__ __attribute__((aligned(16))) GemmStage st[GB_S];
+    __shared__ float s_rs[W8A8 ? 1 : GB_M + GB_N];     // FP8: token scales, then weight-row scales
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wv = tid >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches, SGPR resources
     const int wm = wv & 1, wn = wv >> 1;
-    const int64_t m0 = (int64_t)blockIdx.y * GM_BM;
-    const int64_t n0 = (int64_t)blockIdx.x * GM_BN;
-    const int64_t nsteps = (K + BK - 1) / BK;
-    const int64_t G = K / 64;
+    const int m0 = blockIdx.y * GB_M;
+    const int n0 = blockIdx.x * GB_N;
+    const int G = K >> 6;
+    const int nsteps = (K + GB_K - 1) / GB_K;
+    const int rows_a = min(M - m0, GB_M);
+    const int rows_b = min(N - n0, GB_N);
 
-    // register prefetch of one K step
-    uint4 ra[LOADS], rb[LOADS];
-    float r_as = 0.f, r_ws = 0.f;
-    auto load_step = [&](int64_t s) {
-        const int64_t k0 = s * BK;
+    // Buffer ranges start at the tile: rows past M / N fall outside them.
+    const v4u ra = buffer_desc(A + (int64_t)m0 * K, (uint32_t)(rows_a * K));
+    const v4u rb = buffer_desc(W + (int64_t)n0 * K, (uint32_t)(rows_b * K));
+    v4u rs = ra;
+    if constexpr (W8A8) {
+        if (wv < 2) rs = buffer_desc(a_scale + (int64_t)m0 * G, (uint32_t)(rows_a * G * 4));
+        else rs = buffer_desc(w_scale + (int64_t)n0 * G, (uint32_t)(rows_b * G * 2));
+    }
+
+    // Loader lanes: wave wv fills fragment blocks (i4 = wv, p = 0, 1) of both
+    // panels; lane L fetches row 32 wv + L % 32, columns k0 + 32 p + 16 (L / 32) + [0, 16).
+    const int lrow = 32 * wv + (lane & 31);
+    const int lk = 16 * (lane >> 5);
+    const int voff_ab = lrow * K + lk;
+    const int voff_s = W8A8 ? (wv < 2 ? (64 * wv + lane) * G * 4 : (64 * (wv - 2) + lane) * G * 2) : 0;
+
+    auto issue = [&](GemmStage& S, int s) {
+        const int k0 = s < nsteps ? s * GB_K : GB_OOB;   // stages past the end load nothing
 #pragma unroll
-        for (int j = 0; j < LOADS; ++j) {
-            const int idx = tid + 256 * j;
-            const int r = idx / CHUNKS, c = idx % CHUNKS;
-            const int64_t k = k0 + 16 * c;
-            int64_t am = m0 + r; if (am >= M) am = M - 1;
-            int64_t bn = n0 + r; if (bn >= N) bn = N - 1;
-            if (k < K) {
-                ra[j] = *reinterpret_cast<const uint4*>(A + am * K + k);
-                rb[j] = ld_nt16(W + bn * K + k);
-            } else {
-                ra[j] = make_uint4(0, 0, 0, 0);
-                rb[j] = make_uint4(0, 0, 0, 0);
+        for (int p = 0; p < 2; ++p) {
+            int vo = voff_ab + k0 + 32 * p;
+            if constexpr (KTAIL) {
+                if (k0 + 32 * p + lk >= K) vo = GB_OOB;      // K % 16 == 0: pieces are whole
             }
+            lds_dma<16>(ra, lds_addr(&S.a[(2 * wv + p) * 1024]), vo);
+            lds_dma<16>(rb, lds_addr(&S.b[(2 * wv + p) * 1024]), vo);
         }
         if constexpr (W8A8) {
-            if (tid < GM_BM) {
-                int64_t am = m0 + tid; if (am >= M) am = M - 1;
-                r_as = a_scale[am * G + s];
-            } else {
-                int64_t bn = n0 + (tid - GM_BM); if (bn >= N) bn = N - 1;
-                r_ws = f16_bits_to_f32(w_scale[bn * G + s]);
-            }
-        }
-    };
-    auto store_step = [&]() {
-#pragma unroll
-        for (int j = 0; j < LOADS; ++j) {
-            const int idx = tid + 256 * j;
-            const int r = idx / CHUNKS, c = idx % CHUNKS;
-            *reinterpret_cast<uint4*>(&sm.a[r * PITCH + 16 * c]) = ra[j];
-            *reinterpret_cast<uint4*>(&sm.b[r * PITCH + 16 * c]) = rb[j];
-        }
-        if constexpr (W8A8) {
-            if (tid < GM_BM) s_as[tid] = r_as;
-            else {
-                s_ws[2 * (tid - GM_BM)] = r_ws;
-                s_ws[2 * (tid - GM_BM) + 1] = -12582912.0f * r_ws;
-            }
+            const int g = s < nsteps ? s : GB_OOB / 8;
+            if (wv < 2) lds_dma<4>(rs, lds_addr(&S.as[64 * wv]), voff_s + 4 * g);
+            else lds_dma<2>(rs, lds_addr(&S.ws[64 * (wv - 2)]), voff_s + 2 * g);
         }
     };
 
@@ -115,15 +159,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    const int fr = lane & 31;       // fragment row (A) / column (B) within a 32 tile
-    const int fk = lane >> 5;       // k half of the fragment
-
-    if (nsteps > 0) load_step(0);
-    for (int64_t s = 0; s < nsteps; ++s) {
-        __syncthreads();
-        store_step();
-        __syncthreads();
-        if (s + 1 < nsteps) load_step(s + 1);
+    auto compute = [&](const GemmStage& S, int s) {
         if constexpr (W8A8) {
             const v16i bias = {0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000,
                                0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000,
@@ -134,100 +170,159 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
                 v4i af[2], bf[2];
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
-                    af[i] = *reinterpret_cast<const v4i*>(&sm.a[(wm * 64 + 32 * i + fr) * PITCH + 32 * h + 16 * fk]);
+                    af[i] = *reinterpret_cast<const v4i*>(&S.a[((2 * wm + i) * 2 + h) * 1024 + 16 * lane]);
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    bf[j] = *reinterpret_cast<const v4i*>(&sm.b[(wn * 64 + 32 * j + fr) * PITCH + 32 * h + 16 * fk]);
+                    bf[j] = *reinterpret_cast<const v4i*>(&S.b[((2 * wn + j) * 2 + h) * 1024 + 16 * lane]);
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
                         d[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], h == 0 ? bias : d[i][j], 0, 0, 0);
             }
+            float wsf[2], wsc[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const float2 wsp = *reinterpret_cast<const float2*>(&s_ws[2 * (wn * 64 + 32 * j + fr)]);
+                wsf[j] = f16_bits_to_f32(S.ws[64 * wn + 32 * j + (lane & 31)] & 0xFFFFu);
+                wsc[j] = -12582912.0f * wsf[j];
+            }
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < 2; ++i) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const v4f as4 = *reinterpret_cast<const v4f*>(&s_as[wm * 64 + 32 * i + 8 * q + 4 * fk]);
+                for (int q = 0; q < 4; ++q) {
+                    const v4f as4 = *reinterpret_cast<const v4f*>(&S.as[64 * wm + 32 * i + 8 * q + 4 * (lane >> 5)]);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int e = 4 * q + r;
-                            const float X = fmaf(__int_as_float(d[i][j][e]), wsp.x, wsp.y);
+                            const float X = fmaf(__int_as_float(d[i][j][e]), wsf[j], wsc[j]);
                             acc[i][j][e] = fmaf(X, as4[r], acc[i][j][e]);
                         }
-                    }
-                    if (group_sums != nullptr) {
-                        const int64_t n = n0 + wn * 64 + 32 * j + fr;
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) {
-                            const int64_t m = m0 + wm * 64 + 32 * i + d_row(lane, e);
-                            if (m < M && n < N) group_sums[(m * N + n) * G + s] = d[i][j][e] - 0x4B400000;
-                        }
-                    }
                 }
             }
-        } else {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                v8i af[2], bf[2];
+            if constexpr (SUMS) {
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
-                    af[i] = *reinterpret_cast<const v8i*>(&sm.a[(wm * 64 + 32 * i + fr) * PITCH + 64 * h + 32 * fk]);
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    bf[j] = *reinterpret_cast<const v8i*>(&sm.b[(wn * 64 + 32 * j + fr) * PITCH + 64 * h + 32 * fk]);
+                    for (int j = 0; j < 2; ++j) {
+                        const int n = n0 + 64 * wn + 32 * j + (lane & 31);
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            const int m = m0 + 64 * wm + 32 * i + d_row(lane, e);
+                            if (m < M && n < N) group_sums[((int64_t)m * N + n) * G + s] = d[i][j][e] - 0x4B400000;
+                        }
+                    }
+                // the ring's wait counts only loads: drain these stores here
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+        } else {
+            (void)s;
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const int off = (s4 >> 1) * 1024 + (s4 & 1) * 512 + 16 * (lane & 31) + 8 * (lane >> 5);
+                v8bf af[2], bf[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const uint2 c = *reinterpret_cast<const uint2*>(&S.a[(2 * wm + i) * 2048 + off]);
+                    af[i] = __builtin_bit_cast(v8bf, make_uint4(e4m3x2_to_bf16x2<false>(c.x, 1.0f),
+                                                                e4m3x2_to_bf16x2<true>(c.x, 1.0f),
+                                                                e4m3x2_to_bf16x2<false>(c.y, 1.0f),
+                                                                e4m3x2_to_bf16x2<true>(c.y, 1.0f)));
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const uint2 c = *reinterpret_cast<const uint2*>(&S.b[(2 * wn + j) * 2048 + off]);
+                    bf[j] = __builtin_bit_cast(v8bf, make_uint4(e4m3x2_to_bf16x2<false>(c.x, 1.0f),
+                                                                e4m3x2_to_bf16x2<true>(c.x, 1.0f),
+                                                                e4m3x2_to_bf16x2<false>(c.y, 1.0f),
+                                                                e4m3x2_to_bf16x2<true>(c.y, 1.0f)));
+                }
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0,
-                                                                                   0, 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
             }
         }
-    }
+    };
 
-    // epilogue: write y
+    // Ring: stage s lives in buffer s % GB_S.  Before consuming stage s this
+    // wave waits for its own loads of stage s (the GB_S - 2 later stages may
+    // stay in flight), then the barrier makes every wave's loads visible and
+    // guarantees that buffer (s - 1) % GB_S, refilled next, is no longer read.
+#pragma unroll
+    for (int s = 0; s < GB_S - 1; ++s) issue(st[s], s);
+    if constexpr (!W8A8) {
+        const float v = tid < GB_M ? (tid < rows_a ? a_scale[m0 + tid] : 0.f)
+                                   : (tid - GB_M < rows_b ? bf16_bits_to_f32(w_scale[n0 + tid - GB_M]) : 0.f);
+        s_rs[tid] = v;
+        __syncthreads();
+    }
+    for (int s = 0; s < nsteps; ++s) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_PER_STAGE * (GB_S - 2)) : "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue(st[(s + GB_S - 1) & (GB_S - 1)], s + GB_S - 1);
+        compute(st[s & (GB_S - 1)], s);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the empty tail loads
+
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int64_t n = n0 + wn * 64 + 32 * j + fr;
+            const int n = n0 + 64 * wn + 32 * j + (lane & 31);
             if (n >= N) continue;
             float sw = 1.0f;
-            if constexpr (!W8A8) sw = bf16_bits_to_f32(w_scale[n]);
+            if constexpr (!W8A8) sw = s_rs[GB_M + 64 * wn + 32 * j + (lane & 31)];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t m = m0 + wm * 64 + 32 * i + d_row(lane, e);
+                const int ml = 64 * wm + 32 * i + d_row(lane, e);
+                const int m = m0 + ml;
                 if (m >= M) continue;
                 float v = acc[i][j][e];
-                if constexpr (!W8A8) v = (v * a_scale[m]) * sw;
-                if (bf16_out) reinterpret_cast<uint16_t*>(y)[m * N + n] = (uint16_t)f32_to_bf16_rne(v);
-                else reinterpret_cast<float*>(y)[m * N + n] = v;
+                if constexpr (!W8A8) v = (v * s_rs[ml]) * sw;
+                if (bf16_out) reinterpret_cast<uint16_t*>(y)[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v);
+                else reinterpret_cast<float*>(y)[(int64_t)m * N + n] = v;
             }
         }
+}
+
+template <bool W8A8, bool SUMS, bool KTAIL>
+static hipError_t launch_gemm_t(const uint8_t* A, const float* a_scale, const uint8_t* W, const uint16_t* w_scale,
+                                int64_t M, int64_t N, int64_t K, bool bf16_out, void* y, int32_t* sums,
+                                hipStream_t stream) {
+    dim3 grid((unsigned)((N + GB_N - 1) / GB_N), (unsigned)((M + GB_M - 1) / GB_M));
+    gemm_kernel<W8A8, SUMS, KTAIL><<<grid, 256, 0, stream>>>(A, a_scale, W, w_scale, (int)M, (int)N, (int)K,
+                                                             bf16_out ? 1 : 0, y, sums);
+    return hipGetLastError();
+}
+
+// Offsets inside a tile are 32-bit: 128 rows x K bytes, and the scale rows.
+static bool gemm_shape_ok(int64_t M, int64_t N, int64_t K) {
+    return M < ((int64_t)1 << 31) && N < ((int64_t)1 << 31) && (int64_t)GB_M * K * 4 < ((int64_t)1 << 30);
 }
 
 hipError_t launch_gemm_w8a8(const int8_t* a_q, const float* a_scale, const int8_t* w_q, const uint16_t* w_scale,
                             int64_t M, int64_t N, int64_t K, bool bf16_out, void* y, int32_t* group_sums,
                             hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
-    dim3 grid((unsigned)((N + GM_BN - 1) / GM_BN), (unsigned)((M + GM_BM - 1) / GM_BM));
-    gemm_kernel<true><<<grid, 256, 0, stream>>>(reinterpret_cast<const uint8_t*>(a_q), a_scale,
-                                                reinterpret_cast<const uint8_t*>(w_q), w_scale, (int)M, (int)N, K,
-                                                bf16_out ? 1 : 0, y, group_sums);
-    return hipGetLastError();
+    if (!gemm_shape_ok(M, N, K) || K % 64 != 0) return hipErrorInvalidValue;
+    const uint8_t* A = reinterpret_cast<const uint8_t*>(a_q);
+    const uint8_t* W = reinterpret_cast<const uint8_t*>(w_q);
+    if (group_sums != nullptr)
+        return launch_gemm_t<true, true, false>(A, a_scale, W, w_scale, M, N, K, bf16_out, y, group_sums, stream);
+    return launch_gemm_t<true, false, false>(A, a_scale, W, w_scale, M, N, K, bf16_out, y, nullptr, stream);
 }
 
 hipError_t launch_gemm_fp8(const uint8_t* a_codes, const float* a_scale, const uint8_t* w, const uint16_t* w_scale,
                            int64_t M, int64_t N, int64_t K, bool bf16_out, void* y, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
-    dim3 grid((unsigned)((N + GM_BN - 1) / GM_BN), (unsigned)((M + GM_BM - 1) / GM_BM));
-    gemm_kernel<false><<<grid, 256, 0, stream>>>(a_codes, a_scale, w, w_scale, (int)M, (int)N, K,
-                                                 bf16_out ? 1 : 0, y, nullptr);
-    return hipGetLastError();
+    if (!gemm_shape_ok(M, N, K) || K % 16 != 0) return hipErrorInvalidValue;
+    if (K % GB_K == 0)
+        return launch_gemm_t<false, false, false>(a_codes, a_scale, w, w_scale, M, N, K, bf16_out, y, nullptr, stream);
+    return launch_gemm_t<false, false, true>(a_codes, a_scale, w, w_scale, M, N, K, bf16_out, y, nullptr, stream);
 }
 
 }  // namespace nq
