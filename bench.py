@@ -31,6 +31,23 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+# HBM traffic of the headline GEMV launches (packed row-FP8 17408x5120), from
+# `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` runs of
+# `bench.py --rows gemv_fp8row`, in KiB per dispatch, scaled by the same
+# counters on `bench.py --calibrate-copy` (a 256 MiB copy reads FETCH_SIZE
+# 131083.5 KiB and writes WRITE_SIZE 262144 KiB: factors 1.99983 and 1.0).
+# Summaries: profiles/gemv_fp8row_17408x5120_hbm_traffic.md.  Valid only for
+# the GEMV source they were taken on (sha256 prefix of nq_gemv.hip).
+GEMV_TRAFFIC = {
+    "source_sha256_16": "41a20ae910f989a9",
+    "fetch_factor": 262144.0 / 131083.5,
+    "write_factor": 1.0,
+    "fetch_kib": {"gemv_fp8row_T1": 43699.0, "gemv_fp8row_T4": 44023.5, "gemv_fp8row_T16": 46085.6,
+                  "gemv_fp8row_T33": 44951.5},
+    "write_kib": {"gemv_fp8row_T1": 603.5, "gemv_fp8row_T4": 2337.5, "gemv_fp8row_T16": 13634.0,
+                  "gemv_fp8row_T33": 1122.0},
+}
+
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 FP8_PEAK_TFLOPS = 5000.0
@@ -50,7 +67,23 @@ def parse():
     p.add_argument("--rows", default="all", help="comma list of row groups to run (default: all)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--rows-json", default=None, help="also write per-row results to this file")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 256 MiB device copy 4 times: the reference for scaling the "
+                        "FETCH_SIZE / WRITE_SIZE counters to bytes")
     return p.parse_args()
+
+
+def calibrate_copy():
+    """A copy of known size for the HBM traffic counters: each launch reads and
+    writes exactly 256 MiB (torch's copy kernel, buffers far larger than L2)."""
+    torch = _torch()
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=DEV).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": 256 << 20, "launches": 4}), flush=True)
 
 
 class Row:
@@ -316,8 +349,25 @@ def cpu_baseline():
                       "T = 1, 4, 16, 33 once each; the oracle's weight encode is not timed"}
 
 
+def gemv_traffic(names):
+    """Measured HBM bytes per launch of the headline GEMV, or None when the
+    kernel source changed since the counters were taken."""
+    import hashlib
+    src = os.path.join(ROOT, "quantized_weight_linear_amd", "csrc", "nq_gemv.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    t = GEMV_TRAFFIC
+    if sha != t["source_sha256_16"] or any(n not in t["fetch_kib"] for n in names):
+        return None
+    return {n: round(1024 * (t["fetch_kib"][n] * t["fetch_factor"] + t["write_kib"][n] * t["write_factor"]))
+            for n in names}
+
+
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(how the path would shard is described in DESIGN.md)"}))
@@ -410,10 +460,17 @@ def main():
         sec = sum(sum(r.ms) * 1e-3 for r in head)
         gbs = byt / sec / 1e9
         line["value"] = round(gbs, 2)
+        per_launch = gemv_traffic([r.name for r in head])
+        traffic = None
+        if per_launch is not None:
+            # whole-job HBM bytes per launch, averaged like `achieved`
+            traffic = round(sum(per_launch[r.name] * len(r.ms) for r in head) / sum(len(r.ms) for r in head))
         line["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                            "kernel": "gemv_mfma_kernel, row-FP8 17408x5120, launches T=1,4,16,33",
+                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                            "kernel": "gemv_resident_kernel (T=1,4,16) / gemv_mfma_kernel (T=33), packed "
+                                      "row-FP8 17408x5120",
                             "bytes_per_launch": {r.name: r.work for r in head},
+                            "hbm_traffic_per_launch": per_launch,
                             "us_per_launch": {r.name: results[r.name]["us"] for r in head}}
     pre = {}
     for name in ("gemm_w8a8", "gemm_fp8"):

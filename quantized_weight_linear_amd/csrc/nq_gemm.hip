@@ -159,84 +159,104 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    auto compute = [&](const GemmStage& S, int s) {
-        if constexpr (W8A8) {
-            const v16i bias = {0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000,
-                               0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000,
-                               0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000};
-            v16i d[2][2];
+    // W8A8, MFMA part of one stage: d = 12582912 + P (as float bits) for the
+    // wave's 2 x 2 tiles.
+    auto mfma_i8 = [&](const GemmStage& S, v16i (&d)[2][2]) {
+        const v16i bias = {0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000,
+                           0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000,
+                           0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000};
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                v4i af[2], bf[2];
+        for (int h = 0; h < 2; ++h) {
+            v4i af[2], bf[2];
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    af[i] = *reinterpret_cast<const v4i*>(&S.a[((2 * wm + i) * 2 + h) * 1024 + 16 * lane]);
+            for (int i = 0; i < 2; ++i)
+                af[i] = *reinterpret_cast<const v4i*>(&S.a[((2 * wm + i) * 2 + h) * 1024 + 16 * lane]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bf[j] = *reinterpret_cast<const v4i*>(&S.b[((2 * wn + j) * 2 + h) * 1024 + 16 * lane]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    bf[j] = *reinterpret_cast<const v4i*>(&S.b[((2 * wn + j) * 2 + h) * 1024 + 16 * lane]);
+                    d[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], h == 0 ? bias : d[i][j], 0, 0, 0);
+        }
+    };
+
+    // W8A8, rescale part: acc += (P * ws) * as with the group's scales.
+    auto rescale = [&](const GemmStage& S, const v16i (&d)[2][2], int s) {
+        float wsf[2], wsc[2];
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 2; ++j) {
+            wsf[j] = f16_bits_to_f32(S.ws[64 * wn + 32 * j + (lane & 31)] & 0xFFFFu);
+            wsc[j] = -12582912.0f * wsf[j];
+        }
 #pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        d[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], h == 0 ? bias : d[i][j], 0, 0, 0);
-            }
-            float wsf[2], wsc[2];
+        for (int i = 0; i < 2; ++i) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                wsf[j] = f16_bits_to_f32(S.ws[64 * wn + 32 * j + (lane & 31)] & 0xFFFFu);
-                wsc[j] = -12582912.0f * wsf[j];
-            }
+            for (int q = 0; q < 4; ++q) {
+                const v4f as4 = *reinterpret_cast<const v4f*>(&S.as[64 * wm + 32 * i + 8 * q + 4 * (lane >> 5)]);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const v4f as4 = *reinterpret_cast<const v4f*>(&S.as[64 * wm + 32 * i + 8 * q + 4 * (lane >> 5)]);
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int e = 4 * q + r;
-                            const float X = fmaf(__int_as_float(d[i][j][e]), wsf[j], wsc[j]);
-                            acc[i][j][e] = fmaf(X, as4[r], acc[i][j][e]);
-                        }
-                }
-            }
-            if constexpr (SUMS) {
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int n = n0 + 64 * wn + 32 * j + (lane & 31);
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) {
-                            const int m = m0 + 64 * wm + 32 * i + d_row(lane, e);
-                            if (m < M && n < N) group_sums[((int64_t)m * N + n) * G + s] = d[i][j][e] - 0x4B400000;
-                        }
+                    for (int r = 0; r < 4; ++r) {
+                        const int e = 4 * q + r;
+                        const float X = fmaf(__int_as_float(d[i][j][e]), wsf[j], wsc[j]);
+                        acc[i][j][e] = fmaf(X, as4[r], acc[i][j][e]);
                     }
-                // the ring's wait counts only loads: drain these stores here
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
-        } else {
-            (void)s;
+        }
+        if constexpr (SUMS) {
 #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-                const int off = (s4 >> 1) * 1024 + (s4 & 1) * 512 + 16 * (lane & 31) + 8 * (lane >> 5);
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int n = n0 + 64 * wn + 32 * j + (lane & 31);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int m = m0 + 64 * wm + 32 * i + d_row(lane, e);
+                        if (m < M && n < N) group_sums[((int64_t)m * N + n) * G + s] = d[i][j][e] - 0x4B400000;
+                    }
+                }
+            // the ring's wait counts only loads: drain these stores here
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+    };
+
+    // FP8, one stage.  A fragment block holds, for lane L, 16 consecutive
+    // codes of one row (k = 32 p + 16 (L / 32) + [0, 16)); each lane reads its
+    // 16 bytes at once (a contiguous, conflict-free 1 KB per wave) and feeds
+    // bytes [0, 8) to one 32x32x16 MFMA and bytes [8, 16) to a second.  The
+    // first MFMA thus sums k in {32p + [0,8), 32p + 16 + [0,8)}, the second the
+    // other 16: the A and B fragments use the same lane -> k assignment, so
+    // the two MFMAs together form the exact dot product over the 32 columns.
+    auto compute_fp8 = [&](const GemmStage& S) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            uint4 ca[2], cb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                ca[i] = *reinterpret_cast<const uint4*>(&S.a[((2 * wm + i) * 2 + p) * 1024 + 16 * lane]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                cb[j] = *reinterpret_cast<const uint4*>(&S.b[((2 * wn + j) * 2 + p) * 1024 + 16 * lane]);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
                 v8bf af[2], bf[2];
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    const uint2 c = *reinterpret_cast<const uint2*>(&S.a[(2 * wm + i) * 2048 + off]);
-                    af[i] = __builtin_bit_cast(v8bf, make_uint4(e4m3x2_to_bf16x2<false>(c.x, 1.0f),
-                                                                e4m3x2_to_bf16x2<true>(c.x, 1.0f),
-                                                                e4m3x2_to_bf16x2<false>(c.y, 1.0f),
-                                                                e4m3x2_to_bf16x2<true>(c.y, 1.0f)));
+                    const uint32_t w0 = hh ? ca[i].z : ca[i].x, w1 = hh ? ca[i].w : ca[i].y;
+                    af[i] = __builtin_bit_cast(v8bf, make_uint4(e4m3x2_to_bf16x2<false>(w0, 1.0f),
+                                                                e4m3x2_to_bf16x2<true>(w0, 1.0f),
+                                                                e4m3x2_to_bf16x2<false>(w1, 1.0f),
+                                                                e4m3x2_to_bf16x2<true>(w1, 1.0f)));
                 }
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const uint2 c = *reinterpret_cast<const uint2*>(&S.b[(2 * wn + j) * 2048 + off]);
-                    bf[j] = __builtin_bit_cast(v8bf, make_uint4(e4m3x2_to_bf16x2<false>(c.x, 1.0f),
-                                                                e4m3x2_to_bf16x2<true>(c.x, 1.0f),
-                                                                e4m3x2_to_bf16x2<false>(c.y, 1.0f),
-                                                                e4m3x2_to_bf16x2<true>(c.y, 1.0f)));
+                    const uint32_t w0 = hh ? cb[j].z : cb[j].x, w1 = hh ? cb[j].w : cb[j].y;
+                    bf[j] = __builtin_bit_cast(v8bf, make_uint4(e4m3x2_to_bf16x2<false>(w0, 1.0f),
+                                                                e4m3x2_to_bf16x2<true>(w0, 1.0f),
+                                                                e4m3x2_to_bf16x2<false>(w1, 1.0f),
+                                                                e4m3x2_to_bf16x2<true>(w1, 1.0f)));
                 }
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
@@ -247,10 +267,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
         }
     };
 
-    // Ring: stage s lives in buffer s % GB_S.  Before consuming stage s this
-    // wave waits for its own loads of stage s (the GB_S - 2 later stages may
-    // stay in flight), then the barrier makes every wave's loads visible and
-    // guarantees that buffer (s - 1) % GB_S, refilled next, is no longer read.
+    auto sync_stage = [&]() {
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
 #pragma unroll
     for (int s = 0; s < GB_S - 1; ++s) issue(st[s], s);
     if constexpr (!W8A8) {
@@ -259,12 +280,44 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
         s_rs[tid] = v;
         __syncthreads();
     }
-    for (int s = 0; s < nsteps; ++s) {
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_PER_STAGE * (GB_S - 2)) : "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        issue(st[(s + GB_S - 1) & (GB_S - 1)], s + GB_S - 1);
-        compute(st[s & (GB_S - 1)], s);
+
+    if constexpr (W8A8) {
+        // Software pipeline: iteration s issues stage s + 1's MFMAs and then
+        // rescales stage s, whose MFMAs were issued one iteration earlier, so
+        // the matrix unit and the vector ALU of a wave work side by side.
+        // Buffers: MFMA(s + 1) reads stage s + 1, the rescale reads stage s's
+        // scales, and the refill of iteration s (stage s + 3) goes into the
+        // buffer of stage s - 1, which the barrier shows nobody reads any more.
+        // Stage s + 1 must have landed: only stage s + 2 may still be in flight.
+        v16i d0[2][2], d1[2][2];
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_PER_STAGE * 2) : "memory");
+        sync_stage();
+        if (nsteps > 0) mfma_i8(st[0], d0);
+        for (int s = 0; s < nsteps; s += 2) {
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_PER_STAGE) : "memory");
+            sync_stage();
+            issue(st[(s + 3) & (GB_S - 1)], s + 3);
+            if (s + 1 < nsteps) mfma_i8(st[(s + 1) & (GB_S - 1)], d1);
+            rescale(st[s & (GB_S - 1)], d0, s);
+            if (s + 1 < nsteps) {
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_PER_STAGE) : "memory");
+                sync_stage();
+                issue(st[(s + 4) & (GB_S - 1)], s + 4);
+                if (s + 2 < nsteps) mfma_i8(st[(s + 2) & (GB_S - 1)], d0);
+                rescale(st[(s + 1) & (GB_S - 1)], d1, s + 1);
+            }
+        }
+    } else {
+        // Ring: before consuming stage s this wave waits for its own loads of
+        // stage s (the GB_S - 2 later stages may stay in flight); the barrier
+        // makes every wave's loads visible and shows that buffer (s - 1) %
+        // GB_S, refilled next, is no longer read.
+        for (int s = 0; s < nsteps; ++s) {
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_PER_STAGE * (GB_S - 2)) : "memory");
+            sync_stage();
+            issue(st[(s + GB_S - 1) & (GB_S - 1)], s + GB_S - 1);
+            compute_fp8(st[s & (GB_S - 1)]);
+        }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the empty tail loads
 
