@@ -176,10 +176,12 @@ int64_t nq_gemv_workspace_bytes(int fmt, int64_t T, int64_t N, int64_t K);
  * Packed weight layout for the decode GEMVs.  A one-time permutation of a
  * row-major weight matrix (codes only; scales stay as they are) into the
  * order in which the GEMV kernels stream it: rows in blocks of 16 (the last
- * block zero-padded); chunk-major: for every chunk of KC columns (KC = 256
- * when K % 256 == 0, else 128), for every row block, for every 8- or 16-byte
- * piece of the chunk, the pieces of all 64 lanes of a wavefront stored
- * contiguously (lane 16 g + i holds row i of the block, lane group g).  Every
+ * block zero-padded); chunk-major: for every chunk of 256 columns, for every
+ * row block, for every 8- or 16-byte piece of the chunk, the pieces of all 64
+ * lanes of a wavefront stored contiguously (lane 16 g + i holds row i of the
+ * block, lane group g).  Pieces per row and chunk: FP8 / MXFP8 / Q8G64 four
+ * of 16 B (64 columns each, lane group g at byte 16 g), Q4G64 four of 8 B,
+ * Q8G32 eight of 8 B (32 columns, byte 8 g), BF16 eight of 16 B.  Every
  * load instruction of the GEMV reads a contiguous 512 B or 1 KiB, and the
  * grid, walking chunk by chunk, sweeps one contiguous window at a time.  The pages store weights in engine-specific tiled
  * layouts too ([NVFP4 card, "How it was created"]: the NVFP4 storage layout
@@ -187,7 +189,7 @@ int64_t nq_gemv_workspace_bytes(int fmt, int64_t T, int64_t N, int64_t K);
  *   fmt       an nq_wfmt, or -1 for row-scaled FP8 codes
  *   w         row-major codes as nq_gemv_fp8row / nq_gemv_qgroup take them
  *   w_packed  nq_packed_weight_bytes(fmt, N, K) bytes, caller-owned
- * Errors: K % 128 != 0 (or K == 0 with N > 0) -> NQ_ERR_SHAPE; unknown fmt ->
+ * Errors: K % 256 != 0 (or K == 0 with N > 0) -> NQ_ERR_SHAPE; unknown fmt ->
  * NQ_ERR_FORMAT.
  */
 int64_t nq_packed_weight_bytes(int fmt, int64_t N, int64_t K);

@@ -165,7 +165,7 @@ namespace {
 
 // The packed layout needs whole 128-column chunks and 32-bit buffer offsets.
 bool packed_shape_ok(int64_t N, int64_t K) {
-    return K % 128 == 0 && K > 0 && 64 * K * 2 < ((int64_t)1 << 31) && N * (K / 32) * 2 < ((int64_t)1 << 31);
+    return K % 256 == 0 && K > 0 && 64 * K * 2 < ((int64_t)1 << 31) && N * (K / 32) * 2 < ((int64_t)1 << 31);
 }
 
 nq_status gemv_fp8row_impl(const uint8_t* w, const uint16_t* w_scale, const uint16_t* x, int64_t T, int64_t N,

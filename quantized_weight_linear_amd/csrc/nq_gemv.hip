@@ -1,23 +1,26 @@
 // Decode GEMV / skinny GEMM: y[t][n] = sum_k x[t][k] * W[n][k] for a few
 // tokens (T <= 64 per pass), weights decoded on the fly in registers.
 //
-// Main path (K % 128 == 0): BF16 MFMA 16x16x32 on exactly decoded weights.
-//   - A workgroup of 4 waves owns 64 weight rows and a K range; each wave owns
-//     16 rows over the whole range and streams them chunk by chunk (KC = 256
-//     or 128 columns, whichever divides K) sharing only the activation chunk.
+// Main path (K % 256 == 0): BF16 MFMA 16x16x32 on exactly decoded weights.
+//   - A workgroup of 4 waves owns 64 weight rows (4 row blocks of 16) and a K
+//     range walked in chunks of 256 columns.  Wave w takes columns
+//     [64 w, 64 w + 64) of every chunk for all 4 row blocks, so each wave
+//     reads only the activation fragments of its own two k-steps (a quarter of
+//     what a wave owning 16 rows over the whole chunk would read from LDS) and
+//     runs 4 x (token blocks) independent MFMA chains.  At the end the four
+//     waves' partial sums are added in LDS, in wave order.
 //   - Weights go from HBM straight into registers, depth<FMT>() chunks ahead
 //     of use, in a static register ring (the loop is unrolled by the depth).
-//     Each lane reads 16-byte pieces so that one load instruction covers 64
-//     contiguous bytes of 16 rows.
+//     Each lane reads 8- or 16-byte pieces; one load instruction covers 64
+//     contiguous bytes of 16 rows (row-major) or 512 B / 1 KiB (packed).
 //   - The hot loop has no branches: every chunk is full, prefetch indices are
 //     clamped to the last chunk (the repeated loads at the end hit in cache),
 //     and activations / scales come through buffer loads whose out-of-range
 //     offsets read as zero.  Branches inside the loop would make the compiler
 //     drain every outstanding load at each join.
-//   - The activation chunk [T_pad][KC] is double-buffered in LDS (rows past T
-//     read as zero); the next chunk's activations are requested before the
-//     next weights so that waiting for them never waits for weights.  One
-//     barrier per chunk.
+//   - Activations: either staged once in LDS for the whole K range of the
+//     workgroup (resident variant) or double-buffered chunk by chunk with one
+//     barrier per chunk (streaming variant).  Rows past T read as zero.
 //   - Decode in registers: E4M3 -> BF16 by the hardware scaled convert
 //     (exact; MXFP8 passes its power-of-two group scale to the convert),
 //     int8 / int4 -> FP32 -> BF16 (exact for |q| <= 128), BF16 as stored.
@@ -33,7 +36,8 @@
 
 namespace nq {
 
-constexpr int GV_ROWS = 64;   // rows per workgroup (4 waves x 16)
+constexpr int GV_ROWS = 64;   // rows per workgroup (4 row blocks of 16)
+constexpr int GV_KC = 256;    // columns per chunk
 constexpr unsigned BUF_FLAGS = 0x00020000u;
 
 template <int FMT>
@@ -41,9 +45,12 @@ constexpr int group_size() {
     return FMT == W_Q8G32 ? 32 : ((FMT == W_Q4G64 || FMT == W_Q8G64) ? 64 : 0);
 }
 
-template <int FMT>
+// Ring depth (chunks in flight per wave) of the streaming variant; shallower
+// with three or more token blocks so that two waves fit per SIMD (a second
+// round of workgroups costs more than the shorter prefetch).
+template <int FMT, int NCB>
 constexpr int depth() {
-    return FMT == W_BF16 ? 2 : (FMT == W_Q4G64 ? 4 : 3);
+    return (FMT == W_BF16 || NCB >= 3) ? 2 : (FMT == W_Q4G64 ? 4 : 3);
 }
 
 template <int FMT>
@@ -53,83 +60,93 @@ __device__ __forceinline__ int64_t row_bytes(int64_t K) {
     return K;
 }
 
-// Pieces per lane per 16-row block and chunk, and their size.
-//   FP8ROW / MXFP8 / Q8G64: KC/64 x 16 B at byte 64q + 16g     (k = 64q + 16g + [0,16))
-//   Q4G64:                  KC/64 x  8 B at byte 32q + 8g      (k = 64q + 16g + [0,16))
-//   Q8G32:                  KC/32 x  8 B at byte 32s + 8g      (k = 32s + 8g + [0,8))
-//   BF16:                   KC/32 x 16 B at byte 64s + 16g     (k = 32s + 8g + [0,8))
-template <int FMT, int KC>
-struct WChunk {
+// Pieces.  Within a chunk of 256 columns, lane 16 g + i of a row block (row i,
+// lane group g) owns, per piece q, these bytes of its row:
+//   FP8ROW / MXFP8 / Q8G64: 4 pieces of 16 B at byte 64q + 16g   (k = 64q + 16g + [0,16))
+//   Q4G64:                  4 pieces of  8 B at byte 32q + 8g    (k = 64q + 16g + [0,16))
+//   Q8G32:                  8 pieces of  8 B at byte 32q + 8g    (k = 32q + 8g + [0,8))
+//   BF16:                   8 pieces of 16 B at byte 64q + 16g   (k = 32q + 8g + [0,8))
+// Wave w takes the PW pieces covering chunk columns [64w, 64w + 64) of each of
+// the 4 row blocks.
+template <int FMT>
+struct PieceFmt {
     static constexpr bool WIDE = (FMT == W_FP8ROW || FMT == W_MXFP8 || FMT == W_Q8G64 || FMT == W_BF16);
-    static constexpr int NP = (FMT == W_Q8G32 || FMT == W_BF16) ? KC / 32 : KC / 64;
-    typename std::conditional<WIDE, uint4, uint2>::type p[NP];
-    uint32_t e8[FMT == W_MXFP8 ? NP : 1];
+    static constexpr int NP = (FMT == W_Q8G32 || FMT == W_BF16) ? 8 : 4;   // pieces per row block and chunk
+    static constexpr int PW = NP / 4;                                     // ... per row block and wave
+    static constexpr int PB = WIDE ? 16 : 8;                               // bytes per lane and piece
+    static constexpr int64_t BLOCK_CHUNK = (int64_t)NP * 64 * PB;         // packed bytes per (chunk, row block)
+    using Piece = typename std::conditional<WIDE, uint4, uint2>::type;
 };
 
-// Where a wave's weights come from.  Row-major: the lane's row.  Packed (see
-// pack_weights_kernel): the lane's piece 0 of chunk 0 in its 16-row block;
-// pieces of one (chunk, block) are stored lane-major, so one load instruction
-// of the wave reads 64 x piece contiguous bytes, and the blocks of one chunk
-// are adjacent (cstride bytes from one chunk to the next).
-struct WSrc {
-    const uint8_t* w;       // row-major base, or packed base of (row block, lane)
-    const uint8_t* e8;      // MXFP8 scale bytes [N][K/32]
-    int64_t row;            // this lane's row (clamped to N - 1)
-    int64_t K;
-    int64_t cstride;        // packed: bytes between chunk c and c + 1 of a block
+// One wave's share of a chunk: slot j = PW * (row block) + (piece of the wave).
+template <int FMT>
+struct WChunk {
+    typename PieceFmt<FMT>::Piece p[4 * PieceFmt<FMT>::PW];
+    uint32_t e8[FMT == W_MXFP8 ? 4 : 1];
 };
-
-template <int FMT, int KC>
-constexpr int piece_bytes() {
-    return WChunk<FMT, KC>::WIDE ? 16 : 8;
-}
 
 // Byte offset, within a row-major row, of piece q of chunk c for lane group g.
-template <int FMT, int KC>
+template <int FMT>
 __host__ __device__ __forceinline__ int64_t piece_offset(int64_t c, int q, int g) {
-    const int64_t kc0 = c * KC;
+    const int64_t kc0 = c * GV_KC;
     if (FMT == W_Q4G64) return (kc0 >> 1) + 32 * q + 8 * g;
     if (FMT == W_Q8G32) return kc0 + 32 * q + 8 * g;
     if (FMT == W_BF16) return 2 * kc0 + 64 * q + 16 * g;
     return kc0 + 64 * q + 16 * g;
 }
 
-template <int FMT, int KC, bool PK>
-__device__ __forceinline__ void load_chunk(WChunk<FMT, KC>& r, const WSrc& src, int64_t c, int g) {
-    constexpr int NP = WChunk<FMT, KC>::NP;
-    constexpr int PB = piece_bytes<FMT, KC>();
-#pragma unroll
-    for (int q = 0; q < NP; ++q) {
-        const uint8_t* p = PK ? src.w + c * src.cstride + q * (64 * PB)
-                              : src.w + src.row * row_bytes<FMT>(src.K) + piece_offset<FMT, KC>(c, q, g);
-        if constexpr (PB == 16) r.p[q] = *reinterpret_cast<const uint4*>(p);
-        else r.p[q] = *reinterpret_cast<const uint2*>(p);
-        if constexpr (FMT == W_MXFP8)
-            r.e8[q] = src.e8[src.row * (src.K >> 5) + (piece_offset<FMT, KC>(c, q, g) >> 5)];
-    }
-}
+// Where a wave's weights come from: per row block, the lane's row (row-major)
+// or the lane's piece base in the packed layout (see pack_weights_kernel).
+// Rows past N are clamped (their outputs are never written).
+struct WSrc {
+    const uint8_t* base[4];
+    const uint8_t* e8[4];    // MXFP8: the lane's row of scale bytes [K/32]
+    int64_t cstride;         // packed: bytes from chunk c to chunk c + 1
+    int q0;                  // first piece of this wave
+    int g;                   // lane group
+};
 
-// WSrc of a lane: rows past N are clamped (their outputs are never written).
-template <int FMT, int KC, bool PK>
-__device__ __forceinline__ WSrc make_wsrc(const uint8_t* w, const void* scales, int64_t row, int N, int64_t K,
-                                          int lane) {
+template <int FMT, bool PK>
+__device__ __forceinline__ WSrc make_wsrc(const uint8_t* w, const void* scales, int64_t row0, int N, int64_t K,
+                                          int lane, int wv) {
+    using P = PieceFmt<FMT>;
     WSrc s;
-    s.e8 = reinterpret_cast<const uint8_t*>(scales);
-    s.K = K;
-    s.row = row < N ? row : (int64_t)N - 1;
-    s.cstride = 0;
-    if (PK) {
-        constexpr int64_t BLOCK_CHUNK = (int64_t)WChunk<FMT, KC>::NP * 64 * piece_bytes<FMT, KC>();
-        const int64_t rb = s.row >> 4;                 // row block of the (clamped) row
-        s.cstride = ((int64_t)N + 15) / 16 * BLOCK_CHUNK;
-        s.w = w + rb * BLOCK_CHUNK + (int64_t)lane * piece_bytes<FMT, KC>();
-    } else {
-        s.w = w;
+    const int64_t nrb = ((int64_t)N + 15) / 16;
+    s.cstride = PK ? nrb * P::BLOCK_CHUNK : 0;
+    s.q0 = P::PW * wv;
+    s.g = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        int64_t row = row0 + 16 * r + (lane & 15);
+        if (row > N - 1) row = N - 1;
+        if (PK) {
+            int64_t rb = (row0 >> 4) + r;
+            if (rb > nrb - 1) rb = nrb - 1;
+            s.base[r] = w + rb * P::BLOCK_CHUNK + (int64_t)lane * P::PB;
+        } else {
+            s.base[r] = w + row * row_bytes<FMT>(K);
+        }
+        s.e8[r] = reinterpret_cast<const uint8_t*>(scales) + row * (K >> 5);
     }
     return s;
 }
 
-// LDS column (within the chunk) of k-step s for lane group g.
+template <int FMT, bool PK>
+__device__ __forceinline__ void load_chunk(WChunk<FMT>& r, const WSrc& src, int64_t c) {
+    using P = PieceFmt<FMT>;
+#pragma unroll
+    for (int j = 0; j < 4 * P::PW; ++j) {
+        const int rb = j / P::PW;
+        const int q = src.q0 + j % P::PW;
+        const uint8_t* p = PK ? src.base[rb] + c * src.cstride + q * (64 * P::PB)
+                              : src.base[rb] + piece_offset<FMT>(c, q, src.g);
+        r.p[j] = *reinterpret_cast<const typename P::Piece*>(p);
+        if constexpr (FMT == W_MXFP8) r.e8[j] = src.e8[rb][(c * GV_KC + 64 * q + 16 * src.g) >> 5];
+    }
+}
+
+// Chunk column of k-step s (0..7) for lane group g: the B fragment of lane
+// (i, g) holds activations [t = i][col, col + 8).
 template <int FMT>
 __device__ __forceinline__ int kstep_col(int s, int g) {
     if constexpr (FMT == W_Q8G32 || FMT == W_BF16) return 32 * s + 8 * g;
@@ -148,209 +165,138 @@ __device__ __forceinline__ uint32_t i4x2_to_bf16x2(uint32_t d, int sh) {
     return f32x2_to_bf16x2(a, b);
 }
 
-// The A fragment (8 BF16 weights) of k-step s.
-template <int FMT, int KC>
-__device__ __forceinline__ v8bf decode_afrag(const WChunk<FMT, KC>& r, int s) {
+// The A fragment (8 BF16 weights) of row block rb at the wave's local k-step ls.
+template <int FMT>
+__device__ __forceinline__ v8bf decode_afrag(const WChunk<FMT>& r, int rb, int ls) {
     uint32_t o[4];
     if constexpr (FMT == W_FP8ROW || FMT == W_MXFP8) {
-        const uint4 q = r.p[s >> 1];
-        const uint32_t d0 = (s & 1) ? q.z : q.x, d1 = (s & 1) ? q.w : q.y;
+        const uint4 q = r.p[rb];
+        const uint32_t d0 = ls ? q.z : q.x, d1 = ls ? q.w : q.y;
         float sc = 1.0f;
-        if constexpr (FMT == W_MXFP8) sc = ue8m0_to_f32(r.e8[s >> 1]);
+        if constexpr (FMT == W_MXFP8) sc = ue8m0_to_f32(r.e8[rb]);
         o[0] = e4m3x2_to_bf16x2<false>(d0, sc);
         o[1] = e4m3x2_to_bf16x2<true>(d0, sc);
         o[2] = e4m3x2_to_bf16x2<false>(d1, sc);
         o[3] = e4m3x2_to_bf16x2<true>(d1, sc);
     } else if constexpr (FMT == W_Q8G64) {
-        const uint4 q = r.p[s >> 1];
-        const uint32_t d0 = (s & 1) ? q.z : q.x, d1 = (s & 1) ? q.w : q.y;
+        const uint4 q = r.p[rb];
+        const uint32_t d0 = ls ? q.z : q.x, d1 = ls ? q.w : q.y;
         o[0] = i8x2_to_bf16x2(d0, 0);
         o[1] = i8x2_to_bf16x2(d0, 16);
         o[2] = i8x2_to_bf16x2(d1, 0);
         o[3] = i8x2_to_bf16x2(d1, 16);
     } else if constexpr (FMT == W_Q4G64) {
-        const uint2 q = r.p[s >> 1];
-        const uint32_t d0 = (s & 1) ? q.y : q.x;
+        const uint2 q = r.p[rb];
+        const uint32_t d0 = ls ? q.y : q.x;
         o[0] = i4x2_to_bf16x2(d0, 0);
         o[1] = i4x2_to_bf16x2(d0, 8);
         o[2] = i4x2_to_bf16x2(d0, 16);
         o[3] = i4x2_to_bf16x2(d0, 24);
     } else if constexpr (FMT == W_Q8G32) {
-        const uint2 q = r.p[s];
+        const uint2 q = r.p[2 * rb + ls];
         o[0] = i8x2_to_bf16x2(q.x, 0);
         o[1] = i8x2_to_bf16x2(q.x, 16);
         o[2] = i8x2_to_bf16x2(q.y, 0);
         o[3] = i8x2_to_bf16x2(q.y, 16);
     } else {  // W_BF16
-        const uint4 q = r.p[s];
+        const uint4 q = r.p[2 * rb + ls];
         o[0] = q.x; o[1] = q.y; o[2] = q.z; o[3] = q.w;
     }
     return __builtin_bit_cast(v8bf, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
-template <int FMT, int NCB, int KC, bool PK>
-__global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint8_t* __restrict__ w,
-                                                        const void* __restrict__ scales,
-                                                        const uint16_t* __restrict__ x, int T, int N, int64_t K,
-                                                        int chunks_per_split, int splits,
-                                                        float* __restrict__ partial,
-                                                        unsigned* __restrict__ counters, int bf16_out,
-                                                        void* __restrict__ y) {
-    constexpr int TP = 16 * NCB;
-    constexpr int KS = KC / 32;                       // k-steps per chunk
-    constexpr int XPITCH = KC + 8;                    // bf16 per LDS row: rows shift by 4 banks
-    constexpr int XPR = KC / 8;                       // 16-byte activation pieces per row and chunk
-    constexpr int XP = TP * XPR / 256;                // ... per thread
+// One chunk of one wave: xrow(cb) gives the LDS element index of the B
+// fragment row for token block cb (lane's token), kl the chunk's first column
+// in the LDS activation rows, scs / sbase the group scales of the chunk.
+template <int FMT, int NCB>
+__device__ __forceinline__ void chunk_mfma(const WChunk<FMT>& wc, const uint16_t* xs, const int (&xrow)[NCB], int kl,
+                                           const uint16_t* scs, int sgroup0, int wv, int lg,
+                                           v4f (&acc)[4][NCB]) {
     constexpr int GS = group_size<FMT>();
-    constexpr int NG = GS ? KC / (GS ? GS : 1) : 1;   // scale groups per chunk
-    constexpr int SP = GS ? (NG * GV_ROWS + 255) / 256 : 1;
-    constexpr int D = depth<FMT>();
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][TP * XPITCH];
-    __shared__ __attribute__((aligned(16))) uint16_t scs[2][GS ? NG * GV_ROWS : 1];
-    __shared__ int s_last;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wv = tid >> 6;
-    const int li = lane & 15;
-    const int lg = lane >> 4;
-    const int tile = blockIdx.x;
-    const int split = blockIdx.y;
-    const int64_t row0 = (int64_t)tile * GV_ROWS;
-    const int64_t total_chunks = K / KC;
-    const int64_t c_begin = (int64_t)split * chunks_per_split;
-    int nch = (int)(total_chunks - c_begin);
-    if (nch > chunks_per_split) nch = chunks_per_split;
-    const int64_t k_begin = c_begin * KC;
-
-    const WSrc src = make_wsrc<FMT, KC, PK>(w, scales, row0 + wv * 16 + li, N, K, lane);
-
-    // activations: rows >= T fall outside the buffer and read as zero
-    const __amdgpu_buffer_rsrc_t xrsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)((int64_t)T * K * 2), BUF_FLAGS);
-    __amdgpu_buffer_rsrc_t srsrc = xrsrc;
-    if constexpr (GS != 0)
-        srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)scales, (short)0, (int)((int64_t)N * (K / GS) * 2),
-                                                  BUF_FLAGS);
-
-    uint4 xreg[XP];
-    uint32_t sreg[SP];
-    auto load_x = [&](int c) {
-        const int64_t kc0 = k_begin + (int64_t)c * KC;
+    if constexpr (GS == 0) {
 #pragma unroll
-        for (int j = 0; j < XP; ++j) {
-            const int idx = tid + 256 * j;
-            const int t = idx / XPR, pc = idx % XPR;
-            const int off = (int)(((int64_t)t * K + kc0 + 8 * pc) * 2);
-            xreg[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, off, 0, 0));
-        }
-        if constexpr (GS != 0) {
+        for (int ls = 0; ls < 2; ++ls) {
+            const int col = kl + kstep_col<FMT>(2 * wv + ls, lg);
+            v8bf b[NCB];
 #pragma unroll
-            for (int j = 0; j < SP; ++j) {
-                const int idx = tid + 256 * j;          // idx = row * NG + group
-                const int r = idx / NG, gi = idx % NG;
-                const int64_t row = row0 + r;           // rows >= N read as zero
-                const int off = (int)((row * (K / GS) + kc0 / GS + gi) * 2);
-                sreg[j] = __builtin_amdgcn_raw_buffer_load_b16(srsrc, off, 0, 0);
+            for (int cb = 0; cb < NCB; ++cb) b[cb] = *reinterpret_cast<const v8bf*>(&xs[xrow[cb] + col]);
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const v8bf a = decode_afrag<FMT>(wc, rb, ls);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[cb], acc[rb][cb], 0, 0, 0);
             }
         }
-    };
-    auto store_x = [&](int buf) {
+    } else {
+        // GS == 64: the wave's two k-steps are one group; GS == 32: each k-step is one.
+        constexpr int NGW = 64 / GS;                     // groups per wave and chunk
+        v4f d[4][NCB];
 #pragma unroll
-        for (int j = 0; j < XP; ++j) {
-            const int idx = tid + 256 * j;
-            const int t = idx / XPR, pc = idx % XPR;
-            *reinterpret_cast<uint4*>(&xs[buf][t * XPITCH + 8 * pc]) = xreg[j];
-        }
-        if constexpr (GS != 0) {
+        for (int ls = 0; ls < 2; ++ls) {
+            const int col = kl + kstep_col<FMT>(2 * wv + ls, lg);
+            v8bf b[NCB];
 #pragma unroll
-            for (int j = 0; j < SP; ++j) {
-                const int idx = tid + 256 * j;
-                if (SP * 256 == NG * GV_ROWS || idx < NG * GV_ROWS)
-                    scs[buf][(idx % NG) * GV_ROWS + idx / NG] = (uint16_t)sreg[j];
-            }
-        }
-    };
-
-    v4f acc[NCB];
+            for (int cb = 0; cb < NCB; ++cb) b[cb] = *reinterpret_cast<const v8bf*>(&xs[xrow[cb] + col]);
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) acc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    auto compute = [&](const WChunk<FMT, KC>& wc, int buf) {
-        if constexpr (GS == 0) {
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const int col = kstep_col<FMT>(s, lg);
-                const v8bf a = decode_afrag<FMT, KC>(wc, s);
+            for (int rb = 0; rb < 4; ++rb) {
+                const v8bf a = decode_afrag<FMT>(wc, rb, ls);
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) {
-                    const v8bf b = *reinterpret_cast<const v8bf*>(&xs[buf][(cb * 16 + li) * XPITCH + col]);
-                    acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[cb], 0, 0, 0);
+                    const v4f c0 = (NGW == 2 || ls == 0) ? v4f{0.f, 0.f, 0.f, 0.f} : d[rb][cb];
+                    d[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[cb], c0, 0, 0, 0);
                 }
             }
-        } else {
-            constexpr int KPG = GS / 32;                 // k-steps per scale group
+            if (NGW == 2 || ls == 1) {
+                const int gi = sgroup0 + (NGW == 2 ? 2 * wv + ls : wv);
 #pragma unroll
-            for (int gq = 0; gq < KS / KPG; ++gq) {
-                v4f d[NCB];
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) d[cb] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < KPG; ++kk) {
-                    const int s = gq * KPG + kk;
-                    const int col = kstep_col<FMT>(s, lg);
-                    const v8bf a = decode_afrag<FMT, KC>(wc, s);
+                for (int rb = 0; rb < 4; ++rb) {
+                    const uint2 s4 = *reinterpret_cast<const uint2*>(&scs[gi * GV_ROWS + 16 * rb + 4 * lg]);
+                    const float s0 = f16_bits_to_f32(s4.x & 0xFFFFu), s1 = f16_bits_to_f32(s4.x >> 16);
+                    const float s2 = f16_bits_to_f32(s4.y & 0xFFFFu), s3 = f16_bits_to_f32(s4.y >> 16);
 #pragma unroll
                     for (int cb = 0; cb < NCB; ++cb) {
-                        const v8bf b = *reinterpret_cast<const v8bf*>(&xs[buf][(cb * 16 + li) * XPITCH + col]);
-                        d[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, d[cb], 0, 0, 0);
+                        acc[rb][cb][0] = fmaf(d[rb][cb][0], s0, acc[rb][cb][0]);
+                        acc[rb][cb][1] = fmaf(d[rb][cb][1], s1, acc[rb][cb][1]);
+                        acc[rb][cb][2] = fmaf(d[rb][cb][2], s2, acc[rb][cb][2]);
+                        acc[rb][cb][3] = fmaf(d[rb][cb][3], s3, acc[rb][cb][3]);
                     }
-                }
-                const uint2 s4 = *reinterpret_cast<const uint2*>(&scs[buf][gq * GV_ROWS + wv * 16 + 4 * lg]);
-                const float s0 = f16_bits_to_f32(s4.x & 0xFFFFu), s1 = f16_bits_to_f32(s4.x >> 16);
-                const float s2 = f16_bits_to_f32(s4.y & 0xFFFFu), s3 = f16_bits_to_f32(s4.y >> 16);
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-                    acc[cb][0] = fmaf(d[cb][0], s0, acc[cb][0]);
-                    acc[cb][1] = fmaf(d[cb][1], s1, acc[cb][1]);
-                    acc[cb][2] = fmaf(d[cb][2], s2, acc[cb][2]);
-                    acc[cb][3] = fmaf(d[cb][3], s3, acc[cb][3]);
                 }
             }
         }
-    };
-
-    // One chunk: compute from ring slot u, stage the next activation chunk,
-    // request the one after it, refill slot u with the chunk D ahead (indices
-    // clamped to the last chunk, so the body has no branch), barrier.
-    WChunk<FMT, KC> ring[D];
-    auto body = [&](int c, int u) {
-        compute(ring[u], c & 1);
-        store_x((c + 1) & 1);
-        load_x(min(c + 2, nch - 1));
-        load_chunk<FMT, KC, PK>(ring[u], src, c_begin + min(c + D, nch - 1), lg);
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-    };
-
-    if (nch > 0) {
-        load_x(0);
-#pragma unroll
-        for (int d = 0; d < D; ++d)
-            load_chunk<FMT, KC, PK>(ring[d], src, c_begin + min(d, nch - 1), lg);
-        store_x(0);
-        load_x(min(1, nch - 1));
-        __syncthreads();
-        int c = 0;
-        for (; c + D <= nch; c += D) {
-#pragma unroll
-            for (int u = 0; u < D; ++u) body(c + u, u);
-        }
-#pragma unroll
-        for (int u = 0; u < D - 1; ++u)
-            if (c + u < nch) body(c + u, u);
     }
+}
 
+// Sum the four waves' partials of row block wv in wave order through LDS
+// (red: 16 KiB per token block, 16-byte aligned; the caller's LDS reads of the
+// main loop must be finished, which the leading barrier guarantees).
+template <int NCB>
+__device__ __forceinline__ void reduce_waves(v4f (&acc)[4][NCB], v4f (&fin)[NCB], v4f* red, int wv, int lane) {
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) red[((wv * 4 + rb) * NCB + cb) * 64 + lane] = acc[rb][cb];
+    __syncthreads();
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        v4f s = red[((0 * 4 + wv) * NCB + cb) * 64 + lane];
+#pragma unroll
+        for (int w2 = 1; w2 < 4; ++w2) s += red[((w2 * 4 + wv) * NCB + cb) * 64 + lane];
+        fin[cb] = s;
+    }
+}
+
+// Output of row block wv: the FP32 values fin (row-FP8 scale applied here),
+// either written to y or, with splits > 1, published as a partial and summed
+// by the last workgroup of the tile.
+template <int FMT, int NCB>
+__device__ __forceinline__ void finish_tile(v4f (&fin)[NCB], const void* __restrict__ scales, int T, int N,
+                                            int64_t row0, int wv, int lane, int tile, int split, int splits,
+                                            float* __restrict__ partial, unsigned* __restrict__ counters,
+                                            int bf16_out, void* __restrict__ y, int* s_last) {
+    const int li = lane & 15, lg = lane >> 4;
+    const int tid = threadIdx.x;
     const int64_t npad = (int64_t)gridDim.x * GV_ROWS;
     const int64_t n0 = row0 + wv * 16 + 4 * lg;           // this lane's 4 output rows
     auto write_out = [&](int cb, v4f v) {
@@ -386,7 +332,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint8_t* __restric
 
     if (splits == 1) {
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) write_out(cb, acc[cb]);
+        for (int cb = 0; cb < NCB; ++cb) write_out(cb, fin[cb]);
         return;
     }
 
@@ -402,17 +348,17 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint8_t* __restric
             uint32_t* p = reinterpret_cast<uint32_t*>(&partial[((int64_t)split * T + t) * npad + n0]);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                __hip_atomic_store(p + r, __float_as_uint(acc[cb][r]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(p + r, __float_as_uint(fin[cb][r]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0) {
         const unsigned prev = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == (unsigned)(splits - 1));
+        *s_last = (prev == (unsigned)(splits - 1));
     }
     __syncthreads();
-    if (!s_last) return;
+    if (!*s_last) return;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         const int t = cb * 16 + li;
@@ -432,6 +378,149 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint8_t* __restric
 }
 
 // ---------------------------------------------------------------------------
+// Streaming variant: the activation chunk [16 NCB][256] is double-buffered in
+// LDS (rows past T read as zero); the next chunk's activations are requested
+// before the next weights so that waiting for them never waits for weights.
+// One barrier per chunk.
+// ---------------------------------------------------------------------------
+template <int FMT, int NCB, bool PK>
+__global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint8_t* __restrict__ w,
+                                                        const void* __restrict__ scales,
+                                                        const uint16_t* __restrict__ x, int T, int N, int64_t K,
+                                                        int chunks_per_split, int splits,
+                                                        float* __restrict__ partial,
+                                                        unsigned* __restrict__ counters, int bf16_out,
+                                                        void* __restrict__ y) {
+    constexpr int TP = 16 * NCB;
+    constexpr int XPITCH = GV_KC + 8;                 // bf16 per LDS row: rows shift by 4 banks
+    constexpr int XPR = GV_KC / 8;                    // 16-byte activation pieces per row and chunk
+    constexpr int XP = TP * XPR / 256;                // ... per thread
+    constexpr int GS = group_size<FMT>();
+    constexpr int NG = GS ? GV_KC / (GS ? GS : 1) : 1;   // scale groups per chunk
+    constexpr int SP = GS ? (NG * GV_ROWS + 255) / 256 : 1;
+    constexpr int D = depth<FMT, NCB>();
+    // xs doubles as the buffer of the final cross-wave sum (16 KiB per token block)
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][TP * XPITCH];
+    __shared__ __attribute__((aligned(16))) uint16_t scs[2][GS ? NG * GV_ROWS : 1];
+    __shared__ int s_last;
+    static_assert(sizeof(xs) >= 16384 * NCB, "reduction buffer");
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    const int li = lane & 15;
+    const int lg = lane >> 4;
+    const int tile = blockIdx.x;
+    const int split = blockIdx.y;
+    const int64_t row0 = (int64_t)tile * GV_ROWS;
+    const int64_t total_chunks = K / GV_KC;
+    const int64_t c_begin = (int64_t)split * chunks_per_split;
+    int nch = (int)(total_chunks - c_begin);
+    if (nch > chunks_per_split) nch = chunks_per_split;
+    const int64_t k_begin = c_begin * GV_KC;
+
+    const WSrc src = make_wsrc<FMT, PK>(w, scales, row0, N, K, lane, wv);
+
+    // activations: rows >= T fall outside the buffer and read as zero
+    const __amdgpu_buffer_rsrc_t xrsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)((int64_t)T * K * 2), BUF_FLAGS);
+    __amdgpu_buffer_rsrc_t srsrc = xrsrc;
+    if constexpr (GS != 0)
+        srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)scales, (short)0, (int)((int64_t)N * (K / GS) * 2),
+                                                  BUF_FLAGS);
+
+    // Activations (and group scales) of a chunk are loaded into registers D
+    // chunks ahead, in the same order as the chunk's weights, and stored to
+    // LDS one chunk ahead of use: waiting for them then never waits for more
+    // than the weights the current chunk needs anyway.
+    uint4 xreg[D][XP];
+    uint32_t sreg[D][SP];
+    auto load_x = [&](int slot, int c) {
+        const int64_t kc0 = k_begin + (int64_t)c * GV_KC;
+#pragma unroll
+        for (int j = 0; j < XP; ++j) {
+            const int idx = tid + 256 * j;
+            const int t = idx / XPR, pc = idx % XPR;
+            const int off = (int)(((int64_t)t * K + kc0 + 8 * pc) * 2);
+            xreg[slot][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, off, 0, 0));
+        }
+        if constexpr (GS != 0) {
+#pragma unroll
+            for (int j = 0; j < SP; ++j) {
+                const int idx = tid + 256 * j;          // idx = row * NG + group
+                const int r = idx / NG, gi = idx % NG;
+                const int64_t row = row0 + r;           // rows >= N read as zero
+                const int off = (int)((row * (K / GS) + kc0 / GS + gi) * 2);
+                sreg[slot][j] = __builtin_amdgcn_raw_buffer_load_b16(srsrc, off, 0, 0);
+            }
+        }
+    };
+    auto store_x = [&](int buf, int slot) {
+#pragma unroll
+        for (int j = 0; j < XP; ++j) {
+            const int idx = tid + 256 * j;
+            const int t = idx / XPR, pc = idx % XPR;
+            *reinterpret_cast<uint4*>(&xs[buf][t * XPITCH + 8 * pc]) = xreg[slot][j];
+        }
+        if constexpr (GS != 0) {
+#pragma unroll
+            for (int j = 0; j < SP; ++j) {
+                const int idx = tid + 256 * j;
+                if (SP * 256 == NG * GV_ROWS || idx < NG * GV_ROWS)
+                    scs[buf][(idx % NG) * GV_ROWS + idx / NG] = (uint16_t)sreg[slot][j];
+            }
+        }
+    };
+
+    v4f acc[4][NCB];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = v4f{0.f, 0.f, 0.f, 0.f};
+    int xrow[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) xrow[cb] = (cb * 16 + li) * XPITCH;
+
+    // One chunk c (c = u mod D): compute from ring slot u and LDS buffer c & 1,
+    // stage the activations of chunk c + 1 (register slot (u + 1) mod D),
+    // request activations and weights of chunk c + D into slot u (indices
+    // clamped to the last chunk, so the body has no branch), barrier.
+    WChunk<FMT> ring[D];
+    auto body = [&](int c, int u) {
+        const int buf = c & 1;
+        chunk_mfma<FMT, NCB>(ring[u], xs[buf], xrow, 0, scs[buf], 0, wv, lg, acc);
+        store_x((c + 1) & 1, (u + 1) % D);
+        load_x(u, min(c + D, nch - 1));
+        load_chunk<FMT, PK>(ring[u], src, c_begin + min(c + D, nch - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+    };
+
+    if (nch > 0) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            load_x(d, min(d, nch - 1));
+            load_chunk<FMT, PK>(ring[d], src, c_begin + min(d, nch - 1));
+        }
+        store_x(0, 0);
+        __syncthreads();
+        int c = 0;
+        for (; c + D <= nch; c += D) {
+#pragma unroll
+            for (int u = 0; u < D; ++u) body(c + u, u);
+        }
+#pragma unroll
+        for (int u = 0; u < D - 1; ++u)
+            if (c + u < nch) body(c + u, u);
+    }
+
+    v4f fin[NCB];
+    reduce_waves<NCB>(acc, fin, reinterpret_cast<v4f*>(&xs[0][0]), wv, lane);
+    finish_tile<FMT, NCB>(fin, scales, T, N, row0, wv, lane, tile, split, splits, partial, counters, bf16_out, y,
+                          &s_last);
+}
+
+// ---------------------------------------------------------------------------
 // Resident-activation variant: when the workgroup's activation slice
 // [T][k range] (and its rows' group scales) fits in LDS, it is staged once and
 // the waves then stream weights with no barrier at all, each with its own
@@ -445,7 +534,7 @@ constexpr int depth_resident() {
     return FMT == W_MXFP8 ? 4 : 3;
 }
 
-template <int FMT, int NCB, int KC, bool PK>
+template <int FMT, int NCB, bool PK>
 __global__ __launch_bounds__(256) void gemv_resident_kernel(const uint8_t* __restrict__ w,
                                                             const void* __restrict__ scales,
                                                             const uint16_t* __restrict__ x, int T, int N,
@@ -453,9 +542,9 @@ __global__ __launch_bounds__(256) void gemv_resident_kernel(const uint8_t* __res
                                                             float* __restrict__ partial,
                                                             unsigned* __restrict__ counters, int bf16_out,
                                                             void* __restrict__ y) {
-    constexpr int KS = KC / 32;
     constexpr int GS = group_size<FMT>();
     constexpr int D = depth_resident<FMT>();
+    // The dynamic LDS also holds the final cross-wave sum (16 KiB per token block).
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     __shared__ int s_last;
 
@@ -467,24 +556,23 @@ __global__ __launch_bounds__(256) void gemv_resident_kernel(const uint8_t* __res
     const int tile = blockIdx.x;
     const int split = blockIdx.y;
     const int64_t row0 = (int64_t)tile * GV_ROWS;
-    const int64_t total_chunks = K / KC;
+    const int64_t total_chunks = K / GV_KC;
     const int64_t c_begin = (int64_t)split * chunks_per_split;
     int nch = (int)(total_chunks - c_begin);
     if (nch > chunks_per_split) nch = chunks_per_split;
-    const int64_t k_begin = c_begin * KC;
-    const int krange = nch * KC;
-    const int xpitch = chunks_per_split * KC + 8;         // bf16 per LDS row (rows shift by 4 banks)
-    const int ng_all = GS ? chunks_per_split * KC / (GS ? GS : 1) : 0;
+    const int64_t k_begin = c_begin * GV_KC;
+    const int krange = nch * GV_KC;
+    const int xpitch = chunks_per_split * GV_KC + 8;      // bf16 per LDS row (rows shift by 4 banks)
     uint16_t* xs = lds;                                    // [T + 1][xpitch], row T is zero
-    uint16_t* scs = lds + (T + 1) * xpitch;                // [ng_all][64 rows]
+    uint16_t* scs = lds + (T + 1) * xpitch;                // [groups of the slice][64 rows]
 
-    const WSrc src = make_wsrc<FMT, KC, PK>(w, scales, row0 + wv * 16 + li, N, K, lane);
+    const WSrc src = make_wsrc<FMT, PK>(w, scales, row0, N, K, lane, wv);
 
     // the first weight chunks are requested before the activations are staged
-    WChunk<FMT, KC> ring[D];
+    WChunk<FMT> ring[D];
     if (nch > 0) {
 #pragma unroll
-        for (int d = 0; d < D; ++d) load_chunk<FMT, KC, PK>(ring[d], src, c_begin + min(d, nch - 1), lg);
+        for (int d = 0; d < D; ++d) load_chunk<FMT, PK>(ring[d], src, c_begin + min(d, nch - 1));
     }
 
     // stage activations (16-byte pieces), the zero row and the group scales
@@ -508,59 +596,18 @@ __global__ __launch_bounds__(256) void gemv_resident_kernel(const uint8_t* __res
         }
         __syncthreads();
     }
-    (void)ng_all;
 
-    v4f acc[NCB];
+    v4f acc[4][NCB];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) acc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
-    int brow[NCB];
+    for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) brow[cb] = min(cb * 16 + li, T) * xpitch;
+        for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = v4f{0.f, 0.f, 0.f, 0.f};
+    int xrow[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) xrow[cb] = min(cb * 16 + li, T) * xpitch;
 
-    auto compute = [&](const WChunk<FMT, KC>& wc, int c) {
-        const int kl = c * KC;                             // column of the chunk within the slice
-        if constexpr (GS == 0) {
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const int col = kl + kstep_col<FMT>(s, lg);
-                const v8bf a = decode_afrag<FMT, KC>(wc, s);
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-                    const v8bf b = *reinterpret_cast<const v8bf*>(&xs[brow[cb] + col]);
-                    acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[cb], 0, 0, 0);
-                }
-            }
-        } else {
-            constexpr int KPG = GS / 32;
-#pragma unroll
-            for (int gq = 0; gq < KS / KPG; ++gq) {
-                v4f d[NCB];
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) d[cb] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < KPG; ++kk) {
-                    const int s = gq * KPG + kk;
-                    const int col = kl + kstep_col<FMT>(s, lg);
-                    const v8bf a = decode_afrag<FMT, KC>(wc, s);
-#pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb) {
-                        const v8bf b = *reinterpret_cast<const v8bf*>(&xs[brow[cb] + col]);
-                        d[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, d[cb], 0, 0, 0);
-                    }
-                }
-                const int gi = kl / GS + gq;
-                const uint2 s4 = *reinterpret_cast<const uint2*>(&scs[gi * GV_ROWS + wv * 16 + 4 * lg]);
-                const float s0 = f16_bits_to_f32(s4.x & 0xFFFFu), s1 = f16_bits_to_f32(s4.x >> 16);
-                const float s2 = f16_bits_to_f32(s4.y & 0xFFFFu), s3 = f16_bits_to_f32(s4.y >> 16);
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-                    acc[cb][0] = fmaf(d[cb][0], s0, acc[cb][0]);
-                    acc[cb][1] = fmaf(d[cb][1], s1, acc[cb][1]);
-                    acc[cb][2] = fmaf(d[cb][2], s2, acc[cb][2]);
-                    acc[cb][3] = fmaf(d[cb][3], s3, acc[cb][3]);
-                }
-            }
-        }
+    auto compute = [&](const WChunk<FMT>& wc, int c) {
+        chunk_mfma<FMT, NCB>(wc, xs, xrow, c * GV_KC, scs, GS ? c * GV_KC / (GS ? GS : 1) : 0, wv, lg, acc);
     };
 
     if (nch > 0) {
@@ -569,7 +616,7 @@ __global__ __launch_bounds__(256) void gemv_resident_kernel(const uint8_t* __res
 #pragma unroll
             for (int u = 0; u < D; ++u) {
                 compute(ring[u], c + u);
-                load_chunk<FMT, KC, PK>(ring[u], src, c_begin + min(c + u + D, nch - 1), lg);
+                load_chunk<FMT, PK>(ring[u], src, c_begin + min(c + u + D, nch - 1));
                 // keep each refill right after the compute that frees its slot
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -579,79 +626,119 @@ __global__ __launch_bounds__(256) void gemv_resident_kernel(const uint8_t* __res
             if (c + u < nch) compute(ring[u], c + u);
     }
 
-    const int64_t npad = (int64_t)gridDim.x * GV_ROWS;
-    const int64_t n0 = row0 + wv * 16 + 4 * lg;
-    auto write_out = [&](int cb, v4f v) {
-        const int t = cb * 16 + li;
-        if (t >= T) return;
-        if constexpr (FMT == W_FP8ROW) {
-            const uint16_t* rs = reinterpret_cast<const uint16_t*>(scales);
+    v4f fin[NCB];
+    reduce_waves<NCB>(acc, fin, reinterpret_cast<v4f*>(lds), wv, lane);
+    finish_tile<FMT, NCB>(fin, scales, T, N, row0, wv, lane, tile, split, splits, partial, counters, bf16_out, y,
+                          &s_last);
+}
+
+// ---------------------------------------------------------------------------
+// Direct variant (formats without group scales): each wave loads the
+// activation fragments of its own k-steps straight from memory (L2: the
+// activations are small and read by every workgroup) into the same register
+// ring as its weights, so nothing is staged in LDS, no barrier runs in the
+// loop, and waiting for a chunk never waits for anything but that chunk.
+// Tokens t >= T lie outside the activation buffer and read as zero.
+// ---------------------------------------------------------------------------
+template <int NCB>
+constexpr int depth_direct() {
+    return NCB >= 3 ? 2 : 3;
+}
+
+template <int FMT, int NCB, bool PK>
+__global__ __launch_bounds__(256) void gemv_direct_kernel(const uint8_t* __restrict__ w,
+                                                          const void* __restrict__ scales,
+                                                          const uint16_t* __restrict__ x, int T, int N, int64_t K,
+                                                          int chunks_per_split, int splits,
+                                                          float* __restrict__ partial,
+                                                          unsigned* __restrict__ counters, int bf16_out,
+                                                          void* __restrict__ y) {
+    static_assert(group_size<FMT>() == 0, "grouped formats stage their scales in LDS");
+    constexpr int D = depth_direct<NCB>();
+    __shared__ __attribute__((aligned(16))) v4f red[4 * 4 * NCB * 64];   // final cross-wave sum
+    __shared__ int s_last;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    const int li = lane & 15;
+    const int lg = lane >> 4;
+    const int tile = blockIdx.x;
+    const int split = blockIdx.y;
+    const int64_t row0 = (int64_t)tile * GV_ROWS;
+    const int64_t total_chunks = K / GV_KC;
+    const int64_t c_begin = (int64_t)split * chunks_per_split;
+    int nch = (int)(total_chunks - c_begin);
+    if (nch > chunks_per_split) nch = chunks_per_split;
+
+    const WSrc src = make_wsrc<FMT, PK>(w, scales, row0, N, K, lane, wv);
+    const __amdgpu_buffer_rsrc_t xrsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)((int64_t)T * K * 2), BUF_FLAGS);
+    // byte offset of the lane's B fragment (token cb * 16 + li, k-step 2 wv + ls) in chunk 0
+    int xoff[2][NCB];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = (n0 + r < N) ? v[r] * bf16_bits_to_f32(rs[n0 + r]) : 0.f;
-        }
-        if (bf16_out) {
-            uint16_t* yo = reinterpret_cast<uint16_t*>(y) + (int64_t)t * N;
-            if (n0 + 3 < N && (N & 3) == 0) {
-                *reinterpret_cast<uint2*>(yo + n0) =
-                    make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                               f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
-            } else {
+    for (int ls = 0; ls < 2; ++ls)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (n0 + r < N) yo[n0 + r] = (uint16_t)f32_to_bf16_rne(v[r]);
-            }
-        } else {
-            float* yo = reinterpret_cast<float*>(y) + (int64_t)t * N;
-            if (n0 + 3 < N && (N & 3) == 0) {
-                *reinterpret_cast<v4f*>(yo + n0) = v;
-            } else {
+        for (int cb = 0; cb < NCB; ++cb)
+            xoff[ls][cb] = (int)(((int64_t)(cb * 16 + li) * K + kstep_col<FMT>(2 * wv + ls, lg)) * 2);
+
+    struct XFrag {
+        uint4 v[2][NCB];
+    };
+    WChunk<FMT> wr[D];
+    XFrag xr[D];
+    auto load = [&](int u, int64_t c) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (n0 + r < N) yo[n0 + r] = v[r];
+        for (int ls = 0; ls < 2; ++ls)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+                xr[u].v[ls][cb] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, xoff[ls][cb] + (int)(c * GV_KC * 2), 0, 0));
+        load_chunk<FMT, PK>(wr[u], src, c);
+    };
+
+    v4f acc[4][NCB];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int u) {
+#pragma unroll
+        for (int ls = 0; ls < 2; ++ls) {
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const v8bf a = decode_afrag<FMT>(wr[u], rb, ls);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        a, __builtin_bit_cast(v8bf, xr[u].v[ls][cb]), acc[rb][cb], 0, 0, 0);
             }
         }
     };
 
-    if (splits == 1) {
+    if (nch > 0) {
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) write_out(cb, acc[cb]);
-        return;
-    }
-    // Split-K through device-coherent atomic stores / loads (see gemv_mfma_kernel).
+        for (int d = 0; d < D; ++d) load(d, c_begin + min(d, nch - 1));
+        int c = 0;
+        for (; c + D <= nch; c += D) {
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-        const int t = cb * 16 + li;
-        if (t < T) {
-            uint32_t* p = reinterpret_cast<uint32_t*>(&partial[((int64_t)split * T + t) * npad + n0]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                __hip_atomic_store(p + r, __float_as_uint(acc[cb][r]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int u = 0; u < D; ++u) {
+                compute(u);
+                load(u, c_begin + min(c + u + D, nch - 1));
+                // keep each refill right after the compute that frees its slot
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == (unsigned)(splits - 1));
-    }
-    __syncthreads();
-    if (!s_last) return;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-        const int t = cb * 16 + li;
-        if (t >= T) continue;
-        v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < splits; ++s) {
-            const uint32_t* p = reinterpret_cast<const uint32_t*>(&partial[((int64_t)s * T + t) * npad + n0]);
-            v4f part;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                part[r] = __uint_as_float(__hip_atomic_load(p + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-            sum += part;
-        }
-        write_out(cb, sum);
+        for (int u = 0; u < D - 1; ++u)
+            if (c + u < nch) compute(u);
     }
-    if (tid == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    v4f fin[NCB];
+    reduce_waves<NCB>(acc, fin, red, wv, lane);
+    finish_tile<FMT, NCB>(fin, scales, T, N, row0, wv, lane, tile, split, splits, partial, counters, bf16_out, y,
+                          &s_last);
 }
 
 // ---------------------------------------------------------------------------
@@ -718,8 +805,9 @@ __global__ __launch_bounds__(64) void gemv_generic_kernel(const uint8_t* __restr
 // ---------------------------------------------------------------------------
 struct GemvPlan {
     bool mfma;
+    bool direct;             // activation fragments loaded per wave (formats without group scales)
     bool resident;           // activation slice staged once in LDS (no barriers in the loop)
-    int kc;                  // chunk width (256 or 128)
+    int kc;                  // chunk width (always GV_KC)
     int64_t tiles;
     int splits;
     int chunks_per_split;
@@ -736,18 +824,22 @@ static double fmt_bytes_per_weight(int fmt) {
     return fmt == W_Q4G64 ? 0.5 : (fmt == W_BF16 ? 2.0 : 1.0);
 }
 
+// Staged activations [Tc + 1][span + 8] and group scales [span / G][64]; at
+// least the 16 KiB per token block that the final cross-wave sum reuses.
 static int64_t resident_lds(int fmt, int64_t Tc, int64_t cps, int kc) {
     const int gs = fmt_group(fmt);
     const int64_t span = cps * kc;
-    return ((Tc + 1) * (span + 8) + (gs ? span / gs * GV_ROWS : 0)) * 2;
+    const int64_t stage = ((Tc + 1) * (span + 8) + (gs ? span / gs * GV_ROWS : 0)) * 2;
+    const int64_t red = 16384 * ((Tc + 15) / 16);
+    return stage > red ? stage : red;
 }
 
 static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K) {
     GemvPlan p{};
     // buffer offsets are 32-bit: the activation block must stay below 2 GiB
-    p.mfma = (K > 0) && (K % 128 == 0) && (Tc * K * 2 < ((int64_t)1 << 31)) &&
+    p.mfma = (K > 0) && (K % GV_KC == 0) && (Tc * K * 2 < ((int64_t)1 << 31)) &&
              (N * (K / 32) * 2 < ((int64_t)1 << 31));
-    p.kc = (K % 256 == 0) ? 256 : 128;
+    p.kc = GV_KC;
     p.tiles = (N + GV_ROWS - 1) / GV_ROWS;
     p.splits = 1;
     p.chunks_per_split = p.mfma ? (int)(K / p.kc) : 0;
@@ -768,10 +860,29 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K) {
     if (s0 > chunks / min_chunks) s0 = chunks / min_chunks;   // keep whole chunks per split
     if (s0 > 32) s0 = 32;
     if (s0 < 1) s0 = 1;
+    static const int mode = [] {      // 0 auto, 1 direct, 2 resident / streaming only
+        const char* e = getenv("NQ_GEMV_MODE");
+        return e ? atoi(e) : 0;
+    }();
+    if (fmt_group(fmt) == 0 && Tc <= 16 && mode != 2) {
+        // direct variant (no group scales, one token block): one workgroup per
+        // CU is enough (measured: more workgroups per CU only slow it down)
+        int64_t sd = ((int64_t)device_cu_count() + p.tiles - 1) / p.tiles;
+        if (sd > chunks / min_chunks) sd = chunks / min_chunks;
+        if (sd > 32) sd = 32;
+        if (sd < 1) sd = 1;
+        const int64_t cps = (chunks + sd - 1) / sd;
+        p.direct = true;
+        p.chunks_per_split = (int)cps;
+        p.splits = (int)((chunks + cps - 1) / cps);
+        return p;
+    }
     // resident variant: smallest split count >= s0 whose slice fits in LDS and
-    // whose FP32 partials stay within 12% of the weight bytes
+    // whose FP32 partials stay within 12% of the weight bytes; with more than
+    // one token block, only when the row tiles alone do not cover the CUs
     const double wbytes = (double)N * (double)K * fmt_bytes_per_weight(fmt);
-    for (int64_t s = s0; s <= 32 && s <= chunks; ++s) {
+    const bool try_resident = Tc <= 16 || p.tiles < (int64_t)device_cu_count();
+    for (int64_t s = s0; try_resident && s <= 32 && s <= chunks; ++s) {
         const int64_t cps = (chunks + s - 1) / s;
         const int64_t se = (chunks + cps - 1) / cps;
         const double partial_bytes = se > 1 ? 8.0 * (double)se * (double)Tc * (double)N : 0.0;
@@ -814,29 +925,37 @@ int64_t gemv_workspace_bytes(int fmt, int64_t T, int64_t N, int64_t K) {
     return need;
 }
 
-template <int FMT, int NCB, int KC, bool PK>
+template <int FMT, int NCB, bool PK>
 static void launch_mfma(const GemvPlan& p, const void* w, const void* scales, const uint16_t* x, int Tc, int64_t N,
                         int64_t K, bool bf16_out, void* y, float* partial, unsigned* counters,
                         hipStream_t stream) {
     dim3 grid((unsigned)p.tiles, (unsigned)p.splits);
+    if constexpr (group_size<FMT>() == 0) {
+        if (p.direct) {
+            gemv_direct_kernel<FMT, NCB, PK><<<grid, 256, 0, stream>>>(
+                reinterpret_cast<const uint8_t*>(w), scales, x, Tc, (int)N, K, p.chunks_per_split, p.splits, partial,
+                counters, bf16_out ? 1 : 0, y);
+            return;
+        }
+    }
     if (p.resident)
-        gemv_resident_kernel<FMT, NCB, KC, PK><<<grid, 256, (size_t)p.lds_bytes, stream>>>(
+        gemv_resident_kernel<FMT, NCB, PK><<<grid, 256, (size_t)p.lds_bytes, stream>>>(
             reinterpret_cast<const uint8_t*>(w), scales, x, Tc, (int)N, K, p.chunks_per_split, p.splits, partial,
             counters, bf16_out ? 1 : 0, y);
     else
-        gemv_mfma_kernel<FMT, NCB, KC, PK><<<grid, 256, 0, stream>>>(reinterpret_cast<const uint8_t*>(w), scales, x,
+        gemv_mfma_kernel<FMT, NCB, PK><<<grid, 256, 0, stream>>>(reinterpret_cast<const uint8_t*>(w), scales, x,
                                                                      Tc, (int)N, K, p.chunks_per_split, p.splits,
                                                                      partial, counters, bf16_out ? 1 : 0, y);
 }
 
-template <int FMT, int KC, bool PK>
+template <int FMT, bool PK>
 static void launch_ncb(const GemvPlan& p, const void* w, const void* scales, const uint16_t* x, int Tc, int64_t N,
                        int64_t K, bool bf16_out, void* y, float* partial, unsigned* counters, hipStream_t stream) {
     switch ((Tc + 15) / 16) {
-        case 1: launch_mfma<FMT, 1, KC, PK>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
-        case 2: launch_mfma<FMT, 2, KC, PK>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
-        case 3: launch_mfma<FMT, 3, KC, PK>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
-        default: launch_mfma<FMT, 4, KC, PK>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+        case 1: launch_mfma<FMT, 1, PK>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+        case 2: launch_mfma<FMT, 2, PK>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+        case 3: launch_mfma<FMT, 3, PK>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+        default: launch_mfma<FMT, 4, PK>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
     }
 }
 
@@ -845,13 +964,8 @@ static void launch_fmt(const GemvPlan& p, bool packed, const void* w, const void
                        int64_t N, int64_t K, bool bf16_out, void* y, float* partial, unsigned* counters,
                        hipStream_t stream) {
     if (p.mfma) {
-        if (packed) {
-            if (p.kc == 256) launch_ncb<FMT, 256, true>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream);
-            else launch_ncb<FMT, 128, true>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream);
-        } else {
-            if (p.kc == 256) launch_ncb<FMT, 256, false>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream);
-            else launch_ncb<FMT, 128, false>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream);
-        }
+        if (packed) launch_ncb<FMT, true>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream);
+        else launch_ncb<FMT, false>(p, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream);
     } else {
         dim3 grid((unsigned)N, (unsigned)((Tc + 7) / 8));
         gemv_generic_kernel<FMT><<<grid, 64, 0, stream>>>(reinterpret_cast<const uint8_t*>(w), scales, x, Tc,
@@ -861,19 +975,19 @@ static void launch_fmt(const GemvPlan& p, bool packed, const void* w, const void
 
 // ---------------------------------------------------------------------------
 // Packed weight layout.  Rows are grouped in blocks of 16 (the last block
-// zero-padded).  Chunk-major: for every chunk c of KC columns, for every row
-// block, for every piece q of the chunk, the 64 lanes' pieces are stored one
-// after another in lane order (lane = 16 g + i holds row i, lane group g).  A
-// wave reading chunk c of its block reads NP runs of 64 x piece contiguous
+// zero-padded).  Chunk-major: for every chunk c of 256 columns, for every row
+// block, for every piece q of the chunk (see PieceFmt), the 64 lanes' pieces
+// are stored one after another in lane order (lane = 16 g + i holds row i,
+// lane group g).  Every load instruction of a wave reads 64 x piece contiguous
 // bytes, and the waves of the whole grid, walking chunk by chunk, sweep one
 // contiguous window of memory at a time.  A pure permutation of the row-major
-// bytes; KC is 256 when K % 256 == 0, else 128.
+// bytes (K % 256 == 0).
 // ---------------------------------------------------------------------------
-template <int FMT, int KC>
+template <int FMT>
 __global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* __restrict__ src, int64_t N, int64_t K,
                                                            uint8_t* __restrict__ dst, int64_t n_pieces) {
-    constexpr int NP = WChunk<FMT, KC>::NP;
-    constexpr int PB = piece_bytes<FMT, KC>();
+    constexpr int NP = PieceFmt<FMT>::NP;
+    constexpr int PB = PieceFmt<FMT>::PB;
     const int64_t nrb = (N + 15) / 16;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_pieces; i += (int64_t)gridDim.x * 256) {
         // i = ((c * nrb + rb) * NP + q) * 64 + lane
@@ -885,7 +999,7 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* __rest
         const int64_t row = rb * 16 + (lane & 15);
         uint8_t* d = dst + i * PB;
         if (row < N) {
-            const uint8_t* s = src + row * row_bytes<FMT>(K) + piece_offset<FMT, KC>(c, q, lane >> 4);
+            const uint8_t* s = src + row * row_bytes<FMT>(K) + piece_offset<FMT>(c, q, lane >> 4);
             if constexpr (PB == 16) *reinterpret_cast<uint4*>(d) = *reinterpret_cast<const uint4*>(s);
             else *reinterpret_cast<uint2*>(d) = *reinterpret_cast<const uint2*>(s);
         } else {
@@ -903,20 +1017,13 @@ int64_t packed_weight_bytes(int fmt, int64_t N, int64_t K) {
     return (N + 15) / 16 * 16 * row_bytes_host(fmt, K);
 }
 
-template <int FMT, int KC>
-static void launch_pack(const void* src, int64_t N, int64_t K, void* dst, hipStream_t stream) {
-    constexpr int NP = WChunk<FMT, KC>::NP;
-    const int64_t n_pieces = (N + 15) / 16 * (K / KC) * NP * 64;
-    int64_t blocks = (n_pieces + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    pack_weights_kernel<FMT, KC><<<(unsigned)blocks, 256, 0, stream>>>(reinterpret_cast<const uint8_t*>(src), N, K,
-                                                                       reinterpret_cast<uint8_t*>(dst), n_pieces);
-}
-
 template <int FMT>
 static void launch_pack_fmt(const void* src, int64_t N, int64_t K, void* dst, hipStream_t stream) {
-    if (K % 256 == 0) launch_pack<FMT, 256>(src, N, K, dst, stream);
-    else launch_pack<FMT, 128>(src, N, K, dst, stream);
+    const int64_t n_pieces = (N + 15) / 16 * (K / GV_KC) * PieceFmt<FMT>::NP * 64;
+    int64_t blocks = (n_pieces + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    pack_weights_kernel<FMT><<<(unsigned)blocks, 256, 0, stream>>>(reinterpret_cast<const uint8_t*>(src), N, K,
+                                                                   reinterpret_cast<uint8_t*>(dst), n_pieces);
 }
 
 hipError_t launch_pack_weights(int fmt, const void* src, int64_t N, int64_t K, void* dst, hipStream_t stream) {

@@ -132,6 +132,17 @@ def test_linear_validation(L):
     assert f(A, 0, A, A, 8, 64, 1, None, None, 0, None, None, 0, None) == nq.NQ_OK
 
 
+def test_packed_validation(L):
+    # the packed layout exists for K % 256 == 0 only
+    assert L.nq_pack_weights(-1, A, 8, 384, A, None) == nq.NQ_ERR_SHAPE
+    assert L.nq_pack_weights(9, A, 8, 512, A, None) == nq.NQ_ERR_FORMAT
+    assert L.nq_pack_weights(-1, None, 8, 512, A, None) == nq.NQ_ERR_NULL
+    assert L.nq_gemv_fp8row_packed(A, A, A, 4, 8, 384, 0, A, None, 0, None) == nq.NQ_ERR_SHAPE
+    assert L.nq_gemv_qgroup_packed(nq.NQ_W_Q8G32_F16S, A, A, A, 4, 8, 640, 0, A, None, 0, None) == nq.NQ_ERR_SHAPE
+    assert L.nq_packed_weight_bytes(nq.NQ_W_Q4G64_F16S, 17, 512) == 32 * 256
+    assert L.nq_packed_weight_bytes(nq.NQ_W_BF16, 16, 256) == 16 * 512
+
+
 def test_workspace_query_is_host_only(L):
     assert L.nq_gemv_workspace_bytes(-1, -1, 8, 64) == 0
     assert L.nq_gemv_workspace_bytes(-1, 4, 8, 100) == 0       # fallback path needs none
