@@ -168,7 +168,23 @@ __global__ __launch_bounds__(256) void encode_rows_kernel(RowSource<SRC> src, in
     if (tid == 0) out_scale[orow] = (uint16_t)s_bits;
 
     uint8_t* orow_ptr = out_codes + orow * K;
-    if (vec) {
+    // A finite positive scale bounds every quotient by 448 / (1 - 2^-9) < 464,
+    // the range where the hardware convert is exact; other rows (all zero, NaN,
+    // infinite) take the per-element path.
+    const bool fast = s > 0.0f && s < __uint_as_float(0x7F800000u);
+    const double r = 1.0 / (double)s;
+    if (vec && fast) {
+        for (int64_t k = (int64_t)tid * 16; k < K; k += 256 * 16) {
+            float v[16];
+            src.load16(row, k, v);
+            uint32_t d[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                d[q] = f32x4_to_e4m3_hw(div_via_recip64(v[4 * q], r), div_via_recip64(v[4 * q + 1], r),
+                                        div_via_recip64(v[4 * q + 2], r), div_via_recip64(v[4 * q + 3], r));
+            *reinterpret_cast<uint4*>(orow_ptr + k) = make_uint4(d[0], d[1], d[2], d[3]);
+        }
+    } else if (vec) {
         for (int64_t k = (int64_t)tid * 16; k < K; k += 256 * 16) {
             float v[16];
             src.load16(row, k, v);
@@ -237,11 +253,12 @@ __global__ __launch_bounds__(256) void quantize_int8_g64_kernel(const uint16_t* 
         nan |= __shfl_xor(nan, off, 64);
     }
     const float s = nan ? __uint_as_float(0x7FC00000u) : m / 127.0f;
+    const double r = 1.0 / (double)s;          // x / s below: BF16 over FP32, exact (div_via_recip64)
     uint32_t lo = 0, hi = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) lo |= ((uint32_t)f32_to_i8_sat(v[e] / s) & 0xFFu) << (8 * e);
+    for (int e = 0; e < 4; ++e) lo |= ((uint32_t)f32_to_i8_sat(div_via_recip64(v[e], r)) & 0xFFu) << (8 * e);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) hi |= ((uint32_t)f32_to_i8_sat(v[4 + e] / s) & 0xFFu) << (8 * e);
+    for (int e = 0; e < 4; ++e) hi |= ((uint32_t)f32_to_i8_sat(div_via_recip64(v[4 + e], r)) & 0xFFu) << (8 * e);
     if (live) {
         reinterpret_cast<uint2*>(q)[i] = make_uint2(lo, hi);
         if ((i & 7) == 0) scale[i >> 3] = s;
@@ -301,7 +318,23 @@ __global__ __launch_bounds__(256) void quantize_fp8_row_kernel(const uint16_t* _
     const float s = nan ? __uint_as_float(0x7FC00000u) : m / 448.0f;
     if (tid == 0) scale[row] = s;
     uint8_t* cr = codes + row * K;
-    if (vec) {
+    // finite positive scale: every quotient is at most 448 (1 + 2^-23) < 464
+    const bool fast = s > 0.0f && s < __uint_as_float(0x7F800000u);
+    const double r = 1.0 / (double)s;
+    if (vec && fast) {
+        for (int64_t k = (int64_t)tid * 8; k < K; k += 256 * 8) {
+            const uint4 a = *reinterpret_cast<const uint4*>(xr + k);
+            const uint32_t d[4] = {a.x, a.y, a.z, a.w};
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[2 * e] = div_via_recip64(__uint_as_float(d[e] << 16), r);
+                f[2 * e + 1] = div_via_recip64(__uint_as_float(d[e] & 0xFFFF0000u), r);
+            }
+            *reinterpret_cast<uint2*>(cr + k) =
+                make_uint2(f32x4_to_e4m3_hw(f[0], f[1], f[2], f[3]), f32x4_to_e4m3_hw(f[4], f[5], f[6], f[7]));
+        }
+    } else if (vec) {
         for (int64_t k = (int64_t)tid * 8; k < K; k += 256 * 8) {
             const uint4 a = *reinterpret_cast<const uint4*>(xr + k);
             const uint32_t d[4] = {a.x, a.y, a.z, a.w};

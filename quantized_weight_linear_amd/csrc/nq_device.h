@@ -81,6 +81,26 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_sat(float f) {
     return sign | (uint32_t)__builtin_rintf(t);           // 0..8 quanta of 2^-9, RNE
 }
 
+// x / s as the IEEE FP32 quotient, computed as RN32((double)x * r) with
+// r = RN64(1 / s) (one FP64 division per row or group).  Exact whenever x and
+// s together carry at most 32 significant bits (an FP32 numerator over a BF16
+// scale, or a BF16 numerator over an FP32 scale): such a quotient is either an
+// FP32 value itself or at least 2^-33 (relative) away from every FP32 rounding
+// boundary, while the FP64 product lies within 2^-52 of it, so both round to
+// the same FP32 value.  The IEEE special cases carry over: x * inf = x / 0,
+// 0 * inf = NaN = 0 / 0, x * 0 = x / inf, NaN stays NaN.
+__device__ __forceinline__ float div_via_recip64(float x, double r) { return (float)((double)x * r); }
+
+// Four FP32 values -> four E4M3 codes (bytes 0..3), round to nearest even, by
+// the hardware convert.  It agrees with f32_to_e4m3_sat for every |v| < 464
+// (checked exhaustively on all such FP32 inputs, both signs); callers pass
+// only such values.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3_hw(float a, float b, float c, float d) {
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+    return (uint32_t)r;
+}
+
 // FP32 -> int8 code: round to nearest even, clamp to [-127, 127], NaN -> 0.
 __device__ __forceinline__ int32_t f32_to_i8_sat(float f) {
     float r = __builtin_rintf(f);
