@@ -7,9 +7,9 @@
 //
 // Staging.  Codes go from memory straight into LDS with buffer loads in LDS
 // mode (no VGPR round trip, no VALU work): one load instruction of a wave
-// writes 1 KB of LDS in lane order, and each lane fetches the 16 bytes that
-// the MFMA fragment read of the same lane wants, so a fragment read is a
-// contiguous, conflict-free ds_read.  One stage holds 64 K-columns of both
+// writes 1 KB of LDS in lane order, four lanes per row reading the row's 64
+// contiguous bytes of the stage; the 16-byte pieces of a row are XOR-swizzled
+// so that the MFMA fragment reads (16 bytes per lane) are conflict-free.  One stage holds 64 K-columns of both
 // panels (plus, for W8A8, the group's activation and weight scales); a ring of
 // 4 stages keeps 3 stages in flight while one is consumed, with one barrier
 // per stage.  Rows past M / N and columns past K are out of the buffer range
@@ -126,10 +126,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
         else rs = buffer_desc(w_scale + (int64_t)n0 * G, (uint32_t)(rows_b * G * 2));
     }
 
-    // Loader lanes: wave wv fills fragment blocks (i4 = wv, p = 0, 1) of both
-    // panels; lane L fetches row 32 wv + L % 32, columns k0 + 32 p + 16 (L / 32) + [0, 16).
-    const int lrow = 32 * wv + (lane & 31);
-    const int lk = 16 * (lane >> 5);
+    // Panel layout in LDS: row r of the tile at byte 64 r, its 16-byte piece c
+    // (columns k0 + 16 c + [0, 16)) in slot c ^ ((r >> 2) & 3).  Loader lanes:
+    // wave wv issues two loads per panel, load p covering rows 32 wv + 16 p +
+    // [0, 16); lane L writes slot L % 4 of row L / 4 of those, so four lanes
+    // read one row's 64 contiguous bytes (one full memory request).  The XOR
+    // keeps fragment reads conflict-free (see frag_off).
+    const int lrow = 32 * wv + (lane >> 2);             // + 16 p
+    const int lk = 16 * ((lane & 3) ^ ((lrow >> 2) & 3));
     const int voff_ab = lrow * K + lk;
     const int voff_s = W8A8 ? (wv < 2 ? (64 * wv + lane) * G * 4 : (64 * (wv - 2) + lane) * G * 2) : 0;
 
@@ -137,9 +141,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
         const int k0 = s < nsteps ? s * GB_K : GB_OOB;   // stages past the end load nothing
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            int vo = voff_ab + k0 + 32 * p;
+            // rows 16 p further down keep (r >> 2) & 3, so the same piece order applies
+            int vo = voff_ab + 16 * p * K + k0;
             if constexpr (KTAIL) {
-                if (k0 + 32 * p + lk >= K) vo = GB_OOB;      // K % 16 == 0: pieces are whole
+                if (k0 + lk >= K) vo = GB_OOB;                // K % 16 == 0: pieces are whole
             }
             lds_dma<16>(ra, lds_addr(&S.a[(2 * wv + p) * 1024]), vo);
             lds_dma<16>(rb, lds_addr(&S.b[(2 * wv + p) * 1024]), vo);
@@ -159,6 +164,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+    // Byte offset of this lane's 16-byte fragment piece in a panel: row
+    // rt + lane % 32 of the tile, piece c0 + lane / 32.  Within a quarter wave
+    // (16 lanes, 16 rows, one piece) the XOR spreads the rows over all 16
+    // four-bank groups.
+    auto frag_off = [&](int rt, int c0) {
+        const int r = rt + (lane & 31);
+        return 64 * r + 16 * ((c0 + (lane >> 5)) ^ ((r >> 2) & 3));
+    };
+
     // W8A8, MFMA part of one stage: d = 12582912 + P (as float bits) for the
     // wave's 2 x 2 tiles.
     auto mfma_i8 = [&](const GemmStage& S, v16i (&d)[2][2]) {
@@ -170,10 +184,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
             v4i af[2], bf[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                af[i] = *reinterpret_cast<const v4i*>(&S.a[((2 * wm + i) * 2 + h) * 1024 + 16 * lane]);
+                af[i] = *reinterpret_cast<const v4i*>(&S.a[frag_off(64 * wm + 32 * i, 2 * h)]);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                bf[j] = *reinterpret_cast<const v4i*>(&S.b[((2 * wn + j) * 2 + h) * 1024 + 16 * lane]);
+                bf[j] = *reinterpret_cast<const v4i*>(&S.b[frag_off(64 * wn + 32 * j, 2 * h)]);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -222,10 +236,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
         }
     };
 
-    // FP8, one stage.  A fragment block holds, for lane L, 16 consecutive
-    // codes of one row (k = 32 p + 16 (L / 32) + [0, 16)); each lane reads its
-    // 16 bytes at once (a contiguous, conflict-free 1 KB per wave) and feeds
-    // bytes [0, 8) to one 32x32x16 MFMA and bytes [8, 16) to a second.  The
+    // FP8, one stage.  For column pair p each lane reads 16 consecutive codes
+    // of its row (k = 32 p + 16 (lane / 32) + [0, 16)) in one conflict-free
+    // read and feeds bytes [0, 8) to one 32x32x16 MFMA and bytes [8, 16) to a
+    // second.  The
     // first MFMA thus sums k in {32p + [0,8), 32p + 16 + [0,8)}, the second the
     // other 16: the A and B fragments use the same lane -> k assignment, so
     // the two MFMAs together form the exact dot product over the 32 columns.
@@ -235,10 +249,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
             uint4 ca[2], cb[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                ca[i] = *reinterpret_cast<const uint4*>(&S.a[((2 * wm + i) * 2 + p) * 1024 + 16 * lane]);
+                ca[i] = *reinterpret_cast<const uint4*>(&S.a[frag_off(64 * wm + 32 * i, 2 * p)]);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                cb[j] = *reinterpret_cast<const uint4*>(&S.b[((2 * wn + j) * 2 + p) * 1024 + 16 * lane]);
+                cb[j] = *reinterpret_cast<const uint4*>(&S.b[frag_off(64 * wn + 32 * j, 2 * p)]);
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 v8bf af[2], bf[2];
