@@ -1,16 +1,17 @@
 """Benchmark of the quantized-weight linear projection on one MI355X.
 
 One step runs every row of the hot path once on its workload, inputs already
-resident in HBM:
-  decode_mxfp8   MXFP8 256x512 decode (FP32 out)            + MXFP8 GEMV T=1
-  reencode       block-128 E4M3 -> per-row FP8, 5120x17408
-  gemv_fp8row    row-FP8 17408x5120, T = 1, 4, 16, 33 (BF16 out)   <- headline
-  gemv_down      re-encoded 5120x17408, T = 1, 33; BF16 gate 96x5120, T = 1, 33
-  gemv_q4g64 / gemv_q8g32   at 17408x5120 and 5120x17408, T = 1, 8, 33
-  head           row-FP8 152064x5120, T = 1..64
+resident in HBM, in this order (prefill and conversions before decode, as in
+an engine step):
   quant_int8     1792x5120 per-token-per-64 int8 quantization
   gemm_w8a8      W8A8 GEMM M=1792, N=17408, K=5120
   gemm_fp8       per-token E4M3 quantization + FP8 GEMM, same shape
+  reencode       block-128 E4M3 -> per-row FP8, 5120x17408
+  gemv_down      re-encoded 5120x17408, T = 1, 33; BF16 gate 96x5120, T = 1, 33
+  decode_mxfp8   MXFP8 256x512 decode (FP32 out)            + MXFP8 GEMV T=1
+  head           row-FP8 152064x5120, T = 1..64
+  gemv_q4g64 / gemv_q8g32   at 17408x5120 and 5120x17408, T = 1, 8, 33
+  gemv_fp8row    row-FP8 17408x5120, T = 1, 4, 16, 33 (BF16 out)   <- headline
 Weights of the decode GEMVs rotate over copies totalling more than 512 MB so
 that the 256 MB last-level cache cannot serve them.  Every launch is bracketed
 by HIP events on the stream it runs on; per-row averages come from those.
@@ -304,20 +305,26 @@ def build_rows(selected):
     def want(name):
         return groups is None or name in groups
 
+    # Order within a step: prefill and conversion work first, decode work
+    # after it, as in an engine step.  Kernels that write large outputs (the
+    # GEMMs' 125 MB, the re-encode's 89 MB) leave dirty lines in the
+    # memory-side cache, and the next kernel pays for writing them back
+    # (a decode GEMV measured right after a 256 MiB fill runs ~16 us slower),
+    # so the decode rows follow other decode rows, whose outputs are small.
     rows = []
-    if want("decode_mxfp8"):
-        rows += rows_mxfp8(nq, W)
-    if want("gemv_fp8row"):
-        rows += rows_gemv_fp8row(nq, W)
+    if want("quant_int8") or want("gemm_w8a8") or want("gemm_fp8"):
+        rows += rows_prefill(nq, W, want("quant_int8"), want("gemm_w8a8"), want("gemm_fp8"))
     if want("reencode") or want("gemv_down"):
         rows += rows_reencode_and_down(nq, W, want("reencode"), want("gemv_down"))
+    if want("decode_mxfp8"):
+        rows += rows_mxfp8(nq, W)
+    if want("head"):
+        rows += rows_head(nq, W)
     for name in ("q4g64", "q8g32"):
         if want(f"gemv_{name}"):
             rows += rows_grouped(nq, W, name)
-    if want("head"):
-        rows += rows_head(nq, W)
-    if want("quant_int8") or want("gemm_w8a8") or want("gemm_fp8"):
-        rows += rows_prefill(nq, W, want("quant_int8"), want("gemm_w8a8"), want("gemm_fp8"))
+    if want("gemv_fp8row"):
+        rows += rows_gemv_fp8row(nq, W)
     _torch().cuda.synchronize()
     return rows
 
