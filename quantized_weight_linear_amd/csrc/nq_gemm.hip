@@ -61,8 +61,10 @@ struct GemmCfg {
     static_assert((BM + BN) % (16 * NW) == 0, "panel loads must divide evenly over the waves");
 };
 
+// 16-byte aligned size: every stage of the ring starts on a 16-byte boundary,
+// so fragment reads stay single 16-byte LDS reads.
 template <bool W8A8>
-struct GemmStage {
+struct alignas(16) GemmStage {
     static constexpr int BM = GemmCfg<W8A8>::BM, BN = GemmCfg<W8A8>::BN;
     uint8_t a[BM * GB_K];
     uint8_t b[BN * GB_K];
