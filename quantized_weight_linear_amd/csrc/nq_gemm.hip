@@ -11,16 +11,18 @@
 //
 // Staging.  Codes go from memory straight into LDS with buffer loads in LDS
 // mode (no VGPR round trip, no VALU work): one load instruction of a wave
-// writes 1 KB of LDS in lane order, four lanes per row reading the row's 64
-// contiguous bytes of the stage; the 16-byte pieces of a row are XOR-swizzled
-// so that the MFMA fragment reads (16 bytes per lane) are conflict-free.  One
-// stage holds 64 K-columns of both panels (plus, for W8A8, the group's
-// activation and weight scales); a ring of S stages keeps S - 1 in flight
-// while one is consumed, with one barrier per stage.  Rows past M / N and
-// columns past K are out of the buffer range and read as zero.
+// writes 1 KB of LDS in lane order, eight lanes per row reading the row's 128
+// contiguous bytes of the stage.  Whole 128-byte lines per row matter: loads
+// of 64 bytes per row reach about half the L2-to-CU rate.  The 16-byte pieces
+// of a row are XOR-swizzled so that the MFMA fragment reads (16 bytes per
+// lane) are conflict-free.  One stage holds 128 K-columns of both panels
+// (plus, for W8A8, the activation and weight scales of its two groups); a
+// ring of S stages (W8A8 3, FP8 2: as many as LDS holds) with one barrier per
+// stage.  Rows past M / N and columns past K are out of the buffer range or
+// masked, and read as zero.
 //
-// W8A8 (one stage = one 64-channel group): two v_mfma_i32_32x32x32_i8 per
-// tile sum the group exactly in int32.  The first MFMA's C operand is the
+// W8A8 (64-channel groups, two per stage): two v_mfma_i32_32x32x32_i8 per
+// tile sum a group exactly in int32.  The first MFMA's C operand is the
 // constant 0x4B400000 (the float 1.5 * 2^23), so the int32 result D = C + P
 // read as a float is exactly 12582912 + P for |P| < 2^22 (here |P| <= 64 *
 // 128^2).  The rescale is then two FP32 FMAs per element:
@@ -38,6 +40,8 @@
 // MFMA is not used: its dot products are not FP32-accurate (relative errors of
 // a few 1e-5 were measured on one instruction), outside this path's 1e-5
 // bound.  y = (acc * a_scale[m]) * w_scale[n] at the end.
+#include <type_traits>
+
 #include "nq_device.h"
 #include "nq_launch.h"
 
@@ -46,7 +50,7 @@
 
 namespace nq {
 
-constexpr int GB_K = 64;     // K columns (bytes) per stage
+constexpr int GB_K = 128;    // K columns (bytes) per stage: whole 128-byte lines of every row
 constexpr unsigned GB_FLAGS = 0x00020000u;
 constexpr int GB_OOB = 0x40000000;   // a buffer offset past every range used here
 
@@ -54,11 +58,15 @@ template <bool W8A8>
 struct GemmCfg {
     static constexpr int WM = W8A8 ? 4 : 4, WN = W8A8 ? 2 : 2;   // wave grid
     static constexpr int TM = W8A8 ? 2 : 2, TN = W8A8 ? 2 : 4;   // 32 x 32 tiles per wave
-    static constexpr int S = W8A8 ? 4 : 4;                       // stages in the LDS ring
+    static constexpr int S = W8A8 ? 3 : 2;                       // stages in the LDS ring
     static constexpr int NW = WM * WN;
     static constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
-    static constexpr int LOADS = (BM + BN) / 16 / NW;   // panel loads per wave and stage (16 rows each)
-    static_assert((BM + BN) % (16 * NW) == 0, "panel loads must divide evenly over the waves");
+    static constexpr int LOADS = (BM + BN) / 8 / NW;    // panel loads per wave and stage (8 rows each)
+    static_assert((BM + BN) % (8 * NW) == 0, "panel loads must divide evenly over the waves");
+    // W8A8 scale loads per stage: two groups of activation scales (BM / 64
+    // loads each) and of weight scales (BN / 64 each), two per wave.
+    static constexpr int SCALE_LOADS = W8A8 ? 2 : 0;
+    static_assert(!W8A8 || BM / 64 + BN / 64 <= NW, "scale load plan");
 };
 
 // 16-byte aligned size: every stage of the ring starts on a 16-byte boundary,
@@ -68,10 +76,10 @@ struct alignas(16) GemmStage {
     static constexpr int BM = GemmCfg<W8A8>::BM, BN = GemmCfg<W8A8>::BN;
     uint8_t a[BM * GB_K];
     uint8_t b[BN * GB_K];
-    float as[W8A8 ? BM : 1];       // W8A8: activation scales of the stage's group
-    uint32_t ws[W8A8 ? BN : 1];    // W8A8: weight scales of the stage's group (FP16 bits, zero-extended:
-                                   // a 2-byte load in LDS mode still writes 4 bytes per lane)
-    uint32_t sink[W8A8 ? 64 : 1];  // W8A8: target of the empty scale loads (they write zeros)
+    float as[W8A8 ? 2 * BM : 1];       // W8A8: activation scales of the stage's two groups
+    uint32_t ws[W8A8 ? 2 * BN : 1];    // W8A8: weight scales of the two groups (FP16 bits, zero-extended:
+                                       // a 2-byte load in LDS mode still writes 4 bytes per lane)
+    uint32_t sink[W8A8 ? 128 : 1];     // W8A8: target of the empty scale loads (they write zeros)
 };
 
 // 32x32 MFMA output layout: lane l holds column (l % 32) and rows
@@ -120,7 +128,7 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
     int32_t* __restrict__ group_sums) {
     using C = GemmCfg<W8A8>;
     constexpr int BM = C::BM, BN = C::BN, TM = C::TM, TN = C::TN, S = C::S;
-    constexpr int DMA_PER_STAGE = C::LOADS + (W8A8 ? 1 : 0);   // load instructions per wave and stage
+    constexpr int DMA_PER_STAGE = C::LOADS + C::SCALE_LOADS;   // load instructions per wave and stage
     __shared__ __attribute__((aligned(16))) GemmStage<W8A8> st[S];
     __shared__ float s_rs[W8A8 ? 1 : BM + BN];                 // FP8: token scales, then weight-row scales
 
@@ -128,9 +136,18 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches, SGPR resources
     const int wm = wv % C::WM, wn = wv / C::WM;
-    const int m0 = blockIdx.y * BM;
-    const int n0 = blockIdx.x * BN;
-    const int G = K >> 6;
+    // Tile order.  Workgroups are handed to the 8 XCDs round-robin by linear
+    // id, and each XCD has its own L2.  Workgroup b runs on XCD b % 8, and
+    // XCD j's workgroups take a contiguous range of tiles in M-fastest order:
+    // the ones that share an L2 at the same time cover all M tiles of a few
+    // N tiles, so each panel slice enters that L2 about once.
+    const int tiles_m = (M + BM - 1) / BM;
+    const int b = blockIdx.x;
+    const int xq = (int)gridDim.x / 8, xr = (int)gridDim.x % 8;   // XCD j gets xq + (j < xr) tiles
+    const int t = (b % 8) * xq + min(b % 8, xr) + b / 8;
+    const int m0 = (t % tiles_m) * BM;
+    const int n0 = (t / tiles_m) * BN;
+    const int G = K >> 6;                       // W8A8: 64-channel groups, two per stage
     const int nsteps = (K + GB_K - 1) / GB_K;
     const int rows_a = min(M - m0, BM);
     const int rows_b = min(N - n0, BN);
@@ -139,63 +156,88 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
     const v4u ra = buffer_desc(A + (int64_t)m0 * K, (uint32_t)(rows_a * K));
     const v4u rb = buffer_desc(W + (int64_t)n0 * K, (uint32_t)(rows_b * K));
 
-    // Panel layout in LDS: row r of a panel at byte 64 r, its 16-byte piece c
-    // (columns k0 + 16 c + [0, 16)) in slot c ^ ((r >> 2) & 3).  Panel loads
-    // cover 16 rows each: A rows first, then B rows; wave wv issues loads
-    // wv * LOADS + [0, LOADS).  Lane L writes slot L % 4 of row L / 4 of its
-    // load, so four lanes read one row's 64 contiguous bytes (one full memory
-    // request).  The XOR keeps fragment reads conflict-free (see frag_off).
-    const int lr = lane >> 2;
-    const int lk = 16 * ((lane & 3) ^ ((lr >> 2) & 3));   // (r >> 2) & 3 is the same for r = 16 q + lr
+    // Panel layout in LDS: row r of a panel at byte 128 r, its 16-byte piece
+    // c (columns k0 + 16 c + [0, 16)) in slot c ^ ((r >> 1) & 7).  Panel
+    // loads cover 8 rows each: A rows first, then B rows; wave wv issues loads
+    // wv * LOADS + [0, LOADS).  Lane L writes slot L % 8 of row L / 8 of its
+    // load, so eight lanes read one row's 128 contiguous bytes (one whole
+    // cache line).  The XOR keeps fragment reads conflict-free (see frag_off).
+    const int lslot = lane & 7;
     int voff_ld[C::LOADS];
     uint32_t lds_ld_a[C::LOADS];   // LDS byte offset within the stage
+    int lk_ld[C::LOADS];           // column of the lane's piece within the stage
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
         const int q = wv * C::LOADS + i;                  // wave-uniform
-        const int row = 16 * (q < BM / 16 ? q : q - BM / 16) + lr;
-        voff_ld[i] = row * K + lk;
-        lds_ld_a[i] = (q < BM / 16) ? (uint32_t)(1024 * q) : (uint32_t)(BM * GB_K + 1024 * (q - BM / 16));
+        const int rq = q < BM / 8 ? q : q - BM / 8;       // load index within its panel
+        const int r = 8 * rq + (lane >> 3);               // row within the panel
+        lk_ld[i] = 16 * (lslot ^ ((r >> 1) & 7));
+        voff_ld[i] = r * K + lk_ld[i];
+        lds_ld_a[i] = (q < BM / 8) ? (uint32_t)(1024 * q) : (uint32_t)(BM * GB_K + 1024 * rq);
     }
-    // W8A8 scale loads: as rows in loads of 64 (BM / 64 of them), then ws rows
-    // (BN / 64); a wave without one issues an empty load so that every wave
-    // issues the same number per stage.
-    constexpr int NSL = W8A8 ? (BM + BN) / 64 : 0;
-    static_assert(NSL <= C::NW, "one scale load per wave at most");
+    // W8A8 scale loads, two per wave: slot z = 2 wv + u.  Slots [0, 2 BM/64)
+    // load activation scales (group h = z / (BM/64) of the stage, rows
+    // 64 (z % (BM/64)) + lane), the next 2 BN/64 slots weight scales alike,
+    // and the rest issue empty loads into sink, so that every wave issues the
+    // same number of loads per stage.
+    constexpr int NAS = W8A8 ? 2 * (BM / 64) : 0, NWS = W8A8 ? 2 * (BN / 64) : 0;
     v4u rs = ra;
-    int voff_s = GB_OOB, sz_s = 0;
-    uint32_t lds_s = 0;
+    int voff_s[2] = {GB_OOB, GB_OOB}, grp_s[2] = {0, 0}, sz_s = 0;
+    uint32_t lds_s[2] = {0, 0};
     if constexpr (W8A8) {
-        if (wv < BM / 64) {
+        if (2 * wv < NAS) {
             rs = buffer_desc(a_scale + (int64_t)m0 * G, (uint32_t)(rows_a * G * 4));
-            voff_s = (64 * wv + lane) * G * 4;
             sz_s = 4;
-            lds_s = (uint32_t)(offsetof(GemmStage<W8A8>, as) + 256 * wv);
-        } else {
-            const int j = wv - BM / 64;                    // past the ws loads: an empty load into sink
+        } else if (2 * wv < NAS + NWS) {
             rs = buffer_desc(w_scale + (int64_t)n0 * G, (uint32_t)(rows_b * G * 2));
-            voff_s = j < BN / 64 ? (64 * j + lane) * G * 2 : GB_OOB;
             sz_s = 2;
-            lds_s = j < BN / 64 ? (uint32_t)(offsetof(GemmStage<W8A8>, ws) + 256 * j)
-                                : (uint32_t)offsetof(GemmStage<W8A8>, sink);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int z = 2 * wv + u;
+            if (z < NAS) {
+                const int h = z / (BM / 64), jj = z % (BM / 64);
+                voff_s[u] = (64 * jj + lane) * G * 4;
+                grp_s[u] = h;
+                lds_s[u] = (uint32_t)(offsetof(GemmStage<W8A8>, as) + 4 * (h * BM + 64 * jj));
+            } else if (z < NAS + NWS) {
+                const int h = (z - NAS) / (BN / 64), jj = (z - NAS) % (BN / 64);
+                voff_s[u] = (64 * jj + lane) * G * 2;
+                grp_s[u] = h;
+                lds_s[u] = (uint32_t)(offsetof(GemmStage<W8A8>, ws) + 4 * (h * BN + 64 * jj));
+            } else {
+                lds_s[u] = (uint32_t)(offsetof(GemmStage<W8A8>, sink) + 256 * u);
+            }
         }
     }
 
-    auto issue = [&](GemmStage<W8A8>& Sg, int s) {
+    // Loads [lo, hi) of stage s (and, with lo == 0, its scale loads).  The
+    // loops issue a stage's loads in two parts after MFMAs have been queued:
+    // a wave blocks while the address unit takes its loads (64 per CU and
+    // stage), so issuing them all right after the barrier would leave the
+    // matrix unit idle.
+    auto issue = [&](GemmStage<W8A8>& Sg, int s, int lo, int hi) {
         const uint32_t base = lds_addr(&Sg);
         const int k0 = s < nsteps ? s * GB_K : GB_OOB;   // stages past the end load nothing
 #pragma unroll
         for (int i = 0; i < C::LOADS; ++i) {
+            if (i < lo || i >= hi) continue;
             const int q = wv * C::LOADS + i;
             int vo = voff_ld[i] + k0;
             if constexpr (KTAIL) {
-                if (k0 + lk >= K) vo = GB_OOB;                // K % 16 == 0: pieces are whole
+                if (k0 + lk_ld[i] >= K) vo = GB_OOB;          // K % 16 == 0: pieces are whole
             }
-            lds_dma<16>(q < BM / 16 ? ra : rb, base + lds_ld_a[i], vo);
+            lds_dma<16>(q < BM / 8 ? ra : rb, base + lds_ld_a[i], vo);
         }
         if constexpr (W8A8) {
-            const int g = s < nsteps ? s : GB_OOB / 8;
-            if (sz_s == 4) lds_dma<4>(rs, base + lds_s, voff_s + 4 * g);
-            else lds_dma<2>(rs, base + lds_s, voff_s >= GB_OOB ? GB_OOB : voff_s + 2 * g);
+            if (lo != 0) return;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int g = 2 * s + grp_s[u];                 // past the last group: an empty load
+                const bool live = voff_s[u] < GB_OOB && g < G;
+                if (sz_s == 4) lds_dma<4>(rs, base + lds_s[u], live ? voff_s[u] + 4 * g : GB_OOB);
+                else lds_dma<2>(rs, base + lds_s[u], live ? voff_s[u] + 2 * g : GB_OOB);
+            }
         }
     };
 
@@ -209,73 +251,91 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
 
     // Byte offset of this lane's 16-byte fragment piece in a panel: row
     // rt + lane % 32 of the panel, piece c0 + lane / 32.  Within a quarter
-    // wave (16 lanes, 16 rows, one piece) the XOR spreads the rows over all 16
-    // four-bank groups.
+    // wave (16 lanes, 16 rows, one piece) r & 1 and the XOR spread the rows
+    // over all 16 four-bank groups.
     auto frag_off = [&](int rt, int c0) {
         const int r = rt + (lane & 31);
-        return 64 * r + 16 * ((c0 + (lane >> 5)) ^ ((r >> 2) & 3));
+        return 128 * r + 16 * ((c0 + (lane >> 5)) ^ ((r >> 1) & 7));
     };
     const int wr0 = 32 * TM * wm;       // first panel row of the wave, A
     const int wc0 = 32 * TN * wn;       // ... and B
 
-    // W8A8, MFMA part of one stage: d = 12582912 + P (as float bits) for the
-    // wave's tiles.
-    auto mfma_i8 = [&](const GemmStage<W8A8>& Sg, v16i (&d)[TM][TN]) {
-        const v16i bias = {0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000,
-                           0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000,
-                           0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000};
+    // W8A8.  d holds 12582912 + P (as float bits) for the wave's tiles of one
+    // group.  mfma_group fills it for group gh of stage Mst.
+    v16i bias = {0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000,
+                 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000,
+                 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000};
+    v16i d[W8A8 ? TM : 1][W8A8 ? TN : 1];
+    auto load_frags = [&](const GemmStage<W8A8>& Mst, int mgh, v4i (&af)[2][TM], v4i (&bf)[2][TN]) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            v4i af[TM], bf[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const v4i*>(&Sg.a[frag_off(wr0 + 32 * i, 2 * h)]);
-#pragma unroll
-            for (int j = 0; j < TN; ++j) bf[j] = *reinterpret_cast<const v4i*>(&Sg.b[frag_off(wc0 + 32 * j, 2 * h)]);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
+                af[h][i] = *reinterpret_cast<const v4i*>(&Mst.a[frag_off(wr0 + 32 * i, 4 * mgh + 2 * h)]);
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    d[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], h == 0 ? bias : d[i][j], 0, 0, 0);
+            for (int j = 0; j < TN; ++j)
+                bf[h][j] = *reinterpret_cast<const v4i*>(&Mst.b[frag_off(wc0 + 32 * j, 4 * mgh + 2 * h)]);
         }
     };
-
-    // W8A8, rescale part: acc += (P * ws) * as with the group's scales.
-    auto rescale = [&](const GemmStage<W8A8>& Sg, const v16i (&d)[TM][TN], int s) {
+    auto mfma_group = [&](const GemmStage<W8A8>& Mst, int mgh) {
+        v4i af[2][TM], bf[2][TN];
+        load_frags(Mst, mgh, af, bf);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                d[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[0][i], bf[0][j], bias, 0, 0, 0);
+                d[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[1][i], bf[1][j], d[i][j], 0, 0, 0);
+            }
+    };
+    // One group step: rescale group g (group rgh of stage R) from d,
+    //     acc += (P * ws) * as,
+    // and, with MF, refill d tile by tile with the next group (group mgh of
+    // stage Mst): the matrix unit works on tile t while the vector ALU
+    // rescales tile t + 1, and only one set of group sums is live.  The MFMAs
+    // have no memory effects, so the compiler would otherwise hoist them all
+    // ahead of the rescale (keeping old and new sums live together): the
+    // empty asm takes the tile's rescaled acc as input and passes the bias
+    // operand through, which pins the tile's MFMAs after its rescale.
+    auto group_step = [&](auto mf, const GemmStage<W8A8>& R, int rgh, int g, const GemmStage<W8A8>& Mst, int mgh,
+                          auto after_row) {
+        constexpr bool MF = decltype(mf)::value;
+        v4i af[2][TM], bf[2][TN];
+        if constexpr (MF) load_frags(Mst, mgh, af, bf);
         float wsf[TN], wsc[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            wsf[j] = f16_bits_to_f32(Sg.ws[wc0 + 32 * j + (lane & 31)] & 0xFFFFu);
+            wsf[j] = f16_bits_to_f32(R.ws[rgh * BN + wc0 + 32 * j + (lane & 31)] & 0xFFFFu);
             wsc[j] = -12582912.0f * wsf[j];
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
+            v4f as4[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const v4f as4 = *reinterpret_cast<const v4f*>(&Sg.as[wr0 + 32 * i + 8 * q + 4 * (lane >> 5)]);
+            for (int q = 0; q < 4; ++q)
+                as4[q] = *reinterpret_cast<const v4f*>(&R.as[rgh * BM + wr0 + 32 * i + 8 * q + 4 * (lane >> 5)]);
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
+            for (int j = 0; j < TN; ++j) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int e = 4 * q + r;
-                        const float X = fmaf(__int_as_float(d[i][j][e]), wsf[j], wsc[j]);
-                        acc[i][j][e] = fmaf(X, as4[r], acc[i][j][e]);
-                    }
-            }
-        }
-        if constexpr (SUMS) {
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
+                for (int e = 0; e < 16; ++e) {
+                    const float X = fmaf(__int_as_float(d[i][j][e]), wsf[j], wsc[j]);
+                    acc[i][j][e] = fmaf(X, as4[e >> 2][e & 3], acc[i][j][e]);
+                }
+                if constexpr (SUMS) {
                     const int n = n0 + wc0 + 32 * j + (lane & 31);
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int m = m0 + wr0 + 32 * i + d_row(lane, e);
-                        if (m < M && n < N) group_sums[((int64_t)m * N + n) * G + s] = d[i][j][e] - 0x4B400000;
+                        if (m < M && n < N) group_sums[((int64_t)m * N + n) * G + g] = d[i][j][e] - 0x4B400000;
                     }
                 }
-            // the ring's wait counts only loads: drain these stores here
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                if constexpr (MF) {
+                    asm volatile("" : "+v"(bias) : "v"(acc[i][j]));
+                    d[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[0][i], bf[0][j], bias, 0, 0, 0);
+                    d[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[1][i], bf[1][j], d[i][j], 0, 0, 0);
+                }
+            }
+            after_row(i);
         }
     };
 
@@ -286,14 +346,31 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
     // the second the other 16: the A and B fragments use the same lane -> k
     // assignment, so the two MFMAs together form the exact dot product over
     // the 32 columns.
-    auto compute_fp8 = [&](const GemmStage<W8A8>& Sg) {
+    auto compute_fp8 = [&](const GemmStage<W8A8>& Sg, auto after_pair) {
+        constexpr int NP = GB_K / 32;
+        v4u ca[TM], cb[TN];
+        auto read_pair = [&](int p, v4u (&xa)[TM], v4u (&xb)[TN]) {
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            uint4 ca[TM], cb[TN];
+            for (int i = 0; i < TM; ++i) xa[i] = *reinterpret_cast<const v4u*>(&Sg.a[frag_off(wr0 + 32 * i, 2 * p)]);
 #pragma unroll
-            for (int i = 0; i < TM; ++i) ca[i] = *reinterpret_cast<const uint4*>(&Sg.a[frag_off(wr0 + 32 * i, 2 * p)]);
+            for (int j = 0; j < TN; ++j) xb[j] = *reinterpret_cast<const v4u*>(&Sg.b[frag_off(wc0 + 32 * j, 2 * p)]);
+        };
+        read_pair(0, ca, cb);
 #pragma unroll
-            for (int j = 0; j < TN; ++j) cb[j] = *reinterpret_cast<const uint4*>(&Sg.b[frag_off(wc0 + 32 * j, 2 * p)]);
+        for (int p = 0; p < NP; ++p) {
+            // The reads of pair p + 1 go out before pair p is converted and
+            // multiplied, so their latency hides behind this pair's MFMAs.
+            // The empty asm (a memory clobber, with pair p's codes passed
+            // through it) keeps the compiler from sinking those reads below
+            // the MFMAs.
+            v4u na[TM], nb[TN];
+            if (p + 1 < NP) read_pair(p + 1, na, nb);
+            if constexpr (TM == 2 && TN == 4)
+                asm volatile("" : "+v"(ca[0]), "+v"(ca[1]), "+v"(cb[0]), "+v"(cb[1]), "+v"(cb[2]), "+v"(cb[3]) :: "memory");
+            else if constexpr (TM == 2 && TN == 2)
+                asm volatile("" : "+v"(ca[0]), "+v"(ca[1]), "+v"(cb[0]), "+v"(cb[1]) :: "memory");
+            else
+                static_assert(TM == 2 && (TN == 2 || TN == 4), "operand list of the ordering asm");
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 v8bf af[TM], bf[TN];
@@ -319,6 +396,14 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
                     for (int j = 0; j < TN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
             }
+            __builtin_amdgcn_sched_barrier(0);   // pair p's MFMAs stay ahead of pair p + 1's wait
+            after_pair(p);
+            if (p + 1 < NP) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i) ca[i] = na[i];
+#pragma unroll
+                for (int j = 0; j < TN; ++j) cb[j] = nb[j];
+            }
         }
     };
 
@@ -328,7 +413,7 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
     };
 
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s) issue(st[s], s);
+    for (int s = 0; s < S - 1; ++s) issue(st[s], s, 0, C::LOADS);
     if constexpr (!W8A8) {
         for (int i = tid; i < BM + BN; i += 64 * C::NW) {
             s_rs[i] = i < BM ? (i < rows_a ? a_scale[m0 + i] : 0.f)
@@ -338,33 +423,32 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
     }
 
     if constexpr (W8A8) {
-        // Software pipeline: iteration s issues stage s + 1's MFMAs and then
-        // rescales stage s, whose MFMAs were issued one iteration earlier, so
-        // the matrix unit and the vector ALU of a wave work side by side.
-        // Buffers: MFMA(s + 1) reads stage s + 1, the rescale reads stage s's
-        // scales, and the refill of iteration s (stage s + S - 1) goes into
-        // the buffer of stage s - 1, which the barrier shows nobody reads any
-        // more.  Stage s + 1 must have landed: stages s + 2 .. s + S - 2 may
-        // still be in flight.
-        static_assert(S >= 3, "pipelined ring");
-        v16i d0[TM][TN], d1[TM][TN];
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_PER_STAGE * (S - 2)) : "memory");
+        // Stage s holds groups 2s and 2s + 1.  Iteration s: rescale(2s) with
+        // the MFMAs of 2s + 1 (both stage s); wait for stage s + 1 and pass the
+        // barrier; refill the buffer of stage s - 1 (whose last reader, the
+        // step of group 2s - 1, every wave has finished) with stage s + S - 1;
+        // rescale(2s + 1) from stage s with the MFMAs of 2s + 2 from stage
+        // s + 1.  Those MFMAs run unconditionally: past the last group the
+        // stage holds zeros and d is not used.  An odd last group (K % 128 ==
+        // 64) is rescaled after the loop.  With S = 3 one stage is in flight
+        // while two are read.
+        static_assert(S == 3, "ring of three stages");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_PER_STAGE) : "memory");
         sync_stage();
-        if (nsteps > 0) mfma_i8(st[0], d0);
-        for (int s = 0; s < nsteps; s += 2) {
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_PER_STAGE * (S - 3)) : "memory");
+        mfma_group(st[0], 0);
+        const int full = G >> 1;                       // stages with two groups
+        auto no_hook = [](int) {};
+        for (int s = 0; s < full; ++s) {
+            group_step(std::true_type{}, st[s % S], 0, 2 * s, st[s % S], 1, no_hook);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // also drains group-sum stores
             sync_stage();
-            issue(st[(s + S - 1) % S], s + S - 1);
-            if (s + 1 < nsteps) mfma_i8(st[(s + 1) % S], d1);
-            rescale(st[s % S], d0, s);
-            if (s + 1 < nsteps) {
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_PER_STAGE * (S - 3)) : "memory");
-                sync_stage();
-                issue(st[(s + S) % S], s + S);
-                if (s + 2 < nsteps) mfma_i8(st[(s + 2) % S], d0);
-                rescale(st[(s + 1) % S], d1, s + 1);
-            }
+            GemmStage<W8A8>& nxt = st[(s + S - 1) % S];
+            group_step(std::true_type{}, st[s % S], 1, 2 * s + 1, st[(s + 1) % S], 0, [&](int i) {
+                if (i == 0) issue(nxt, s + S - 1, 0, C::LOADS / 2);
+                if (i == TM - 1) issue(nxt, s + S - 1, C::LOADS / 2, C::LOADS);
+            });
         }
+        if (G & 1) group_step(std::false_type{}, st[full % S], 0, 2 * full, st[full % S], 0, no_hook);
     } else {
         // Ring: before consuming stage s this wave waits for its own loads of
         // stage s (the S - 2 later stages may stay in flight); the barrier
@@ -373,8 +457,11 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
         for (int s = 0; s < nsteps; ++s) {
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_PER_STAGE * (S - 2)) : "memory");
             sync_stage();
-            issue(st[(s + S - 1) % S], s + S - 1);
-            compute_fp8(st[s % S]);
+            GemmStage<W8A8>& nxt = st[(s + S - 1) % S];
+            compute_fp8(st[s % S], [&](int p) {
+                if (p == 0) issue(nxt, s + S - 1, 0, C::LOADS / 2);
+                if (p == 1) issue(nxt, s + S - 1, C::LOADS / 2, C::LOADS);
+            });
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the empty tail loads
@@ -406,8 +493,9 @@ static hipError_t launch_gemm_t(const uint8_t* A, const float* a_scale, const ui
                                 int64_t M, int64_t N, int64_t K, bool bf16_out, void* y, int32_t* sums,
                                 hipStream_t stream) {
     using C = GemmCfg<W8A8>;
-    dim3 grid((unsigned)((N + C::BN - 1) / C::BN), (unsigned)((M + C::BM - 1) / C::BM));
-    gemm_kernel<W8A8, SUMS, KTAIL><<<grid, 64 * C::NW, 0, stream>>>(A, a_scale, W, w_scale, (int)M, (int)N, (int)K,
+    const int64_t tiles = ((N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
+    if (tiles >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    gemm_kernel<W8A8, SUMS, KTAIL><<<dim3((unsigned)tiles), 64 * C::NW, 0, stream>>>(A, a_scale, W, w_scale, (int)M, (int)N, (int)K,
                                                                      bf16_out ? 1 : 0, y, sums);
     return hipGetLastError();
 }
@@ -424,9 +512,12 @@ hipError_t launch_gemm_w8a8(const int8_t* a_q, const float* a_scale, const int8_
     if (!gemm_shape_ok(M, N, K) || K % 64 != 0) return hipErrorInvalidValue;
     const uint8_t* A = reinterpret_cast<const uint8_t*>(a_q);
     const uint8_t* W = reinterpret_cast<const uint8_t*>(w_q);
+    const bool tail = K % GB_K != 0;   // an odd number of groups: the last stage holds one
     if (group_sums != nullptr)
-        return launch_gemm_t<true, true, false>(A, a_scale, W, w_scale, M, N, K, bf16_out, y, group_sums, stream);
-    return launch_gemm_t<true, false, false>(A, a_scale, W, w_scale, M, N, K, bf16_out, y, nullptr, stream);
+        return tail ? launch_gemm_t<true, true, true>(A, a_scale, W, w_scale, M, N, K, bf16_out, y, group_sums, stream)
+                    : launch_gemm_t<true, true, false>(A, a_scale, W, w_scale, M, N, K, bf16_out, y, group_sums, stream);
+    return tail ? launch_gemm_t<true, false, true>(A, a_scale, W, w_scale, M, N, K, bf16_out, y, nullptr, stream)
+                : launch_gemm_t<true, false, false>(A, a_scale, W, w_scale, M, N, K, bf16_out, y, nullptr, stream);
 }
 
 hipError_t launch_gemm_fp8(const uint8_t* a_codes, const float* a_scale, const uint8_t* w, const uint16_t* w_scale,

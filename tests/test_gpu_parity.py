@@ -409,7 +409,10 @@ def _w8a8_inputs(m, n, k, seed):
     return qa, sa, w, ws
 
 
-@pytest.mark.parametrize("m,n,k", [(64, 128, 5120), (70, 100, 640), (130, 257, 128), (1, 1, 64)])
+# (300, 300, 192) and (257, 129, 320): odd group counts (the last 128-column
+# stage holds one group) over several tiles in both directions
+@pytest.mark.parametrize("m,n,k", [(64, 128, 5120), (70, 100, 640), (130, 257, 128), (1, 1, 64), (300, 300, 192),
+                                   (257, 129, 320)])
 def test_w8a8_group_sums_and_output(m, n, k):
     qa, sa, w, ws = _w8a8_inputs(m, n, k, m + n + k)
     y32, y16 = empty((m, n), np.float32), empty((m, n), np.uint16)
@@ -451,7 +454,8 @@ def test_w8a8_config5_full_sampled():
     assert rel_fro(got, ref) <= FP32_TOL
 
 
-@pytest.mark.parametrize("m,n,k", [(70, 100, 400), (128, 256, 5120), (1, 3, 16), (129, 130, 256)])
+# (300, 520, 1040): K % 128 == 16 over 2 x 3 tiles
+@pytest.mark.parametrize("m,n,k", [(70, 100, 400), (128, 256, 5120), (1, 3, 16), (129, 130, 256), (300, 520, 1040)])
 def test_fp8_gemm(m, n, k):
     x = W.bf16_normal(W.rng(105, m + n + k), (m, k), outlier_p=0.01)
     w = W.bf16_normal(W.rng(106, m + n + k), (n, k), std=0.02)
