@@ -1,8 +1,8 @@
 """Benchmark of the quantized-weight linear projection on one MI355X.
 
-One step runs every row of the hot path once on its workload, inputs already
-resident in HBM, in this order (prefill and conversions before decode, as in
-an engine step):
+One step runs every row of the hot path on its workload, `--burst` launches
+of a row back to back (default 8), inputs already resident in HBM, in this
+order (prefill and conversions before decode, as in an engine step):
   quant_int8     1792x5120 per-token-per-64 int8 quantization
   gemm_w8a8      W8A8 GEMM M=1792, N=17408, K=5120
   gemm_fp8       per-token E4M3 quantization + FP8 GEMM, same shape
@@ -13,8 +13,10 @@ an engine step):
   gemv_q4g64 / gemv_q8g32   at 17408x5120 and 5120x17408, T = 1, 8, 33
   gemv_fp8row    row-FP8 17408x5120, T = 1, 4, 16, 33 (BF16 out)   <- headline
 Weights of the decode GEMVs rotate over copies totalling more than 512 MB so
-that the 256 MB last-level cache cannot serve them.  Every launch is bracketed
-by HIP events on the stream it runs on; per-row averages come from those.
+that the 256 MB last-level cache cannot serve them.  Every burst is bracketed
+by HIP events on the stream it runs on (per-launch time = burst time / burst;
+no event packet sits between two launches of a burst); per-row averages come
+from those.
 
 `value` is the headline: decode GEMV HBM GB/s on row-FP8 17408x5120 over
 T = 1, 4, 16, 33 (algorithmic bytes / kernel time).  The prefill GEMMs are
@@ -36,16 +38,16 @@ sys.path.insert(0, ROOT)
 # `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` runs of
 # `bench.py --rows gemv_fp8row`, in KiB per dispatch, scaled by the same
 # counters on `bench.py --calibrate-copy` (a 256 MiB copy reads FETCH_SIZE
-# 131083.5 KiB and writes WRITE_SIZE 262144 KiB: factors 1.99983 and 1.0).
+# 131083.5 KiB and writes WRITE_SIZE 262144 KiB: factors 1.99982 and 1.0).
 # Summaries: profiles/gemv_fp8row_17408x5120_hbm_traffic.md.  Valid only for
 # the GEMV source they were taken on (sha256 prefix of nq_gemv.hip).
 GEMV_TRAFFIC = {
-    "source_sha256_16": "41a20ae910f989a9",
+    "source_sha256_16": "dc8fe1bf0581f6b0",
     "fetch_factor": 262144.0 / 131083.5,
     "write_factor": 1.0,
-    "fetch_kib": {"gemv_fp8row_T1": 43699.0, "gemv_fp8row_T4": 44023.5, "gemv_fp8row_T16": 46085.6,
-                  "gemv_fp8row_T33": 44951.5},
-    "write_kib": {"gemv_fp8row_T1": 603.5, "gemv_fp8row_T4": 2337.5, "gemv_fp8row_T16": 13634.0,
+    "fetch_kib": {"gemv_fp8row_T1": 43646.2, "gemv_fp8row_T4": 43813.9, "gemv_fp8row_T16": 44509.5,
+                  "gemv_fp8row_T33": 45179.1},
+    "write_kib": {"gemv_fp8row_T1": 34.0, "gemv_fp8row_T4": 136.0, "gemv_fp8row_T16": 544.0,
                   "gemv_fp8row_T33": 1122.0},
 }
 
@@ -66,6 +68,8 @@ def parse():
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--rows", default="all", help="comma list of row groups to run (default: all)")
+    p.add_argument("--burst", type=int, default=8,
+                   help="launches per row back to back between one pair of HIP events (default 8)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--rows-json", default=None, help="also write per-row results to this file")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -394,11 +398,8 @@ def main():
     for i in range(max(1, args.warmup)):
         t0 = time.perf_counter()
         for r in rows:
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            r.fn()
-            b.record(stream)
+            for _ in range(args.burst):
+                r.fn()
         enqueue_s = max(enqueue_s, time.perf_counter() - t0)
         torch.cuda.synchronize()
         log(f"warmup step {i + 1}/{args.warmup} done (host enqueue {enqueue_s * 1e3:.1f} ms)")
@@ -423,10 +424,15 @@ def main():
         s0 = torch.cuda.Event(enable_timing=True)
         s0.record(stream)
         for r in rows:
+            # a burst of launches between one pair of events: no event packet
+            # sits between two launches, so the per-launch time is the
+            # kernel's own duration plus the dispatch gap, as in a model's
+            # back-to-back layers
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            r.fn()
+            for _ in range(args.burst):
+                r.fn()
             b.record(stream)
             events.append((r, a, b))
         s1 = torch.cuda.Event(enable_timing=True)
@@ -436,7 +442,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     for r, a, b in events:
-        r.ms.append(a.elapsed_time(b))
+        r.ms.append(a.elapsed_time(b) / args.burst)
     gpu_step_ms = float(np.mean([s0.elapsed_time(s1) for s0, s1 in steps_ev]))
     log(f"timed {args.steps} steps: GPU {gpu_step_ms:.3f} ms/step, wall {wall:.3f}s "
         f"(enqueue {enq * 1e3:.1f} ms, hold {hold_ms:.1f} ms)")
@@ -474,7 +480,7 @@ def main():
             traffic = round(sum(per_launch[r.name] * len(r.ms) for r in head) / sum(len(r.ms) for r in head))
         line["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                            "kernel": "gemv_resident_kernel (T=1,4,16) / gemv_mfma_kernel (T=33), packed "
+                            "kernel": "gemv_direct_kernel (T=1,4,16) / gemv_mfma_kernel (T=33), packed "
                                       "row-FP8 17408x5120",
                             "bytes_per_launch": {r.name: r.work for r in head},
                             "hbm_traffic_per_launch": per_launch,

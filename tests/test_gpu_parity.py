@@ -252,6 +252,21 @@ def test_gemv_fp8row(n, k, t):
             assert int(wsp.view(torch.int32)[:64].abs().sum().item()) == 0     # counters reset
 
 
+# Tile counts just above / well below the CU count, and a K split over many
+# workgroups (partials exchanged through the workspace).
+@pytest.mark.parametrize("n,k,t", [(4160, 8192, 1), (16448, 1024, 16), (17408, 1280, 4), (1000, 1536, 16)])
+def test_gemv_fp8row_irregular_tile_counts(n, k, t):
+    w = W.bf16_normal(W.rng(96, n * 7 + k), (n, k), std=0.02)
+    wq, ws = M.encode_fp8row_bf16(w)
+    x = W.bf16_normal(W.rng(97, t * 3 + k), (t, k))
+    ref = M.gemv_fp8row(wq, ws, x)
+    y32, wsp = _run_gemv_fp8row(wq, ws, x, True, "f32")
+    y16, _ = _run_gemv_fp8row(wq, ws, x, True, "bf16")
+    _check_float_out(y32, y16, ref)
+    if wsp is not None:
+        assert int(wsp.view(torch.int32)[:(n + 63) // 64].abs().sum().item()) == 0     # counters reset
+
+
 def test_gemv_fp8row_one_hot_is_exact():
     n, k = 300, 512
     w = W.bf16_normal(W.rng(98, 0), (n, k), std=0.02)
