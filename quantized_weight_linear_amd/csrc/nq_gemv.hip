@@ -287,6 +287,56 @@ __device__ __forceinline__ void reduce_waves(v4f (&acc)[4][NCB], v4f (&fin)[NCB]
     }
 }
 
+// FP32 partials between workgroups: 16-byte buffer stores and loads with the
+// cache policy the compiler gives an agent-scope atomic access (sc1), so they
+// bypass the per-XCD L2, which is not coherent across XCDs.  Ordering comes
+// from the exchange protocol: stores complete (s_waitcnt) before the counter
+// moves, loads are issued after the counter is seen.
+constexpr int CPOL_DEVICE = 16;    // sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(float* p) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, 0x7FFFFFF0, BUF_FLAGS);
+}
+__device__ __forceinline__ void store_partial(__amdgpu_buffer_rsrc_t r, int64_t idx, v4f v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, (int)(idx * 4), 0, CPOL_DEVICE);
+}
+__device__ __forceinline__ v4f load_partial(__amdgpu_buffer_rsrc_t r, int64_t idx) {
+    return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(idx * 4), 0, CPOL_DEVICE));
+}
+
+// Output rows n0 .. n0 + 3 of token t from FP32 values v (row-FP8: the row
+// scale is applied here).
+template <int FMT>
+__device__ __forceinline__ void write_rows(v4f v, int t, int64_t n0, const void* __restrict__ scales, int T, int N,
+                                           int bf16_out, void* __restrict__ y) {
+    if (t >= T) return;
+    if constexpr (FMT == W_FP8ROW) {
+        const uint16_t* rs = reinterpret_cast<const uint16_t*>(scales);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (n0 + r < N) ? v[r] * bf16_bits_to_f32(rs[n0 + r]) : 0.f;
+    }
+    if (bf16_out) {
+        uint16_t* yo = reinterpret_cast<uint16_t*>(y) + (int64_t)t * N;
+        if (n0 + 3 < N && (N & 3) == 0) {
+            *reinterpret_cast<uint2*>(yo + n0) =
+                make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                           f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (n0 + r < N) yo[n0 + r] = (uint16_t)f32_to_bf16_rne(v[r]);
+        }
+    } else {
+        float* yo = reinterpret_cast<float*>(y) + (int64_t)t * N;
+        if (n0 + 3 < N && (N & 3) == 0) {
+            *reinterpret_cast<v4f*>(yo + n0) = v;
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (n0 + r < N) yo[n0 + r] = v[r];
+        }
+    }
+}
+
 // Output of row block wv: the FP32 values fin (row-FP8 scale applied here),
 // either written to y or, with splits > 1, published as a partial and summed
 // by the last workgroup of the tile.
@@ -299,36 +349,7 @@ __device__ __forceinline__ void finish_tile(v4f (&fin)[NCB], const void* __restr
     const int tid = threadIdx.x;
     const int64_t npad = (int64_t)gridDim.x * GV_ROWS;
     const int64_t n0 = row0 + wv * 16 + 4 * lg;           // this lane's 4 output rows
-    auto write_out = [&](int cb, v4f v) {
-        const int t = cb * 16 + li;
-        if (t >= T) return;
-        if constexpr (FMT == W_FP8ROW) {
-            const uint16_t* rs = reinterpret_cast<const uint16_t*>(scales);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = (n0 + r < N) ? v[r] * bf16_bits_to_f32(rs[n0 + r]) : 0.f;
-        }
-        if (bf16_out) {
-            uint16_t* yo = reinterpret_cast<uint16_t*>(y) + (int64_t)t * N;
-            if (n0 + 3 < N && (N & 3) == 0) {
-                *reinterpret_cast<uint2*>(yo + n0) =
-                    make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                               f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (n0 + r < N) yo[n0 + r] = (uint16_t)f32_to_bf16_rne(v[r]);
-            }
-        } else {
-            float* yo = reinterpret_cast<float*>(y) + (int64_t)t * N;
-            if (n0 + 3 < N && (N & 3) == 0) {
-                *reinterpret_cast<v4f*>(yo + n0) = v;
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (n0 + r < N) yo[n0 + r] = v[r];
-            }
-        }
-    };
+    auto write_out = [&](int cb, v4f v) { write_rows<FMT>(v, cb * 16 + li, n0, scales, T, N, bf16_out, y); };
 
     if (splits == 1) {
 #pragma unroll
@@ -337,19 +358,15 @@ __device__ __forceinline__ void finish_tile(v4f (&fin)[NCB], const void* __restr
     }
 
     // Split-K: publish this split's partial; the last workgroup of the tile sums.
-    // Partials move only through device-coherent (agent-scope) atomic stores
-    // and loads, which bypass the per-XCD L2; each wave waits for its stores to
-    // complete before the counter is bumped.  No device-scope fence: on this
-    // part it would write back and invalidate the whole L2.
+    // Partials move only through device-coherent stores and loads (see
+    // store_partial); each wave waits for its stores to complete before the
+    // counter is bumped.  No device-scope fence: on this part it would write
+    // back and invalidate the whole L2.
+    const __amdgpu_buffer_rsrc_t pr = partial_rsrc(partial);
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         const int t = cb * 16 + li;
-        if (t < T) {
-            uint32_t* p = reinterpret_cast<uint32_t*>(&partial[((int64_t)split * T + t) * npad + n0]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                __hip_atomic_store(p + r, __float_as_uint(fin[cb][r]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        if (t < T) store_partial(pr, ((int64_t)split * T + t) * npad + n0, fin[cb]);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -363,18 +380,237 @@ __device__ __forceinline__ void finish_tile(v4f (&fin)[NCB], const void* __restr
     for (int cb = 0; cb < NCB; ++cb) {
         const int t = cb * 16 + li;
         if (t >= T) continue;
+        // all splits' loads of a batch are in flight together; the sum runs in split order
+        constexpr int SB = 8;
         v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < splits; ++s) {
-            const uint32_t* p = reinterpret_cast<const uint32_t*>(&partial[((int64_t)s * T + t) * npad + n0]);
-            v4f part;
+        for (int sb = 0; sb < splits; sb += SB) {
+            v4f part[SB];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                part[r] = __uint_as_float(__hip_atomic_load(p + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-            sum += part;
+            for (int j = 0; j < SB; ++j)
+                part[j] = sb + j < splits ? load_partial(pr, ((int64_t)(sb + j) * T + t) * npad + n0)
+                                          : v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < SB; ++j)
+                if (sb + j < splits) sum += part[j];
         }
         write_out(cb, sum);
     }
     if (tid == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Spread workgroups (see gemv_direct_kernel, gemv_mfma_kernel): workgroup e
+// of E owns the units [e U / E, (e + 1) U / E) of the leftover tiles
+// [tile0, tile0 + R) (U = R x chunks, one unit = one chunk of one tile,
+// tile-major; E <= U so no range is empty).  Activation fragments come
+// straight from memory as in the direct kernel.  When the range leaves a tile
+// (and at its end) the tile's sums are added across the waves and published
+// as an FP32 partial in slot (e - first workgroup of the tile), or written
+// directly when the range covers the tile; the last workgroup of a tile to
+// arrive (atomic counter) adds the slots in slot order, so the result does
+// not depend on timing.  A spread workgroup runs a few units, so the
+// boundary work (which waits for its loads) costs little.
+constexpr int SPREAD_MAXSEG = 3;
+
+// The spread workgroup whose range holds leftover unit v.
+__device__ __forceinline__ int spread_owner(int64_t v, int64_t U, int E) { return (int)(((v + 1) * E - 1) / U); }
+
+template <int FMT, int NCB, bool PK>
+__device__ __forceinline__ void direct_spread(const uint8_t* __restrict__ w, const void* __restrict__ scales,
+                                              const uint16_t* __restrict__ x, int T, int N, int64_t K, int tile0,
+                                              int R, int e, int E, int maxslots, float* __restrict__ partial,
+                                              unsigned* __restrict__ counters, int bf16_out, void* __restrict__ y,
+                                              v4f* red, int* s_last) {
+    using P = PieceFmt<FMT>;
+    constexpr int D = 2;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    const int li = lane & 15;
+    const int lg = lane >> 4;
+    const int C = (int)(K / GV_KC);
+    const int64_t U = (int64_t)R * C;
+    const int64_t u0 = (int64_t)e * U / E, u1 = (int64_t)(e + 1) * U / E;
+    const int nu = (int)(u1 - u0);
+    const int lt0 = (int)(u0 / C);                           // first leftover tile touched (local index)
+    const int nseg = (int)((u1 - 1) / C) - lt0 + 1;
+
+    const int64_t nrb = ((int64_t)N + 15) / 16;
+    const int64_t cstride = PK ? nrb * P::BLOCK_CHUNK : 0;
+    const int q0 = P::PW * wv;
+    const uint8_t* wlane = w + (int64_t)lane * P::PB;     // packed: the lane's piece within a block chunk
+    const __amdgpu_buffer_rsrc_t xrsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)((int64_t)T * K * 2), BUF_FLAGS);
+    const __amdgpu_buffer_rsrc_t pr = partial_rsrc(partial);
+    int xoff[2][NCB];
+#pragma unroll
+    for (int ls = 0; ls < 2; ++ls)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+            xoff[ls][cb] = (int)(((int64_t)(cb * 16 + li) * K + kstep_col<FMT>(2 * wv + ls, lg)) * 2);
+
+    struct XFrag {
+        uint4 v[2][NCB];
+    };
+    WChunk<FMT> wr[D];
+    XFrag xr[D];
+    // (tile, chunk) of the next unit to load (stops at the last unit) and the
+    // chunk of the next unit to compute
+    int ld_t = tile0 + lt0, ld_c = (int)(u0 - (int64_t)lt0 * C), ld_i = 0;
+    int cp_c = ld_c, cp_i = 0;
+    auto load = [&](int slot) {
+        const int tl = ld_t, c = ld_c;
+        if (ld_i < nu - 1) {
+            ++ld_i;
+            if (++ld_c == C) {
+                ld_c = 0;
+                ++ld_t;
+            }
+        }
+#pragma unroll
+        for (int ls = 0; ls < 2; ++ls)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+                xr[slot].v[ls][cb] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, xoff[ls][cb] + c * (GV_KC * 2), 0, 0));
+#pragma unroll
+        for (int j = 0; j < 4 * P::PW; ++j) {
+            const int rb = j / P::PW;
+            const int q = q0 + j % P::PW;
+            const int64_t rowb = (int64_t)tl * GV_ROWS + 16 * rb;             // first row of the row block
+            const uint8_t* pw;
+            int64_t row = 0;
+            if constexpr (PK) {
+                const int64_t rbg = rowb / 16 < nrb - 1 ? rowb / 16 : nrb - 1;   // blocks past N are clamped
+                pw = wlane + (rbg * P::BLOCK_CHUNK + (int64_t)c * cstride + q * (64 * P::PB));
+            }
+            if constexpr (!PK || FMT == W_MXFP8) {
+                const int64_t lim = (int64_t)N - 1 - rowb;                   // rows past N are clamped
+                const int lr = (int64_t)li < lim ? li : (int)lim;
+                row = rowb + lr;
+            }
+            if constexpr (!PK) pw = w + row * row_bytes<FMT>(K) + piece_offset<FMT>(c, q, lg);
+            wr[slot].p[j] = *reinterpret_cast<const typename P::Piece*>(pw);
+            if constexpr (FMT == W_MXFP8)
+                wr[slot].e8[j] = reinterpret_cast<const uint8_t*>(scales)[row * (K >> 5) +
+                                                                          ((c * GV_KC + 64 * q + 16 * lg) >> 5)];
+        }
+    };
+
+    auto seg_full = [&](int k) {        // segment k (leftover tile lt0 + k) covered whole by this range
+        const int64_t tb = (int64_t)(lt0 + k) * C;
+        const int64_t b = tb > u0 ? tb : u0, en = tb + C < u1 ? tb + C : u1;
+        return en - b == C;
+    };
+    auto seg_slots = [&](int k) {       // this workgroup's slot and the tile's slot count
+        const int64_t tb = (int64_t)(lt0 + k) * C;
+        const int first = spread_owner(tb, U, E);
+        return make_int2(e - first, spread_owner(tb + C - 1, U, E) - first + 1);
+    };
+    v4f acc[4][NCB];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = v4f{0.f, 0.f, 0.f, 0.f};
+    // segment k's sums: written directly or published as a partial; acc restarts
+    auto close_segment = [&](int k) {
+        v4f fin[NCB];
+        reduce_waves<NCB>(acc, fin, red, wv, lane);
+        const int tl = tile0 + lt0 + k;
+        const int64_t n0 = (int64_t)tl * GV_ROWS + wv * 16 + 4 * lg;
+        if (seg_full(k)) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) write_rows<FMT>(fin[cb], cb * 16 + li, n0, scales, T, N, bf16_out, y);
+        } else {
+            const int slot = seg_slots(k).x;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                const int t = cb * 16 + li;
+                if (t < T)
+                    store_partial(pr, (((int64_t)(lt0 + k) * maxslots + slot) * T + t) * GV_ROWS + wv * 16 + 4 * lg,
+                                  fin[cb]);
+            }
+        }
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = v4f{0.f, 0.f, 0.f, 0.f};
+    };
+    int kseg = 0;
+    auto step = [&](int slot) {
+        if (cp_c == 0 && cp_i > 0) close_segment(kseg++);   // this unit opens the next tile (uniform)
+        ++cp_i;
+        if (++cp_c == C) cp_c = 0;
+#pragma unroll
+        for (int ls = 0; ls < 2; ++ls) {
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const v8bf a = decode_afrag<FMT>(wr[slot], rb, ls);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        a, __builtin_bit_cast(v8bf, xr[slot].v[ls][cb]), acc[rb][cb], 0, 0, 0);
+            }
+        }
+    };
+
+#pragma unroll
+    for (int d = 0; d < D; ++d) load(d);
+    int i = 0;
+    for (; i + D <= nu; i += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            step(u);
+            load(u);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < D - 1; ++u)
+        if (i + u < nu) step(u);
+    close_segment(kseg);
+
+    // Each wave waits for its partial stores before the counters move.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+#pragma unroll
+        for (int k = 0; k < SPREAD_MAXSEG; ++k) {
+            s_last[k] = 0;
+            if (k >= nseg || seg_full(k)) continue;
+            const unsigned prev = __hip_atomic_fetch_add(&counters[tile0 + lt0 + k], 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            s_last[k] = (prev == (unsigned)(seg_slots(k).y - 1));
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < SPREAD_MAXSEG; ++k) {
+        if (k >= nseg || !s_last[k]) continue;
+        const int tl = tile0 + lt0 + k;
+        const int nslots = seg_slots(k).y;
+        const int64_t n0 = (int64_t)tl * GV_ROWS + wv * 16 + 4 * lg;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int t = cb * 16 + li;
+            if (t >= T) continue;
+            // all slots' loads of a batch are in flight together; the sum runs in slot order
+            constexpr int SB = 16;
+            v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
+            for (int sb = 0; sb < nslots; sb += SB) {
+                v4f part[SB];
+#pragma unroll
+                for (int j = 0; j < SB; ++j)
+                    part[j] = sb + j < nslots
+                                  ? load_partial(pr, (((int64_t)(lt0 + k) * maxslots + sb + j) * T + t) * GV_ROWS +
+                                                         wv * 16 + 4 * lg)
+                                  : v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < SB; ++j)
+                    if (sb + j < nslots) sum += part[j];
+            }
+            write_rows<FMT>(sum, t, n0, scales, T, N, bf16_out, y);
+        }
+        if (tid == 0) __hip_atomic_store(&counters[tl], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -383,14 +619,24 @@ __device__ __forceinline__ void finish_tile(v4f (&fin)[NCB], const void* __restr
 // before the next weights so that waiting for them never waits for weights.
 // One barrier per chunk.
 // ---------------------------------------------------------------------------
+// Waves per SIMD the streaming kernel is compiled for: two for the formats
+// without group scales, so that a spread workgroup fits beside a whole-tile
+// one on every CU (see direct_spread); one for the grouped formats, and for
+// BF16 weights at four token blocks, which would spill at that budget (a
+// spread launch then runs its spread workgroups after the whole tiles).
+template <int FMT, int NCB>
+constexpr int stream_min_waves() {
+    return (group_size<FMT>() == 0 && !(FMT == W_BF16 && NCB == 4)) ? 2 : 1;
+}
+
+// With spread_wgs > 0 (formats without group scales, one split): workgroups
+// [0, main_tiles) take one whole tile each as below and the spread_wgs after
+// them share the other tiles unit by unit (direct_spread).
 template <int FMT, int NCB, bool PK>
-__global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint8_t* __restrict__ w,
-                                                        const void* __restrict__ scales,
-                                                        const uint16_t* __restrict__ x, int T, int N, int64_t K,
-                                                        int chunks_per_split, int splits,
-                                                        float* __restrict__ partial,
-                                                        unsigned* __restrict__ counters, int bf16_out,
-                                                        void* __restrict__ y) {
+__global__ __launch_bounds__(256, (stream_min_waves<FMT, NCB>())) void gemv_mfma_kernel(
+    const uint8_t* __restrict__ w, const void* __restrict__ scales, const uint16_t* __restrict__ x, int T, int N,
+    int64_t K, int chunks_per_split, int splits, float* __restrict__ partial, unsigned* __restrict__ counters,
+    int bf16_out, void* __restrict__ y, int main_tiles, int spread_wgs, int maxslots) {
     constexpr int TP = 16 * NCB;
     constexpr int XPITCH = GV_KC + 8;                 // bf16 per LDS row: rows shift by 4 banks
     constexpr int XPR = GV_KC / 8;                    // 16-byte activation pieces per row and chunk
@@ -404,6 +650,16 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint8_t* __restric
     __shared__ __attribute__((aligned(16))) uint16_t scs[2][GS ? NG * GV_ROWS : 1];
     __shared__ int s_last;
     static_assert(sizeof(xs) >= 16384 * NCB, "reduction buffer");
+    if constexpr (GS == 0) {
+        __shared__ int s_last_sp[SPREAD_MAXSEG];
+        if (spread_wgs > 0 && (int)blockIdx.x >= main_tiles) {
+            const int tiles_all = (int)((N + GV_ROWS - 1) / GV_ROWS);
+            direct_spread<FMT, NCB, PK>(w, scales, x, T, N, K, main_tiles, tiles_all - main_tiles,
+                                        (int)blockIdx.x - main_tiles, spread_wgs, maxslots, partial, counters,
+                                        bf16_out, y, reinterpret_cast<v4f*>(&xs[0][0]), s_last_sp);
+            return;
+        }
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -645,6 +901,13 @@ constexpr int depth_direct() {
     return NCB >= 3 ? 2 : 3;
 }
 
+// With spread_wgs > 0 (and one split): workgroups [0, main_tiles) each take
+// one whole tile as below, and the spread_wgs workgroups after them share the
+// tiles [main_tiles, tiles) unit by unit (direct_spread).  With more tiles
+// than CUs but not a multiple of them, whole tiles alone leave a few CUs with
+// one tile more and the launch takes nearly twice as long; the spread
+// workgroups (a few units each, resident beside the whole-tile ones) even the
+// CUs out, and their partial exchange ends long before the whole tiles do.
 template <int FMT, int NCB, bool PK>
 __global__ __launch_bounds__(256) void gemv_direct_kernel(const uint8_t* __restrict__ w,
                                                           const void* __restrict__ scales,
@@ -652,11 +915,20 @@ __global__ __launch_bounds__(256) void gemv_direct_kernel(const uint8_t* __restr
                                                           int chunks_per_split, int splits,
                                                           float* __restrict__ partial,
                                                           unsigned* __restrict__ counters, int bf16_out,
-                                                          void* __restrict__ y) {
+                                                          void* __restrict__ y, int main_tiles, int spread_wgs,
+                                                          int maxslots) {
     static_assert(group_size<FMT>() == 0, "grouped formats stage their scales in LDS");
     constexpr int D = depth_direct<NCB>();
     __shared__ __attribute__((aligned(16))) v4f red[4 * 4 * NCB * 64];   // final cross-wave sum
     __shared__ int s_last;
+    __shared__ int s_last_sp[SPREAD_MAXSEG];
+    if (spread_wgs > 0 && (int)blockIdx.x >= main_tiles) {
+        const int tiles_all = (int)((N + GV_ROWS - 1) / GV_ROWS);
+        direct_spread<FMT, NCB, PK>(w, scales, x, T, N, K, main_tiles, tiles_all - main_tiles,
+                                    (int)blockIdx.x - main_tiles, spread_wgs, maxslots, partial, counters, bf16_out,
+                                    y, red, s_last_sp);
+        return;
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -807,6 +1079,9 @@ struct GemvPlan {
     bool mfma;
     bool direct;             // activation fragments loaded per wave (formats without group scales)
     bool resident;           // activation slice staged once in LDS (no barriers in the loop)
+    int64_t main_tiles;      // direct variant with spread workgroups: tiles taken whole
+    int spread_wgs;          // ... workgroups sharing the other tiles (0: none)
+    int maxslots;            // ... partial slots per shared tile
     int kc;                  // chunk width (always GV_KC)
     int64_t tiles;
     int splits;
@@ -834,7 +1109,22 @@ static int64_t resident_lds(int fmt, int64_t Tc, int64_t cps, int kc) {
     return stage > red ? stage : red;
 }
 
-static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K) {
+// More tiles than CUs, not a multiple of them, one split: whole tiles for the
+// first m x CUs, the R others spread over one more workgroup per CU (at most
+// SPREAD_MAXSEG tiles each).
+static void plan_spread(GemvPlan& p, int64_t chunks) {
+    const int64_t cus = (int64_t)device_cu_count();
+    const int64_t R = p.tiles % cus, U = R * chunks;
+    if (p.splits != 1 || p.tiles <= cus || R == 0 || U >= ((int64_t)1 << 31)) return;
+    const int64_t E = U < cus ? U : cus;
+    const int64_t lmin = U / E, lmax = (U + E - 1) / E;
+    if ((lmax - 1 + chunks - 1) / chunks + 1 > SPREAD_MAXSEG) return;
+    p.main_tiles = p.tiles - R;
+    p.spread_wgs = (int)E;
+    p.maxslots = (int)((chunks + lmin - 1) / lmin + 1);
+}
+
+static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_spread = true) {
     GemvPlan p{};
     // buffer offsets are 32-bit: the activation block must stay below 2 GiB
     p.mfma = (K > 0) && (K % GV_KC == 0) && (Tc * K * 2 < ((int64_t)1 << 31)) &&
@@ -860,7 +1150,7 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K) {
     if (s0 > chunks / min_chunks) s0 = chunks / min_chunks;   // keep whole chunks per split
     if (s0 > 32) s0 = 32;
     if (s0 < 1) s0 = 1;
-    static const int mode = [] {      // 0 auto, 1 direct, 2 resident / streaming only
+    static const int mode = [] {      // 0 auto, 1 direct, 2 resident / streaming only, 3 no spread
         const char* e = getenv("NQ_GEMV_MODE");
         return e ? atoi(e) : 0;
     }();
@@ -875,6 +1165,7 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K) {
         p.direct = true;
         p.chunks_per_split = (int)cps;
         p.splits = (int)((chunks + cps - 1) / cps);
+        if (mode != 3 && allow_spread) plan_spread(p, chunks);
         return p;
     }
     // resident variant: smallest split count >= s0 whose slice fits in LDS and
@@ -901,12 +1192,14 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K) {
     const int64_t cps = (chunks + s0 - 1) / s0;
     p.chunks_per_split = (int)cps;
     p.splits = (int)((chunks + cps - 1) / cps);
+    if (fmt_group(fmt) == 0 && mode != 3 && allow_spread) plan_spread(p, chunks);
     return p;
 }
 
 static int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
 
 static int64_t plan_workspace(const GemvPlan& p, int64_t Tc) {
+    if (p.spread_wgs > 0) return align256(p.tiles * 4) + (p.tiles - p.main_tiles) * p.maxslots * Tc * GV_ROWS * 4;
     if (!p.mfma || p.splits == 1) return 0;
     return align256(p.tiles * 4) + (int64_t)p.splits * Tc * p.tiles * GV_ROWS * 4;
 }
@@ -932,9 +1225,10 @@ static void launch_mfma(const GemvPlan& p, const void* w, const void* scales, co
     dim3 grid((unsigned)p.tiles, (unsigned)p.splits);
     if constexpr (group_size<FMT>() == 0) {
         if (p.direct) {
-            gemv_direct_kernel<FMT, NCB, PK><<<grid, 256, 0, stream>>>(
+            const dim3 g = p.spread_wgs > 0 ? dim3((unsigned)(p.main_tiles + p.spread_wgs)) : grid;
+            gemv_direct_kernel<FMT, NCB, PK><<<g, 256, 0, stream>>>(
                 reinterpret_cast<const uint8_t*>(w), scales, x, Tc, (int)N, K, p.chunks_per_split, p.splits, partial,
-                counters, bf16_out ? 1 : 0, y);
+                counters, bf16_out ? 1 : 0, y, (int)p.main_tiles, p.spread_wgs, p.maxslots);
             return;
         }
     }
@@ -942,10 +1236,13 @@ static void launch_mfma(const GemvPlan& p, const void* w, const void* scales, co
         gemv_resident_kernel<FMT, NCB, PK><<<grid, 256, (size_t)p.lds_bytes, stream>>>(
             reinterpret_cast<const uint8_t*>(w), scales, x, Tc, (int)N, K, p.chunks_per_split, p.splits, partial,
             counters, bf16_out ? 1 : 0, y);
-    else
-        gemv_mfma_kernel<FMT, NCB, PK><<<grid, 256, 0, stream>>>(reinterpret_cast<const uint8_t*>(w), scales, x,
-                                                                     Tc, (int)N, K, p.chunks_per_split, p.splits,
-                                                                     partial, counters, bf16_out ? 1 : 0, y);
+    else {
+        const dim3 g = p.spread_wgs > 0 ? dim3((unsigned)(p.main_tiles + p.spread_wgs)) : grid;
+        gemv_mfma_kernel<FMT, NCB, PK><<<g, 256, 0, stream>>>(reinterpret_cast<const uint8_t*>(w), scales, x, Tc,
+                                                                  (int)N, K, p.chunks_per_split, p.splits, partial,
+                                                                  counters, bf16_out ? 1 : 0, y, (int)p.main_tiles,
+                                                                  p.spread_wgs, p.maxslots);
+    }
 }
 
 template <int FMT, bool PK>
@@ -1051,6 +1348,14 @@ hipError_t launch_gemv(int fmt, const void* w, const void* scales, const uint16_
         if (packed && !p.mfma) return hipErrorInvalidValue;    // only the MFMA kernels read packed weights
         float* partial = nullptr;
         unsigned* counters = nullptr;
+        if (p.spread_wgs > 0) {
+            if (workspace != nullptr && workspace_bytes >= plan_workspace(p, Tc)) {
+                counters = reinterpret_cast<unsigned*>(workspace);
+                partial = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + align256(p.tiles * 4));
+            } else {
+                p = plan_gemv(fmt, Tc, N, K, false);           // no room for partials: whole tiles only
+            }
+        }
         if (p.splits > 1) {
             const int64_t need = plan_workspace(p, Tc);
             if (workspace != nullptr && workspace_bytes >= need) {
