@@ -572,14 +572,17 @@ __device__ __forceinline__ void direct_spread(const uint8_t* __restrict__ w, con
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0) {
+        // all counters move before any result is looked at: one round trip
+        unsigned prev[SPREAD_MAXSEG];
 #pragma unroll
-        for (int k = 0; k < SPREAD_MAXSEG; ++k) {
-            s_last[k] = 0;
-            if (k >= nseg || seg_full(k)) continue;
-            const unsigned prev = __hip_atomic_fetch_add(&counters[tile0 + lt0 + k], 1u, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT);
-            s_last[k] = (prev == (unsigned)(seg_slots(k).y - 1));
-        }
+        for (int k = 0; k < SPREAD_MAXSEG; ++k)
+            prev[k] = (k < nseg && !seg_full(k))
+                          ? __hip_atomic_fetch_add(&counters[tile0 + lt0 + k], 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                          : 0u;
+#pragma unroll
+        for (int k = 0; k < SPREAD_MAXSEG; ++k)
+            s_last[k] = (k < nseg && !seg_full(k)) && prev[k] == (unsigned)(seg_slots(k).y - 1);
     }
     __syncthreads();
 #pragma unroll
@@ -630,8 +633,10 @@ constexpr int stream_min_waves() {
 }
 
 // With spread_wgs > 0 (formats without group scales, one split): workgroups
-// [0, main_tiles) take one whole tile each as below and the spread_wgs after
-// them share the other tiles unit by unit (direct_spread).
+// [0, spread_wgs) share the tiles [main_tiles, tiles) unit by unit
+// (direct_spread) and the main_tiles after them take one whole tile each as
+// below.  The spread workgroups come first so that they are dispatched first:
+// their partial exchange then ends well inside the whole tiles' time.
 template <int FMT, int NCB, bool PK>
 __global__ __launch_bounds__(256, (stream_min_waves<FMT, NCB>())) void gemv_mfma_kernel(
     const uint8_t* __restrict__ w, const void* __restrict__ scales, const uint16_t* __restrict__ x, int T, int N,
@@ -652,10 +657,10 @@ __global__ __launch_bounds__(256, (stream_min_waves<FMT, NCB>())) void gemv_mfma
     static_assert(sizeof(xs) >= 16384 * NCB, "reduction buffer");
     if constexpr (GS == 0) {
         __shared__ int s_last_sp[SPREAD_MAXSEG];
-        if (spread_wgs > 0 && (int)blockIdx.x >= main_tiles) {
+        if ((int)blockIdx.x < spread_wgs) {
             const int tiles_all = (int)((N + GV_ROWS - 1) / GV_ROWS);
             direct_spread<FMT, NCB, PK>(w, scales, x, T, N, K, main_tiles, tiles_all - main_tiles,
-                                        (int)blockIdx.x - main_tiles, spread_wgs, maxslots, partial, counters,
+                                        (int)blockIdx.x, spread_wgs, maxslots, partial, counters,
                                         bf16_out, y, reinterpret_cast<v4f*>(&xs[0][0]), s_last_sp);
             return;
         }
@@ -666,7 +671,7 @@ __global__ __launch_bounds__(256, (stream_min_waves<FMT, NCB>())) void gemv_mfma
     const int wv = tid >> 6;
     const int li = lane & 15;
     const int lg = lane >> 4;
-    const int tile = blockIdx.x;
+    const int tile = (int)blockIdx.x - spread_wgs;   // spread workgroups come first
     const int split = blockIdx.y;
     const int64_t row0 = (int64_t)tile * GV_ROWS;
     const int64_t total_chunks = K / GV_KC;
@@ -901,9 +906,10 @@ constexpr int depth_direct() {
     return NCB >= 3 ? 2 : 3;
 }
 
-// With spread_wgs > 0 (and one split): workgroups [0, main_tiles) each take
-// one whole tile as below, and the spread_wgs workgroups after them share the
-// tiles [main_tiles, tiles) unit by unit (direct_spread).  With more tiles
+// With spread_wgs > 0 (and one split): workgroups [0, spread_wgs) share the
+// tiles [main_tiles, tiles) unit by unit (direct_spread), dispatched first so
+// that their partial exchange ends well inside the whole tiles' time, and the
+// main_tiles workgroups after them each take one whole tile as below.  With more tiles
 // than CUs but not a multiple of them, whole tiles alone leave a few CUs with
 // one tile more and the launch takes nearly twice as long; the spread
 // workgroups (a few units each, resident beside the whole-tile ones) even the
@@ -922,10 +928,10 @@ __global__ __launch_bounds__(256) void gemv_direct_kernel(const uint8_t* __restr
     __shared__ __attribute__((aligned(16))) v4f red[4 * 4 * NCB * 64];   // final cross-wave sum
     __shared__ int s_last;
     __shared__ int s_last_sp[SPREAD_MAXSEG];
-    if (spread_wgs > 0 && (int)blockIdx.x >= main_tiles) {
+    if ((int)blockIdx.x < spread_wgs) {
         const int tiles_all = (int)((N + GV_ROWS - 1) / GV_ROWS);
         direct_spread<FMT, NCB, PK>(w, scales, x, T, N, K, main_tiles, tiles_all - main_tiles,
-                                    (int)blockIdx.x - main_tiles, spread_wgs, maxslots, partial, counters, bf16_out,
+                                    (int)blockIdx.x, spread_wgs, maxslots, partial, counters, bf16_out,
                                     y, red, s_last_sp);
         return;
     }
@@ -935,7 +941,7 @@ __global__ __launch_bounds__(256) void gemv_direct_kernel(const uint8_t* __restr
     const int wv = tid >> 6;
     const int li = lane & 15;
     const int lg = lane >> 4;
-    const int tile = blockIdx.x;
+    const int tile = (int)blockIdx.x - spread_wgs;   // spread workgroups come first
     const int split = blockIdx.y;
     const int64_t row0 = (int64_t)tile * GV_ROWS;
     const int64_t total_chunks = K / GV_KC;
