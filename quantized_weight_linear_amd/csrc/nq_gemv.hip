@@ -1130,6 +1130,24 @@ static void plan_spread(GemvPlan& p, int64_t chunks) {
     p.maxslots = (int)((chunks + lmin - 1) / lmin + 1);
 }
 
+// K split count for fewer row tiles than CUs: the one (up to smax) that
+// minimizes the chunks of the busiest CU, ceil(tiles s / CUs) x ceil(chunks / s)
+// with one workgroup per (tile, split); ties go to fewer splits.
+static int64_t balanced_splits(int64_t tiles, int64_t chunks, int64_t smax) {
+    const int64_t cus = (int64_t)device_cu_count();
+    int64_t best = 1, best_cost = -1;
+    for (int64_t s = 1; s <= smax; ++s) {
+        const int64_t cps = (chunks + s - 1) / s;
+        const int64_t se = (chunks + cps - 1) / cps;
+        const int64_t cost = ((tiles * se + cus - 1) / cus) * cps;
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best = se;
+        }
+    }
+    return best;
+}
+
 static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_spread = true) {
     GemvPlan p{};
     // buffer offsets are 32-bit: the activation block must stay below 2 GiB
@@ -1160,13 +1178,14 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
         const char* e = getenv("NQ_GEMV_MODE");
         return e ? atoi(e) : 0;
     }();
+    int64_t smax = chunks / min_chunks;        // keep whole chunks, at least min_chunks per split
+    if (smax > 32) smax = 32;
+    if (smax < 1) smax = 1;
     if (fmt_group(fmt) == 0 && Tc <= 16 && mode != 2) {
-        // direct variant (no group scales, one token block): one workgroup per
-        // CU is enough (measured: more workgroups per CU only slow it down)
-        int64_t sd = ((int64_t)device_cu_count() + p.tiles - 1) / p.tiles;
-        if (sd > chunks / min_chunks) sd = chunks / min_chunks;
-        if (sd > 32) sd = 32;
-        if (sd < 1) sd = 1;
+        // direct variant (no group scales, one token block): about one
+        // workgroup per CU (measured: more per CU only slow it down); with
+        // fewer tiles than CUs, K split so that the busiest CU has the fewest chunks
+        const int64_t sd = p.tiles < (int64_t)device_cu_count() ? balanced_splits(p.tiles, chunks, smax) : 1;
         const int64_t cps = (chunks + sd - 1) / sd;
         p.direct = true;
         p.chunks_per_split = (int)cps;
@@ -1193,8 +1212,9 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
         }
     }
     // streaming variant: once the row tiles alone cover every CU, splitting K
-    // only adds workgroups that compete for LDS bandwidth plus the partial exchange
-    if (p.tiles >= (int64_t)device_cu_count()) s0 = 1;
+    // only adds workgroups that compete for LDS bandwidth plus the partial
+    // exchange; below that, the split that leaves the busiest CU the fewest chunks
+    s0 = p.tiles >= (int64_t)device_cu_count() ? 1 : balanced_splits(p.tiles, chunks, smax);
     const int64_t cps = (chunks + s0 - 1) / s0;
     p.chunks_per_split = (int)cps;
     p.splits = (int)((chunks + cps - 1) / cps);
