@@ -1174,7 +1174,8 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     if (s0 > chunks / min_chunks) s0 = chunks / min_chunks;   // keep whole chunks per split
     if (s0 > 32) s0 = 32;
     if (s0 < 1) s0 = 1;
-    static const int mode = [] {      // 0 auto, 1 direct, 2 resident / streaming only, 3 no spread
+    static const int mode = [] {      // 0 auto, 1 direct, 2 resident / streaming only, 3 no spread,
+                                      // 4 resident split by workgroups per CU
         const char* e = getenv("NQ_GEMV_MODE");
         return e ? atoi(e) : 0;
     }();
@@ -1193,12 +1194,14 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
         if (mode != 3 && allow_spread) plan_spread(p, chunks);
         return p;
     }
-    // resident variant: smallest split count >= s0 whose slice fits in LDS and
-    // whose FP32 partials stay within 12% of the weight bytes; with more than
-    // one token block, only when the row tiles alone do not cover the CUs
+    // resident variant: from the split count that leaves the busiest CU the
+    // fewest chunks, the smallest whose slice fits in LDS and whose FP32
+    // partials stay within 12% of the weight bytes; with more than one token
+    // block, only when the row tiles alone do not cover the CUs
     const double wbytes = (double)N * (double)K * fmt_bytes_per_weight(fmt);
     const bool try_resident = Tc <= 16 || p.tiles < (int64_t)device_cu_count();
-    for (int64_t s = s0; try_resident && s <= 32 && s <= chunks; ++s) {
+    const int64_t sr = mode == 4 ? s0 : balanced_splits(p.tiles, chunks, smax);
+    for (int64_t s = sr; try_resident && s <= 32 && s <= chunks; ++s) {
         const int64_t cps = (chunks + s - 1) / s;
         const int64_t se = (chunks + cps - 1) / cps;
         const double partial_bytes = se > 1 ? 8.0 * (double)se * (double)Tc * (double)N : 0.0;
