@@ -16,9 +16,10 @@
 // of 64 bytes per row reach about half the L2-to-CU rate.  The 16-byte pieces
 // of a row are XOR-swizzled so that the MFMA fragment reads (16 bytes per
 // lane) are conflict-free.  One stage holds 128 K-columns of both panels
-// (plus, for W8A8, the activation and weight scales of its two groups); a
-// ring of S stages (W8A8 3, FP8 2: as many as LDS holds) with one barrier per
-// stage.  Rows past M / N and columns past K are out of the buffer range or
+// (plus, for W8A8 with K % 512 != 0, the activation and weight scales of its
+// two groups; with K % 512 == 0 the scales come in windows of several stages,
+// see ScaleWin); a ring of S stages (W8A8 3, FP8 2: as many as LDS holds) with
+// one barrier per stage.  Rows past M / N and columns past K are out of the buffer range or
 // masked, and read as zero.
 //
 // W8A8 (64-channel groups, two per stage): two v_mfma_i32_32x32x32_i8 per
@@ -41,6 +42,7 @@
 // a few 1e-5 were measured on one instruction), outside this path's 1e-5
 // bound.  y = (acc * a_scale[m]) * w_scale[n] at the end.
 #include <type_traits>
+#include <utility>
 
 #include "nq_device.h"
 #include "nq_launch.h"
@@ -71,20 +73,62 @@ struct GemmCfg {
 
 // 16-byte aligned size: every stage of the ring starts on a 16-byte boundary,
 // so fragment reads stay single 16-byte LDS reads.
-template <bool W8A8>
+template <bool W8A8, bool SW>
 struct alignas(16) GemmStage {
     static constexpr int BM = GemmCfg<W8A8>::BM, BN = GemmCfg<W8A8>::BN;
+    static constexpr bool PER_STAGE = W8A8 && !SW;   // scales staged with the panels
     uint8_t a[BM * GB_K];
     uint8_t b[BN * GB_K];
-    float as[W8A8 ? 2 * BM : 1];       // W8A8: activation scales of the stage's two groups
-    uint32_t ws[W8A8 ? 2 * BN : 1];    // W8A8: weight scales of the two groups (FP16 bits, zero-extended:
-                                       // a 2-byte load in LDS mode still writes 4 bytes per lane)
-    uint32_t sink[W8A8 ? 128 : 1];     // W8A8: target of the empty scale loads (they write zeros)
+    float as[PER_STAGE ? 2 * BM : 1];       // activation scales of the stage's two groups
+    uint32_t ws[PER_STAGE ? 2 * BN : 1];    // weight scales of the two groups (FP16 bits, zero-extended:
+                                            // a 2-byte load in LDS mode still writes 4 bytes per lane)
+    uint32_t sink[PER_STAGE ? 128 : 1];     // target of the empty scale loads (they write zeros)
+};
+
+// W8A8 scale windows (K % 512 == 0, so that scale rows start on 16-byte
+// boundaries).  Staging two groups of scales per stage takes one gather per
+// row and group: a 64-lane load that touches 64 cache lines, as many address
+// lookups as 8 panel loads, which made the address unit the bottleneck.  A
+// window instead takes one 16-byte load per row for the activation scales of
+// four groups (two stages) or the FP16 weight scales of eight groups (four
+// stages), five times fewer lookups; two slots each, the one in use and the
+// one being filled.  Layout [slot][row][group within the window].
+template <bool SW>
+struct alignas(16) ScaleWin {
+    static constexpr int BM = GemmCfg<true>::BM, BN = GemmCfg<true>::BN;
+    float as[SW ? 2 : 1][SW ? 4 * BM : 1];
+    uint16_t ws[SW ? 2 : 1][SW ? 8 * BN : 1];
 };
 
 // 32x32 MFMA output layout: lane l holds column (l % 32) and rows
 // 8 j + 4 (l / 32) + r for j, r in 0..3 (element 4 j + r).
 __device__ __forceinline__ int d_row(int lane, int e) { return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
+
+// Row scales for the W8A8 rescale.  Accumulator element e of a 32 x 32 tile
+// sits on row d_row(lane, e): 8 (e / 4) + e % 4 in lanes [0, 32) and 4 more in
+// lanes [32, 64), the same row across each half wave.  A register whose lane
+// n + 16 r (r = 0..3) holds the scale of row d_row(32 (r / 2), n) carries the
+// 32 row scales a tile needs; DPP row_newbcast:e hands lane e of each 16-lane
+// row to the whole row, which is then the scale of element e's row in every
+// lane.  One 4-byte LDS read per tile replaces eight 16-byte ones.
+__device__ __forceinline__ int row_scale_lane_row(int lane) {
+    return 8 * ((lane & 15) >> 2) + 4 * (lane >> 5) + (lane & 3);
+}
+// acc + bcast_e(s) * x, one v_fmac_f32 with the DPP broadcast on its first
+// source (the compiler does not fold a separate DPP move into the FMA).  s is
+// never written by the vector ALU (it comes from an LDS read), so the DPP
+// source needs no wait states.
+template <int E>
+__device__ __forceinline__ float fmac_row_bcast(float acc, float s, float x) {
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc) : "v"(s), "v"(x), "n"(E));
+    return acc;
+}
+template <int... E>
+__device__ __forceinline__ void rescale_tile(v16f& acc, const v16i& d, float ws, float wsc, float s,
+                                             std::integer_sequence<int, E...>) {
+    ((acc[E] = fmac_row_bcast<E>(acc[E], s, fmaf(__int_as_float(d[E]), ws, wsc))), ...);
+}
 
 // Buffer descriptor (base, no stride, num_records bytes): offsets at or past
 // num_records read as zero.
@@ -121,7 +165,7 @@ __device__ __forceinline__ void lds_dma(v4u desc, uint32_t lds, int voff) {
                      :: "v"(voff), "s"(desc), "s"(lds) : "memory", "m0");
 }
 
-template <bool W8A8, bool SUMS, bool KTAIL>
+template <bool W8A8, bool SUMS, bool KTAIL, bool SW>
 __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ a_scale, const uint8_t* __restrict__ W,
     const uint16_t* __restrict__ w_scale, int M, int N, int K, int bf16_out, void* __restrict__ y,
@@ -129,7 +173,10 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
     using C = GemmCfg<W8A8>;
     constexpr int BM = C::BM, BN = C::BN, TM = C::TM, TN = C::TN, S = C::S;
     constexpr int DMA_PER_STAGE = C::LOADS + C::SCALE_LOADS;   // load instructions per wave and stage
-    __shared__ __attribute__((aligned(16))) GemmStage<W8A8> st[S];
+    static_assert(!SW || (W8A8 && !KTAIL), "scale windows: W8A8 with K % 512 == 0");
+    using Stage = GemmStage<W8A8, SW>;
+    __shared__ __attribute__((aligned(16))) Stage st[S];
+    __shared__ __attribute__((aligned(16))) ScaleWin<SW> win;
     __shared__ float s_rs[W8A8 ? 1 : BM + BN];                 // FP8: token scales, then weight-row scales
 
     const int tid = threadIdx.x;
@@ -184,7 +231,22 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
     v4u rs = ra;
     int voff_s[2] = {GB_OOB, GB_OOB}, grp_s[2] = {0, 0}, sz_s = 0;
     uint32_t lds_s[2] = {0, 0};
-    if constexpr (W8A8) {
+    if constexpr (W8A8 && SW) {
+        // Windows: waves [0, BM/64) load the activation rows 64 wv + lane,
+        // the next BN/64 waves the weight rows; lane L writes LDS bytes
+        // 16 L + [0, 16) of its 64-row block.
+        if (wv < BM / 64) {
+            rs = buffer_desc(a_scale + (int64_t)m0 * G, (uint32_t)(rows_a * G * 4));
+            voff_s[0] = (64 * wv + lane) * G * 4;
+            lds_s[0] = (uint32_t)(1024 * wv);
+            sz_s = 4;
+        } else if (wv < BM / 64 + BN / 64) {
+            rs = buffer_desc(w_scale + (int64_t)n0 * G, (uint32_t)(rows_b * G * 2));
+            voff_s[0] = (64 * (wv - BM / 64) + lane) * G * 2;
+            lds_s[0] = (uint32_t)(1024 * (wv - BM / 64));
+            sz_s = 2;
+        }
+    } else if constexpr (W8A8) {
         if (2 * wv < NAS) {
             rs = buffer_desc(a_scale + (int64_t)m0 * G, (uint32_t)(rows_a * G * 4));
             sz_s = 4;
@@ -199,14 +261,14 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
                 const int h = z / (BM / 64), jj = z % (BM / 64);
                 voff_s[u] = (64 * jj + lane) * G * 4;
                 grp_s[u] = h;
-                lds_s[u] = (uint32_t)(offsetof(GemmStage<W8A8>, as) + 4 * (h * BM + 64 * jj));
+                lds_s[u] = (uint32_t)(offsetof(Stage, as) + 4 * (h * BM + 64 * jj));
             } else if (z < NAS + NWS) {
                 const int h = (z - NAS) / (BN / 64), jj = (z - NAS) % (BN / 64);
                 voff_s[u] = (64 * jj + lane) * G * 2;
                 grp_s[u] = h;
-                lds_s[u] = (uint32_t)(offsetof(GemmStage<W8A8>, ws) + 4 * (h * BN + 64 * jj));
+                lds_s[u] = (uint32_t)(offsetof(Stage, ws) + 4 * (h * BN + 64 * jj));
             } else {
-                lds_s[u] = (uint32_t)(offsetof(GemmStage<W8A8>, sink) + 256 * u);
+                lds_s[u] = (uint32_t)(offsetof(Stage, sink) + 256 * u);
             }
         }
     }
@@ -216,7 +278,7 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
     // a wave blocks while the address unit takes its loads (64 per CU and
     // stage), so issuing them all right after the barrier would leave the
     // matrix unit idle.
-    auto issue = [&](GemmStage<W8A8>& Sg, int s, int lo, int hi) {
+    auto issue = [&](Stage& Sg, int s, int lo, int hi) {
         const uint32_t base = lds_addr(&Sg);
         const int k0 = s < nsteps ? s * GB_K : GB_OOB;   // stages past the end load nothing
 #pragma unroll
@@ -229,7 +291,21 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
             }
             lds_dma<16>(q < BM / 8 ? ra : rb, base + lds_ld_a[i], vo);
         }
-        if constexpr (W8A8) {
+        if constexpr (W8A8 && SW) {
+            // Stage s = 2w issues activation window w (stages 2w, 2w + 1),
+            // stage s = 4v weight window v (stages 4v .. 4v + 3).  A window
+            // goes out with its first stage's panels, two stages ahead of its
+            // use, into the slot whose last reader every wave has passed.
+            if (lo != 0) return;
+            const bool live = s < nsteps;
+            if (sz_s == 4 && (s & 1) == 0) {
+                const int w = s >> 1;
+                lds_dma<16>(rs, lds_addr(&win.as[w & 1][0]) + lds_s[0], live ? voff_s[0] + 16 * w : GB_OOB);
+            } else if (sz_s == 2 && (s & 3) == 0) {
+                const int v = s >> 2;
+                lds_dma<16>(rs, lds_addr(&win.ws[v & 1][0]) + lds_s[0], live ? voff_s[0] + 16 * v : GB_OOB);
+            }
+        } else if constexpr (W8A8) {
             if (lo != 0) return;
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -266,7 +342,7 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
                  0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000,
                  0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000};
     v16i d[W8A8 ? TM : 1][W8A8 ? TN : 1];
-    auto load_frags = [&](const GemmStage<W8A8>& Mst, int mgh, v4i (&af)[2][TM], v4i (&bf)[2][TN]) {
+    auto load_frags = [&](const Stage& Mst, int mgh, v4i (&af)[2][TM], v4i (&bf)[2][TN]) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -277,7 +353,7 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
                 bf[h][j] = *reinterpret_cast<const v4i*>(&Mst.b[frag_off(wc0 + 32 * j, 4 * mgh + 2 * h)]);
         }
     };
-    auto mfma_group = [&](const GemmStage<W8A8>& Mst, int mgh) {
+    auto mfma_group = [&](const Stage& Mst, int mgh) {
         v4i af[2][TM], bf[2][TN];
         load_frags(Mst, mgh, af, bf);
 #pragma unroll
@@ -297,30 +373,30 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
     // ahead of the rescale (keeping old and new sums live together): the
     // empty asm takes the tile's rescaled acc as input and passes the bias
     // operand through, which pins the tile's MFMAs after its rescale.
-    auto group_step = [&](auto mf, const GemmStage<W8A8>& R, int rgh, int g, const GemmStage<W8A8>& Mst, int mgh,
+    auto group_step = [&](auto mf, const Stage& R, int rgh, int g, const Stage& Mst, int mgh,
                           auto after_row) {
         constexpr bool MF = decltype(mf)::value;
         v4i af[2][TM], bf[2][TN];
         if constexpr (MF) load_frags(Mst, mgh, af, bf);
-        float wsf[TN], wsc[TN];
+        float wsf[TN], wsc[TN], asr[TM];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            wsf[j] = f16_bits_to_f32(R.ws[rgh * BN + wc0 + 32 * j + (lane & 31)] & 0xFFFFu);
+            const int col = wc0 + 32 * j + (lane & 31);
+            if constexpr (SW) wsf[j] = f16_bits_to_f32(win.ws[(g >> 3) & 1][8 * col + (g & 7)]);
+            else wsf[j] = f16_bits_to_f32(R.ws[rgh * BN + col] & 0xFFFFu);
             wsc[j] = -12582912.0f * wsf[j];
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            v4f as4[4];
+            const int row = wr0 + 32 * i + row_scale_lane_row(lane);
+            if constexpr (SW) asr[i] = win.as[(g >> 2) & 1][4 * row + (g & 3)];
+            else asr[i] = R.as[rgh * BM + row];
+        }
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                as4[q] = *reinterpret_cast<const v4f*>(&R.as[rgh * BM + wr0 + 32 * i + 8 * q + 4 * (lane >> 5)]);
+        for (int i = 0; i < TM; ++i) {
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float X = fmaf(__int_as_float(d[i][j][e]), wsf[j], wsc[j]);
-                    acc[i][j][e] = fmaf(X, as4[e >> 2][e & 3], acc[i][j][e]);
-                }
+                rescale_tile(acc[i][j], d[i][j], wsf[j], wsc[j], asr[i], std::make_integer_sequence<int, 16>{});
                 if constexpr (SUMS) {
                     const int n = n0 + wc0 + 32 * j + (lane & 31);
 #pragma unroll
@@ -346,7 +422,7 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
     // the second the other 16: the A and B fragments use the same lane -> k
     // assignment, so the two MFMAs together form the exact dot product over
     // the 32 columns.
-    auto compute_fp8 = [&](const GemmStage<W8A8>& Sg, auto after_pair) {
+    auto compute_fp8 = [&](const Stage& Sg, auto after_pair) {
         constexpr int NP = GB_K / 32;
         v4u ca[TM], cb[TN];
         auto read_pair = [&](int p, v4u (&xa)[TM], v4u (&xb)[TN]) {
@@ -433,7 +509,8 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
         // 64) is rescaled after the loop.  With S = 3 one stage is in flight
         // while two are read.
         static_assert(S == 3, "ring of three stages");
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_PER_STAGE) : "memory");
+        // Stage 1 (odd) carries no scale window: its loads are the last LOADS.
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(SW ? C::LOADS : DMA_PER_STAGE) : "memory");
         sync_stage();
         mfma_group(st[0], 0);
         const int full = G >> 1;                       // stages with two groups
@@ -442,7 +519,7 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
             group_step(std::true_type{}, st[s % S], 0, 2 * s, st[s % S], 1, no_hook);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // also drains group-sum stores
             sync_stage();
-            GemmStage<W8A8>& nxt = st[(s + S - 1) % S];
+            Stage& nxt = st[(s + S - 1) % S];
             group_step(std::true_type{}, st[s % S], 1, 2 * s + 1, st[(s + 1) % S], 0, [&](int i) {
                 if (i == 0) issue(nxt, s + S - 1, 0, C::LOADS / 2);
                 if (i == TM - 1) issue(nxt, s + S - 1, C::LOADS / 2, C::LOADS);
@@ -457,7 +534,7 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
         for (int s = 0; s < nsteps; ++s) {
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_PER_STAGE * (S - 2)) : "memory");
             sync_stage();
-            GemmStage<W8A8>& nxt = st[(s + S - 1) % S];
+            Stage& nxt = st[(s + S - 1) % S];
             compute_fp8(st[s % S], [&](int p) {
                 if (p == 0) issue(nxt, s + S - 1, 0, C::LOADS / 2);
                 if (p == 1) issue(nxt, s + S - 1, C::LOADS / 2, C::LOADS);
@@ -488,14 +565,14 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
         }
 }
 
-template <bool W8A8, bool SUMS, bool KTAIL>
+template <bool W8A8, bool SUMS, bool KTAIL, bool SW = false>
 static hipError_t launch_gemm_t(const uint8_t* A, const float* a_scale, const uint8_t* W, const uint16_t* w_scale,
                                 int64_t M, int64_t N, int64_t K, bool bf16_out, void* y, int32_t* sums,
                                 hipStream_t stream) {
     using C = GemmCfg<W8A8>;
     const int64_t tiles = ((N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
     if (tiles >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-    gemm_kernel<W8A8, SUMS, KTAIL><<<dim3((unsigned)tiles), 64 * C::NW, 0, stream>>>(A, a_scale, W, w_scale, (int)M, (int)N, (int)K,
+    gemm_kernel<W8A8, SUMS, KTAIL, SW><<<dim3((unsigned)tiles), 64 * C::NW, 0, stream>>>(A, a_scale, W, w_scale, (int)M, (int)N, (int)K,
                                                                      bf16_out ? 1 : 0, y, sums);
     return hipGetLastError();
 }
@@ -513,10 +590,13 @@ hipError_t launch_gemm_w8a8(const int8_t* a_q, const float* a_scale, const int8_
     const uint8_t* A = reinterpret_cast<const uint8_t*>(a_q);
     const uint8_t* W = reinterpret_cast<const uint8_t*>(w_q);
     const bool tail = K % GB_K != 0;   // an odd number of groups: the last stage holds one
+    const bool win = K % 512 == 0;     // scale windows (16-byte aligned scale rows)
     if (group_sums != nullptr)
-        return tail ? launch_gemm_t<true, true, true>(A, a_scale, W, w_scale, M, N, K, bf16_out, y, group_sums, stream)
+        return win ? launch_gemm_t<true, true, false, true>(A, a_scale, W, w_scale, M, N, K, bf16_out, y, group_sums, stream)
+             : tail ? launch_gemm_t<true, true, true>(A, a_scale, W, w_scale, M, N, K, bf16_out, y, group_sums, stream)
                     : launch_gemm_t<true, true, false>(A, a_scale, W, w_scale, M, N, K, bf16_out, y, group_sums, stream);
-    return tail ? launch_gemm_t<true, false, true>(A, a_scale, W, w_scale, M, N, K, bf16_out, y, nullptr, stream)
+    return win ? launch_gemm_t<true, false, false, true>(A, a_scale, W, w_scale, M, N, K, bf16_out, y, nullptr, stream)
+         : tail ? launch_gemm_t<true, false, true>(A, a_scale, W, w_scale, M, N, K, bf16_out, y, nullptr, stream)
                 : launch_gemm_t<true, false, false>(A, a_scale, W, w_scale, M, N, K, bf16_out, y, nullptr, stream);
 }
 

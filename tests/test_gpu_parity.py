@@ -425,9 +425,11 @@ def _w8a8_inputs(m, n, k, seed):
 
 
 # (300, 300, 192) and (257, 129, 320): odd group counts (the last 128-column
-# stage holds one group) over several tiles in both directions
+# stage holds one group) over several tiles in both directions.  K % 512 == 0
+# takes the scale-window path: (257, 129, 1536) and (300, 300, 2048) reuse both
+# window slots of both scale kinds on ragged tiles.
 @pytest.mark.parametrize("m,n,k", [(64, 128, 5120), (70, 100, 640), (130, 257, 128), (1, 1, 64), (300, 300, 192),
-                                   (257, 129, 320)])
+                                   (257, 129, 320), (257, 129, 1536), (300, 300, 2048), (513, 385, 512)])
 def test_w8a8_group_sums_and_output(m, n, k):
     qa, sa, w, ws = _w8a8_inputs(m, n, k, m + n + k)
     y32, y16 = empty((m, n), np.float32), empty((m, n), np.uint16)
