@@ -67,7 +67,8 @@ __device__ __forceinline__ int64_t row_bytes(int64_t K) {
 //   Q8G32:                  8 pieces of  8 B at byte 32q + 8g    (k = 32q + 8g + [0,8))
 //   BF16:                   8 pieces of 16 B at byte 64q + 16g   (k = 32q + 8g + [0,8))
 // Wave w takes the PW pieces covering chunk columns [64w, 64w + 64) of each of
-// the 4 row blocks.
+// the 4 row blocks.  Packed Q4G64 pieces hold their codes biased and reordered
+// within each 32-bit word (q4_pack_word); every other format's bytes are copied.
 template <int FMT>
 struct PieceFmt {
     static constexpr bool WIDE = (FMT == W_FP8ROW || FMT == W_MXFP8 || FMT == W_Q8G64 || FMT == W_BF16);
@@ -165,8 +166,36 @@ __device__ __forceinline__ uint32_t i4x2_to_bf16x2(uint32_t d, int sh) {
     return f32x2_to_bf16x2(a, b);
 }
 
+// With one token block, Q4 codes are multiplied in a biased form: the nibble
+// u = q + 8 (0..15) written into mantissa bits 3..6 of the BF16 1.0 is
+// exactly 1 + u / 16 = 1.5 + q / 16, so a group's MFMA sum D over the biased
+// weights gives the exact group sum as sum x q = 16 (D - 1.5 sum x) (sum x
+// from one more MFMA against a fragment of ones).  The packed layout stores u
+// with the two codes of a BF16 pair 16 bits apart (code 2i at bits 4i, code
+// 2i + 1 at bits 16 + 4i of each 32-bit word), so a pair costs one shift and
+// one and-or; the row-major layout (natural order, two's complement) builds
+// the same values with a few more operations.  With more token blocks the
+// decode is shared by their MFMAs while the sum of x and the correction are
+// per block, so there both layouts decode q itself (the same values, so
+// packed and row-major results stay identical).
+constexpr uint32_t Q4_ONE = 0x3F803F80u;        // two BF16 1.0
+constexpr uint32_t Q4_MANT = 0x00780078u;       // mantissa bits 3..6 of both halves
+__device__ __forceinline__ uint32_t q4_packed_pair(uint32_t d, int i) {   // pair i of a packed word
+    const uint32_t t = i == 0 ? (d << 3) : (d >> (4 * i - 3));
+    return (t & Q4_MANT) | Q4_ONE;
+}
+__device__ __forceinline__ uint32_t q4_natural_pair(uint32_t d, int i) {  // codes 2i, 2i + 1 of a row-major word
+    const uint32_t b = ((d >> (8 * i)) ^ 0x88u) & 0xFFu;                  // u of both codes
+    return ((b & 0xFu) << 3) | ((b & 0xF0u) << 15) | Q4_ONE;
+}
+__device__ __forceinline__ uint32_t q4_packed_exact_pair(uint32_t x, int i) {   // x = packed word ^ 0x88888888
+    const float a = (float)((int32_t)(x << (28 - 4 * i)) >> 28);
+    const float b = (float)((int32_t)(x << (12 - 4 * i)) >> 28);
+    return f32x2_to_bf16x2(a, b);
+}
+
 // The A fragment (8 BF16 weights) of row block rb at the wave's local k-step ls.
-template <int FMT>
+template <int FMT, bool PK = false, bool BIAS = false>
 __device__ __forceinline__ v8bf decode_afrag(const WChunk<FMT>& r, int rb, int ls) {
     uint32_t o[4];
     if constexpr (FMT == W_FP8ROW || FMT == W_MXFP8) {
@@ -188,10 +217,11 @@ __device__ __forceinline__ v8bf decode_afrag(const WChunk<FMT>& r, int rb, int l
     } else if constexpr (FMT == W_Q4G64) {
         const uint2 q = r.p[rb];
         const uint32_t d0 = ls ? q.y : q.x;
-        o[0] = i4x2_to_bf16x2(d0, 0);
-        o[1] = i4x2_to_bf16x2(d0, 8);
-        o[2] = i4x2_to_bf16x2(d0, 16);
-        o[3] = i4x2_to_bf16x2(d0, 24);
+        const uint32_t xq = d0 ^ 0x88888888u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o[i] = BIAS ? (PK ? q4_packed_pair(d0, i) : q4_natural_pair(d0, i))
+                        : (PK ? q4_packed_exact_pair(xq, i) : i4x2_to_bf16x2(d0, 8 * i));
     } else if constexpr (FMT == W_Q8G32) {
         const uint2 q = r.p[2 * rb + ls];
         o[0] = i8x2_to_bf16x2(q.x, 0);
@@ -208,7 +238,7 @@ __device__ __forceinline__ v8bf decode_afrag(const WChunk<FMT>& r, int rb, int l
 // One chunk of one wave: xrow(cb) gives the LDS element index of the B
 // fragment row for token block cb (lane's token), kl the chunk's first column
 // in the LDS activation rows, scs / sbase the group scales of the chunk.
-template <int FMT, int NCB>
+template <int FMT, int NCB, bool PK>
 __device__ __forceinline__ void chunk_mfma(const WChunk<FMT>& wc, const uint16_t* xs, const int (&xrow)[NCB], int kl,
                                            const uint16_t* scs, int sgroup0, int wv, int lg,
                                            v4f (&acc)[4][NCB]) {
@@ -231,16 +261,25 @@ __device__ __forceinline__ void chunk_mfma(const WChunk<FMT>& wc, const uint16_t
     } else {
         // GS == 64: the wave's two k-steps are one group; GS == 32: each k-step is one.
         constexpr int NGW = 64 / GS;                     // groups per wave and chunk
+        constexpr bool BIAS = FMT == W_Q4G64 && NCB == 1;   // biased Q4 weights: also sum x per group
         v4f d[4][NCB];
+        v4f xsum[NCB];
 #pragma unroll
         for (int ls = 0; ls < 2; ++ls) {
             const int col = kl + kstep_col<FMT>(2 * wv + ls, lg);
             v8bf b[NCB];
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) b[cb] = *reinterpret_cast<const v8bf*>(&xs[xrow[cb] + col]);
+            if constexpr (BIAS) {
+                const v8bf ones = __builtin_bit_cast(v8bf, make_uint4(Q4_ONE, Q4_ONE, Q4_ONE, Q4_ONE));
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    xsum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        ones, b[cb], ls == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : xsum[cb], 0, 0, 0);
+            }
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
-                const v8bf a = decode_afrag<FMT>(wc, rb, ls);
+                const v8bf a = decode_afrag<FMT, PK, BIAS>(wc, rb, ls);
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) {
                     const v4f c0 = (NGW == 2 || ls == 0) ? v4f{0.f, 0.f, 0.f, 0.f} : d[rb][cb];
@@ -252,15 +291,17 @@ __device__ __forceinline__ void chunk_mfma(const WChunk<FMT>& wc, const uint16_t
 #pragma unroll
                 for (int rb = 0; rb < 4; ++rb) {
                     const uint2 s4 = *reinterpret_cast<const uint2*>(&scs[gi * GV_ROWS + 16 * rb + 4 * lg]);
-                    const float s0 = f16_bits_to_f32(s4.x & 0xFFFFu), s1 = f16_bits_to_f32(s4.x >> 16);
-                    const float s2 = f16_bits_to_f32(s4.y & 0xFFFFu), s3 = f16_bits_to_f32(s4.y >> 16);
+                    // biased Q4: sum x q = 16 (D - 1.5 sum x); the factor 16 goes into the scale (exact)
+                    const float m = BIAS ? 16.0f : 1.0f;
+                    const float sc[4] = {m * f16_bits_to_f32(s4.x & 0xFFFFu), m * f16_bits_to_f32(s4.x >> 16),
+                                         m * f16_bits_to_f32(s4.y & 0xFFFFu), m * f16_bits_to_f32(s4.y >> 16)};
 #pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb) {
-                        acc[rb][cb][0] = fmaf(d[rb][cb][0], s0, acc[rb][cb][0]);
-                        acc[rb][cb][1] = fmaf(d[rb][cb][1], s1, acc[rb][cb][1]);
-                        acc[rb][cb][2] = fmaf(d[rb][cb][2], s2, acc[rb][cb][2]);
-                        acc[rb][cb][3] = fmaf(d[rb][cb][3], s3, acc[rb][cb][3]);
-                    }
+                    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float v = BIAS ? fmaf(xsum[cb][e], -1.5f, d[rb][cb][e]) : d[rb][cb][e];
+                            acc[rb][cb][e] = fmaf(v, sc[e], acc[rb][cb][e]);
+                        }
                 }
             }
         }
@@ -749,7 +790,7 @@ __global__ __launch_bounds__(256, (stream_min_waves<FMT, NCB>())) void gemv_mfma
     WChunk<FMT> ring[D];
     auto body = [&](int c, int u) {
         const int buf = c & 1;
-        chunk_mfma<FMT, NCB>(ring[u], xs[buf], xrow, 0, scs[buf], 0, wv, lg, acc);
+        chunk_mfma<FMT, NCB, PK>(ring[u], xs[buf], xrow, 0, scs[buf], 0, wv, lg, acc);
         store_x((c + 1) & 1, (u + 1) % D);
         load_x(u, min(c + D, nch - 1));
         load_chunk<FMT, PK>(ring[u], src, c_begin + min(c + D, nch - 1));
@@ -868,7 +909,7 @@ __global__ __launch_bounds__(256) void gemv_resident_kernel(const uint8_t* __res
     for (int cb = 0; cb < NCB; ++cb) xrow[cb] = min(cb * 16 + li, T) * xpitch;
 
     auto compute = [&](const WChunk<FMT>& wc, int c) {
-        chunk_mfma<FMT, NCB>(wc, xs, xrow, c * GV_KC, scs, GS ? c * GV_KC / (GS ? GS : 1) : 0, wv, lg, acc);
+        chunk_mfma<FMT, NCB, PK>(wc, xs, xrow, c * GV_KC, scs, GS ? c * GV_KC / (GS ? GS : 1) : 0, wv, lg, acc);
     };
 
     if (nch > 0) {
@@ -1309,6 +1350,20 @@ static void launch_fmt(const GemvPlan& p, bool packed, const void* w, const void
 // contiguous window of memory at a time.  A pure permutation of the row-major
 // bytes (K % 256 == 0).
 // ---------------------------------------------------------------------------
+// Packed Q4 word: the row-major word's codes c0..c7 (c_j at bits 4j, two's
+// complement) as biased nibbles u = c ^ 8 = c + 8, c_2i at bits 4i and
+// c_2i+1 at bits 16 + 4i (see q4_packed_pair).
+__device__ __forceinline__ uint32_t q4_pack_word(uint32_t w) {
+    w ^= 0x88888888u;
+    uint32_t o = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o |= ((w >> (8 * i)) & 0xFu) << (4 * i);
+        o |= ((w >> (8 * i + 4)) & 0xFu) << (16 + 4 * i);
+    }
+    return o;
+}
+
 template <int FMT>
 __global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* __restrict__ src, int64_t N, int64_t K,
                                                            uint8_t* __restrict__ dst, int64_t n_pieces) {
@@ -1326,8 +1381,14 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* __rest
         uint8_t* d = dst + i * PB;
         if (row < N) {
             const uint8_t* s = src + row * row_bytes<FMT>(K) + piece_offset<FMT>(c, q, lane >> 4);
-            if constexpr (PB == 16) *reinterpret_cast<uint4*>(d) = *reinterpret_cast<const uint4*>(s);
-            else *reinterpret_cast<uint2*>(d) = *reinterpret_cast<const uint2*>(s);
+            if constexpr (PB == 16) {
+                *reinterpret_cast<uint4*>(d) = *reinterpret_cast<const uint4*>(s);
+            } else if constexpr (FMT == W_Q4G64) {
+                const uint2 v = *reinterpret_cast<const uint2*>(s);
+                *reinterpret_cast<uint2*>(d) = make_uint2(q4_pack_word(v.x), q4_pack_word(v.y));
+            } else {
+                *reinterpret_cast<uint2*>(d) = *reinterpret_cast<const uint2*>(s);
+            }
         } else {
             if constexpr (PB == 16) *reinterpret_cast<uint4*>(d) = make_uint4(0, 0, 0, 0);
             else *reinterpret_cast<uint2*>(d) = make_uint2(0, 0);

@@ -515,7 +515,8 @@ PACK_FMTS = [(-1, 1.0, 16), (nq.NQ_W_Q8G64_F16S, 1.0, 16), (nq.NQ_W_MXFP8_G32, 1
 def _unpack_reference(packed, fmt, n, k):
     """Invert the documented layout with numpy: rows in blocks of 16; per chunk
     of KC columns, per row block, per piece q, the 64 lanes' pieces in lane
-    order; lane 16 g + i holds row i of the block and piece q of lane group g."""
+    order; lane 16 g + i holds row i of the block and piece q of lane group g
+    (Q4: each 32-bit word also biased and reordered, see _q4_natural_words)."""
     kc = 256
     row_bytes = {0.5: k // 2, 1.0: k, 2.0: 2 * k}[dict((f, b) for f, b, _ in PACK_FMTS)[fmt]]
     pb = dict((f, p) for f, _, p in PACK_FMTS)[fmt]
@@ -530,7 +531,20 @@ def _unpack_reference(packed, fmt, n, k):
             for c in range(k // kc):
                 base = c * chunk_bytes + off
                 out[:, base:base + pb] = v[c, :, q, 16 * g:16 * g + 16, :].reshape(nrb * 16, pb)
+    if fmt == nq.NQ_W_Q4G64_F16S:
+        out = _q4_natural_words(out)
     return out[:n]
+
+
+def _q4_natural_words(b):
+    """Packed Q4 words hold biased nibbles u = c ^ 8, code 2i at bits 4i and
+    code 2i + 1 at bits 16 + 4i; return the row-major words (code j at bits 4j)."""
+    o = b.view(np.uint32)
+    w = np.zeros_like(o)
+    for i in range(4):
+        w |= ((o >> np.uint32(4 * i)) & np.uint32(0xF)) << np.uint32(8 * i)
+        w |= ((o >> np.uint32(16 + 4 * i)) & np.uint32(0xF)) << np.uint32(8 * i + 4)
+    return (w ^ np.uint32(0x88888888)).view(np.uint8)
 
 
 @pytest.mark.parametrize("fmt,bpe,pb", PACK_FMTS)
