@@ -37,9 +37,10 @@ def hipcc():
     raise RuntimeError("hipcc not found (ROCm is required to build libnq.so)")
 
 
-# Per-source additions.  The GEMM keeps its MFMA results in ordinary VGPRs,
-# where the FP32 rescale reads them directly (no copy out of AGPRs per element).
-EXTRA = {"nq_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source additions.  The GEMM and the GEMVs keep their MFMA results in
+# ordinary VGPRs, where the FP32 rescales read them directly (no copy out of
+# AGPRs per element; measured 5-12 % faster on the grouped GEMV formats).
+EXTRA = {"nq_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "nq_gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src, verbose):

@@ -180,9 +180,13 @@ __device__ __forceinline__ uint32_t i4x2_to_bf16x2(uint32_t d, int sh) {
 // packed and row-major results stay identical).
 constexpr uint32_t Q4_ONE = 0x3F803F80u;        // two BF16 1.0
 constexpr uint32_t Q4_MANT = 0x00780078u;       // mantissa bits 3..6 of both halves
-__device__ __forceinline__ uint32_t q4_packed_pair(uint32_t d, int i) {   // pair i of a packed word
+// (t & mask) | one: with literal constants the compiler emits a separate and
+// + or (the VOP3 and-or takes no literal on this target); with the constants
+// in registers (readfirstlane makes them opaque, once per kernel) it emits
+// one v_and_or_b32.
+__device__ __forceinline__ uint32_t q4_packed_pair(uint32_t d, int i, uint32_t mask, uint32_t one) {
     const uint32_t t = i == 0 ? (d << 3) : (d >> (4 * i - 3));
-    return (t & Q4_MANT) | Q4_ONE;
+    return (t & mask) | (one & ~mask);
 }
 __device__ __forceinline__ uint32_t q4_natural_pair(uint32_t d, int i) {  // codes 2i, 2i + 1 of a row-major word
     const uint32_t b = ((d >> (8 * i)) ^ 0x88u) & 0xFFu;                  // u of both codes
@@ -218,9 +222,10 @@ __device__ __forceinline__ v8bf decode_afrag(const WChunk<FMT>& r, int rb, int l
         const uint2 q = r.p[rb];
         const uint32_t d0 = ls ? q.y : q.x;
         const uint32_t xq = d0 ^ 0x88888888u;
+        const uint32_t mask = __builtin_amdgcn_readfirstlane(Q4_MANT), one = __builtin_amdgcn_readfirstlane(Q4_ONE);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            o[i] = BIAS ? (PK ? q4_packed_pair(d0, i) : q4_natural_pair(d0, i))
+            o[i] = BIAS ? (PK ? q4_packed_pair(d0, i, mask, one) : q4_natural_pair(d0, i))
                         : (PK ? q4_packed_exact_pair(xq, i) : i4x2_to_bf16x2(d0, 8 * i));
     } else if constexpr (FMT == W_Q8G32) {
         const uint2 q = r.p[2 * rb + ls];
@@ -291,10 +296,10 @@ __device__ __forceinline__ void chunk_mfma(const WChunk<FMT>& wc, const uint16_t
 #pragma unroll
                 for (int rb = 0; rb < 4; ++rb) {
                     const uint2 s4 = *reinterpret_cast<const uint2*>(&scs[gi * GV_ROWS + 16 * rb + 4 * lg]);
-                    // biased Q4: sum x q = 16 (D - 1.5 sum x); the factor 16 goes into the scale (exact)
-                    const float m = BIAS ? 16.0f : 1.0f;
-                    const float sc[4] = {m * f16_bits_to_f32(s4.x & 0xFFFFu), m * f16_bits_to_f32(s4.x >> 16),
-                                         m * f16_bits_to_f32(s4.y & 0xFFFFu), m * f16_bits_to_f32(s4.y >> 16)};
+                    // biased Q4: sum x q = 16 (D - 1.5 sum x); the factor 16 is applied once
+                    // to the finished sums (q4_bias_finish: exact, a power of two)
+                    const float sc[4] = {f16_bits_to_f32(s4.x & 0xFFFFu), f16_bits_to_f32(s4.x >> 16),
+                                         f16_bits_to_f32(s4.y & 0xFFFFu), f16_bits_to_f32(s4.y >> 16)};
 #pragma unroll
                     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -306,6 +311,14 @@ __device__ __forceinline__ void chunk_mfma(const WChunk<FMT>& wc, const uint16_t
             }
         }
     }
+}
+
+// The factor 16 of the biased Q4 sums (see chunk_mfma), once per wave.
+template <int FMT, int NCB>
+__device__ __forceinline__ void q4_bias_finish(v4f (&acc)[4][NCB]) {
+    if constexpr (FMT == W_Q4G64 && NCB == 1)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) acc[rb][0] *= 16.0f;
 }
 
 // Sum the four waves' partials of row block wv in wave order through LDS
@@ -817,6 +830,7 @@ __global__ __launch_bounds__(256, (stream_min_waves<FMT, NCB>())) void gemv_mfma
     }
 
     v4f fin[NCB];
+    q4_bias_finish<FMT, NCB>(acc);
     reduce_waves<NCB>(acc, fin, reinterpret_cast<v4f*>(&xs[0][0]), wv, lane);
     finish_tile<FMT, NCB>(fin, scales, T, N, row0, wv, lane, tile, split, splits, partial, counters, bf16_out, y,
                           &s_last);
@@ -929,6 +943,7 @@ __global__ __launch_bounds__(256) void gemv_resident_kernel(const uint8_t* __res
     }
 
     v4f fin[NCB];
+    q4_bias_finish<FMT, NCB>(acc);
     reduce_waves<NCB>(acc, fin, reinterpret_cast<v4f*>(lds), wv, lane);
     finish_tile<FMT, NCB>(fin, scales, T, N, row0, wv, lane, tile, split, splits, partial, counters, bf16_out, y,
                           &s_last);
