@@ -47,10 +47,13 @@ constexpr int group_size() {
 
 // Ring depth (chunks in flight per wave) of the streaming variant; shallower
 // with three or more token blocks so that two waves fit per SIMD (a second
-// round of workgroups costs more than the shorter prefetch).
+// round of workgroups costs more than the shorter prefetch), and with two
+// token blocks for the formats with group scales, whose deeper ring there
+// needs more than 256 VGPRs (the excess lives in AGPRs, copied back and forth).
 template <int FMT, int NCB>
 constexpr int depth() {
-    return (FMT == W_BF16 || NCB >= 3) ? 2 : (FMT == W_Q4G64 ? 4 : 3);
+    constexpr bool grouped = FMT == W_Q4G64 || FMT == W_Q8G32 || FMT == W_Q8G64;
+    return (FMT == W_BF16 || NCB >= 3 || (grouped && NCB == 2)) ? 2 : (FMT == W_Q4G64 ? 4 : 3);
 }
 
 template <int FMT>
@@ -1255,7 +1258,12 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     // partials stay within 12% of the weight bytes; with more than one token
     // block, only when the row tiles alone do not cover the CUs
     const double wbytes = (double)N * (double)K * fmt_bytes_per_weight(fmt);
-    const bool try_resident = Tc <= 16 || p.tiles < (int64_t)device_cu_count();
+    // With at least 4 row tiles per CU whole tiles already balance within a
+    // quarter: the streaming kernel without a K split is faster there
+    // (measured on 2376 tiles, Q8G32: 148-170 us at T = 1..16, against 152-222
+    // us for the resident kernel, whose split adds the partial exchange).
+    const bool many_tiles = p.tiles >= 4 * (int64_t)device_cu_count();
+    const bool try_resident = (Tc <= 16 || p.tiles < (int64_t)device_cu_count()) && !many_tiles;
     const int64_t sr = mode == 4 ? s0 : balanced_splits(p.tiles, chunks, smax);
     for (int64_t s = sr; try_resident && s <= 32 && s <= chunks; ++s) {
         const int64_t cps = (chunks + s - 1) / s;
