@@ -10,6 +10,7 @@ order (prefill and conversions before decode, as in an engine step):
   gemv_down      re-encoded 5120x17408, T = 1, 33; BF16 gate 96x5120, T = 1, 33
   decode_mxfp8   MXFP8 256x512 decode (FP32 out)            + MXFP8 GEMV T=1
   head           row-FP8 152064x5120, T = 1..64
+  head_q8        the same head as Q8 group-32, T = 1..64 (FP8-versus-Q8 crossover)
   gemv_q4g64 / gemv_q8g32   at 17408x5120 and 5120x17408, T = 1, 8, 33
   gemv_fp8row    row-FP8 17408x5120, T = 1, 4, 16, 33 (BF16 out)   <- headline
 Weights of the decode GEMVs rotate over copies totalling more than 512 MB so
@@ -268,6 +269,30 @@ def rows_head(nq, W):
                              rotate=False)
 
 
+def rows_head_q8(nq, W):
+    """The output head stored as Q8 group-32 instead of row-FP8 (same shape,
+    packed, T = 1..64), for the FP8-versus-Q8 crossover: synthetic Q8G32
+    codes and FP16 scales of the head's shape (the GEMV's time does not depend
+    on the code values)."""
+    torch = _torch()
+    n, k = W.HEAD_ROWS, W.HIDDEN
+    dd = W.grouped("q8g32", n, k, seed=7)
+    fmt = nq.NQ_W_Q8G32_F16S
+    cd, sd = to_dev(dd["codes"]), to_dev(dd["scales"])
+    pk = pack(nq, fmt, cd, n, k)
+    del cd
+    x64 = to_dev(W.activations(64, k, workload=5, tensor=4))
+    rows = []
+    for t in range(1, 65):
+        xt = x64[:t].contiguous()
+        y = empty((t, n), torch.int16)
+        ws = nq.alloc_gemv_workspace(fmt, t, n, k, DEV)
+        rows.append(Row(f"head_q8g32_T{t}", "gemv_head_q8g32", "GB/s",
+                        n * k + 2 * n * (k // 32) + 2 * t * k + 2 * t * n,
+                        lambda t=t, xt=xt, y=y, ws=ws: nq.nq_gemv_qgroup_packed(fmt, pk, sd, xt, t, n, k, y, ws)))
+    return rows
+
+
 def rows_prefill(nq, W, want_quant, want_w8a8, want_fp8):
     torch = _torch()
     d = W.w8a8_prefill()
@@ -324,6 +349,8 @@ def build_rows(selected):
         rows += rows_mxfp8(nq, W)
     if want("head"):
         rows += rows_head(nq, W)
+    if want("head_q8"):
+        rows += rows_head_q8(nq, W)
     for name in ("q4g64", "q8g32"):
         if want(f"gemv_{name}"):
             rows += rows_grouped(nq, W, name)
@@ -492,6 +519,14 @@ def main():
                          "frac_of_peak": results[name]["frac"]}
     if pre:
         line["prefill"] = pre
+    cross = [t for t in range(1, 65) if f"head_T{t}" in results and f"head_q8g32_T{t}" in results]
+    if cross:
+        q8_faster = [t for t in cross if results[f"head_q8g32_T{t}"]["us"] < results[f"head_T{t}"]["us"]]
+        line["head_fp8_vs_q8"] = {
+            "shape": "152064x5120", "T": [cross[0], cross[-1]],
+            "q8g32_faster_at_T": q8_faster,
+            "fp8_us": [results[f"head_T{t}"]["us"] for t in cross],
+            "q8g32_us": [results[f"head_q8g32_T{t}"]["us"] for t in cross]}
     line["rows"] = {k: {"us": v["us"], "rate": v["rate"], "unit": v["unit"], "frac": v["frac"]}
                     for k, v in results.items()}
     line["timing"] = {"ms_per_step_gpu_events": round(gpu_step_ms, 3), "wall_s_timed_region": round(wall, 3),

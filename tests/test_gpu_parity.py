@@ -411,6 +411,26 @@ def test_gemv_head_full_size_sweep():
         assert rel_fro(host(y, np.float32)[:, rows], M.gemv_fp8row(qo, so, x)) <= FP32_TOL, t
 
 
+@pytest.mark.slow
+def test_gemv_head_q8g32_full_size_packed():
+    """The output head as Q8 group-32 (the FP8-versus-Q8 comparison's other
+    side), packed as the benchmark runs it, sampled rows against the oracle."""
+    n, k = W.HEAD_ROWS, W.HIDDEN
+    fmt = nq.NQ_W_Q8G32_F16S
+    d = W.grouped("q8g32", n, k, seed=7)
+    cd, sd = dev(d["codes"]), dev(d["scales"])
+    pk = empty((nq.nq_packed_weight_bytes(fmt, n, k),), np.uint8)
+    nq.nq_pack_weights(fmt, cd, n, k, pk)
+    del cd
+    rows = _sampled_rows(n, 5)
+    for t in (1, 33, 34, 64):
+        x = W.activations(t, k, workload=5, tensor=4)
+        y = empty((t, n), np.float32)
+        nq.nq_gemv_qgroup_packed(fmt, pk, sd, dev(x), t, n, k, y, nq.alloc_gemv_workspace(fmt, t, n, k, DEV))
+        ref = M.gemv_qgroup("q8g32", d["codes"][rows], d["scales"][rows], x)
+        assert rel_fro(host(y, np.float32)[:, rows], ref) <= FP32_TOL, t
+
+
 # ---------------------------------------------------------------------------
 # a6: W8A8 GEMM; a7: FP8 GEMM; a8: route
 # ---------------------------------------------------------------------------
