@@ -45,6 +45,8 @@ PARITY = {
     "formats.f16_decode": "pinned: closed form; numpy float16 view",
     "formats.round_rne": "pinned: Fraction brute force; torch/numpy casts",
     "method.decode_mxfp8": "pinned: closed form, Fraction brute force",
+    "method.decode_mlx_affine_int8": "pinned: hand values, ties and a single-rounding case, "
+                                     "Fraction brute force with an independent rounding, NaN/Inf",
     "method.reencode_block128_to_row": "pinned: shared-scale invariant, max-code invariant, "
                                        "per-element half-ulp bound, Fraction brute force",
     "method.encode_fp8row": "pinned: as the re-encode (same row encoder)",

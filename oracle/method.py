@@ -61,6 +61,40 @@ def decode_mxfp8(words, e8m0, out="bf16"):
 
 
 # ---------------------------------------------------------------------------
+# MLX affine int8 decode (the draft layer's storage, the step before the path
+# in the conversion pipeline).
+# [MXFP8 card, "How it was built", item 2]: uint8 codes with one FP16 scale and
+# one FP16 bias per 128-element group decode as w = q * scale + bias, written
+# as BF16.
+# Readings: codes [N][K] uint8, groups of 128 along K, scales and biases
+# [N][K/128] FP16 bits; w is the exact value of q * scale + bias (float64 holds
+# it: q * scale has at most 19 significant bits and every FP16 value is a
+# multiple of 2^-24 below 2^16, so the sum spans under 50 bits) rounded once
+# to BF16 (nearest-even, overflow to infinity; NaN -> 0x7FC0), or to FP32.
+# ---------------------------------------------------------------------------
+
+
+def mlx_affine_int8_values(codes, scales, biases):
+    """Exact values (float64) of an MLX affine int8 matrix."""
+    q = np.asarray(codes, dtype=np.uint8).astype(np.float64)
+    n, k = q.shape
+    s = np.repeat(f16_decode(np.asarray(scales, dtype=np.uint16)), 128, axis=1)[:, :k]
+    b = np.repeat(f16_decode(np.asarray(biases, dtype=np.uint16)), 128, axis=1)[:, :k]
+    with np.errstate(invalid="ignore", over="ignore"):
+        return q * s + b
+
+
+def decode_mlx_affine_int8(codes, scales, biases, out="bf16"):
+    """MLX affine int8 -> BF16 (uint16 bits) or FP32 (uint32 bits), single rounding."""
+    v = mlx_affine_int8_values(codes, scales, biases)
+    if out == "bf16":
+        return encode_bf16(v)
+    r = round_f32(v)
+    bits = f32_bits(np.where(np.isnan(r), 0.0, r))
+    return np.where(np.isnan(r), np.uint32(0x7FC00000), bits).astype(np.uint32)
+
+
+# ---------------------------------------------------------------------------
 # a2. Block-128x128 E4M3 -> one BF16 scale per output row (fp8_row_maxabs).
 # [FP8 card, "Conversion and verification", "Block-wise to per-row,
 # exactly"]: codes carry a weight_scale_inv value per 128x128 block; each code

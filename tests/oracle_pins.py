@@ -277,6 +277,66 @@ def pin_mxfp8_decode():
     assert np.array_equal(gotbf[exact32], _bf16_bits_from_f32(ref32)[exact32])
 
 
+def _brute_bf16_bits(v):
+    """Exact rational -> BF16 bits by round-to-nearest-even on the rational
+    value (normal range only), independent of the oracle's rounding."""
+    if v == 0:
+        return 0
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1                                   # 2^e <= a < 2^(e+1)
+    assert -126 <= e <= 127
+    ulp = Fraction(2) ** (e - 7)
+    m = a / ulp
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    r = float(fl * ulp) * (-1.0 if v < 0 else 1.0)
+    return int(np.array([r], np.float32).view(np.uint32)[0] >> 16)
+
+
+def pin_mlx_affine_int8():
+    """[MXFP8 card, "How it was built", item 2]: w = q * scale + bias per
+    128-element group, written as BF16."""
+    one_group = lambda q: np.array([q + [0] * (128 - len(q))], np.uint8)
+    # hand values: 3 * 0.5 - 1 = 0.5; 0 * 0.5 - 1 = -1
+    out = M.decode_mlx_affine_int8(one_group([3]), np.array([[0x3800]], np.uint16), np.array([[0xBC00]], np.uint16))
+    assert out[0, 0] == 0x3F00 and out[0, 1] == 0xBF80
+    # ties to even: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 (-> 1);
+    # 1 + 3 * 2^-8 halfway between 1 + 2^-7 and 1 + 2^-6 (-> the even 1 + 2^-6)
+    out = M.decode_mlx_affine_int8(one_group([1, 3]), np.array([[0x1C00]], np.uint16), np.array([[0x3C00]], np.uint16))
+    assert out[0, 0] == 0x3F80 and out[0, 1] == 0x3F82
+    # one rounding of the exact value: 1 + 2^-8 + 2^-24 is above the tie (-> 1 + 2^-7);
+    # rounding it to FP32 first would land on the tie and then on 1
+    out = M.decode_mlx_affine_int8(one_group([1]), np.array([[0x0001]], np.uint16), np.array([[0x3C04]], np.uint16))
+    assert out[0, 0] == 0x3F81
+    # groups of 128 along K: element 127 takes group 0, element 128 group 1
+    q2 = np.full((1, 256), 2, np.uint8)
+    out = M.decode_mlx_affine_int8(q2, np.array([[0x3C00, 0x4000]], np.uint16), np.array([[0, 0]], np.uint16))
+    assert out[0, 127] == 0x4000 and out[0, 128] == 0x4080          # 2 * 1, 2 * 2
+    # brute force with exact rationals on random groups
+    rng = np.random.default_rng(11)
+    n, k = 3, 384
+    q = rng.integers(0, 256, (n, k)).astype(np.uint8)
+    sc = np.exp2(rng.uniform(-14, -4, (n, k // 128))).astype(np.float16).view(np.uint16)
+    bi = (-rng.uniform(96, 160, (n, k // 128)) * F.f16_decode(sc)).astype(np.float16).view(np.uint16)
+    got = M.decode_mlx_affine_int8(q, sc, bi)
+    got32 = M.decode_mlx_affine_int8(q, sc, bi, out="f32")
+    for i in range(n):
+        for j in range(k):
+            g = j // 128
+            v = int(q[i, j]) * Fraction(F.f16_decode(sc[i, g])) + Fraction(F.f16_decode(bi[i, g]))
+            assert got[i, j] == _brute_bf16_bits(v), (i, j)
+            assert Fraction(float(got32[i:i + 1, j:j + 1].view(np.float32)[0, 0])) == Fraction(float(np.float32(float(v))))
+    # NaN scale -> canonical NaN, infinite bias -> infinity
+    out = M.decode_mlx_affine_int8(one_group([5]), np.array([[0x7E00]], np.uint16), np.array([[0x7C00]], np.uint16))
+    assert out[0, 0] == 0x7FC0
+    out = M.decode_mlx_affine_int8(one_group([5]), np.array([[0x3C00]], np.uint16), np.array([[0xFC00]], np.uint16))
+    assert out[0, 0] == 0xFF80
+
+
 def _brute_reencode_row(codes_row, wsi_row_blocks):
     """One row by exact rationals: returns (codes list, scale Fraction)."""
     k = len(codes_row)
@@ -591,7 +651,7 @@ def pin_route():
     assert not np.array_equal(at[:128], below)        # a different rounding of the activations
 
 
-ORACLE_METHOD_PINS = [pin_mxfp8_decode, pin_reencode_bruteforce, pin_reencode_invariants,
+ORACLE_METHOD_PINS = [pin_mxfp8_decode, pin_mlx_affine_int8, pin_reencode_bruteforce, pin_reencode_invariants,
                       pin_encode_fp8row_bf16, pin_quantize_int8, pin_gemv_fp8row, pin_gemv_qgroup,
                       pin_w8a8, pin_fp8_act_and_gemm, pin_route]
 

@@ -156,7 +156,38 @@ def _quant_fp8_amax127(x_bf16):
     return F.encode_e4m3(q), F.f32_bits(s)
 
 
+def _mlx_group64(codes, scales, biases):
+    q = np.asarray(codes, dtype=np.uint8).astype(np.float64)
+    n, k = q.shape
+    s = np.repeat(F.f16_decode(scales), 64, axis=1)[:, :k]
+    b = np.repeat(F.f16_decode(biases), 64, axis=1)[:, :k]
+    s = np.pad(s, ((0, 0), (0, k - s.shape[1])), mode="edge")
+    b = np.pad(b, ((0, 0), (0, k - b.shape[1])), mode="edge")
+    return q * s + b
+
+
+def _mlx_minus_bias(codes, scales, biases):
+    q = np.asarray(codes, dtype=np.uint8).astype(np.float64)
+    n, k = q.shape
+    return q * np.repeat(F.f16_decode(scales), 128, axis=1)[:, :k] - np.repeat(F.f16_decode(biases), 128, axis=1)[:, :k]
+
+
+def _mlx_through_f32(codes, scales, biases):
+    q = np.asarray(codes, dtype=np.uint8).astype(np.float32)
+    n, k = q.shape
+    s = np.repeat(F.f16_decode(scales), 128, axis=1)[:, :k].astype(np.float32)
+    b = np.repeat(F.f16_decode(biases), 128, axis=1)[:, :k].astype(np.float32)
+    return (q * s + b).astype(np.float64)           # an FP32 value first, then BF16: two roundings
+
+
 MUTATIONS = [
+    ("mlx groups of 64", lambda mp: mp.setattr(M, "mlx_affine_int8_values", _mlx_group64),
+     [P.pin_mlx_affine_int8]),
+    ("mlx bias subtracted", lambda mp: mp.setattr(M, "mlx_affine_int8_values", _mlx_minus_bias),
+     [P.pin_mlx_affine_int8]),
+    ("mlx value rounded to FP32 first", lambda mp: mp.setattr(M, "mlx_affine_int8_values", _mlx_through_f32),
+     [P.pin_mlx_affine_int8]),
+
     ("e4m3 bias 8", lambda mp: mp.setattr(F, "E4M3_TABLE", _table_with(bias=8)),
      [P.pin_e4m3_golden, P.pin_e4m3_vs_torch]),
     ("e4m3 subnormal exponent", lambda mp: mp.setattr(F, "E4M3_TABLE", _table_with(sub_exp=-7)),
