@@ -9,6 +9,7 @@ order (prefill and conversions before decode, as in an engine step):
   reencode       block-128 E4M3 -> per-row FP8, 5120x17408
   gemv_down      re-encoded 5120x17408, T = 1, 33; BF16 gate 96x5120, T = 1, 33
   decode_mxfp8   MXFP8 256x512 decode (FP32 out)            + MXFP8 GEMV T=1
+  decode_mlx     MLX affine int8 17408x5120 -> BF16 (the draft layer's storage)
   head           row-FP8 152064x5120, T = 1..64
   head_q8        the same head as Q8 group-32, T = 1..64 (FP8-versus-Q8 crossover)
   gemv_q4g64 / gemv_q8g32   at 17408x5120 and 5120x17408, T = 1, 8, 33
@@ -146,6 +147,18 @@ def rows_mxfp8(nq, W):
                 lambda: nq.nq_decode_mxfp8(words, e8, n, k, out)),
             Row("gemv_mxfp8_T1", "gemv_mxfp8", "GB/s", n * k + n * k // 32 + 2 * k + 4 * n,
                 lambda: nq.nq_gemv_qgroup(nq.NQ_W_MXFP8_G32, words, e8, x, 1, n, k, y))]
+
+
+def rows_mlx(nq, W):
+    """MLX affine int8 -> BF16 decode on a 17408x5120 projection (the draft
+    layer's storage, decoded by the converter)."""
+    torch = _torch()
+    n, k = W.FFN, W.HIDDEN
+    d = W.mlx_affine_int8(n, k)
+    c, s, b = to_dev(d["codes"]), to_dev(d["scales"]), to_dev(d["biases"])
+    out = empty((n, k), torch.int16)
+    return [Row("decode_mlx_int8", "decode_mlx_int8", "GB/s", n * k + 4 * n * (k // 128) + 2 * n * k,
+                lambda: nq.nq_decode_mlx_affine_int8(c, s, b, n, k, out))]
 
 
 def pack(nq, fmt, codes, n, k):
@@ -347,6 +360,8 @@ def build_rows(selected):
         rows += rows_reencode_and_down(nq, W, want("reencode"), want("gemv_down"))
     if want("decode_mxfp8"):
         rows += rows_mxfp8(nq, W)
+    if want("decode_mlx"):
+        rows += rows_mlx(nq, W)
     if want("head"):
         rows += rows_head(nq, W)
     if want("head_q8"):

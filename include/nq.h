@@ -90,6 +90,20 @@ nq_status nq_decode_mxfp8(const uint32_t* words, const uint8_t* e8m0, int64_t N,
                           int out_dt, void* w_out, void* stream);
 
 /*
+ * MLX affine int8 decode.  [MXFP8 card, "How it was built", item 2]: uint8
+ * codes with one FP16 scale and one FP16 bias per 128-element group decode as
+ * w = q * scale + bias, written as BF16.
+ *   codes          [N][K] u8 (16-byte aligned)
+ *   scales, biases [N][K/128] FP16 bits, groups along K
+ *   w_out          [N][K] FP32 (out_dt = NQ_OUT_F32) or BF16 bits (NQ_OUT_BF16,
+ *                  16-byte aligned): the exact value of q * scale + bias
+ *                  rounded once to nearest-even (NaN -> 0x7FC00000 / 0x7FC0).
+ * Errors: K % 128 != 0 -> NQ_ERR_SHAPE.
+ */
+nq_status nq_decode_mlx_affine_int8(const uint8_t* codes, const uint16_t* scales, const uint16_t* biases,
+                                    int64_t N, int64_t K, int out_dt, void* w_out, void* stream);
+
+/*
  * Block-128x128 E4M3 -> one BF16 scale per output row ("fp8_row_maxabs").
  * [FP8 card, "Conversion and verification", "Block-wise to per-row,
  * exactly"]: each code is decoded in FP32 as e4m3(code) times the scale of its

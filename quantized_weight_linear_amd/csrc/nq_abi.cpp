@@ -97,6 +97,21 @@ nq_status nq_decode_mxfp8(const uint32_t* words, const uint8_t* e8m0, int64_t N,
     return from_hip(nq::launch_decode_mxfp8(words, e8m0, N, K, out_dt == NQ_OUT_BF16, w_out, as_stream(stream)));
 }
 
+nq_status nq_decode_mlx_affine_int8(const uint8_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t N,
+                                    int64_t K, int out_dt, void* w_out, void* stream) {
+    if (N < 0 || K < 0 || K % 128 != 0) return NQ_ERR_SHAPE;
+    if (!out_ok(out_dt)) return NQ_ERR_FORMAT;
+    NQ_TRY(need(codes, N * K));
+    NQ_TRY(need(scales, N * K));
+    NQ_TRY(need(biases, N * K));
+    NQ_TRY(need(w_out, N * K));
+    NQ_TRY(align_ok(codes));
+    NQ_TRY(align_ok(w_out));
+    if (N == 0 || K == 0) return NQ_OK;
+    return from_hip(nq::launch_decode_mlx_affine_int8(codes, scales, biases, N, K, out_dt == NQ_OUT_BF16, w_out,
+                                                      as_stream(stream)));
+}
+
 nq_status nq_reencode_block128_to_row(const uint8_t* codes, const float* wsi, int64_t N, int64_t K, int64_t gr,
                                       int64_t gc, int64_t row_begin, int64_t row_end, uint8_t* out_codes,
                                       uint16_t* out_scale, void* stream) {

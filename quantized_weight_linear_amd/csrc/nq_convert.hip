@@ -1,4 +1,4 @@
-// Format conversion kernels: MXFP8 decode, per-row FP8 encode (from
+// Format conversion kernels: MXFP8 decode, MLX affine int8 decode, per-row FP8 encode (from
 // block-128 E4M3 or from BF16), per-token-per-64 int8 activation quantization
 // and per-token E4M3 activation quantization.
 #include "nq_device.h"
@@ -52,6 +52,75 @@ hipError_t launch_decode_mxfp8(const uint32_t* words, const uint8_t* e8, int64_t
         decode_mxfp8_kernel<true><<<(unsigned)blocks, 256, 0, stream>>>(words, e8, n_words, K / 4, K / 32, out);
     else
         decode_mxfp8_kernel<false><<<(unsigned)blocks, 256, 0, stream>>>(words, e8, n_words, K / 4, K / 32, out);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// MLX affine int8 -> BF16 / FP32: w = q * scale + bias, one FP16 scale and one
+// FP16 bias per 128 codes along K.  One thread per 16 codes (one 16-byte load;
+// 8 threads per group).  The value is formed in FP64, where it is exact (q *
+// scale has at most 19 significant bits and every FP16 value is a multiple of
+// 2^-24 below 2^16), and rounded once: to FP32 by the hardware convert, to
+// BF16 by rounding the FP64 significand to 8 bits, nearest-even.  Every such
+// value lies far inside BF16's normal range (nonzero |w| in [2^-24, 2^25)), so
+// no subnormal or overflow case arises; an infinite bias stays infinite and
+// NaN gives the canonical quiet NaN.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f64_to_bf16_rne(double v) {
+    if (!(v == v)) return 0x7FC0u;
+    uint64_t b = (uint64_t)__double_as_longlong(v);
+    b += ((uint64_t)1 << 44) - 1 + ((b >> 45) & 1);   // round the 52-bit fraction to 7 bits
+    b &= ~(((uint64_t)1 << 45) - 1);
+    return __float_as_uint((float)__longlong_as_double((long long)b)) >> 16;   // exact
+}
+
+template <bool BF16_OUT>
+__global__ __launch_bounds__(256) void decode_mlx_affine_int8_kernel(const uint8_t* __restrict__ codes,
+                                                                     const uint16_t* __restrict__ scales,
+                                                                     const uint16_t* __restrict__ biases,
+                                                                     int64_t n_pieces, int64_t pieces_per_row,
+                                                                     int64_t groups_per_row, void* __restrict__ out) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_pieces;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = i / pieces_per_row;
+        const int64_t g = row * groups_per_row + ((i - row * pieces_per_row) >> 3);
+        const double s = (double)f16_bits_to_f32(scales[g]);
+        const double b = (double)f16_bits_to_f32(biases[g]);
+        const uint4 c = reinterpret_cast<const uint4*>(codes)[i];
+        const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+        uint32_t bits[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const double v = fma((double)((w[e >> 2] >> (8 * (e & 3))) & 0xFFu), s, b);
+            if (BF16_OUT) bits[e] = f64_to_bf16_rne(v);
+            else bits[e] = (v == v) ? __float_as_uint((float)v) : 0x7FC00000u;
+        }
+        if (BF16_OUT) {
+            uint4* o = reinterpret_cast<uint4*>(out) + 2 * i;
+            o[0] = make_uint4(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16), bits[4] | (bits[5] << 16),
+                              bits[6] | (bits[7] << 16));
+            o[1] = make_uint4(bits[8] | (bits[9] << 16), bits[10] | (bits[11] << 16), bits[12] | (bits[13] << 16),
+                              bits[14] | (bits[15] << 16));
+        } else {
+            uint4* o = reinterpret_cast<uint4*>(out) + 4 * i;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = make_uint4(bits[4 * q], bits[4 * q + 1], bits[4 * q + 2], bits[4 * q + 3]);
+        }
+    }
+}
+
+hipError_t launch_decode_mlx_affine_int8(const uint8_t* codes, const uint16_t* scales, const uint16_t* biases,
+                                         int64_t N, int64_t K, bool bf16_out, void* out, hipStream_t stream) {
+    const int64_t n_pieces = N * (K / 16);
+    if (n_pieces == 0) return hipSuccess;
+    int64_t blocks = (n_pieces + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (bf16_out)
+        decode_mlx_affine_int8_kernel<true><<<(unsigned)blocks, 256, 0, stream>>>(codes, scales, biases, n_pieces,
+                                                                                 K / 16, K / 128, out);
+    else
+        decode_mlx_affine_int8_kernel<false><<<(unsigned)blocks, 256, 0, stream>>>(codes, scales, biases, n_pieces,
+                                                                                  K / 16, K / 128, out);
     return hipGetLastError();
 }
 

@@ -11,6 +11,8 @@ enum WFmt { W_Q4G64 = 0, W_Q8G32 = 1, W_Q8G64 = 2, W_MXFP8 = 3, W_BF16 = 4, W_FP
 
 hipError_t launch_decode_mxfp8(const uint32_t* words, const uint8_t* e8, int64_t N, int64_t K, bool bf16_out,
                                void* out, hipStream_t stream);
+hipError_t launch_decode_mlx_affine_int8(const uint8_t* codes, const uint16_t* scales, const uint16_t* biases,
+                                         int64_t N, int64_t K, bool bf16_out, void* out, hipStream_t stream);
 hipError_t launch_reencode_block128(const uint8_t* codes, const float* wsi, int64_t N, int64_t K, int64_t gc,
                                     int64_t r0, int64_t r1, uint8_t* out_codes, uint16_t* out_scale,
                                     hipStream_t stream);

@@ -26,6 +26,7 @@ SIGNATURES = {
     "nq_abi_version": (ctypes.c_int, []),
     "nq_status_string": (ctypes.c_char_p, [_I]),
     "nq_decode_mxfp8": (_I, [_P, _P, _I64, _I64, _I, _P, _P]),
+    "nq_decode_mlx_affine_int8": (_I, [_P, _P, _P, _I64, _I64, _I, _P, _P]),
     "nq_reencode_block128_to_row": (_I, [_P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P]),
     "nq_encode_fp8row_bf16": (_I, [_P, _I64, _I64, _P, _P, _P]),
     "nq_quantize_act_int8_g64": (_I, [_P, _I64, _I64, _P, _P, _P]),
@@ -128,6 +129,13 @@ def nq_decode_mxfp8(words, e8m0, N, K, w_out):
     _size(w_out, N * K * w_out.element_size(), "w_out")
     _check(lib().nq_decode_mxfp8(_ptr(words), _ptr(e8m0), N, K, _out_dt(w_out), _ptr(w_out),
                                  _stream(words, w_out)), "nq_decode_mxfp8")
+
+
+def nq_decode_mlx_affine_int8(codes, scales, biases, N, K, w_out):
+    _size(codes, N * K, "codes"); _size(scales, N * (K // 128) * 2, "scales"); _size(biases, N * (K // 128) * 2, "biases")
+    _size(w_out, N * K * w_out.element_size(), "w_out")
+    _check(lib().nq_decode_mlx_affine_int8(_ptr(codes), _ptr(scales), _ptr(biases), N, K, _out_dt(w_out), _ptr(w_out),
+                                           _stream(codes, w_out)), "nq_decode_mlx_affine_int8")
 
 
 def nq_reencode_block128_to_row(codes, wsi, N, K, row_begin, row_end, out_codes, out_scale):

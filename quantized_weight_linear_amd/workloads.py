@@ -126,6 +126,19 @@ def grouped(fmt, n, k, seed=0):
     return dict(codes=codes, scales=scales)
 
 
+def mlx_affine_int8(n, k, seed=0):
+    """MLX affine int8 weights (the draft layer's storage): uint8 codes uniform
+    over 0..255, one FP16 scale per 128 codes log-uniform in [2^-12, 2^-6] and
+    one FP16 bias per 128 codes, -scale * uniform(96, 160) (a group's minimum
+    lies near -128 scales when its values centre on zero)."""
+    g = rng(6, 0, seed)
+    codes = g.integers(0, 256, (n, k), dtype=np.int16).astype(np.uint8)
+    scales = f16_log_uniform(rng(6, 1, seed), (n, k // 128), -12, -6)
+    s = scales.view(np.float16).astype(np.float64)
+    biases = (-s * rng(6, 2, seed).uniform(96, 160, s.shape)).astype(np.float16).view(np.uint16)
+    return dict(codes=codes, scales=scales, biases=biases)
+
+
 def w8a8_prefill(m=PREFILL_CHUNK, n=FFN, k=HIDDEN, seed=0):
     """x ~ N(0,1) with 1% of elements x20; Q8 group-64 weights, FP16 scales."""
     x = bf16_normal(rng(5, 0, seed), (m, k), outlier_p=0.01)

@@ -64,6 +64,20 @@ def test_decode_mxfp8_validation(L):
     assert f(None, None, 0, 32, 0, None, None) == nq.NQ_OK      # empty: nothing to do
 
 
+def test_decode_mlx_affine_int8_validation(L):
+    f = L.nq_decode_mlx_affine_int8
+    assert f(A, A, A, 4, 192, 0, A, None) == nq.NQ_ERR_SHAPE          # K % 128
+    assert f(A, A, A, -1, 128, 0, A, None) == nq.NQ_ERR_SHAPE
+    assert f(A, A, A, 4, 128, 5, A, None) == nq.NQ_ERR_FORMAT
+    assert f(None, A, A, 4, 128, 0, A, None) == nq.NQ_ERR_NULL
+    assert f(A, None, A, 4, 128, 0, A, None) == nq.NQ_ERR_NULL
+    assert f(A, A, None, 4, 128, 0, A, None) == nq.NQ_ERR_NULL
+    assert f(A, A, A, 4, 128, 1, None, None) == nq.NQ_ERR_NULL
+    assert f(MIS, A, A, 4, 128, 0, A, None) == nq.NQ_ERR_ALIGN
+    assert f(A, A, A, 4, 128, 1, MIS, None) == nq.NQ_ERR_ALIGN
+    assert f(None, None, None, 0, 128, 0, None, None) == nq.NQ_OK    # empty: nothing to do
+
+
 def test_reencode_validation(L):
     f = L.nq_reencode_block128_to_row
     assert f(A, A, 300, 520, 2, 5, 0, 300, A, A, None) == nq.NQ_ERR_SHAPE    # ceil(300/128) = 3

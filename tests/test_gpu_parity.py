@@ -432,6 +432,48 @@ def test_gemv_head_q8g32_full_size_packed():
 
 
 # ---------------------------------------------------------------------------
+# MLX affine int8 decode (the draft layer's storage): bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,k", [(1, 128), (3, 384), (257, 1024), (130, 5120)])
+def test_decode_mlx_affine_int8(n, k):
+    d = W.mlx_affine_int8(n, k, seed=n + k)
+    c, s, b = dev(d["codes"]), dev(d["scales"]), dev(d["biases"])
+    ybf, y32 = empty((n, k), np.uint16), empty((n, k), np.float32)
+    nq.nq_decode_mlx_affine_int8(c, s, b, n, k, ybf)
+    nq.nq_decode_mlx_affine_int8(c, s, b, n, k, y32)
+    assert np.array_equal(host(ybf, np.uint16), M.decode_mlx_affine_int8(d["codes"], d["scales"], d["biases"]))
+    assert np.array_equal(host(y32, np.uint32), M.decode_mlx_affine_int8(d["codes"], d["scales"], d["biases"], out="f32"))
+
+
+def test_decode_mlx_affine_int8_edges():
+    # per group (row r, two groups): ties, the single-rounding case, subnormal,
+    # zero, NaN and infinite scales and biases, the largest magnitudes
+    pairs = [(0x1C00, 0x3C00), (0x0001, 0x3C04), (0x0001, 0x8000), (0x0000, 0x0000), (0x7E00, 0x3C00),
+             (0x3C00, 0xFC00), (0x7C00, 0x0000), (0x7BFF, 0x7BFF), (0x7BFF, 0xFBFF), (0x03FF, 0x8400)]
+    n, k = len(pairs), 256
+    codes = np.tile(np.arange(256, dtype=np.uint8), (n, 1))
+    scales = np.array([[p[0], p[0] ^ 0x8000] for p in pairs], np.uint16)
+    biases = np.array([[p[1], p[1]] for p in pairs], np.uint16)
+    ybf, y32 = empty((n, k), np.uint16), empty((n, k), np.float32)
+    nq.nq_decode_mlx_affine_int8(dev(codes), dev(scales), dev(biases), n, k, ybf)
+    nq.nq_decode_mlx_affine_int8(dev(codes), dev(scales), dev(biases), n, k, y32)
+    assert np.array_equal(host(ybf, np.uint16), M.decode_mlx_affine_int8(codes, scales, biases))
+    assert np.array_equal(host(y32, np.uint32), M.decode_mlx_affine_int8(codes, scales, biases, out="f32"))
+
+
+@pytest.mark.slow
+def test_decode_mlx_affine_int8_full_size_sampled():
+    n, k = W.FFN, W.HIDDEN
+    d = W.mlx_affine_int8(n, k)
+    y = empty((n, k), np.uint16)
+    nq.nq_decode_mlx_affine_int8(dev(d["codes"]), dev(d["scales"]), dev(d["biases"]), n, k, y)
+    rows = _sampled_rows(n, 9)
+    got = host(y, np.uint16)[rows]
+    assert np.array_equal(got, M.decode_mlx_affine_int8(d["codes"][rows], d["scales"][rows], d["biases"][rows]))
+
+
+# ---------------------------------------------------------------------------
 # a6: W8A8 GEMM; a7: FP8 GEMM; a8: route
 # ---------------------------------------------------------------------------
 
