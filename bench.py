@@ -6,6 +6,8 @@ order (prefill and conversions before decode, as in an engine step):
   quant_int8     1792x5120 per-token-per-64 int8 quantization
   gemm_w8a8      W8A8 GEMM M=1792, N=17408, K=5120
   gemm_fp8       per-token E4M3 quantization + FP8 GEMM, same shape
+  q4_a8          Q4 group-64 weights on the A8 route, same shape: widening to
+                 int8, and the routed projection (quantize + widen + GEMM)
   reencode       block-128 E4M3 -> per-row FP8, 5120x17408
   gemv_down      re-encoded 5120x17408, T = 1, 33; BF16 gate 96x5120, T = 1, 33
   decode_mxfp8   MXFP8 256x512 decode (FP32 out)            + MXFP8 GEMV T=1
@@ -328,6 +330,25 @@ def rows_prefill(nq, W, want_quant, want_w8a8, want_fp8):
     return rows
 
 
+def rows_q4_a8(nq, W):
+    """Q4 group-64 weights on the A8 route at the prefill chunk (1792 x 17408 x
+    5120): the codes widened to int8, and the routed projection (activation
+    quantization + widening + W8A8 GEMM)."""
+    torch = _torch()
+    d = W.grouped("q4g64", W.FFN, W.HIDDEN)
+    n, k = W.FFN, W.HIDDEN
+    m = W.PREFILL_CHUNK
+    wc, ws = to_dev(d["codes"]), to_dev(d["scales"])
+    x = to_dev(W.w8a8_prefill()["x"])
+    aq, asc = empty((m, k), torch.int8), empty((m, k // 64), torch.float32)
+    wi8 = empty((n, k), torch.int8)
+    y = empty((m, n), torch.float32)
+    return [Row("unpack_q4", "unpack_q4", "GB/s", n * k // 2 + n * k,
+                lambda: nq.nq_unpack_q4_to_int8(wc, n, k, wi8)),
+            Row("linear_q4g64_a8", "linear_q4g64_a8", "TOPS", 2 * m * n * k,
+                lambda: nq.nq_linear_q4g64(x, m, wc, ws, n, k, True, aq, asc, wi8, y))]
+
+
 def _fp8_gemm_row(nq, W, m, n, k):
     torch = _torch()
     q, s = _encode_bf16_on_gpu(nq, W.fp8row_weights_bf16(n, k))
@@ -356,6 +377,8 @@ def build_rows(selected):
     rows = []
     if want("quant_int8") or want("gemm_w8a8") or want("gemm_fp8"):
         rows += rows_prefill(nq, W, want("quant_int8"), want("gemm_w8a8"), want("gemm_fp8"))
+    if want("q4_a8"):
+        rows += rows_q4_a8(nq, W)
     if want("reencode") or want("gemv_down"):
         rows += rows_reencode_and_down(nq, W, want("reencode"), want("gemv_down"))
     if want("decode_mxfp8"):

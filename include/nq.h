@@ -282,6 +282,31 @@ nq_status nq_linear_q8g64(const uint16_t* x, int64_t T, const int8_t* w_q, const
                           int64_t N, int64_t K, int allow_a8, int8_t* a_q_ws, float* a_scale_ws,
                           int out_dt, void* y, void* workspace, int64_t workspace_bytes, void* stream);
 
+/*
+ * Q4 group-64 codes as int8 (the A8 route's weights).  [int8 card, "What
+ * changes"]: in prefill the Q4 codes feed the int8 matrix units exactly.
+ *   codes [N][K/2] bytes, two's complement nibbles, low nibble first
+ *         (16-byte aligned)
+ *   out   [N][K] int8 in [-8, 7] (16-byte aligned)
+ * Errors: K % 64 != 0 -> NQ_ERR_SHAPE.
+ */
+nq_status nq_unpack_q4_to_int8(const uint8_t* codes, int64_t N, int64_t K, int8_t* out, void* stream);
+
+/*
+ * The Q4 group-64 projection as an engine step runs it: routed by nq_route.
+ * [int8 card, "What changes"]: BF16 route nq_gemv_qgroup(NQ_W_Q4G64_F16S, ...);
+ * A8 route: nq_quantize_act_int8_g64 into a_q_ws [T][K] and a_scale_ws
+ * [T][K/64], the codes widened by nq_unpack_q4_to_int8 into w_i8_ws [N][K]
+ * (caller-owned; a caller that keeps a widened copy can call
+ * nq_gemm_w8a8_g64 directly), then nq_gemm_w8a8_g64 with the same FP16 scales.
+ * The A8 workspaces are needed only when that route is taken; `workspace` is
+ * the optional GEMV workspace.
+ */
+nq_status nq_linear_q4g64(const uint16_t* x, int64_t T, const uint8_t* w_codes, const uint16_t* w_scale,
+                          int64_t N, int64_t K, int allow_a8, int8_t* a_q_ws, float* a_scale_ws,
+                          int8_t* w_i8_ws, int out_dt, void* y, void* workspace, int64_t workspace_bytes,
+                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

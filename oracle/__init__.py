@@ -60,4 +60,5 @@ PARITY = {
     "method.gemm_fp8row": "parity unpinned with respect to the pages (same reason); "
                           "pinned to its reading by Fraction brute force",
     "method.route": "pinned: the 129-token threshold",
+    "method.linear_q4g64": "pinned: route composition, group sums by nibble brute force",
 }

@@ -345,6 +345,22 @@ def linear_w8g64(x_bf16, w_q, w_scale_f16, allow_a8):
     return gemv_qgroup("q8g64", w_q, w_scale_f16, x_bf16)
 
 
+# Q4 group-64 weights on both routes.  [int8 card, "What changes"]: in
+# prefill the Q4 (and Q5) codes feed the int8 matrix units exactly, with the
+# per-64 weight scales applied to each group's int32 sum as for Q8.
+# Reading: the A8 route is the W8A8 GEMM on the Q4 codes taken as int8 values
+# in [-8, 7]; the BF16 route is the grouped GEMV.
+
+
+def linear_q4g64(x_bf16, w_packed, w_scale_f16, allow_a8):
+    """The Q4 group-64 projection routed by token count."""
+    t, k = np.asarray(x_bf16).shape
+    if route(t, allow_a8) == "a8":
+        qa, sa = quantize_act_int8_g64(x_bf16)
+        return gemm_w8a8_g64(qa, sa, unpack_q4(w_packed, k), w_scale_f16)
+    return gemv_qgroup("q4g64", w_packed, w_scale_f16, x_bf16)
+
+
 # ---------------------------------------------------------------------------
 # Output roundings (what an FP32- or BF16-output kernel should produce from
 # the float64 result, up to the kernel's own summation order).

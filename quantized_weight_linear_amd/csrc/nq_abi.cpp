@@ -112,6 +112,16 @@ nq_status nq_decode_mlx_affine_int8(const uint8_t* codes, const uint16_t* scales
                                                       as_stream(stream)));
 }
 
+nq_status nq_unpack_q4_to_int8(const uint8_t* codes, int64_t N, int64_t K, int8_t* out, void* stream) {
+    if (N < 0 || K < 0 || K % 64 != 0) return NQ_ERR_SHAPE;
+    NQ_TRY(need(codes, N * K));
+    NQ_TRY(need(out, N * K));
+    NQ_TRY(align_ok(codes));
+    NQ_TRY(align_ok(out));
+    if (N == 0 || K == 0) return NQ_OK;
+    return from_hip(nq::launch_unpack_q4_to_int8(codes, N, K, out, as_stream(stream)));
+}
+
 nq_status nq_reencode_block128_to_row(const uint8_t* codes, const float* wsi, int64_t N, int64_t K, int64_t gr,
                                       int64_t gc, int64_t row_begin, int64_t row_end, uint8_t* out_codes,
                                       uint16_t* out_scale, void* stream) {
@@ -350,6 +360,42 @@ nq_status nq_linear_q8g64(const uint16_t* x, int64_t T, const int8_t* w_q, const
     hipError_t e = nq::launch_quantize_int8_g64(x, T, K, a_q_ws, a_scale_ws, s);
     if (e != hipSuccess) return NQ_ERR_HIP;
     return from_hip(nq::launch_gemm_w8a8(a_q_ws, a_scale_ws, w_q, w_scale, T, N, K, out_dt == NQ_OUT_BF16, y,
+                                         nullptr, s));
+}
+
+nq_status nq_linear_q4g64(const uint16_t* x, int64_t T, const uint8_t* w_codes, const uint16_t* w_scale, int64_t N,
+                          int64_t K, int allow_a8, int8_t* a_q_ws, float* a_scale_ws, int8_t* w_i8_ws, int out_dt,
+                          void* y, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (T < 0 || N < 0 || K < 0 || K % 64 != 0 || workspace_bytes < 0) return NQ_ERR_SHAPE;
+    if (!out_ok(out_dt)) return NQ_ERR_FORMAT;
+    const bool a8 = nq_route(T, allow_a8) == NQ_ROUTE_A8;
+    NQ_TRY(need(x, T * K));
+    NQ_TRY(need(w_codes, N * K));
+    NQ_TRY(need(w_scale, N * K));
+    NQ_TRY(need(y, T * N));
+    if (a8) {
+        NQ_TRY(need(a_q_ws, T * K));
+        NQ_TRY(need(a_scale_ws, T * K));
+        NQ_TRY(need(w_i8_ws, N * K));
+        NQ_TRY(align_ok(a_q_ws));
+        NQ_TRY(align_ok(a_scale_ws));
+        NQ_TRY(align_ok(w_i8_ws));
+    }
+    NQ_TRY(align_ok(x));
+    NQ_TRY(align_ok(w_codes));
+    NQ_TRY(align_ok(w_scale));
+    NQ_TRY(align_ok(y));
+    NQ_TRY(align_ok(workspace));
+    if (T == 0 || N == 0) return NQ_OK;
+    hipStream_t s = as_stream(stream);
+    if (!a8)
+        return from_hip(nq::launch_gemv(nq::W_Q4G64, w_codes, w_scale, x, T, N, K, out_dt == NQ_OUT_BF16, y,
+                                        workspace, workspace ? workspace_bytes : 0, s, false));
+    hipError_t e = nq::launch_quantize_int8_g64(x, T, K, a_q_ws, a_scale_ws, s);
+    if (e != hipSuccess) return NQ_ERR_HIP;
+    e = nq::launch_unpack_q4_to_int8(w_codes, N, K, w_i8_ws, s);
+    if (e != hipSuccess) return NQ_ERR_HIP;
+    return from_hip(nq::launch_gemm_w8a8(a_q_ws, a_scale_ws, w_i8_ws, w_scale, T, N, K, out_dt == NQ_OUT_BF16, y,
                                          nullptr, s));
 }
 

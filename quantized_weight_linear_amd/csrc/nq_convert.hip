@@ -125,6 +125,41 @@ hipError_t launch_decode_mlx_affine_int8(const uint8_t* codes, const uint16_t* s
 }
 
 // ---------------------------------------------------------------------------
+// Q4 codes -> int8 (the A8 route's weights): two's complement nibbles, low
+// nibble first, each sign-extended to one byte.  One thread per 8 bytes (16
+// codes, a 16-byte store).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t q4x4_to_i8x4(uint32_t b2) {   // 2 bytes -> 4 int8 codes
+    uint32_t o = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int v = (int)(b2 >> (4 * j)) & 15;
+        o |= ((uint32_t)((v ^ 8) - 8) & 0xFFu) << (8 * j);
+    }
+    return o;
+}
+
+__global__ __launch_bounds__(256) void unpack_q4_to_int8_kernel(const uint2* __restrict__ codes, int64_t n_pieces,
+                                                                uint4* __restrict__ out) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_pieces;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const uint2 c = codes[i];
+        out[i] = make_uint4(q4x4_to_i8x4(c.x & 0xFFFFu), q4x4_to_i8x4(c.x >> 16), q4x4_to_i8x4(c.y & 0xFFFFu),
+                            q4x4_to_i8x4(c.y >> 16));
+    }
+}
+
+hipError_t launch_unpack_q4_to_int8(const uint8_t* codes, int64_t N, int64_t K, int8_t* out, hipStream_t stream) {
+    const int64_t n_pieces = N * (K / 16);
+    if (n_pieces == 0) return hipSuccess;
+    int64_t blocks = (n_pieces + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    unpack_q4_to_int8_kernel<<<(unsigned)blocks, 256, 0, stream>>>(reinterpret_cast<const uint2*>(codes), n_pieces,
+                                                                  reinterpret_cast<uint4*>(out));
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Per-row FP8 encode ("fp8_row_maxabs").  One workgroup per output row, two
 // passes over the row: (1) decode every element to FP32 and take the largest
 // magnitude (NaN tracked separately so that it propagates), (2) s = bf16(m /

@@ -13,6 +13,7 @@ hipError_t launch_decode_mxfp8(const uint32_t* words, const uint8_t* e8, int64_t
                                void* out, hipStream_t stream);
 hipError_t launch_decode_mlx_affine_int8(const uint8_t* codes, const uint16_t* scales, const uint16_t* biases,
                                          int64_t N, int64_t K, bool bf16_out, void* out, hipStream_t stream);
+hipError_t launch_unpack_q4_to_int8(const uint8_t* codes, int64_t N, int64_t K, int8_t* out, hipStream_t stream);
 hipError_t launch_reencode_block128(const uint8_t* codes, const float* wsi, int64_t N, int64_t K, int64_t gc,
                                     int64_t r0, int64_t r1, uint8_t* out_codes, uint16_t* out_scale,
                                     hipStream_t stream);

@@ -42,6 +42,8 @@ SIGNATURES = {
     "nq_gemv_fp8row_packed": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I64, _P]),
     "nq_gemv_qgroup_packed": (_I, [_I, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I64, _P]),
     "nq_linear_q8g64": (_I, [_P, _I64, _P, _P, _I64, _I64, _I, _P, _P, _I, _P, _P, _I64, _P]),
+    "nq_unpack_q4_to_int8": (_I, [_P, _I64, _I64, _P, _P]),
+    "nq_linear_q4g64": (_I, [_P, _I64, _P, _P, _I64, _I64, _I, _P, _P, _P, _I, _P, _P, _I64, _P]),
 }
 
 _lib = None
@@ -212,6 +214,23 @@ def nq_linear_q8g64(x, T, w_q, w_scale, N, K, allow_a8, a_q_ws, a_scale_ws, y, w
     _check(lib().nq_linear_q8g64(_ptr(x), T, _ptr(w_q), _ptr(w_scale), N, K, 1 if allow_a8 else 0,
                                  _ptr(a_q_ws), _ptr(a_scale_ws), _out_dt(y), _ptr(y), wp, wb,
                                  _stream(x, w_q)), "nq_linear_q8g64")
+
+
+def nq_unpack_q4_to_int8(codes, N, K, out):
+    _size(codes, N * K // 2, "codes"); _size(out, N * K, "out")
+    _check(lib().nq_unpack_q4_to_int8(_ptr(codes), N, K, _ptr(out), _stream(codes, out)), "nq_unpack_q4_to_int8")
+
+
+def nq_linear_q4g64(x, T, w_codes, w_scale, N, K, allow_a8, a_q_ws, a_scale_ws, w_i8_ws, y, workspace=None):
+    _size(x, 2 * T * K, "x"); _size(w_codes, N * K // 2, "w_codes"); _size(w_scale, 2 * N * (K // 64), "w_scale")
+    _size(y, T * N * y.element_size(), "y")
+    if nq_route(T, allow_a8) == NQ_ROUTE_A8:
+        _size(a_q_ws, T * K, "a_q_ws"); _size(a_scale_ws, 4 * T * (K // 64), "a_scale_ws")
+        _size(w_i8_ws, N * K, "w_i8_ws")
+    wp, wb = _ws(workspace)
+    _check(lib().nq_linear_q4g64(_ptr(x), T, _ptr(w_codes), _ptr(w_scale), N, K, 1 if allow_a8 else 0,
+                                 _ptr(a_q_ws), _ptr(a_scale_ws), _ptr(w_i8_ws), _out_dt(y), _ptr(y), wp, wb,
+                                 _stream(x, w_codes)), "nq_linear_q4g64")
 
 
 NQ_FMT_FP8ROW = -1     # the format code the packing calls use for row-scaled FP8

@@ -651,8 +651,34 @@ def pin_route():
     assert not np.array_equal(at[:128], below)        # a different rounding of the activations
 
 
+def pin_linear_q4g64():
+    """Q4 on both routes: below 129 tokens the grouped GEMV, from 129 on the
+    W8A8 GEMM whose int32 group sums are the exact integer dot products of
+    the int8 activation codes and the Q4 codes."""
+    rng = np.random.default_rng(23)
+    n, k = 5, 128
+    w = rng.integers(0, 256, (n, k // 2)).astype(np.uint8)
+    ws = np.exp2(rng.uniform(-9, -5, (n, 2))).astype(np.float16).view(np.uint16)
+    x = _bf16_bits_from_f32(rng.standard_normal((129, k)).astype(np.float32))
+    assert np.array_equal(M.linear_q4g64(x[:128], w, ws, True), M.gemv_qgroup("q4g64", w, ws, x[:128]))
+    assert np.array_equal(M.linear_q4g64(x[:130], w, ws, False), M.gemv_qgroup("q4g64", w, ws, x[:130]))
+    qa, sa = M.quantize_act_int8_g64(x)
+    y, sums = M.gemm_w8a8_g64(qa, sa, M.unpack_q4(w, k), ws, return_sums=True)
+    assert np.array_equal(M.linear_q4g64(x, w, ws, True), y)
+    # the group sums by brute force over the nibbles (low nibble first, two's complement)
+    for i in (0, 64, 128):
+        for j in range(n):
+            for g in range(2):
+                acc = 0
+                for kk in range(64 * g, 64 * g + 64):
+                    b = int(w[j, kk // 2])
+                    nib = (b >> 4) if kk % 2 else (b & 15)
+                    acc += int(qa[i, kk]) * (nib - 16 if nib >= 8 else nib)
+                assert sums[i, j, g] == acc
+
+
 ORACLE_METHOD_PINS = [pin_mxfp8_decode, pin_mlx_affine_int8, pin_reencode_bruteforce, pin_reencode_invariants,
                       pin_encode_fp8row_bf16, pin_quantize_int8, pin_gemv_fp8row, pin_gemv_qgroup,
-                      pin_w8a8, pin_fp8_act_and_gemm, pin_route]
+                      pin_w8a8, pin_fp8_act_and_gemm, pin_route, pin_linear_q4g64]
 
 ALL_PINS = ORACLE_FORMAT_PINS + ORACLE_METHOD_PINS

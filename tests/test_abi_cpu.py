@@ -146,6 +146,22 @@ def test_linear_validation(L):
     assert f(A, 0, A, A, 8, 64, 1, None, None, 0, None, None, 0, None) == nq.NQ_OK
 
 
+def test_q4_a8_validation(L):
+    u = L.nq_unpack_q4_to_int8
+    assert u(A, 4, 96, A, None) == nq.NQ_ERR_SHAPE
+    assert u(None, 4, 128, A, None) == nq.NQ_ERR_NULL
+    assert u(A, 4, 128, None, None) == nq.NQ_ERR_NULL
+    assert u(MIS, 4, 128, A, None) == nq.NQ_ERR_ALIGN
+    assert u(None, 0, 128, None, None) == nq.NQ_OK
+    f = L.nq_linear_q4g64
+    assert f(A, 200, A, A, 8, 96, 1, A, A, A, 0, A, None, 0, None) == nq.NQ_ERR_SHAPE
+    assert f(A, 200, A, A, 8, 128, 1, A, A, A, 3, A, None, 0, None) == nq.NQ_ERR_FORMAT
+    assert f(A, 200, A, A, 8, 128, 1, A, A, None, 0, A, None, 0, None) == nq.NQ_ERR_NULL     # A8 route needs w_i8_ws
+    assert f(A, 200, A, A, 8, 128, 1, A, A, MIS, 0, A, None, 0, None) == nq.NQ_ERR_ALIGN
+    # the BF16 route does not need the A8 workspaces (nothing is launched: N = 0)
+    assert f(A, 100, A, A, 0, 128, 1, None, None, None, 0, A, None, 0, None) == nq.NQ_OK
+
+
 def test_packed_validation(L):
     # the packed layout exists for K % 256 == 0 only
     assert L.nq_pack_weights(-1, A, 8, 384, A, None) == nq.NQ_ERR_SHAPE

@@ -672,3 +672,48 @@ def test_linear_route(t):
     else:
         nq.nq_gemv_qgroup(nq.NQ_W_Q8G64_F16S, wd, wsd, xd, t, n, k, direct, wsp)
     assert np.array_equal(host(direct, np.uint32), got.view(np.uint32))
+
+
+@pytest.mark.parametrize("n,k", [(3, 128), (257, 1024), (130, 5120)])
+def test_unpack_q4_to_int8(n, k):
+    codes = W.q4_packed_uniform(W.rng(113, n + k), n, k)
+    out = empty((n, k), np.int8)
+    nq.nq_unpack_q4_to_int8(dev(codes), n, k, out)
+    assert np.array_equal(host(out, np.int8).astype(np.int64), M.unpack_q4(codes, k))
+
+
+@pytest.mark.parametrize("t", [1, 33, 128, 129, 300])
+def test_linear_q4g64_route(t):
+    n, k = 200, 1280
+    d = W.grouped("q4g64", n, k, seed=t)
+    x = W.bf16_normal(W.rng(114, t), (t, k))
+    xd, wd, wsd = dev(x), dev(d["codes"]), dev(d["scales"])
+    y = empty((t, n), np.float32)
+    aq, asc, wi8 = empty((t, k), np.int8), empty((t, k // 64), np.float32), empty((n, k), np.int8)
+    wsp = nq.alloc_gemv_workspace(nq.NQ_W_Q4G64_F16S, t, n, k, DEV)
+    nq.nq_linear_q4g64(xd, t, wd, wsd, n, k, True, aq, asc, wi8, y, wsp)
+    got = host(y, np.float32)
+    assert rel_fro(got, M.linear_q4g64(x, d["codes"], d["scales"], True)) <= FP32_TOL
+    direct = empty((t, n), np.float32)
+    if t >= 129:
+        assert np.array_equal(host(wi8, np.int8).astype(np.int64), M.unpack_q4(d["codes"], k))
+        nq.nq_gemm_w8a8_g64(aq, asc, wi8, wsd, t, n, k, direct)
+    else:
+        nq.nq_gemv_qgroup(nq.NQ_W_Q4G64_F16S, wd, wsd, xd, t, n, k, direct, wsp)
+    assert np.array_equal(host(direct, np.uint32), got.view(np.uint32))
+
+
+@pytest.mark.slow
+def test_linear_q4g64_prefill_full_size_sampled():
+    """Q4 weights on the A8 route at the prefill chunk: 1792 x 17408 x 5120."""
+    m, n, k = W.PREFILL_CHUNK, W.FFN, W.HIDDEN
+    d = W.grouped("q4g64", n, k)
+    x = W.w8a8_prefill()["x"]
+    y = empty((m, n), np.float32)
+    aq, asc, wi8 = empty((m, k), np.int8), empty((m, k // 64), np.float32), empty((n, k), np.int8)
+    nq.nq_linear_q4g64(dev(x), m, dev(d["codes"]), dev(d["scales"]), n, k, True, aq, asc, wi8, y)
+    rows = _sampled_rows(m, 12, count=24)
+    cols = _sampled_rows(n, 13, count=48)
+    qa, sa = M.quantize_act_int8_g64(x[rows])
+    ref = M.gemm_w8a8_g64(qa, sa, M.unpack_q4(d["codes"][cols], k), d["scales"][cols])
+    assert rel_fro(host(y, np.float32)[np.ix_(rows, cols)], ref) <= FP32_TOL
