@@ -681,12 +681,14 @@ __device__ __forceinline__ void direct_spread(const uint8_t* __restrict__ w, con
 // ---------------------------------------------------------------------------
 // Waves per SIMD the streaming kernel is compiled for: two for the formats
 // without group scales, so that a spread workgroup fits beside a whole-tile
-// one on every CU (see direct_spread); one for the grouped formats, and for
-// BF16 weights at four token blocks, which would spill at that budget (a
-// spread launch then runs its spread workgroups after the whole tiles).
+// one on every CU (see direct_spread), and for the grouped formats at three
+// token blocks (two K splits per tile then share a CU); one for the other
+// grouped cases, and for BF16 weights at four token blocks, which would spill
+// at that budget (a spread launch then runs its spread workgroups after the
+// whole tiles).
 template <int FMT, int NCB>
 constexpr int stream_min_waves() {
-    return (group_size<FMT>() == 0 && !(FMT == W_BF16 && NCB == 4)) ? 2 : 1;
+    return (!(FMT == W_BF16 && NCB == 4) && (group_size<FMT>() == 0 || NCB == 3)) ? 2 : 1;
 }
 
 // With spread_wgs > 0 (formats without group scales, one split): workgroups
@@ -1281,7 +1283,12 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     // streaming variant: once the row tiles alone cover every CU, splitting K
     // only adds workgroups that compete for LDS bandwidth plus the partial
     // exchange; below that, the split that leaves the busiest CU the fewest chunks
-    s0 = p.tiles >= (int64_t)device_cu_count() ? 1 : balanced_splits(p.tiles, chunks, smax);
+    // Grouped formats with more than one token block (their per-weight work
+    // is heavier) gain from two workgroups per CU: with up to 4 tiles per CU,
+    // K is split in two (17408x5120 T = 33: Q4 36.4 -> 35.4 us, Q8G32 42.6 ->
+    // 40.4 us); the formats without group scales do not (FP8 28 -> 31 us).
+    const bool two_per_cu = fmt_group(fmt) != 0 && Tc > 16 && p.tiles < 4 * (int64_t)device_cu_count();
+    s0 = p.tiles >= (int64_t)device_cu_count() ? (two_per_cu ? 2 : 1) : balanced_splits(p.tiles, chunks, smax);
     const int64_t cps = (chunks + s0 - 1) / s0;
     p.chunks_per_split = (int)cps;
     p.splits = (int)((chunks + cps - 1) / cps);
