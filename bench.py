@@ -46,13 +46,13 @@ sys.path.insert(0, ROOT)
 # Summaries: profiles/gemv_fp8row_17408x5120_hbm_traffic.md.  Valid only for
 # the GEMV source they were taken on (sha256 prefix of nq_gemv.hip).
 GEMV_TRAFFIC = {
-    "source_sha256_16": "184b689833c7f702",
+    "source_sha256_16": "b4a4228930227a85",
     "fetch_factor": 262144.0 / 131083.5,
     "write_factor": 1.0,
-    "fetch_kib": {"gemv_fp8row_T1": 43788.7, "gemv_fp8row_T4": 44008.7, "gemv_fp8row_T16": 44895.0,
-                  "gemv_fp8row_T33": 46221.8},
+    "fetch_kib": {"gemv_fp8row_T1": 43800.1, "gemv_fp8row_T4": 44021.2, "gemv_fp8row_T16": 44908.1,
+                  "gemv_fp8row_T33": 46232.6},
     "write_kib": {"gemv_fp8row_T1": 106.5, "gemv_fp8row_T4": 400.5, "gemv_fp8row_T16": 1576.5,
-                  "gemv_fp8row_T33": 3242.6},
+                  "gemv_fp8row_T33": 3242.5},
 }
 
 HBM_PEAK_GBS = 8000.0
