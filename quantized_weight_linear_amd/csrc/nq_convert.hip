@@ -163,8 +163,10 @@ hipError_t launch_unpack_q4_to_int8(const uint8_t* codes, int64_t N, int64_t K, 
 // Per-row FP8 encode ("fp8_row_maxabs").  One workgroup per output row, two
 // passes over the row: (1) decode every element to FP32 and take the largest
 // magnitude (NaN tracked separately so that it propagates), (2) s = bf16(m /
-// 448) and code = e4m3_sat(v / s), both IEEE divisions.  The row is read
-// twice; the second read comes from cache.
+// 448) and code = e4m3_sat(v / s), both IEEE divisions.  Each thread keeps
+// the decoded values of its first ROW_CACHE 16-element steps in registers
+// (rows of up to 20480 elements), so pass 2 reads the row again only beyond
+// that (the unrolled loads of pass 1 are also all in flight at once).
 //
 // Source SRC_BLOCK: E4M3 codes times the FP32 scale of their 128x128 block
 // (one FP32 multiply, rounded once).  Source SRC_BF16: BF16 values (exact).
@@ -235,10 +237,28 @@ __global__ __launch_bounds__(256) void encode_rows_kernel(RowSource<SRC> src, in
     const int tid = threadIdx.x;
     const bool vec = src.vec_ok();
 
+    constexpr int ROW_CACHE = 5;
+    float cache[ROW_CACHE][16];
     float m = 0.0f;
     int nan = 0;
     if (vec) {
-        for (int64_t k = (int64_t)tid * 16; k < K; k += 256 * 16) {
+#pragma unroll
+        for (int it = 0; it < ROW_CACHE; ++it) {
+            const int64_t k = (int64_t)tid * 16 + (int64_t)it * (256 * 16);
+            if (k < K) src.load16(row, k, cache[it]);
+        }
+#pragma unroll
+        for (int it = 0; it < ROW_CACHE; ++it) {
+            const int64_t k = (int64_t)tid * 16 + (int64_t)it * (256 * 16);
+            if (k < K) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    m = fmaxf(m, fabsf(cache[it][e]));
+                    nan |= !(cache[it][e] == cache[it][e]);
+                }
+            }
+        }
+        for (int64_t k = (int64_t)tid * 16 + ROW_CACHE * (256 * 16); k < K; k += 256 * 16) {
             float v[16];
             src.load16(row, k, v);
 #pragma unroll
@@ -278,15 +298,23 @@ __global__ __launch_bounds__(256) void encode_rows_kernel(RowSource<SRC> src, in
     const bool fast = s > 0.0f && s < __uint_as_float(0x7F800000u);
     const double r = 1.0 / (double)s;
     if (vec && fast) {
-        for (int64_t k = (int64_t)tid * 16; k < K; k += 256 * 16) {
-            float v[16];
-            src.load16(row, k, v);
+        auto encode16 = [&](const float* v, int64_t k) {
             uint32_t d[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 d[q] = f32x4_to_e4m3_hw(div_via_recip64(v[4 * q], r), div_via_recip64(v[4 * q + 1], r),
                                         div_via_recip64(v[4 * q + 2], r), div_via_recip64(v[4 * q + 3], r));
             *reinterpret_cast<uint4*>(orow_ptr + k) = make_uint4(d[0], d[1], d[2], d[3]);
+        };
+#pragma unroll
+        for (int it = 0; it < ROW_CACHE; ++it) {
+            const int64_t k = (int64_t)tid * 16 + (int64_t)it * (256 * 16);
+            if (k < K) encode16(cache[it], k);
+        }
+        for (int64_t k = (int64_t)tid * 16 + ROW_CACHE * (256 * 16); k < K; k += 256 * 16) {
+            float v[16];
+            src.load16(row, k, v);
+            encode16(v, k);
         }
     } else if (vec) {
         for (int64_t k = (int64_t)tid * 16; k < K; k += 256 * 16) {
