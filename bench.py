@@ -445,8 +445,8 @@ def main():
         calibrate_copy()
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(how the path would shard is described in DESIGN.md)"}))
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1 (the path would shard "
+                                   "along the output rows, with an all-gather of the outputs)"}))
         sys.exit(2)
     torch = _torch()
     from quantized_weight_linear_amd import nq
