@@ -202,6 +202,50 @@ def test_quantize_int8_config5_full():
     assert np.array_equal(host(q, np.int8), qo)
 
 
+def _near_half_groups(n_groups, seed):
+    """Groups of 64 BF16 values whose quotients x / s (s = f32(amax / 127)) lie
+    within 2^-12 of a half-integer: each group holds its amax and 63 values
+    picked among all BF16 values in [0, amax] by that criterion, random signs."""
+    g = np.random.default_rng(seed)
+    out = np.zeros((n_groups, 64), np.uint16)
+    all_bf = np.arange(0, 0x7F80, dtype=np.uint32)                        # positive finite BF16
+    all_v = (all_bf << 16).view(np.float32).astype(np.float64)
+    for r in range(n_groups):
+        mb = np.uint32(g.integers(0x3C00, 0x4400))                         # amax in [2^-7, 2^9)
+        m = float((np.array([mb << 16], np.uint32)).view(np.float32)[0])
+        sc = float(np.float32(m) / np.float32(127.0))                     # IEEE FP32 division
+        cand = all_bf[(all_v <= m)]
+        t = all_v[(all_v <= m)] / sc
+        d = np.abs((t - np.floor(t)) - 0.5)
+        pick = cand[d < 2.0 ** -12]
+        if len(pick) > 63:
+            pick = g.choice(pick, 63, replace=False)
+        fill = g.choice(cand, 63 - len(pick)) if len(pick) < 63 else np.zeros(0, np.uint32)
+        vals = np.concatenate([pick, fill]).astype(np.uint16)
+        vals = vals | (g.integers(0, 2, 63).astype(np.uint16) << 15)
+        out[r, 0] = mb
+        out[r, 1:] = vals
+    return out
+
+
+def test_quantize_int8_near_half_quotients():
+    x = _near_half_groups(96, 5)
+    # and groups of exact ties: amax = 127 * 2^e makes s = 2^e, and (j + 0.5) 2^e are ties
+    ties = np.zeros((8, 64), np.float32)
+    for r, e in enumerate(range(-4, 4)):
+        ties[r, 0] = 127.0 * 2.0 ** e
+        ties[r, 1:] = (np.arange(63) % 64 + 0.5) * 2.0 ** e * (1 - 2 * (np.arange(63) % 2))
+    tb = (ties.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal((tb.astype(np.uint32) << 16).view(np.float32), ties)   # all BF16-exact
+    x = np.concatenate([x, tb]).reshape(13, 512)
+    t, k = x.shape
+    q, s = empty((t, k), np.int8), empty((t, k // 64), np.float32)
+    nq.nq_quantize_act_int8_g64(dev(x), t, k, q, s)
+    qo, so = M.quantize_act_int8_g64(x)
+    assert np.array_equal(host(s, np.uint32), so)
+    assert np.array_equal(host(q, np.int8), qo)
+
+
 @pytest.mark.parametrize("m,k", [(7, 256), (70, 400), (3, 8)])
 def test_quantize_fp8_row(m, k):
     x = _special_activations(max(m, 5), k)[:m] if m >= 5 else W.bf16_normal(W.rng(95, k), (m, k))
