@@ -356,20 +356,40 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(float* p) {
 __device__ __forceinline__ void store_partial(__amdgpu_buffer_rsrc_t r, int64_t idx, v4f v) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, (int)(idx * 4), 0, CPOL_DEVICE);
 }
+// An element index whose byte offset lies past the partial buffer's range:
+// a load of it reads zeros.
+constexpr int64_t PARTIAL_OOB = 0x7FFFFFF0 / 4;
 __device__ __forceinline__ v4f load_partial(__amdgpu_buffer_rsrc_t r, int64_t idx) {
     return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(idx * 4), 0, CPOL_DEVICE));
 }
 
-// Output rows n0 .. n0 + 3 of token t from FP32 values v (row-FP8: the row
-// scale is applied here).
+// BF16 row scales of rows n0 .. n0 + 3 as FP32 (row-FP8; the other formats
+// need none).  Four 2-byte buffer loads with no branch between them, so they
+// are in flight together; rows past N read as zero (never written).  Loaded
+// once per lane before the token blocks' writes: guarded loads per write
+// would each wait for memory, NCB x 4 round trips at the end of every tile.
 template <int FMT>
-__device__ __forceinline__ void write_rows(v4f v, int t, int64_t n0, const void* __restrict__ scales, int T, int N,
-                                           int bf16_out, void* __restrict__ y) {
+__device__ __forceinline__ v4f row_scales(const void* __restrict__ scales, int64_t n0, int N) {
+    v4f s = v4f{1.f, 1.f, 1.f, 1.f};
+    if constexpr (FMT == W_FP8ROW) {
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(scales), (short)0, N * 2, BUF_FLAGS);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            s[i] = bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, (int)((n0 + i) * 2), 0, 0));
+    }
+    return s;
+}
+
+// Output rows n0 .. n0 + 3 of token t from FP32 values v; rsc from
+// row_scales (row-FP8: the row scale is applied here).
+template <int FMT>
+__device__ __forceinline__ void write_rows(v4f v, int t, int64_t n0, v4f rsc, int T, int N, int bf16_out,
+                                           void* __restrict__ y) {
     if (t >= T) return;
     if constexpr (FMT == W_FP8ROW) {
-        const uint16_t* rs = reinterpret_cast<const uint16_t*>(scales);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (n0 + r < N) ? v[r] * bf16_bits_to_f32(rs[n0 + r]) : 0.f;
+        for (int r = 0; r < 4; ++r) v[r] = v[r] * rsc[r];
     }
     if (bf16_out) {
         uint16_t* yo = reinterpret_cast<uint16_t*>(y) + (int64_t)t * N;
@@ -406,7 +426,8 @@ __device__ __forceinline__ void finish_tile(v4f (&fin)[NCB], const void* __restr
     const int tid = threadIdx.x;
     const int64_t npad = (int64_t)gridDim.x * GV_ROWS;
     const int64_t n0 = row0 + wv * 16 + 4 * lg;           // this lane's 4 output rows
-    auto write_out = [&](int cb, v4f v) { write_rows<FMT>(v, cb * 16 + li, n0, scales, T, N, bf16_out, y); };
+    const v4f rsc = row_scales<FMT>(scales, n0, N);
+    auto write_out = [&](int cb, v4f v) { write_rows<FMT>(v, cb * 16 + li, n0, rsc, T, N, bf16_out, y); };
 
     if (splits == 1) {
 #pragma unroll
@@ -575,8 +596,9 @@ __device__ __forceinline__ void direct_spread(const uint8_t* __restrict__ w, con
         const int tl = tile0 + lt0 + k;
         const int64_t n0 = (int64_t)tl * GV_ROWS + wv * 16 + 4 * lg;
         if (seg_full(k)) {
+            const v4f rsc = row_scales<FMT>(scales, n0, N);
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) write_rows<FMT>(fin[cb], cb * 16 + li, n0, scales, T, N, bf16_out, y);
+            for (int cb = 0; cb < NCB; ++cb) write_rows<FMT>(fin[cb], cb * 16 + li, n0, rsc, T, N, bf16_out, y);
         } else {
             const int slot = seg_slots(k).x;
 #pragma unroll
@@ -648,27 +670,34 @@ __device__ __forceinline__ void direct_spread(const uint8_t* __restrict__ w, con
         const int tl = tile0 + lt0 + k;
         const int nslots = seg_slots(k).y;
         const int64_t n0 = (int64_t)tl * GV_ROWS + wv * 16 + 4 * lg;
+        const v4f rsc = row_scales<FMT>(scales, n0, N);
+        // The loads of a batch of slots, for all token blocks, are in flight
+        // together (one memory round trip per batch; tokens past T and slots
+        // past the last read as zero through out-of-range offsets, so no
+        // branch sits between them); each token block's sum runs in slot order.
+        constexpr int SB = NCB == 1 ? 16 : 12;
+        v4f sum[NCB];
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-            const int t = cb * 16 + li;
-            if (t >= T) continue;
-            // all slots' loads of a batch are in flight together; the sum runs in slot order
-            constexpr int SB = 16;
-            v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
-            for (int sb = 0; sb < nslots; sb += SB) {
-                v4f part[SB];
+        for (int cb = 0; cb < NCB; ++cb) sum[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int sb = 0; sb < nslots; sb += SB) {
+            v4f part[NCB][SB];
 #pragma unroll
-                for (int j = 0; j < SB; ++j)
-                    part[j] = sb + j < nslots
-                                  ? load_partial(pr, (((int64_t)(lt0 + k) * maxslots + sb + j) * T + t) * GV_ROWS +
-                                                         wv * 16 + 4 * lg)
-                                  : v4f{0.f, 0.f, 0.f, 0.f};
+            for (int cb = 0; cb < NCB; ++cb) {
+                const int t = cb * 16 + li;
 #pragma unroll
-                for (int j = 0; j < SB; ++j)
-                    if (sb + j < nslots) sum += part[j];
+                for (int j = 0; j < SB; ++j) {
+                    const int64_t idx = (((int64_t)(lt0 + k) * maxslots + sb + j) * T + t) * GV_ROWS + wv * 16 + 4 * lg;
+                    part[cb][j] = load_partial(pr, (t < T && sb + j < nslots) ? idx : PARTIAL_OOB);
+                }
             }
-            write_rows<FMT>(sum, t, n0, scales, T, N, bf16_out, y);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int j = 0; j < SB; ++j)
+                    if (sb + j < nslots) sum[cb] += part[cb][j];
         }
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) write_rows<FMT>(sum[cb], cb * 16 + li, n0, rsc, T, N, bf16_out, y);
         if (tid == 0) __hip_atomic_store(&counters[tl], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
@@ -1177,14 +1206,21 @@ static int64_t resident_lds(int fmt, int64_t Tc, int64_t cps, int kc) {
 }
 
 // More tiles than CUs, not a multiple of them, one split: whole tiles for the
-// first m x CUs, the R others spread over one more workgroup per CU (at most
-// SPREAD_MAXSEG tiles each).
+// first m x CUs, the R others spread over at most one more workgroup per CU
+// (at most SPREAD_MAXSEG tiles each).  The busiest CU then holds lmax =
+// ceil(U / min(U, CUs)) units beside its tile; the fewest workgroups that keep
+// that bound, ceil(U / lmax), give a leftover tile the fewest partial slots,
+// and so the shortest final sum for its last workgroup, which slows the
+// whole tile sharing its CU (17408 x 5120: 160 workgroups of 2 chunks, 10
+// slots a tile, instead of 256 of 1 or 2 chunks, 16 or 17 slots).
 static void plan_spread(GemvPlan& p, int64_t chunks) {
     const int64_t cus = (int64_t)device_cu_count();
     const int64_t R = p.tiles % cus, U = R * chunks;
     if (p.splits != 1 || p.tiles <= cus || R == 0 || U >= ((int64_t)1 << 31)) return;
-    const int64_t E = U < cus ? U : cus;
-    const int64_t lmin = U / E, lmax = (U + E - 1) / E;
+    const int64_t E0 = U < cus ? U : cus;
+    const int64_t lmax = (U + E0 - 1) / E0;
+    const int64_t E = (U + lmax - 1) / lmax;
+    const int64_t lmin = U / E;
     if ((lmax - 1 + chunks - 1) / chunks + 1 > SPREAD_MAXSEG) return;
     p.main_tiles = p.tiles - R;
     p.spread_wgs = (int)E;
