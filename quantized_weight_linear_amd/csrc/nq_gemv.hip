@@ -760,6 +760,10 @@ __global__ __launch_bounds__(256, (stream_min_waves<FMT, NCB>())) void gemv_mfma
     const int li = lane & 15;
     const int lg = lane >> 4;
     const int tile = (int)blockIdx.x - spread_wgs;   // spread workgroups come first
+    // A whole tile's waves issue ahead of a spread workgroup's on the same CU
+    // (these are younger, and equal priority favours the oldest wave): the
+    // spread work then fills the cycles the tile leaves idle.
+    if (spread_wgs > 0) __builtin_amdgcn_s_setprio(2);
     const int split = blockIdx.y;
     const int64_t row0 = (int64_t)tile * GV_ROWS;
     const int64_t total_chunks = K / GV_KC;
@@ -1279,7 +1283,14 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     int64_t smax = chunks / min_chunks;        // keep whole chunks, at least min_chunks per split
     if (smax > 32) smax = 32;
     if (smax < 1) smax = 1;
-    if (fmt_group(fmt) == 0 && Tc <= 16 && mode != 2) {
+    // One whole tile per CU plus leftover tiles spread beside them: the
+    // streaming kernel, whose whole tiles issue ahead of the spread work (see
+    // gemv_mfma_kernel), is faster than the direct kernel at every T here
+    // (17408 x 5120: T = 1 17.8 against 18.2 us, T = 4 17.3 / 18.0, T = 16
+    // 18.8 / 20.6); the resident kernel's K split is slower than both.
+    const bool spread_one_round = fmt_group(fmt) == 0 && allow_spread && mode != 3 &&
+                                  p.tiles > (int64_t)device_cu_count() && p.tiles < 2 * (int64_t)device_cu_count();
+    if (fmt_group(fmt) == 0 && Tc <= 16 && mode != 2 && !spread_one_round) {
         // direct variant (no group scales, one token block): about one
         // workgroup per CU (measured: more per CU only slow it down); with
         // fewer tiles than CUs, K split so that the busiest CU has the fewest chunks
@@ -1301,7 +1312,7 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     // (measured on 2376 tiles, Q8G32: 148-170 us at T = 1..16, against 152-222
     // us for the resident kernel, whose split adds the partial exchange).
     const bool many_tiles = p.tiles >= 4 * (int64_t)device_cu_count();
-    const bool try_resident = (Tc <= 16 || p.tiles < (int64_t)device_cu_count()) && !many_tiles;
+    const bool try_resident = (Tc <= 16 || p.tiles < (int64_t)device_cu_count()) && !many_tiles && !spread_one_round;
     const int64_t sr = mode == 4 ? s0 : balanced_splits(p.tiles, chunks, smax);
     for (int64_t s = sr; try_resident && s <= 32 && s <= chunks; ++s) {
         const int64_t cps = (chunks + s - 1) / s;

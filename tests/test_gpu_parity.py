@@ -373,6 +373,34 @@ def _sampled_rows(n, seed, count=96):
     return np.unique(np.concatenate([[0, 63, 64, n - 1], W.rng(101, seed).integers(0, n, count)]))
 
 
+# The timed launch: packed weights of 17408 x 5120 (272 row tiles: whole tiles
+# on every CU plus 16 spread over others), T = 1, 4, 16, 33, BF16 output.
+@pytest.mark.slow
+def test_gemv_fp8row_packed_full_size_sampled():
+    n, k = W.FFN, W.HIDDEN
+    w = W.fp8row_weights_bf16(n, k)
+    rows = _sampled_rows(n, n + 1)
+    wq_o, ws_o = M.encode_fp8row_bf16(w[rows])
+    wd = dev(w)
+    wq_d, ws_d = empty((n, k), np.uint8), empty((n,), np.uint16)
+    nq.nq_encode_fp8row_bf16(wd, n, k, wq_d, ws_d)
+    del wd
+    pk = empty((nq.nq_packed_weight_bytes(-1, n, k),), np.uint8)
+    nq.nq_pack_weights(-1, wq_d, n, k, pk)
+    del wq_d
+    for t in (1, 4, 16, 33):
+        x = W.activations(t, k)
+        y32, y16 = empty((t, n), np.float32), empty((t, n), np.uint16)
+        wsp = nq.alloc_gemv_workspace(-1, t, n, k, DEV)
+        nq.nq_gemv_fp8row_packed(pk, ws_d, dev(x), t, n, k, y32, wsp)
+        nq.nq_gemv_fp8row_packed(pk, ws_d, dev(x), t, n, k, y16, wsp)
+        g32, g16 = host(y32, np.float32), host(y16, np.uint16)
+        assert np.array_equal(g16, bf16_of_f32_bits(g32)), t
+        ref = M.gemv_fp8row(wq_o, ws_o, x)
+        assert rel_fro(g32[:, rows], ref) <= FP32_TOL, t
+        assert int(wsp.view(torch.int32)[:(n + 63) // 64].abs().sum().item()) == 0, t     # counters reset
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("n,k,ts", [(W.FFN, W.HIDDEN, [1, 4, 16, 33]), (W.HIDDEN, W.FFN, [1, 33])])
 def test_gemv_fp8row_full_size(n, k, ts):
@@ -666,8 +694,10 @@ def test_pack_is_the_documented_permutation(fmt, bpe, pb, n, k):
     assert nq.nq_packed_weight_bytes(fmt, n, k) == -(-n // 16) * 16 * int(k * bpe)
 
 
+# 16448 rows: one tile more than 256 CUs, so the row-FP8 kernels run the
+# leftover tile on spread workgroups beside the whole tiles.
 @pytest.mark.parametrize("name,fmt", [("fp8row", -1)] + GROUP_FMTS)
-@pytest.mark.parametrize("n,k", [(1000, 1536), (200, 1280)])
+@pytest.mark.parametrize("n,k", [(1000, 1536), (200, 1280), (16448, 768)])
 @pytest.mark.parametrize("t", [1, 16, 33])
 def test_gemv_packed_equals_row_major(name, fmt, n, k, t):
     if name == "fp8row":
