@@ -46,13 +46,13 @@ sys.path.insert(0, ROOT)
 # Summaries: profiles/gemv_fp8row_17408x5120_hbm_traffic.md.  Valid only for
 # the GEMV source they were taken on (sha256 prefix of nq_gemv.hip).
 GEMV_TRAFFIC = {
-    "source_sha256_16": "b4a4228930227a85",
+    "source_sha256_16": "23793bd1c6ffef2c",
     "fetch_factor": 262144.0 / 131083.5,
     "write_factor": 1.0,
-    "fetch_kib": {"gemv_fp8row_T1": 43800.1, "gemv_fp8row_T4": 44021.2, "gemv_fp8row_T16": 44908.1,
-                  "gemv_fp8row_T33": 46232.6},
-    "write_kib": {"gemv_fp8row_T1": 106.5, "gemv_fp8row_T4": 400.5, "gemv_fp8row_T16": 1576.5,
-                  "gemv_fp8row_T33": 3242.5},
+    "fetch_kib": {"gemv_fp8row_T1": 43828.3, "gemv_fp8row_T4": 44016.2, "gemv_fp8row_T16": 44776.4,
+                  "gemv_fp8row_T33": 45904.0},
+    "write_kib": {"gemv_fp8row_T1": 79.5, "gemv_fp8row_T4": 301.5, "gemv_fp8row_T16": 1189.5,
+                  "gemv_fp8row_T33": 2447.5},
 }
 
 HBM_PEAK_GBS = 8000.0
@@ -545,8 +545,8 @@ def main():
             traffic = round(sum(per_launch[r.name] * len(r.ms) for r in head) / sum(len(r.ms) for r in head))
         line["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                            "kernel": "gemv_direct_kernel (T=1,4,16) / gemv_mfma_kernel (T=33), packed "
-                                      "row-FP8 17408x5120",
+                            "kernel": "gemv_mfma_kernel (one token block at T=1,4,16, three at T=33), "
+                                      "packed row-FP8 17408x5120",
                             "bytes_per_launch": {r.name: r.work for r in head},
                             "hbm_traffic_per_launch": per_launch,
                             "us_per_launch": {r.name: results[r.name]["us"] for r in head}}
