@@ -1283,13 +1283,18 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     int64_t smax = chunks / min_chunks;        // keep whole chunks, at least min_chunks per split
     if (smax > 32) smax = 32;
     if (smax < 1) smax = 1;
-    // One whole tile per CU plus leftover tiles spread beside them: the
-    // streaming kernel, whose whole tiles issue ahead of the spread work (see
-    // gemv_mfma_kernel), is faster than the direct kernel at every T here
+    // One whole tile per CU plus a few leftover tiles (at most CUs / 8)
+    // spread beside them, over a long K (at least 16 chunks): the streaming
+    // kernel, whose whole tiles issue ahead of the spread work (see
+    // gemv_mfma_kernel), is faster than the direct kernel at every T there
     // (17408 x 5120: T = 1 17.8 against 18.2 us, T = 4 17.3 / 18.0, T = 16
-    // 18.8 / 20.6); the resident kernel's K split is slower than both.
-    const bool spread_one_round = fmt_group(fmt) == 0 && allow_spread && mode != 3 &&
-                                  p.tiles > (int64_t)device_cu_count() && p.tiles < 2 * (int64_t)device_cu_count();
+    // 18.8 / 20.6; 16448 x 5120: T = 16 18.1 / 19.2); the resident kernel's K
+    // split is slower than both.  With more leftover tiles or a shorter K the
+    // direct kernel is as fast or faster (24576 x 5120: 24.5 against 26.7 us;
+    // 17408 x 2048: 10.9 against 11.6 us at T = 1).
+    const int64_t cus_n = (int64_t)device_cu_count();
+    const bool spread_one_round = fmt_group(fmt) == 0 && allow_spread && mode != 3 && p.tiles > cus_n &&
+                                  8 * (p.tiles - cus_n) <= cus_n && chunks >= 16;
     if (fmt_group(fmt) == 0 && Tc <= 16 && mode != 2 && !spread_one_round) {
         // direct variant (no group scales, one token block): about one
         // workgroup per CU (measured: more per CU only slow it down); with

@@ -297,8 +297,11 @@ def test_gemv_fp8row(n, k, t):
 
 
 # Tile counts just above / well below the CU count, and a K split over many
-# workgroups (partials exchanged through the workspace).
-@pytest.mark.parametrize("n,k,t", [(4160, 8192, 1), (16448, 1024, 16), (17408, 1280, 4), (1000, 1536, 16)])
+# workgroups (partials exchanged through the workspace).  16448 x 4096: one
+# leftover tile over a long K, where the row-FP8 plan takes the streaming
+# kernel with spread workgroups also for one token block.
+@pytest.mark.parametrize("n,k,t", [(4160, 8192, 1), (16448, 1024, 16), (17408, 1280, 4), (1000, 1536, 16),
+                                   (16448, 4096, 1), (16448, 4096, 16)])
 def test_gemv_fp8row_irregular_tile_counts(n, k, t):
     w = W.bf16_normal(W.rng(96, n * 7 + k), (n, k), std=0.02)
     wq, ws = M.encode_fp8row_bf16(w)
