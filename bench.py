@@ -46,11 +46,11 @@ sys.path.insert(0, ROOT)
 # Summaries: profiles/gemv_fp8row_17408x5120_hbm_traffic.md.  Valid only for
 # the GEMV source they were taken on (sha256 prefix of nq_gemv.hip).
 GEMV_TRAFFIC = {
-    "source_sha256_16": "fb8d7fa7379d693a",
+    "source_sha256_16": "c191b53c4c2f89ee",
     "fetch_factor": 262144.0 / 131083.5,
     "write_factor": 1.0,
-    "fetch_kib": {"gemv_fp8row_T1": 43829.3, "gemv_fp8row_T4": 44016.8, "gemv_fp8row_T16": 44775.2,
-                  "gemv_fp8row_T33": 45899.2},
+    "fetch_kib": {"gemv_fp8row_T1": 43829.3, "gemv_fp8row_T4": 44017.4, "gemv_fp8row_T16": 44775.8,
+                  "gemv_fp8row_T33": 45904.1},
     "write_kib": {"gemv_fp8row_T1": 79.5, "gemv_fp8row_T4": 301.5, "gemv_fp8row_T16": 1189.5,
                   "gemv_fp8row_T33": 2447.5},
 }

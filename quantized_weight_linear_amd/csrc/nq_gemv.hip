@@ -23,13 +23,19 @@
 //     barrier per chunk (streaming variant).  Rows past T read as zero.
 //   - Decode in registers: E4M3 -> BF16 by the hardware scaled convert
 //     (exact; MXFP8 passes its power-of-two group scale to the convert),
-//     int8 / int4 -> FP32 -> BF16 (exact for |q| <= 128), BF16 as stored.
+//     int8 / int4 -> FP32 -> BF16 (exact for |q| <= 128), BF16 as stored;
+//     Q4 with one token block in a biased form (1.5 + q / 16, exact, see
+//     chunk_mfma) corrected by the group's activation sum.
 //   - Grouped formats run one MFMA chain per scale group and fold the FP16
 //     group scale in FP32 (acc += sc * D); row-scaled FP8 applies its BF16
 //     row scale once at the end.
 //   - With a workspace the K range is split across workgroups; each split
 //     writes an FP32 partial and the last workgroup of a row tile (atomic
 //     counter) sums the partials in split order: deterministic results.
+//   - With a few more row tiles than CUs (formats without group scales),
+//     the leftover tiles' chunks are spread over extra workgroups that run
+//     beside the whole tiles (direct_spread), with the same deterministic
+//     exchange; the whole tiles' waves take the higher issue priority.
 // Fallback (any K): one wave per (row, 8 tokens), scalar decode, FP32 sums.
 #include "nq_device.h"
 #include "nq_launch.h"
