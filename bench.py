@@ -46,11 +46,11 @@ sys.path.insert(0, ROOT)
 # Summaries: profiles/gemv_fp8row_17408x5120_hbm_traffic.md.  Valid only for
 # the GEMV source they were taken on (sha256 prefix of nq_gemv.hip).
 GEMV_TRAFFIC = {
-    "source_sha256_16": "c191b53c4c2f89ee",
+    "source_sha256_16": "d966a28b15c30aab",
     "fetch_factor": 262144.0 / 131083.5,
     "write_factor": 1.0,
-    "fetch_kib": {"gemv_fp8row_T1": 43829.3, "gemv_fp8row_T4": 44017.4, "gemv_fp8row_T16": 44775.8,
-                  "gemv_fp8row_T33": 45904.1},
+    "fetch_kib": {"gemv_fp8row_T1": 43829.7, "gemv_fp8row_T4": 44017.5, "gemv_fp8row_T16": 44775.4,
+                  "gemv_fp8row_T33": 45913.6},
     "write_kib": {"gemv_fp8row_T1": 79.5, "gemv_fp8row_T4": 301.5, "gemv_fp8row_T16": 1189.5,
                   "gemv_fp8row_T33": 2447.5},
 }

@@ -1347,6 +1347,14 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     // 40.4 us); the formats without group scales do not (FP8 28 -> 31 us).
     const bool two_per_cu = fmt_group(fmt) != 0 && Tc > 16 && p.tiles < 4 * (int64_t)device_cu_count();
     s0 = p.tiles >= (int64_t)device_cu_count() ? (two_per_cu ? 2 : 1) : balanced_splits(p.tiles, chunks, smax);
+    // Between one and two tiles per CU, not a multiple of the CUs, three
+    // splits leave the busiest CU less work than two (4/3 of a tile against
+    // 3/2 with two workgroups per CU): 17408 x 5120 T = 17 / 33 / 48, Q4 28.0
+    // / 35.9 / 37.5 -> 26.6 / 33.8 / 35.7 us, Q8G32 34.7 / 40.5 / 42.3 -> 32.2
+    // / 37.9 / 40.8 us; four or five splits are slower again (the exchange).
+    if (two_per_cu && p.tiles < 2 * (int64_t)device_cu_count() && p.tiles % (int64_t)device_cu_count() != 0 &&
+        chunks >= 3 * (int64_t)min_chunks)
+        s0 = 3;
     const int64_t cps = (chunks + s0 - 1) / s0;
     p.chunks_per_split = (int)cps;
     p.splits = (int)((chunks + cps - 1) / cps);
