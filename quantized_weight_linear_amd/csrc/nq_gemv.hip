@@ -460,25 +460,32 @@ __device__ __forceinline__ void finish_tile(v4f (&fin)[NCB], const void* __restr
     }
     __syncthreads();
     if (!*s_last) return;
+    // The loads of a batch of splits, for all token blocks, are in flight
+    // together (one memory round trip per batch; tokens past T and splits past
+    // the last read as zero through out-of-range offsets, so no branch sits
+    // between them); each token block's sum runs in split order.
+    constexpr int SB = 8;
+    v4f sum[NCB];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-        const int t = cb * 16 + li;
-        if (t >= T) continue;
-        // all splits' loads of a batch are in flight together; the sum runs in split order
-        constexpr int SB = 8;
-        v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
-        for (int sb = 0; sb < splits; sb += SB) {
-            v4f part[SB];
+    for (int cb = 0; cb < NCB; ++cb) sum[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int sb = 0; sb < splits; sb += SB) {
+        v4f part[NCB][SB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int t = cb * 16 + li;
 #pragma unroll
             for (int j = 0; j < SB; ++j)
-                part[j] = sb + j < splits ? load_partial(pr, ((int64_t)(sb + j) * T + t) * npad + n0)
-                                          : v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < SB; ++j)
-                if (sb + j < splits) sum += part[j];
+                part[cb][j] = load_partial(pr, (t < T && sb + j < splits) ? ((int64_t)(sb + j) * T + t) * npad + n0
+                                                                         : PARTIAL_OOB);
         }
-        write_out(cb, sum);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int j = 0; j < SB; ++j)
+                if (sb + j < splits) sum[cb] += part[cb][j];
     }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) write_out(cb, sum[cb]);
     if (tid == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -1315,15 +1322,21 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     }
     // resident variant: from the split count that leaves the busiest CU the
     // fewest chunks, the smallest whose slice fits in LDS and whose FP32
-    // partials stay within 12% of the weight bytes; with more than one token
-    // block, only when the row tiles alone do not cover the CUs
+    // partials stay within 12% of the weight bytes; only for one token block
+    // with the row tiles covering the CUs (17408 x 5120 T = 1, 5 splits: Q4
+    // 19.4 against 21.3 us for the streaming kernel without a split, Q8G32
+    // 26.8 / 30.7).  With fewer tiles than CUs the streaming kernel with the
+    // balanced split is as fast or faster: the slice that fits in LDS forces
+    // more splits than the balance needs (5120 x 17408: row-FP8 T = 17 32.9
+    // -> 19.3 us, Q8G32 T = 8 36.8 -> 24.8, Q4 T = 1 21.7 -> 19.1; Q8G32
+    // 4096 x 4096 T = 8 11.6 -> 10.0).
     const double wbytes = (double)N * (double)K * fmt_bytes_per_weight(fmt);
     // With at least 4 row tiles per CU whole tiles already balance within a
     // quarter: the streaming kernel without a K split is faster there
     // (measured on 2376 tiles, Q8G32: 148-170 us at T = 1..16, against 152-222
     // us for the resident kernel, whose split adds the partial exchange).
     const bool many_tiles = p.tiles >= 4 * (int64_t)device_cu_count();
-    const bool try_resident = (Tc <= 16 || p.tiles < (int64_t)device_cu_count()) && !many_tiles && !spread_one_round;
+    const bool try_resident = Tc <= 16 && p.tiles >= (int64_t)device_cu_count() && !many_tiles && !spread_one_round;
     const int64_t sr = mode == 4 ? s0 : balanced_splits(p.tiles, chunks, smax);
     for (int64_t s = sr; try_resident && s <= 32 && s <= chunks; ++s) {
         const int64_t cps = (chunks + s - 1) / s;
