@@ -1336,7 +1336,16 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     // (measured on 2376 tiles, Q8G32: 148-170 us at T = 1..16, against 152-222
     // us for the resident kernel, whose split adds the partial exchange).
     const bool many_tiles = p.tiles >= 4 * (int64_t)device_cu_count();
-    const bool try_resident = Tc <= 16 && p.tiles >= (int64_t)device_cu_count() && !many_tiles && !spread_one_round;
+    // Grouped formats between one and two tiles per CU, not a multiple of the
+    // CUs: from 5 tokens on the streaming kernel with K split in three (see
+    // below) beats the resident kernel (17408 x 5120 Q8G32 T = 8 / 16: 30.2 /
+    // 32.6 -> 28.6 / 30.3 us; Q4 level); below that the resident one wins (T = 1:
+    // Q4 19.5 against 21.2 us, Q8G32 26.9 / 28.1).
+    const bool grouped_leftover = fmt_group(fmt) != 0 && p.tiles > (int64_t)device_cu_count() &&
+                                  p.tiles < 2 * (int64_t)device_cu_count() &&
+                                  p.tiles % (int64_t)device_cu_count() != 0 && chunks >= 3 * (int64_t)min_chunks;
+    const bool try_resident = Tc <= 16 && p.tiles >= (int64_t)device_cu_count() && !many_tiles && !spread_one_round &&
+                              !(grouped_leftover && Tc > 4);
     const int64_t sr = mode == 4 ? s0 : balanced_splits(p.tiles, chunks, smax);
     for (int64_t s = sr; try_resident && s <= 32 && s <= chunks; ++s) {
         const int64_t cps = (chunks + s - 1) / s;
@@ -1365,9 +1374,7 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     // 3/2 with two workgroups per CU): 17408 x 5120 T = 17 / 33 / 48, Q4 28.0
     // / 35.9 / 37.5 -> 26.6 / 33.8 / 35.7 us, Q8G32 34.7 / 40.5 / 42.3 -> 32.2
     // / 37.9 / 40.8 us; four or five splits are slower again (the exchange).
-    if (two_per_cu && p.tiles < 2 * (int64_t)device_cu_count() && p.tiles % (int64_t)device_cu_count() != 0 &&
-        chunks >= 3 * (int64_t)min_chunks)
-        s0 = 3;
+    if (grouped_leftover && Tc > 4) s0 = 3;
     const int64_t cps = (chunks + s0 - 1) / s0;
     p.chunks_per_split = (int)cps;
     p.splits = (int)((chunks + cps - 1) / cps);
