@@ -405,7 +405,7 @@ def test_gemv_fp8row_packed_full_size_sampled():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("n,k,ts", [(W.FFN, W.HIDDEN, [1, 4, 16, 33]), (W.HIDDEN, W.FFN, [1, 33])])
+@pytest.mark.parametrize("n,k,ts", [(W.FFN, W.HIDDEN, [1, 4, 16, 33]), (W.HIDDEN, W.FFN, [1, 17, 33])])
 def test_gemv_fp8row_full_size(n, k, ts):
     w = W.fp8row_weights_bf16(n, k)
     wd = dev(w)
@@ -458,7 +458,7 @@ def test_gemv_qgroup_config4_full_size(name, fmt, n, k):
     cd, sd = dev(d["codes"]), dev(d["scales"])
     rows = _sampled_rows(n, n + 1)
     gs = 64 if name == "q4g64" else 32
-    for t in (1, 8, 33):
+    for t in (1, 8, 17, 33):
         x = W.activations(t, k, workload=4, tensor=50)
         y = empty((t, n), np.float32)
         nq.nq_gemv_qgroup(fmt, cd, sd, dev(x), t, n, k, y, nq.alloc_gemv_workspace(fmt, t, n, k, DEV))
