@@ -178,6 +178,29 @@ def test_workspace_query_is_host_only(L):
     assert L.nq_gemv_workspace_bytes(-1, 4, 8, 100) == 0       # fallback path needs none
 
 
+# The GEMV plan, seen through the workspace it asks for (256 CUs: the count
+# the library assumes without a device, and MI355X's).  Layout: a 4-byte
+# counter per 64-row tile (padded to 256 bytes), then FP32 partials of 64
+# rows x T tokens per split and tile, or per slot and leftover tile.
+def test_gemv_plan_workspace(L):
+    c272 = 1280                                  # 272 tiles x 4 bytes, padded to 256
+    # row-FP8 17408 x 5120 (272 tiles, 20 chunks of 256): 16 leftover tiles,
+    # 320 units, at most 2 beside a whole tile, so 160 spread workgroups of 2
+    # units; a leftover tile meets at most 20 / 2 + 1 = 11 of them (slots).
+    assert L.nq_gemv_workspace_bytes(-1, 1, 17408, 5120) == c272 + 16 * 11 * 1 * 64 * 4
+    assert L.nq_gemv_workspace_bytes(-1, 33, 17408, 5120) == c272 + 16 * 11 * 33 * 64 * 4
+    # 16384 rows: one whole tile per CU, nothing to exchange
+    assert L.nq_gemv_workspace_bytes(-1, 1, 16384, 5120) == 0
+    # Q4 group-64, one token: resident kernel, K split in 5 (the split whose
+    # busiest CU has the fewest chunks: ceil(272 x 5 / 256) x 4 = 24)
+    assert L.nq_gemv_workspace_bytes(nq.NQ_W_Q4G64_F16S, 1, 17408, 5120) == c272 + 5 * 1 * 272 * 64 * 4
+    # Q8 group-32, 8 tokens, the same 16-tile leftover: streaming kernel, K in 3
+    assert L.nq_gemv_workspace_bytes(nq.NQ_W_Q8G32_F16S, 8, 17408, 5120) == c272 + 3 * 8 * 272 * 64 * 4
+    # row-FP8 5120 x 17408, 17 tokens (80 tiles, 68 chunks): streaming kernel
+    # with the balanced split, 3 (ceil(80 x 3 / 256) x 23 = 23 chunks at most)
+    assert L.nq_gemv_workspace_bytes(-1, 17, 5120, 17408) == 512 + 3 * 17 * 80 * 64 * 4
+
+
 def test_binding_raises(L):
     with pytest.raises(nq.NQError) as e:
         nq._check(L.nq_gemm_w8a8_g64(A, A, A, A, 4, 8, 96, 0, A, None, None), "nq_gemm_w8a8_g64")
