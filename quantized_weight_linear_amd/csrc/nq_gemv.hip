@@ -1344,8 +1344,16 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     const bool grouped_leftover = fmt_group(fmt) != 0 && p.tiles > (int64_t)device_cu_count() &&
                                   p.tiles < 2 * (int64_t)device_cu_count() &&
                                   p.tiles % (int64_t)device_cu_count() != 0 && chunks >= 3 * (int64_t)min_chunks;
+    // Grouped formats with the tiles a multiple of the CUs (1-3 per CU): from
+    // 4 tokens on the streaming kernel with K split in two beats the resident
+    // kernel too (16384 x 5120 T = 4 / 8 / 12 / 16: Q8G32 25.3 / 26.1 / 31.5 /
+    // 31.9 -> 22.5 / 21.9 / 22.6 / 23.2 us, Q4 21.0 / 18.9 / 19.1 / 16.4 ->
+    // 16.5 / 16.2 / 16.7 / 17.2; 32768 x 5120 Q8G32 T = 8 / 16: 47.1 / 52.0 ->
+    // 39.8 / 41.7).
+    const bool grouped_even = fmt_group(fmt) != 0 && p.tiles >= (int64_t)device_cu_count() &&
+                              p.tiles % (int64_t)device_cu_count() == 0 && !many_tiles;
     const bool try_resident = Tc <= 16 && p.tiles >= (int64_t)device_cu_count() && !many_tiles && !spread_one_round &&
-                              !(grouped_leftover && Tc > 4);
+                              !(grouped_leftover && Tc > 4) && !(grouped_even && Tc >= 4);
     const int64_t sr = mode == 4 ? s0 : balanced_splits(p.tiles, chunks, smax);
     for (int64_t s = sr; try_resident && s <= 32 && s <= chunks; ++s) {
         const int64_t cps = (chunks + s - 1) / s;
@@ -1367,7 +1375,8 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     // is heavier) gain from two workgroups per CU: with up to 4 tiles per CU,
     // K is split in two (17408x5120 T = 33: Q4 36.4 -> 35.4 us, Q8G32 42.6 ->
     // 40.4 us); the formats without group scales do not (FP8 28 -> 31 us).
-    const bool two_per_cu = fmt_group(fmt) != 0 && Tc > 16 && p.tiles < 4 * (int64_t)device_cu_count();
+    const bool two_per_cu = fmt_group(fmt) != 0 && (Tc > 16 || (grouped_even && Tc >= 4)) &&
+                            p.tiles < 4 * (int64_t)device_cu_count();
     s0 = p.tiles >= (int64_t)device_cu_count() ? (two_per_cu ? 2 : 1) : balanced_splits(p.tiles, chunks, smax);
     // Between one and two tiles per CU, not a multiple of the CUs, three
     // splits leave the busiest CU less work than two (4/3 of a tile against

@@ -699,9 +699,10 @@ def test_pack_is_the_documented_permutation(fmt, bpe, pb, n, k):
 
 # 16448 rows: one tile more than 256 CUs, so the row-FP8 kernels run the
 # leftover tile on spread workgroups beside the whole tiles; at 3072 columns
-# the grouped formats split K in three above 16 tokens.
+# the grouped formats split K in three from 5 tokens on.  16384 rows: one
+# tile per CU, where the grouped formats split K in two from 4 tokens on.
 @pytest.mark.parametrize("name,fmt", [("fp8row", -1)] + GROUP_FMTS)
-@pytest.mark.parametrize("n,k", [(1000, 1536), (200, 1280), (16448, 768), (16448, 3072)])
+@pytest.mark.parametrize("n,k", [(1000, 1536), (200, 1280), (16448, 768), (16448, 3072), (16384, 1024)])
 @pytest.mark.parametrize("t", [1, 16, 33])
 def test_gemv_packed_equals_row_major(name, fmt, n, k, t):
     if name == "fp8row":
