@@ -46,11 +46,11 @@ sys.path.insert(0, ROOT)
 # Summaries: profiles/gemv_fp8row_17408x5120_hbm_traffic.md.  Valid only for
 # the GEMV source they were taken on (sha256 prefix of nq_gemv.hip).
 GEMV_TRAFFIC = {
-    "source_sha256_16": "ea79325b4c2f16bc",
+    "source_sha256_16": "3a4533d275c4b80e",
     "fetch_factor": 262144.0 / 131083.5,
     "write_factor": 1.0,
-    "fetch_kib": {"gemv_fp8row_T1": 43816.7, "gemv_fp8row_T4": 44005.6, "gemv_fp8row_T16": 44770.8,
-                  "gemv_fp8row_T33": 45907.2},
+    "fetch_kib": {"gemv_fp8row_T1": 43815.7, "gemv_fp8row_T4": 44003.4, "gemv_fp8row_T16": 44771.9,
+                  "gemv_fp8row_T33": 45902.2},
     "write_kib": {"gemv_fp8row_T1": 79.5, "gemv_fp8row_T4": 301.5, "gemv_fp8row_T16": 1189.5,
                   "gemv_fp8row_T33": 2447.5},
 }

@@ -1378,12 +1378,20 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     const bool two_per_cu = fmt_group(fmt) != 0 && (Tc > 16 || (grouped_even && Tc >= 4)) &&
                             p.tiles < 4 * (int64_t)device_cu_count();
     s0 = p.tiles >= (int64_t)device_cu_count() ? (two_per_cu ? 2 : 1) : balanced_splits(p.tiles, chunks, smax);
-    // Between one and two tiles per CU, not a multiple of the CUs, three
-    // splits leave the busiest CU less work than two (4/3 of a tile against
-    // 3/2 with two workgroups per CU): 17408 x 5120 T = 17 / 33 / 48, Q4 28.0
-    // / 35.9 / 37.5 -> 26.6 / 33.8 / 35.7 us, Q8G32 34.7 / 40.5 / 42.3 -> 32.2
-    // / 37.9 / 40.8 us; four or five splits are slower again (the exchange).
-    if (grouped_leftover && Tc > 4) s0 = 3;
+    // Between one and two tiles per CU, not a multiple of the CUs: two or
+    // three splits, whichever leaves the busiest CU the smaller share of a
+    // tile (ceil(tiles s / CUs) / s).  272 tiles: 4/3 against 3/2, three
+    // splits (17408 x 5120 T = 17 / 33 / 48, Q4 28.0 / 35.9 / 37.5 -> 26.6 /
+    // 33.8 / 35.7 us, Q8G32 34.7 / 40.5 / 42.3 -> 32.2 / 37.9 / 40.8 us; 20480
+    // x 5120 Q8G32 T = 33 40.9 -> 39.1); 384 tiles: 5/3 against 3/2, two
+    // (24576 x 5120 T = 8 / 33: Q8G32 35.9 / 46.8 against 33.0 / 42.1 us, Q4
+    // 26.6 / 40.9 against 24.1 / 37.0).  Four or five splits are slower
+    // again (the exchange).
+    if (grouped_leftover && Tc > 4) {
+        const int64_t cus = (int64_t)device_cu_count();
+        const int64_t w2 = (2 * p.tiles + cus - 1) / cus, w3 = (3 * p.tiles + cus - 1) / cus;
+        s0 = 2 * w3 < 3 * w2 ? 3 : 2;
+    }
     const int64_t cps = (chunks + s0 - 1) / s0;
     p.chunks_per_split = (int)cps;
     p.splits = (int)((chunks + cps - 1) / cps);

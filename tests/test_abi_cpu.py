@@ -199,6 +199,9 @@ def test_gemv_plan_workspace(L):
     # row-FP8 5120 x 17408, 17 tokens (80 tiles, 68 chunks): streaming kernel
     # with the balanced split, 3 (ceil(80 x 3 / 256) x 23 = 23 chunks at most)
     assert L.nq_gemv_workspace_bytes(-1, 17, 5120, 17408) == 512 + 3 * 17 * 80 * 64 * 4
+    # 24576 rows (384 tiles): two splits leave the busiest CU 3/2 of a tile,
+    # three 5/3, so K is split in two
+    assert L.nq_gemv_workspace_bytes(nq.NQ_W_Q8G32_F16S, 8, 24576, 5120) == 1536 + 2 * 8 * 384 * 64 * 4
     # Q8 group-32 at 16384 rows (one tile per CU), 8 tokens: streaming kernel,
     # K in two (two workgroups per CU)
     assert L.nq_gemv_workspace_bytes(nq.NQ_W_Q8G32_F16S, 8, 16384, 5120) == 1024 + 2 * 8 * 256 * 64 * 4
