@@ -292,10 +292,13 @@ __global__ __launch_bounds__(256) void encode_rows_kernel(RowSource<SRC> src, in
     if (tid == 0) out_scale[orow] = (uint16_t)s_bits;
 
     uint8_t* orow_ptr = out_codes + orow * K;
-    // A finite positive scale bounds every quotient by 448 / (1 - 2^-9) < 464,
-    // the range where the hardware convert is exact; other rows (all zero, NaN,
-    // infinite) take the per-element path.
-    const bool fast = s > 0.0f && s < __uint_as_float(0x7F800000u);
+    // A finite scale in BF16's normal range (s >= 2^-126) carries m / 448 to
+    // within 2^-9 relative, so every quotient stays below 448 (1 + 2^-8) < 464,
+    // the range where the hardware convert equals the saturating encoder.  A
+    // subnormal scale has fewer significant bits (m near 1e-37 gives quotients
+    // up to ~670, which must saturate to +-448), so such rows, like the zero,
+    // NaN and infinite ones, take the per-element path.
+    const bool fast = s >= __uint_as_float(0x00800000u) && s < __uint_as_float(0x7F800000u);
     const double r = 1.0 / (double)s;
     if (vec && fast) {
         auto encode16 = [&](const float* v, int64_t k) {
@@ -450,7 +453,10 @@ __global__ __launch_bounds__(256) void quantize_fp8_row_kernel(const uint16_t* _
     const float s = nan ? __uint_as_float(0x7FC00000u) : m / 448.0f;
     if (tid == 0) scale[row] = s;
     uint8_t* cr = codes + row * K;
-    // finite positive scale: every quotient is at most 448 (1 + 2^-23) < 464
+    // Every quotient is below 450 < 464 (the hardware convert's exact range):
+    // s = fp32(m / 448) is within 2^-24 of m / 448 when normal, and an FP32
+    // subnormal s still holds at least 146 quanta of 2^-149 (m is at least
+    // 2^-133, the smallest BF16 magnitude), within 1/292 of it.
     const bool fast = s > 0.0f && s < __uint_as_float(0x7F800000u);
     const double r = 1.0 / (double)s;
     if (vec && fast) {

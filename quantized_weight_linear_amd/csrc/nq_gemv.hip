@@ -1273,26 +1273,7 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     p.chunks_per_split = p.mfma ? (int)(K / p.kc) : 0;
     if (!p.mfma) return p;
     const int64_t chunks = K / p.kc;
-    static const int per_cu = [] {
-        const char* e = getenv("NQ_GEMV_WGS_PER_CU");
-        const int v = e ? atoi(e) : 0;
-        return v > 0 ? v : 2;
-    }();
-    const int64_t target = per_cu * (int64_t)device_cu_count();
-    static const int min_chunks = [] {
-        const char* e = getenv("NQ_GEMV_MIN_CHUNKS");
-        const int v = e ? atoi(e) : 0;
-        return v > 0 ? v : 4;
-    }();
-    int64_t s0 = (target + p.tiles - 1) / p.tiles;
-    if (s0 > chunks / min_chunks) s0 = chunks / min_chunks;   // keep whole chunks per split
-    if (s0 > 32) s0 = 32;
-    if (s0 < 1) s0 = 1;
-    static const int mode = [] {      // 0 auto, 1 direct, 2 resident / streaming only, 3 no spread,
-                                      // 4 resident split by workgroups per CU
-        const char* e = getenv("NQ_GEMV_MODE");
-        return e ? atoi(e) : 0;
-    }();
+    constexpr int64_t min_chunks = 4;          // chunks per K split at least
     int64_t smax = chunks / min_chunks;        // keep whole chunks, at least min_chunks per split
     if (smax > 32) smax = 32;
     if (smax < 1) smax = 1;
@@ -1306,9 +1287,9 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     // direct kernel is as fast or faster (24576 x 5120: 24.5 against 26.7 us;
     // 17408 x 2048: 10.9 against 11.6 us at T = 1).
     const int64_t cus_n = (int64_t)device_cu_count();
-    const bool spread_one_round = fmt_group(fmt) == 0 && allow_spread && mode != 3 && p.tiles > cus_n &&
+    const bool spread_one_round = fmt_group(fmt) == 0 && allow_spread && p.tiles > cus_n &&
                                   8 * (p.tiles - cus_n) <= cus_n && chunks >= 16;
-    if (fmt_group(fmt) == 0 && Tc <= 16 && mode != 2 && !spread_one_round) {
+    if (fmt_group(fmt) == 0 && Tc <= 16 && !spread_one_round) {
         // direct variant (no group scales, one token block): about one
         // workgroup per CU (measured: more per CU only slow it down); with
         // fewer tiles than CUs, K split so that the busiest CU has the fewest chunks
@@ -1317,7 +1298,7 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
         p.direct = true;
         p.chunks_per_split = (int)cps;
         p.splits = (int)((chunks + cps - 1) / cps);
-        if (mode != 3 && allow_spread) plan_spread(p, chunks);
+        if (allow_spread) plan_spread(p, chunks);
         return p;
     }
     // resident variant: from the split count that leaves the busiest CU the
@@ -1354,7 +1335,7 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
                               p.tiles % (int64_t)device_cu_count() == 0 && !many_tiles;
     const bool try_resident = Tc <= 16 && p.tiles >= (int64_t)device_cu_count() && !many_tiles && !spread_one_round &&
                               !(grouped_leftover && Tc > 4) && !(grouped_even && Tc >= 4);
-    const int64_t sr = mode == 4 ? s0 : balanced_splits(p.tiles, chunks, smax);
+    const int64_t sr = balanced_splits(p.tiles, chunks, smax);
     for (int64_t s = sr; try_resident && s <= 32 && s <= chunks; ++s) {
         const int64_t cps = (chunks + s - 1) / s;
         const int64_t se = (chunks + cps - 1) / cps;
@@ -1377,7 +1358,7 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     // 40.4 us); the formats without group scales do not (FP8 28 -> 31 us).
     const bool two_per_cu = fmt_group(fmt) != 0 && (Tc > 16 || (grouped_even && Tc >= 4)) &&
                             p.tiles < 4 * (int64_t)device_cu_count();
-    s0 = p.tiles >= (int64_t)device_cu_count() ? (two_per_cu ? 2 : 1) : balanced_splits(p.tiles, chunks, smax);
+    int64_t s0 = p.tiles >= (int64_t)device_cu_count() ? (two_per_cu ? 2 : 1) : balanced_splits(p.tiles, chunks, smax);
     // Between one and two tiles per CU, not a multiple of the CUs: two or
     // three splits, whichever leaves the busiest CU the smaller share of a
     // tile (ceil(tiles s / CUs) / s).  272 tiles: 4/3 against 3/2, three
@@ -1395,7 +1376,7 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     const int64_t cps = (chunks + s0 - 1) / s0;
     p.chunks_per_split = (int)cps;
     p.splits = (int)((chunks + cps - 1) / cps);
-    if (fmt_group(fmt) == 0 && mode != 3 && allow_spread) plan_spread(p, chunks);
+    if (fmt_group(fmt) == 0 && allow_spread) plan_spread(p, chunks);
     return p;
 }
 

@@ -435,6 +435,83 @@ def pin_encode_fp8row_bf16():
                 (wv[r, j] == 0 and int(q[r, j]) in (0, 0x80))
 
 
+def _brute_encode_row(vals, neg_zero):
+    """fp8_row_maxabs of one row by exact rationals, for any row maximum:
+    vals are the exact FP32 source values (Fractions), neg_zero[j] marks a -0
+    element.  s = bf16(f32(m / 448)); a zero element keeps its signed zero (0 / s
+    is a zero, and 0 / 0 is not evaluated); with s = 0 a nonzero element's
+    quotient is infinite and saturates to +-448; otherwise the E4M3 RNE
+    (saturating) of the FP32 quotient.  Returns (codes, s, largest quotient)."""
+    m = max(abs(a) for a in vals)
+    s = Fraction(float(torch.tensor(float(brute_f32_div(m, 448)), dtype=torch.float32).to(torch.bfloat16).item()))
+    q, zmax = [], Fraction(0)
+    for a, nz in zip(vals, neg_zero):
+        if a == 0:
+            q.append(0x80 if nz else 0x00)
+        elif s == 0:
+            q.append(0xFE if a < 0 else 0x7E)
+        else:
+            z = brute_f32_div(a, s)
+            zmax = max(zmax, abs(z))
+            q.append(brute_e4m3(z))
+    return q, s, zmax
+
+
+def tiny_row_bf16(seed):
+    """BF16 rows whose maxima put m / 448 in or below BF16's subnormal range
+    (m from ~1e-38 to ~5.3e-36, where the row scale keeps 1..7 significant
+    bits), plus the normal boundary s = 2^-126; the other elements uniform in
+    [-m, m] (many of them BF16 subnormals), one -0 and one +0 per row."""
+    rng = np.random.default_rng(seed)
+    maxima = [1e-37, -3.3e-37, 2.0e-36, 5.25e-36, 448 * 2.0 ** -126, 4.0e-38, 2.9e-38, 1.0e-38, 6.1e-38, 7.7e-37]
+    rows = []
+    for m in maxima:
+        r = rng.uniform(-1, 1, 40) * abs(m)
+        r[rng.integers(0, 40)] = m
+        r[3], r[7] = -0.0, 0.0
+        rows.append(r)
+    return _bf16_bits_from_f32(np.array(rows, np.float64).astype(np.float32))
+
+
+def pin_encode_tiny_rows():
+    """[FP8 card, "Conversion and verification"]: the per-row encoding for
+    rows whose scale m / 448 is a BF16 subnormal (or rounds to zero).  The
+    scale then carries few significant bits and quotients reach ~670 (beyond
+    E4M3's 448), which saturate to +-448 (the saturating encode)."""
+    w = tiny_row_bf16(31)
+    q, s = M.encode_fp8row_bf16(w)
+    wv = F.bf16_decode(w)
+    zmax = Fraction(0)
+    for r in range(w.shape[0]):
+        vals = [Fraction(float(v)) for v in wv[r]]
+        qb, sb, zm = _brute_encode_row(vals, [bool(np.signbit(v)) and v == 0 for v in wv[r]])
+        assert Fraction(float(F.bf16_decode(s[r]))) == sb, r
+        assert list(q[r]) == qb, r
+        zmax = max(zmax, zm)
+    assert zmax > 464                      # the saturating case is exercised
+    assert np.any(s == 0) and np.any((s > 0) & (s < 0x80))  # zero and subnormal scales
+    # block-scaled source with a weight_scale_inv near 2^-131 (FP32 subnormal,
+    # not BF16-rounded): decoded values and the row scale are subnormal
+    rng = np.random.default_rng(32)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    codes = rng.choice(finite, size=(3, 200))
+    codes[:, 17] = 0x7E
+    wsi = np.array([[1.37 * 2.0 ** -131, 0.9 * 2.0 ** -131]], np.float32)
+    qo, so = M.reencode_block128_to_row(codes, wsi)
+    zmax = Fraction(0)
+    for r in range(3):
+        vals, nz = [], []
+        for j in range(200):
+            fv = F.e4m3_fraction(int(codes[r, j]))
+            vals.append(Fraction(float(frac_to_f32(fv * Fraction(float(wsi[0, j // 128]))))))
+            nz.append(vals[-1] == 0 and bool(int(codes[r, j]) & 0x80))
+        qb, sb, zm = _brute_encode_row(vals, nz)
+        assert Fraction(float(F.bf16_decode(so[r]))) == sb, r
+        assert list(qo[r]) == qb, r
+        zmax = max(zmax, zm)
+    assert zmax > 464 and np.all(so < 0x80)          # subnormal scales, saturating quotients
+
+
 def pin_quantize_int8():
     # closed-form ties: a group whose amax is 127 has scale exactly 1
     cases = [(Fraction(a), int(b)) for kind, a, b in _read_golden("rounding_cases.txt") if kind == "int8_s1"]
@@ -678,7 +755,7 @@ def pin_linear_q4g64():
 
 
 ORACLE_METHOD_PINS = [pin_mxfp8_decode, pin_mlx_affine_int8, pin_reencode_bruteforce, pin_reencode_invariants,
-                      pin_encode_fp8row_bf16, pin_quantize_int8, pin_gemv_fp8row, pin_gemv_qgroup,
+                      pin_encode_fp8row_bf16, pin_encode_tiny_rows, pin_quantize_int8, pin_gemv_fp8row, pin_gemv_qgroup,
                       pin_w8a8, pin_fp8_act_and_gemm, pin_route, pin_linear_q4g64]
 
 ALL_PINS = ORACLE_FORMAT_PINS + ORACLE_METHOD_PINS

@@ -166,6 +166,51 @@ def test_encode_fp8row_bf16_small(n, k):
     assert np.array_equal(host(osc, np.uint16), so) and np.array_equal(host(oc, np.uint8), qo)
 
 
+def _tiny_rows_bf16(k, seed):
+    """BF16 rows whose maxima put m / 448 in or below BF16's subnormal range
+    (the row scale keeps 0..7 significant bits, quotients reach ~670 and
+    saturate), the normal boundary 448 * 2^-126, and a normal row; elements
+    uniform in [-m, m], with signed zeros."""
+    g = W.rng(120, seed)
+    maxima = [1e-37, -3.3e-37, 2.0e-36, 5.25e-36, 448 * 2.0 ** -126, 4.0e-38, 2.9e-38, 1.0e-38, 6.1e-38,
+              7.7e-37, 1.3e-36, 0.25]
+    rows = []
+    for m in maxima:
+        r = g.uniform(-1, 1, k) * abs(m)
+        r[g.integers(0, k)] = m
+        r[3], r[7] = -0.0, 0.0
+        rows.append(r)
+    return W.to_bf16_bits(np.array(rows, np.float64).astype(np.float32))
+
+
+@pytest.mark.parametrize("k", [256, 5120, 40])
+def test_encode_fp8row_bf16_tiny_rows(k):
+    w = _tiny_rows_bf16(k, k)
+    n = w.shape[0]
+    oc, osc = empty((n, k), np.uint8), empty((n,), np.uint16)
+    nq.nq_encode_fp8row_bf16(dev(w), n, k, oc, osc)
+    qo, so = M.encode_fp8row_bf16(w)
+    assert np.any(so == 0) and np.any((so > 0) & (so < 0x80))     # zero and subnormal scales occur
+    assert np.array_equal(host(osc, np.uint16), so)
+    assert np.array_equal(host(oc, np.uint8), qo)
+
+
+@pytest.mark.parametrize("n,k", [(300, 520), (130, 256)])
+def test_reencode_tiny_block_scales(n, k):
+    """weight_scale_inv near 2^-131 (FP32 subnormal, not BF16-rounded) in some
+    blocks: decoded values and row scales subnormal, quotients saturating."""
+    codes, wsi = _block_inputs(n, k, 77 + n, bf16_scales=False)
+    codes[:, 17] = 0x7E
+    wsi[0, :] = np.array([1.37, 0.9, 1.11, 1.6, 1.2][:wsi.shape[1]], np.float64) * 2.0 ** -131
+    if wsi.shape[0] > 1:
+        wsi[1, 0] = 3.1 * 2.0 ** -140
+    q, s = _gpu_reencode(codes, wsi, 0, n)
+    qo, so = M.reencode_block128_to_row(codes, wsi)
+    assert np.all(so[:128] < 0x80)
+    assert np.array_equal(s, so)
+    assert np.array_equal(q, qo)
+
+
 # ---------------------------------------------------------------------------
 # a5: int8 activation quantization; a7 input: E4M3 per-token quantization
 # ---------------------------------------------------------------------------
@@ -246,9 +291,12 @@ def test_quantize_int8_near_half_quotients():
     assert np.array_equal(host(q, np.int8), qo)
 
 
-@pytest.mark.parametrize("m,k", [(7, 256), (70, 400), (3, 8)])
+@pytest.mark.parametrize("m,k", [(7, 256), (70, 400), (3, 8), (12, 512)])
 def test_quantize_fp8_row(m, k):
-    x = _special_activations(max(m, 5), k)[:m] if m >= 5 else W.bf16_normal(W.rng(95, k), (m, k))
+    if m == 12:
+        x = _tiny_rows_bf16(k, 5)           # FP32-subnormal token scales (quotients stay below 450)
+    else:
+        x = _special_activations(max(m, 5), k)[:m] if m >= 5 else W.bf16_normal(W.rng(95, k), (m, k))
     c, s = empty((m, k), np.uint8), empty((m,), np.float32)
     nq.nq_quantize_act_fp8_row(dev(x), m, k, c, s)
     co, so = M.quantize_act_fp8_row(x)
@@ -376,134 +424,243 @@ def _sampled_rows(n, seed, count=96):
     return np.unique(np.concatenate([[0, 63, 64, n - 1], W.rng(101, seed).integers(0, n, count)]))
 
 
-# The timed launch: packed weights of 17408 x 5120 (272 row tiles: whole tiles
-# on every CU plus 16 spread over others), T = 1, 4, 16, 33, BF16 output.
+def _leftover_rows(n, seed, count=96):
+    """Every row of the row tiles beyond the last whole multiple of 256 tiles
+    (those the GEMV spreads over extra workgroups or splits), plus a sample."""
+    tiles = -(-n // 64)
+    first = (tiles - tiles % 256) * 64 if tiles > 256 and tiles % 256 else n
+    return np.unique(np.concatenate([np.arange(first, n), _sampled_rows(n, seed, count)]))
+
+
+def _banded(fn, n, band=512):
+    """Run a row-wise oracle step over row bands in threads (numpy releases
+    the GIL in its elementwise kernels); the bands are independent rows."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(8) as ex:
+        return list(ex.map(lambda r0: fn(r0, min(n, r0 + band)), range(0, n, band)))
+
+
+def _oracle_fp8row_encode(w):
+    parts = _banded(lambda a, b: M.encode_fp8row_bf16(w[a:b]), w.shape[0])
+    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+
+
+def _gpu_fp8row_weights(w):
+    n, k = w.shape
+    wd = dev(w)
+    q_d, s_d = empty((n, k), np.uint8), empty((n,), np.uint16)
+    nq.nq_encode_fp8row_bf16(wd, n, k, q_d, s_d)
+    del wd
+    return q_d, s_d
+
+
+def _pack_dev(fmt, codes_d, n, k):
+    pk = empty((nq.nq_packed_weight_bytes(fmt, n, k),), np.uint8)
+    nq.nq_pack_weights(fmt, codes_d, n, k, pk)
+    return pk
+
+
+def _counters_zero(wsp, n):
+    return wsp is None or int(wsp.view(torch.int32)[:(n + 63) // 64].abs().sum().item()) == 0
+
+
+def _gemv_both_layouts(fmt, codes_d, pk, scales_d, x, n, k):
+    """The call as bench.py times it (packed, shared workspace, BF16 out) plus
+    FP32 out, and the row-major call; returns (fp32 packed, bf16 packed, fp32
+    row-major) after checking the workspace counters are reset."""
+    t = x.shape[0]
+    xd = dev(x)
+    wsp = nq.alloc_gemv_workspace(fmt, t, n, k, DEV)
+    y32, y16, yr = empty((t, n), np.float32), empty((t, n), np.uint16), empty((t, n), np.float32)
+    if fmt == -1:
+        nq.nq_gemv_fp8row_packed(pk, scales_d, xd, t, n, k, y16, wsp)
+        nq.nq_gemv_fp8row_packed(pk, scales_d, xd, t, n, k, y32, wsp)
+        nq.nq_gemv_fp8row(codes_d, scales_d, xd, t, n, k, yr, wsp)
+    else:
+        nq.nq_gemv_qgroup_packed(fmt, pk, scales_d, xd, t, n, k, y16, wsp)
+        nq.nq_gemv_qgroup_packed(fmt, pk, scales_d, xd, t, n, k, y32, wsp)
+        nq.nq_gemv_qgroup(fmt, codes_d, scales_d, xd, t, n, k, yr, wsp)
+    g32, g16, gr = host(y32, np.float32), host(y16, np.uint16), host(yr, np.float32)
+    assert _counters_zero(wsp, n)
+    assert np.array_equal(g16, bf16_of_f32_bits(g32))          # BF16 = RNE of the same FP32 result
+    assert np.array_equal(g32.view(np.uint32), gr.view(np.uint32))   # packed = row-major, bit for bit
+    return g32, g16, gr
+
+
+# The headline launches: packed row-FP8 17408 x 5120 (272 row tiles: whole
+# tiles on every CU plus 16 spread over extra workgroups), T = 1, 4, 16, 33 as
+# bench.py runs them (shared workspace, BF16 out), every row against the
+# oracle (the oracle encodes the whole matrix in row bands).
 @pytest.mark.slow
-def test_gemv_fp8row_packed_full_size_sampled():
+def test_gemv_fp8row_headline_all_rows():
     n, k = W.FFN, W.HIDDEN
     w = W.fp8row_weights_bf16(n, k)
-    rows = _sampled_rows(n, n + 1)
-    wq_o, ws_o = M.encode_fp8row_bf16(w[rows])
-    wd = dev(w)
-    wq_d, ws_d = empty((n, k), np.uint8), empty((n,), np.uint16)
-    nq.nq_encode_fp8row_bf16(wd, n, k, wq_d, ws_d)
-    del wd
-    pk = empty((nq.nq_packed_weight_bytes(-1, n, k),), np.uint8)
-    nq.nq_pack_weights(-1, wq_d, n, k, pk)
-    del wq_d
+    q_d, s_d = _gpu_fp8row_weights(w)
+    qo, so = _oracle_fp8row_encode(w)
+    assert np.array_equal(host(s_d, np.uint16), so) and np.array_equal(host(q_d, np.uint8), qo)
+    pk = _pack_dev(-1, q_d, n, k)
+    x33 = W.activations(33, k)
+    ref33 = M.gemv_fp8row(qo, so, x33)
     for t in (1, 4, 16, 33):
-        x = W.activations(t, k)
-        y32, y16 = empty((t, n), np.float32), empty((t, n), np.uint16)
-        wsp = nq.alloc_gemv_workspace(-1, t, n, k, DEV)
-        nq.nq_gemv_fp8row_packed(pk, ws_d, dev(x), t, n, k, y32, wsp)
-        nq.nq_gemv_fp8row_packed(pk, ws_d, dev(x), t, n, k, y16, wsp)
-        g32, g16 = host(y32, np.float32), host(y16, np.uint16)
-        assert np.array_equal(g16, bf16_of_f32_bits(g32)), t
-        ref = M.gemv_fp8row(wq_o, ws_o, x)
-        assert rel_fro(g32[:, rows], ref) <= FP32_TOL, t
-        assert int(wsp.view(torch.int32)[:(n + 63) // 64].abs().sum().item()) == 0, t     # counters reset
+        g32, g16, _ = _gemv_both_layouts(-1, q_d, pk, s_d, x33[:t].copy(), n, k)
+        assert rel_fro(g32, ref33[:t]) <= FP32_TOL, t
+        assert rel_fro(F.bf16_decode(g16), ref33[:t]) <= BF16_TOL, t
+        # the leftover tiles' rows on their own (the exchanged partial sums)
+        assert rel_fro(g32[:, 16384:], ref33[:t, 16384:]) <= FP32_TOL, t
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("n,k,ts", [(W.FFN, W.HIDDEN, [1, 4, 16, 33]), (W.HIDDEN, W.FFN, [1, 17, 33])])
+@pytest.mark.parametrize("n,k,ts", [(W.HIDDEN, W.FFN, [1, 17, 33])])
 def test_gemv_fp8row_full_size(n, k, ts):
     w = W.fp8row_weights_bf16(n, k)
-    wd = dev(w)
-    wq_d, ws_d = empty((n, k), np.uint8), empty((n,), np.uint16)
-    nq.nq_encode_fp8row_bf16(wd, n, k, wq_d, ws_d)
-    del wd
+    q_d, s_d = _gpu_fp8row_weights(w)
     rows = _sampled_rows(n, n)
     wq_o, ws_o = M.encode_fp8row_bf16(w[rows])
-    assert np.array_equal(host(wq_d, np.uint8)[rows], wq_o) and np.array_equal(host(ws_d, np.uint16)[rows], ws_o)
+    assert np.array_equal(host(q_d, np.uint8)[rows], wq_o) and np.array_equal(host(s_d, np.uint16)[rows], ws_o)
     for t in ts:
         x = W.activations(t, k)
         y = empty((t, n), np.float32)
         wsp = nq.alloc_gemv_workspace(-1, t, n, k, DEV)
-        nq.nq_gemv_fp8row(wq_d, ws_d, dev(x), t, n, k, y, wsp)
+        nq.nq_gemv_fp8row(q_d, s_d, dev(x), t, n, k, y, wsp)
         got = host(y, np.float32)[:, rows]
         assert rel_fro(got, M.gemv_fp8row(wq_o, ws_o, x)) <= FP32_TOL, t
 
 
+# Config 3 as bench.py times it: the re-encoded 5120 x 17408 down projection,
+# packed, T = 1 and 33, every row; the 96 x 5120 BF16 gate, packed.
 @pytest.mark.slow
 def test_gemv_config3_reencode_then_gemv_and_gate():
     d = W.block128_codes()
     n, k = d["codes"].shape
     q_d, s_d = empty((n, k), np.uint8), empty((n,), np.uint16)
     nq.nq_reencode_block128_to_row(dev(d["codes"]), dev(d["wsi"]), n, k, 0, n, q_d, s_d)
-    rows = _sampled_rows(n, 3)
+    parts = _banded(lambda a, b: M.reencode_block128_to_row(d["codes"][a:b], d["wsi"][a // 128:(b + 127) // 128],
+                                                            0, b - a), n)
+    qo, so = np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+    assert np.array_equal(host(s_d, np.uint16), so) and np.array_equal(host(q_d, np.uint8), qo)
+    pk = _pack_dev(-1, q_d, n, k)
     for t in (1, 33):
         x = W.activations(t, k, workload=3, tensor=3)
-        y = empty((t, n), np.float32)
-        nq.nq_gemv_fp8row(q_d, s_d, dev(x), t, n, k, y, nq.alloc_gemv_workspace(-1, t, n, k, DEV))
-        got = host(y, np.float32)[:, rows]
-        ref = []
-        for r in rows:
-            qo, so = M.reencode_block128_to_row(d["codes"][r:r + 1],
-                                                d["wsi"][r // 128][None, :].copy())
-            ref.append(M.gemv_fp8row(qo, so, x)[:, 0])
-        assert rel_fro(got, np.stack(ref, axis=1)) <= FP32_TOL, t
+        g32, g16, _ = _gemv_both_layouts(-1, q_d, pk, s_d, x, n, k)
+        ref = M.gemv_fp8row(qo, so, x)
+        assert rel_fro(g32, ref) <= FP32_TOL, t
+        assert rel_fro(F.bf16_decode(g16), ref) <= BF16_TOL, t
     gate = W.gate_bf16()
+    gn, gk = gate.shape
+    gd = dev(gate)
+    gpk = _pack_dev(nq.NQ_W_BF16, gd, gn, gk)
     for t in (1, 33):
-        x = W.activations(t, W.HIDDEN, workload=3, tensor=4)
-        y32 = _run_gemv_q(nq.NQ_W_BF16, gate, None, x, gate.shape[0], True, "f32")
-        y16 = _run_gemv_q(nq.NQ_W_BF16, gate, None, x, gate.shape[0], True, "bf16")
-        _check_float_out(y32, y16, M.gemv_qgroup("bf16", gate, None, x))
+        x = W.activations(t, gk, workload=3, tensor=4)
+        g32, g16, _ = _gemv_both_layouts(nq.NQ_W_BF16, gd, gpk, None, x, gn, gk)
+        _check_float_out(g32, g16, M.gemv_qgroup("bf16", gate, None, x))
 
 
+# Config 4 as bench.py times it: Q4 group-64 and Q8 group-32, packed, both
+# shapes, T = 1, 8, 33 (and 17, two token blocks), every row.
 @pytest.mark.slow
 @pytest.mark.parametrize("name,fmt", GROUP_FMTS[:2])
 @pytest.mark.parametrize("n,k", [(W.FFN, W.HIDDEN), (W.HIDDEN, W.FFN)])
 def test_gemv_qgroup_config4_full_size(name, fmt, n, k):
     d = W.grouped(name, n, k)
     cd, sd = dev(d["codes"]), dev(d["scales"])
-    rows = _sampled_rows(n, n + 1)
-    gs = 64 if name == "q4g64" else 32
+    pk = _pack_dev(fmt, cd, n, k)
+    x33 = W.activations(33, k, workload=4, tensor=50)
+    ref33 = M.gemv_qgroup(name, d["codes"], d["scales"], x33)
     for t in (1, 8, 17, 33):
-        x = W.activations(t, k, workload=4, tensor=50)
-        y = empty((t, n), np.float32)
-        nq.nq_gemv_qgroup(fmt, cd, sd, dev(x), t, n, k, y, nq.alloc_gemv_workspace(fmt, t, n, k, DEV))
-        got = host(y, np.float32)[:, rows]
-        ref = M.gemv_qgroup(name, d["codes"][rows], d["scales"][rows], x)
-        assert rel_fro(got, ref) <= FP32_TOL, (name, t)
-        assert gs
+        g32, g16, _ = _gemv_both_layouts(fmt, cd, pk, sd, x33[:t].copy(), n, k)
+        assert rel_fro(g32, ref33[:t]) <= FP32_TOL, (name, t)
+        assert rel_fro(F.bf16_decode(g16), ref33[:t]) <= BF16_TOL, (name, t)
 
 
+# 384 row tiles (1.5 per CU) with 12 chunks: from 5 tokens on the grouped
+# formats split K in two (the busiest CU then holds 3 halves against 5 thirds).
+@pytest.mark.slow
+@pytest.mark.parametrize("name,fmt", GROUP_FMTS[:2])
+def test_gemv_qgroup_two_split_leftover(name, fmt):
+    n, k = 24576, 3072
+    assert nq.nq_gemv_workspace_bytes(fmt, 8, n, k) == 1536 + 2 * 8 * 384 * 64 * 4
+    d = W.grouped(name, n, k, seed=3)
+    cd, sd = dev(d["codes"]), dev(d["scales"])
+    pk = _pack_dev(fmt, cd, n, k)
+    x33 = W.activations(33, k, workload=4, tensor=51)
+    ref33 = M.gemv_qgroup(name, d["codes"], d["scales"], x33)
+    for t in (8, 33):
+        g32, _, _ = _gemv_both_layouts(fmt, cd, pk, sd, x33[:t].copy(), n, k)
+        assert rel_fro(g32, ref33[:t]) <= FP32_TOL, (name, t)
+
+
+# The output head as bench.py times it (packed row-FP8, 2376 row tiles: 2304
+# whole, 72 spread), T = 1, 16, 33, 64; every row of the 72 spread tiles and a
+# sample; plus the row-major sweep.
 @pytest.mark.slow
 def test_gemv_head_full_size_sweep():
     n, k = W.HEAD_ROWS, W.HIDDEN
     w = W.head_weights_bf16()
-    wd = dev(w)
-    q_d, s_d = empty((n, k), np.uint8), empty((n,), np.uint16)
-    nq.nq_encode_fp8row_bf16(wd, n, k, q_d, s_d)
-    del wd
-    rows = _sampled_rows(n, 5)
-    qo, so = M.encode_fp8row_bf16(w[rows])
+    q_d, s_d = _gpu_fp8row_weights(w)
+    rows = _leftover_rows(n, 5)
+    qo, so = _oracle_fp8row_encode(w[rows])
     assert np.array_equal(host(q_d, np.uint8)[rows], qo) and np.array_equal(host(s_d, np.uint16)[rows], so)
-    for t in (1, 2, 7, 16, 33, 34, 48, 64):
-        x = W.activations(t, k, workload=5, tensor=4)
+    pk = _pack_dev(-1, q_d, n, k)
+    x64 = W.activations(64, k, workload=5, tensor=4)
+    ref64 = M.gemv_fp8row(qo, so, x64)
+    for t in (1, 16, 33, 64):
+        g32, g16, _ = _gemv_both_layouts(-1, q_d, pk, s_d, x64[:t].copy(), n, k)
+        assert rel_fro(g32[:, rows], ref64[:t]) <= FP32_TOL, t
+        assert rel_fro(F.bf16_decode(g16[:, rows]), ref64[:t]) <= BF16_TOL, t
+    for t in (2, 7, 34, 48):
+        x = x64[:t].copy()
         y = empty((t, n), np.float32)
         nq.nq_gemv_fp8row(q_d, s_d, dev(x), t, n, k, y, nq.alloc_gemv_workspace(-1, t, n, k, DEV))
-        assert rel_fro(host(y, np.float32)[:, rows], M.gemv_fp8row(qo, so, x)) <= FP32_TOL, t
+        assert rel_fro(host(y, np.float32)[:, rows], ref64[:t]) <= FP32_TOL, t
 
 
 @pytest.mark.slow
 def test_gemv_head_q8g32_full_size_packed():
     """The output head as Q8 group-32 (the FP8-versus-Q8 comparison's other
-    side), packed as the benchmark runs it, sampled rows against the oracle."""
+    side), packed as the benchmark runs it: every row of the spread tiles and
+    a sample, against the oracle."""
     n, k = W.HEAD_ROWS, W.HIDDEN
     fmt = nq.NQ_W_Q8G32_F16S
     d = W.grouped("q8g32", n, k, seed=7)
     cd, sd = dev(d["codes"]), dev(d["scales"])
-    pk = empty((nq.nq_packed_weight_bytes(fmt, n, k),), np.uint8)
-    nq.nq_pack_weights(fmt, cd, n, k, pk)
-    del cd
-    rows = _sampled_rows(n, 5)
-    for t in (1, 33, 34, 64):
-        x = W.activations(t, k, workload=5, tensor=4)
-        y = empty((t, n), np.float32)
-        nq.nq_gemv_qgroup_packed(fmt, pk, sd, dev(x), t, n, k, y, nq.alloc_gemv_workspace(fmt, t, n, k, DEV))
-        ref = M.gemv_qgroup("q8g32", d["codes"][rows], d["scales"][rows], x)
-        assert rel_fro(host(y, np.float32)[:, rows], ref) <= FP32_TOL, t
+    pk = _pack_dev(fmt, cd, n, k)
+    rows = _leftover_rows(n, 5)
+    x64 = W.activations(64, k, workload=5, tensor=4)
+    ref64 = M.gemv_qgroup("q8g32", d["codes"][rows], d["scales"][rows], x64)
+    for t in (1, 16, 33, 34, 64):
+        g32, _, _ = _gemv_both_layouts(fmt, cd, pk, sd, x64[:t].copy(), n, k)
+        assert rel_fro(g32[:, rows], ref64[:t]) <= FP32_TOL, t
+
+
+# bench.py's pattern: back-to-back launches over rotating weight copies (here
+# four different matrices) and distinct activations, all sharing one
+# workspace, nothing synchronized in between; every launch against the oracle
+# on every row of the leftover tiles (the partial exchange) and a sample.
+@pytest.mark.slow
+@pytest.mark.parametrize("t", [33, 16, 1])
+def test_gemv_back_to_back_shared_workspace(t):
+    n, k = W.FFN, W.HIDDEN
+    rows = _leftover_rows(n, 11, 160)
+    mats, refs = [], []
+    for i in range(4):
+        w = W.fp8row_weights_bf16(n, k, seed=20 + i)
+        q_d, s_d = _gpu_fp8row_weights(w)
+        mats.append((_pack_dev(-1, q_d, n, k), s_d))
+        del q_d
+        refs.append(_oracle_fp8row_encode(w[rows]))
+    xs = [W.activations(t, k, seed=30 + j) for j in range(8)]
+    xds = [dev(x) for x in xs]
+    wsp = nq.alloc_gemv_workspace(-1, t, n, k, DEV)
+    ys = [empty((t, n), np.float32) for _ in range(8)]
+    torch.cuda.synchronize()
+    for j in range(8):
+        pk, s_d = mats[j % 4]
+        nq.nq_gemv_fp8row_packed(pk, s_d, xds[j], t, n, k, ys[j], wsp)
+    for j in range(8):
+        qo, so = refs[j % 4]
+        got = host(ys[j], np.float32)[:, rows]
+        assert rel_fro(got, M.gemv_fp8row(qo, so, xs[j])) <= FP32_TOL, j
+    assert _counters_zero(wsp, n)
 
 
 # ---------------------------------------------------------------------------
@@ -791,6 +948,7 @@ def test_linear_q4g64_prefill_full_size_sampled():
     y = empty((m, n), np.float32)
     aq, asc, wi8 = empty((m, k), np.int8), empty((m, k // 64), np.float32), empty((n, k), np.int8)
     nq.nq_linear_q4g64(dev(x), m, dev(d["codes"]), dev(d["scales"]), n, k, True, aq, asc, wi8, y)
+    assert np.array_equal(host(wi8, np.int8).astype(np.int64), M.unpack_q4(d["codes"], k))   # every code
     rows = _sampled_rows(m, 12, count=24)
     cols = _sampled_rows(n, 13, count=48)
     qa, sa = M.quantize_act_int8_g64(x[rows])
