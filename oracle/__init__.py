@@ -53,12 +53,18 @@ PARITY = {
     "method.quantize_act_int8_g64": "pinned: closed-form ties, amax->127, Fraction brute force",
     "method.gemv_fp8row": "pinned: one-hot rows, Fraction brute force",
     "method.gemv_qgroup": "pinned: one-hot rows, Fraction brute force",
+    "method.unpack_qbits": "pinned: hand-packed streams, bit-by-bit brute force with Python integers, "
+                           "equality with the Q4 nibble layout at b = 4",
+    "method.linear_qbits_g64": "pinned: route composition, group sums by integer brute force",
     "method.gemm_w8a8_g64": "pinned: int brute force, power-of-two exact case",
     "method.quantize_act_fp8_row": "parity unpinned with respect to the pages (they do not "
                                    "describe the FP8 activation quantizer); pinned to its own "
                                    "stated reading by Fraction brute force",
     "method.gemm_fp8row": "parity unpinned with respect to the pages (same reason); "
                           "pinned to its reading by Fraction brute force",
-    "method.route": "pinned: the 129-token threshold",
+    "method.route": "pinned: the 129-token threshold; the A8 decode flag below it",
     "method.linear_q4g64": "pinned: route composition, group sums by nibble brute force",
+    "method.linear_w8g64 (A8 decode)": "parity unpinned with respect to the pages (they name the A8 decode "
+                                       "variant without details); pinned to its reading, the W8A8 "
+                                       "arithmetic at decode sizes, by route composition and the W8A8 pins",
 }

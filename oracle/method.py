@@ -193,7 +193,33 @@ def unpack_q4(packed, k):
     return q[:, :k]
 
 
-GROUP = {"q4g64": 64, "q8g32": 32, "q8g64": 64, "mxfp8": 32, "bf16": None}
+# Q3 / Q5 / Q6 group-64 codes.  [RTX5080 card, "Quantization profile"]: the
+# main text weights are Q3, Q4 and Q5 group-64 codes with FP16 scales;
+# [NVFP4 card, "What is in the file"]: grouped Q4 / Q5 / Q6 / Q8 formats.  The
+# pages give no bit layout.  Reading: symmetric b-bit two's-complement codes
+# (q in [-2^(b-1), 2^(b-1) - 1], w = q * scale), stored as a dense
+# little-endian bit stream along each row: element j of a row occupies bits
+# [b j, b j + b) of the row's bytes, bit i of the stream being bit i % 8 of
+# byte i // 8.  For b = 4 this is the nibble layout above (element 2j in the
+# low nibble of byte j).  A group of 64 codes spans 8 b bytes, so groups and
+# rows start on byte boundaries; one FP16 scale per 64 codes, [N][K/64].
+
+
+def unpack_qbits(packed, k, bits):
+    """Dense little-endian b-bit two's-complement codes [N][K*b/8] bytes -> int codes [N][K]."""
+    p = np.asarray(packed, dtype=np.uint8)
+    n = p.shape[0]
+    stream = np.unpackbits(p, axis=1, bitorder="little")[:, :k * bits].astype(np.int64)   # bit i = stream[i]
+    fields = stream.reshape(n, k, bits)
+    u = np.zeros((n, k), dtype=np.int64)
+    for i in range(bits):
+        u += fields[:, :, i] << i
+    return np.where(u >= (1 << (bits - 1)), u - (1 << bits), u)
+
+
+QBITS = {"q3g64": 3, "q5g64": 5, "q6g64": 6}
+
+GROUP = {"q4g64": 64, "q8g32": 32, "q8g64": 64, "mxfp8": 32, "bf16": None, "q3g64": 64, "q5g64": 64, "q6g64": 64}
 
 
 def grouped_codes_and_scales(fmt, codes, scales, k):
@@ -204,6 +230,8 @@ def grouped_codes_and_scales(fmt, codes, scales, k):
         return np.asarray(codes, dtype=np.int8).astype(np.float64), f16_decode(scales)
     if fmt == "mxfp8":
         return e4m3_decode(unpack_mxfp8_codes(codes)), ue8m0_decode(np.asarray(scales, np.uint8))
+    if fmt in QBITS:
+        return unpack_qbits(codes, k, QBITS[fmt]).astype(np.float64), f16_decode(scales)
     raise ValueError(fmt)
 
 
@@ -331,15 +359,25 @@ def gemm_fp8row(x_bf16, w_codes, w_scale_bf16):
 
 A8_MIN_TOKENS = 129
 
+# [FP8 card, "Start the server"]: one server variant also runs the MLP with
+# int8 activations in decode steps.  The pages give no details of it.
+# Reading: an A8 decode step is the W8A8 computation above (per-token-per-64
+# int8 activations, exact int32 group sums, FP32 rescale) at decode sizes,
+# enabled by its own flag for steps of at most 128 tokens.
 
-def route(t, allow_a8):
-    return "a8" if (allow_a8 and t >= A8_MIN_TOKENS) else "bf16"
+
+def route(t, allow_a8, a8_decode=False):
+    if allow_a8 and t >= A8_MIN_TOKENS:
+        return "a8"
+    if a8_decode and t < A8_MIN_TOKENS:
+        return "a8_decode"
+    return "bf16"
 
 
-def linear_w8g64(x_bf16, w_q, w_scale_f16, allow_a8):
+def linear_w8g64(x_bf16, w_q, w_scale_f16, allow_a8, a8_decode=False):
     """The projection as an engine step runs it: routed by token count."""
     t = np.asarray(x_bf16).shape[0]
-    if route(t, allow_a8) == "a8":
+    if route(t, allow_a8, a8_decode) != "bf16":
         qa, sa = quantize_act_int8_g64(x_bf16)
         return gemm_w8a8_g64(qa, sa, w_q, w_scale_f16)
     return gemv_qgroup("q8g64", w_q, w_scale_f16, x_bf16)
@@ -352,13 +390,24 @@ def linear_w8g64(x_bf16, w_q, w_scale_f16, allow_a8):
 # in [-8, 7]; the BF16 route is the grouped GEMV.
 
 
-def linear_q4g64(x_bf16, w_packed, w_scale_f16, allow_a8):
+def linear_q4g64(x_bf16, w_packed, w_scale_f16, allow_a8, a8_decode=False):
     """The Q4 group-64 projection routed by token count."""
     t, k = np.asarray(x_bf16).shape
-    if route(t, allow_a8) == "a8":
+    if route(t, allow_a8, a8_decode) != "bf16":
         qa, sa = quantize_act_int8_g64(x_bf16)
         return gemm_w8a8_g64(qa, sa, unpack_q4(w_packed, k), w_scale_f16)
     return gemv_qgroup("q4g64", w_packed, w_scale_f16, x_bf16)
+
+
+def linear_qbits_g64(fmt, x_bf16, w_packed, w_scale_f16, allow_a8, a8_decode=False):
+    """The Q3 / Q5 / Q6 group-64 projection routed by token count: on the A8
+    routes the codes feed the int8 arithmetic exactly, as Q4's do [int8 card,
+    "What changes": Q4 / Q5 codes go to the int8 units exactly]."""
+    t, k = np.asarray(x_bf16).shape
+    if route(t, allow_a8, a8_decode) != "bf16":
+        qa, sa = quantize_act_int8_g64(x_bf16)
+        return gemm_w8a8_g64(qa, sa, unpack_qbits(w_packed, k, QBITS[fmt]), w_scale_f16)
+    return gemv_qgroup(fmt, w_packed, w_scale_f16, x_bf16)
 
 
 # ---------------------------------------------------------------------------

@@ -113,13 +113,20 @@ def gate_bf16(n=GATE_ROWS, k=HIDDEN, seed=0):
     return bf16_normal(rng(3, 2, seed), (n, k), std=0.02)
 
 
+QBITS = {"q3g64": 3, "q5g64": 5, "q6g64": 6}
+
+
 def grouped(fmt, n, k, seed=0):
-    """Q4 group-64 (codes in [-8,7]) or Q8 group-32/64 (codes in [-127,127]), FP16
-    scales log-uniform in [2^-9, 2^-5]."""
-    gs = {"q4g64": 64, "q8g32": 32, "q8g64": 64}[fmt]
-    tag = {"q4g64": 0, "q8g32": 1, "q8g64": 2}[fmt]
+    """Q4 group-64 (codes in [-8,7]), Q8 group-32/64 (codes in [-127,127]) or
+    Q3 / Q5 / Q6 group-64 (b-bit codes, uniform: uniform random bytes of the
+    dense bit stream, K b / 8 bytes per row), FP16 scales log-uniform in
+    [2^-9, 2^-5]."""
+    gs = {"q4g64": 64, "q8g32": 32, "q8g64": 64, "q3g64": 64, "q5g64": 64, "q6g64": 64}[fmt]
+    tag = {"q4g64": 0, "q8g32": 1, "q8g64": 2, "q3g64": 3, "q5g64": 4, "q6g64": 5}[fmt]
     if fmt == "q4g64":
         codes = q4_packed_uniform(rng(4, 10 * tag, seed), n, k)
+    elif fmt in QBITS:
+        codes = rng(4, 10 * tag, seed).integers(0, 256, (n, k * QBITS[fmt] // 8), dtype=np.int16).astype(np.uint8)
     else:
         codes = int8_uniform(rng(4, 10 * tag, seed), (n, k))
     scales = f16_log_uniform(rng(4, 10 * tag + 1, seed), (n, k // gs), -9, -5)

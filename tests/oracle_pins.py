@@ -646,6 +646,71 @@ def pin_gemv_qgroup():
     assert np.allclose(y, ref.numpy(), rtol=1e-14, atol=1e-14)
 
 
+def _pack_stream(codes, bits):
+    """Independent packer: each row's codes as one Python integer, code j at
+    bit b j (two's complement), written out little-endian."""
+    out = []
+    for row in codes:
+        acc = 0
+        for j, c in enumerate(row):
+            acc |= (int(c) & ((1 << bits) - 1)) << (bits * j)
+        out.append(list(acc.to_bytes(len(row) * bits // 8, "little")))
+    return np.array(out, np.uint8)
+
+
+def pin_qbits():
+    """[RTX5080 card, "Quantization profile"]: Q3 / Q5 group-64 codes; the
+    dense little-endian bit-stream reading (element j at bits [b j, b j + b))."""
+    # hand-packed: Q5 codes -16, 15, 0, -1, 7, -8, 1, 2 are the 5-bit fields
+    # 10000 01111 00000 11111 00111 11000 00001 00010 (written MSB first) at bits
+    # 0, 5, 10, ..., 35: byte 0 = bits 7..0 = 1111 0000, byte 1 = 1000 0001,
+    # byte 2 = 0111 1111, byte 3 = 0111 0000, byte 4 = 0001 0000
+    q5 = M.unpack_qbits(np.array([[0xF0, 0x81, 0x7F, 0x70, 0x10]], np.uint8), 8, 5)
+    assert list(q5[0]) == [-16, 15, 0, -1, 7, -8, 1, 2]
+    # Q3 codes -4, 3, 0, -1, 1, 2, -2, -3: fields 100 011 000 111 001 010 110 101
+    # at bits 0, 3, ..., 21: bytes 0001 1100, 0001 1110, 1011 1001
+    q3 = M.unpack_qbits(np.array([[0x1C, 0x1E, 0xB9]], np.uint8), 8, 3)
+    assert list(q3[0]) == [-4, 3, 0, -1, 1, 2, -2, -3]
+    rng = np.random.default_rng(24)
+    for bits in (3, 5, 6):
+        lo = -(1 << (bits - 1))
+        codes = rng.integers(lo, -lo, (5, 128))
+        packed = _pack_stream(codes, bits)
+        assert packed.shape == (5, 16 * bits)
+        assert np.array_equal(M.unpack_qbits(packed, 128, bits), codes)
+        # and bit by bit from the bytes, with Python integers
+        for r in range(5):
+            v = int.from_bytes(bytes(packed[r]), "little")
+            for j in range(128):
+                u = (v >> (bits * j)) & ((1 << bits) - 1)
+                assert M.unpack_qbits(packed[r:r + 1], 128, bits)[0, j] == (u - (1 << bits) if u >> (bits - 1) else u)
+    # b = 4 is the Q4 nibble layout
+    b4 = rng.integers(0, 256, (3, 64)).astype(np.uint8)
+    assert np.array_equal(M.unpack_qbits(b4, 128, 4), M.unpack_q4(b4, 128))
+    # grouped GEMV on Q5 / Q3 codes by exact rationals
+    t, n, k = 3, 5, 128
+    for fmt, bits in (("q5g64", 5), ("q3g64", 3), ("q6g64", 6)):
+        lo = -(1 << (bits - 1))
+        codes = rng.integers(lo, -lo, (n, k))
+        packed = _pack_stream(codes, bits)
+        scales = np.exp2(rng.uniform(-9, -5, (n, 2))).astype(np.float16).view(np.uint16)
+        scv = [[Fraction(float(v)) for v in row] for row in scales.view(np.float16)]
+        x = _bf16_bits_from_f32(rng.standard_normal((t, k)).astype(np.float32))
+        y = M.gemv_qgroup(fmt, packed, scales, x)
+        ref, mag = _brute_group_gemv(fmt, [[int(v) for v in row] for row in codes], scv, F.bf16_decode(x), 64)
+        assert np.all(np.abs(y - ref) <= mag * 2.0 ** -45), fmt
+        # A8 routes: the codes enter the int8 arithmetic exactly
+        xa = _bf16_bits_from_f32(rng.standard_normal((130, k)).astype(np.float32))
+        qa, sa = M.quantize_act_int8_g64(xa)
+        ya, sums = M.gemm_w8a8_g64(qa, sa, codes.astype(np.int8), scales, return_sums=True)
+        assert np.array_equal(M.linear_qbits_g64(fmt, xa, packed, scales, True), ya)
+        assert np.array_equal(M.linear_qbits_g64(fmt, xa[:9], packed, scales, False, True), ya[:9])
+        assert np.array_equal(M.linear_qbits_g64(fmt, xa[:9], packed, scales, True), M.gemv_qgroup(fmt, packed, scales, xa[:9]))
+        for i in (0, 129):
+            for j in range(n):
+                assert sums[i, j, 1] == sum(int(qa[i, kk]) * int(codes[j, kk]) for kk in range(64, 128))
+
+
 def pin_w8a8():
     rng = np.random.default_rng(15)
     m, n, k = 3, 5, 128
@@ -726,6 +791,17 @@ def pin_route():
     qa, sa = M.quantize_act_int8_g64(x)
     assert np.array_equal(at, M.gemm_w8a8_g64(qa, sa, w, ws))
     assert not np.array_equal(at[:128], below)        # a different rounding of the activations
+    # the A8 decode flag: steps of at most 128 tokens take the W8A8 arithmetic
+    assert M.route(1, False, True) == "a8_decode" and M.route(128, True, True) == "a8_decode"
+    assert M.route(129, False, True) == "bf16" and M.route(129, True, True) == "a8"
+    dec = M.linear_w8g64(x[:33], w, ws, False, True)
+    assert np.array_equal(dec, M.gemm_w8a8_g64(qa[:33], sa[:33], w, ws))      # per-token quantization
+    # the group sums by integer brute force (each 64-channel group exact)
+    _, sums = M.gemm_w8a8_g64(qa[:3], sa[:3], w, ws, return_sums=True)
+    for i in range(3):
+        for j in range(n):
+            for g in range(2):
+                assert sums[i, j, g] == sum(int(qa[i, kk]) * int(w[j, kk]) for kk in range(64 * g, 64 * g + 64))
 
 
 def pin_linear_q4g64():
@@ -742,6 +818,8 @@ def pin_linear_q4g64():
     qa, sa = M.quantize_act_int8_g64(x)
     y, sums = M.gemm_w8a8_g64(qa, sa, M.unpack_q4(w, k), ws, return_sums=True)
     assert np.array_equal(M.linear_q4g64(x, w, ws, True), y)
+    # A8 decode: below 129 tokens with the decode flag, the same W8A8 arithmetic
+    assert np.array_equal(M.linear_q4g64(x[:16], w, ws, False, True), y[:16])
     # the group sums by brute force over the nibbles (low nibble first, two's complement)
     for i in (0, 64, 128):
         for j in range(n):
@@ -756,6 +834,6 @@ def pin_linear_q4g64():
 
 ORACLE_METHOD_PINS = [pin_mxfp8_decode, pin_mlx_affine_int8, pin_reencode_bruteforce, pin_reencode_invariants,
                       pin_encode_fp8row_bf16, pin_encode_tiny_rows, pin_quantize_int8, pin_gemv_fp8row, pin_gemv_qgroup,
-                      pin_w8a8, pin_fp8_act_and_gemm, pin_route, pin_linear_q4g64]
+                      pin_w8a8, pin_fp8_act_and_gemm, pin_route, pin_linear_q4g64, pin_qbits]
 
 ALL_PINS = ORACLE_FORMAT_PINS + ORACLE_METHOD_PINS

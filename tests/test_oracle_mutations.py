@@ -180,7 +180,32 @@ def _mlx_through_f32(codes, scales, biases):
     return (q * s + b).astype(np.float64)           # an FP32 value first, then BF16: two roundings
 
 
+def _unpack_qbits_msb_first(packed, k, bits):
+    p = np.asarray(packed, dtype=np.uint8)
+    n = p.shape[0]
+    stream = np.unpackbits(p, axis=1, bitorder="big")[:, :k * bits].astype(np.int64)
+    fields = stream.reshape(n, k, bits)
+    u = np.zeros((n, k), dtype=np.int64)
+    for i in range(bits):
+        u += fields[:, :, i] << i
+    return np.where(u >= (1 << (bits - 1)), u - (1 << bits), u)
+
+
+def _unpack_qbits_unsigned(packed, k, bits):
+    p = np.asarray(packed, dtype=np.uint8)
+    stream = np.unpackbits(p, axis=1, bitorder="little")[:, :k * bits].astype(np.int64)
+    return (stream.reshape(p.shape[0], k, bits) << np.arange(bits)).sum(axis=2)
+
+
+def _route_no_decode(t, allow_a8, a8_decode=False):
+    return "a8" if (allow_a8 and t >= 129) else "bf16"
+
+
 MUTATIONS = [
+    ("qbits bit order within bytes reversed", lambda mp: mp.setattr(M, "unpack_qbits", _unpack_qbits_msb_first),
+     [P.pin_qbits]),
+    ("qbits unsigned codes", lambda mp: mp.setattr(M, "unpack_qbits", _unpack_qbits_unsigned), [P.pin_qbits]),
+    ("route ignores the A8 decode flag", lambda mp: mp.setattr(M, "route", _route_no_decode), [P.pin_route]),
     ("mlx groups of 64", lambda mp: mp.setattr(M, "mlx_affine_int8_values", _mlx_group64),
      [P.pin_mlx_affine_int8]),
     ("mlx bias subtracted", lambda mp: mp.setattr(M, "mlx_affine_int8_values", _mlx_minus_bias),
