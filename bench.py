@@ -15,7 +15,12 @@ order (prefill and conversions before decode, as in an engine step):
   head           row-FP8 152064x5120, T = 1..64
   head_q8        the same head as Q8 group-32, T = 1..64 (FP8-versus-Q8 crossover)
   gemv_q4g64 / gemv_q8g32   at 17408x5120 and 5120x17408, T = 1, 8, 33
+  a8_decode      A8 decode GEMV (int8 activations) on Q8 / Q4 group-64 weights
+                 at both shapes, T = 1, 8, 33: the kernel, the routed step
+                 (quantize + GEMV), and the BF16-activation Q8 GEMV beside it
   gemv_fp8row    row-FP8 17408x5120, T = 1, 4, 16, 33 (BF16 out)   <- headline
+  hbm_read       a plain streaming read of 89 MB (rotating over > 512 MB) and
+                 of 1 GiB: the measured HBM read ceiling
 Weights of the decode GEMVs rotate over copies totalling more than 512 MB so
 that the 256 MB last-level cache cannot serve them.  Every burst is bracketed
 by HIP events on the stream it runs on (per-launch time = burst time / burst;
@@ -24,7 +29,11 @@ from those.
 
 `value` is the headline: decode GEMV HBM GB/s on row-FP8 17408x5120 over
 T = 1, 4, 16, 33 (algorithmic bytes / kernel time).  The prefill GEMMs are
-reported in `prefill` (TOPS and fraction of the MFMA peak).
+reported in `prefill` and `roofline_prefill` (TOPS and fraction of the MFMA
+peak), the measured HBM read ceiling (a plain streaming read, rows
+hbm_read_*) beside the headline roofline, weight-bytes/s and tokens/s of every
+decode row in `decode_per_shape`, and the oracle per (config, T) in
+`cpu_baseline`.
 """
 
 import argparse
@@ -96,8 +105,13 @@ def calibrate_copy():
 
 
 class Row:
-    def __init__(self, name, kernel, unit, work, fn):
+    """One timed launch: `work` is its algorithmic bytes (GB/s rows) or ops;
+    decode GEMV rows also carry their weight bytes and token count, for the
+    weight-bytes/s and tokens/s per layer shape."""
+
+    def __init__(self, name, kernel, unit, work, fn, wbytes=None, tokens=None):
         self.name, self.kernel, self.unit, self.work, self.fn = name, kernel, unit, work, fn
+        self.wbytes, self.tokens = wbytes, tokens
         self.ms = []
 
 
@@ -163,6 +177,19 @@ def rows_mlx(nq, W):
                 lambda: nq.nq_decode_mlx_affine_int8(c, s, b, n, k, out))]
 
 
+def rows_hbm_read(nq):
+    """The measured HBM read ceiling: a plain streaming read (nq_stream_read)
+    of 89,128,960 bytes (the headline weight's size) rotating over copies
+    totalling more than 512 MB, and of one 1 GiB buffer."""
+    torch = _torch()
+    sink = empty((nq.lib().nq_stream_read_sink_words(),), torch.int32)
+    b89 = empty((89128960,), torch.uint8).fill_(1)
+    nxt = rotation(b89)
+    big = empty((1 << 30,), torch.uint8).fill_(1)
+    return [Row("hbm_read_89MB", "stream_read", "GB/s", 89128960, lambda: nq.nq_stream_read(nxt()[0], sink)),
+            Row("hbm_read_1GiB", "stream_read", "GB/s", 1 << 30, lambda: nq.nq_stream_read(big, sink))]
+
+
 def pack(nq, fmt, codes, n, k):
     """One-time weight packing (setup, not timed)."""
     torch = _torch()
@@ -186,7 +213,8 @@ def _fp8row_gemv_rows(nq, prefix, kernel, q, s, xs, ts, rotate=True, packed=True
         def fn(t=t, xt=xt, y=y, ws=ws):
             qq, ss = nxt()
             gemv(qq, ss, xt, t, n, k, y, ws)
-        rows.append(Row(f"{prefix}_T{t}", kernel, "GB/s", n * k + 2 * n + 2 * t * k + 2 * t * n, fn))
+        rows.append(Row(f"{prefix}_T{t}", kernel, "GB/s", n * k + 2 * n + 2 * t * k + 2 * t * n, fn,
+                        wbytes=n * k + 2 * n, tokens=t))
     return rows
 
 
@@ -242,7 +270,8 @@ def rows_gate(nq, W):
         wg = nq.alloc_gemv_workspace(nq.NQ_W_BF16, t, n, k, DEV)
         rows.append(Row(f"gemv_gate_T{t}", "gemv_bf16", "GB/s", 2 * n * k + 2 * t * k + 2 * t * n,
                         lambda t=t, xg=xg, yg=yg, wg=wg: nq.nq_gemv_qgroup_packed(nq.NQ_W_BF16, gate_pk, None, xg,
-                                                                                  t, n, k, yg, wg)))
+                                                                                  t, n, k, yg, wg),
+                        wbytes=2 * n * k, tokens=t))
     return rows
 
 
@@ -271,7 +300,58 @@ def _grouped_shape_rows(nq, W, name, fmt, gs, n, k, torch):
             cc, ss = nxt()
             nq.nq_gemv_qgroup_packed(fmt, cc, ss, xt, t, n, k, y, ws)
         rows.append(Row(f"gemv_{name}_{n}x{k}_T{t}", f"gemv_{name}", "GB/s",
-                        cbytes + 2 * n * (k // gs) + 2 * t * k + 2 * t * n, fn))
+                        cbytes + 2 * n * (k // gs) + 2 * t * k + 2 * t * n, fn,
+                        wbytes=cbytes + 2 * n * (k // gs), tokens=t))
+    return rows
+
+
+def rows_a8_decode(nq, W):
+    """A8 decode (int8 activations at decode sizes) beside the BF16-activation
+    GEMV on the same packed weights: Q8 group-64 and Q4 group-64 at
+    17408x5120 and 5120x17408, T = 1, 8, 33.  gemv_a8_*: the A8 GEMV on
+    activations already quantized; linear_a8d_*: the routed decode step
+    (quantization + A8 GEMV, row-major weights as the routed call takes
+    them); gemv_bf16act_q8g64_*: the BF16-activation GEMV on the same Q8
+    weights (the Q4 one is the gemv_q4g64 rows)."""
+    torch = _torch()
+    rows = []
+    for name, fmt, bpw in (("q8g64", nq.NQ_W_Q8G64_F16S, 1.0), ("q4g64", nq.NQ_W_Q4G64_F16S, 0.5)):
+        for (n, k) in ((W.FFN, W.HIDDEN), (W.HIDDEN, W.FFN)):
+            dd = W.grouped(name, n, k)
+            cd, sd = to_dev(dd["codes"]), to_dev(dd["scales"])
+            wbytes = int(n * k * bpw) + 2 * n * (k // 64)
+            nxt = rotation(pack(nq, fmt, cd, n, k), sd)
+            nxt_rm = rotation(cd, sd)
+            for t in (1, 8, 33):
+                x = to_dev(W.activations(t, k, workload=4, tensor=50))
+                qa, sa = empty((t, k), torch.int8), empty((t, k // 64), torch.float32)
+                nq.nq_quantize_act_int8_g64(x, t, k, qa, sa)
+                y = empty((t, n), torch.int16)
+                wsa = nq.alloc_gemv_a8_workspace(t, n, k, DEV)
+                abytes = t * k + 4 * t * (k // 64) + 2 * t * n
+
+                def fa(t=t, qa=qa, sa=sa, y=y, wsa=wsa, n=n, k=k, fmt=fmt, nxt=nxt):
+                    cc, ss = nxt()
+                    nq.nq_gemv_a8_g64_packed(fmt, cc, ss, qa, sa, t, n, k, y, wsa)
+
+                def fr(t=t, x=x, qa=qa, sa=sa, y=y, wsa=wsa, n=n, k=k, fmt=fmt, nxt_rm=nxt_rm):
+                    cc, ss = nxt_rm()
+                    if fmt == nq.NQ_W_Q8G64_F16S:
+                        nq.nq_linear_q8g64(x, t, cc, ss, n, k, nq.NQ_A8_DECODE, qa, sa, y, wsa)
+                    else:   # the decode route needs no widened copy of the Q4 codes
+                        nq.nq_linear_q4g64(x, t, cc, ss, n, k, nq.NQ_A8_DECODE, qa, sa, None, y, wsa)
+                rows.append(Row(f"gemv_a8_{name}_{n}x{k}_T{t}", "gemv_a8", "GB/s", wbytes + abytes, fa,
+                                wbytes=wbytes, tokens=t))
+                rows.append(Row(f"linear_a8d_{name}_{n}x{k}_T{t}", "quant_int8+gemv_a8", "GB/s",
+                                wbytes + 2 * t * k + 2 * t * n, fr, wbytes=wbytes, tokens=t))
+                if name == "q8g64":
+                    wsb = nq.alloc_gemv_workspace(fmt, t, n, k, DEV)
+
+                    def fb(t=t, x=x, y=y, wsb=wsb, n=n, k=k, fmt=fmt, nxt=nxt):
+                        cc, ss = nxt()
+                        nq.nq_gemv_qgroup_packed(fmt, cc, ss, x, t, n, k, y, wsb)
+                    rows.append(Row(f"gemv_bf16act_{name}_{n}x{k}_T{t}", "gemv_q8g64", "GB/s",
+                                    wbytes + 2 * t * k + 2 * t * n, fb, wbytes=wbytes, tokens=t))
     return rows
 
 
@@ -304,7 +384,8 @@ def rows_head_q8(nq, W):
         ws = nq.alloc_gemv_workspace(fmt, t, n, k, DEV)
         rows.append(Row(f"head_q8g32_T{t}", "gemv_head_q8g32", "GB/s",
                         n * k + 2 * n * (k // 32) + 2 * t * k + 2 * t * n,
-                        lambda t=t, xt=xt, y=y, ws=ws: nq.nq_gemv_qgroup_packed(fmt, pk, sd, xt, t, n, k, y, ws)))
+                        lambda t=t, xt=xt, y=y, ws=ws: nq.nq_gemv_qgroup_packed(fmt, pk, sd, xt, t, n, k, y, ws),
+                        wbytes=n * k + 2 * n * (k // 32), tokens=t))
     return rows
 
 
@@ -392,37 +473,125 @@ def build_rows(selected):
     for name in ("q4g64", "q8g32"):
         if want(f"gemv_{name}"):
             rows += rows_grouped(nq, W, name)
+    if want("a8_decode"):
+        rows += rows_a8_decode(nq, W)
     if want("gemv_fp8row"):
         rows += rows_gemv_fp8row(nq, W)
+    if want("hbm_read"):
+        rows += rows_hbm_read(nq)
     _torch().cuda.synchronize()
     return rows
 
 
+def _blas_threads():
+    try:
+        import threadpoolctl
+        return max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    except Exception:
+        return None
+
+
 def cpu_baseline():
-    """The oracle (as it stands) on the headline workload: row-FP8 decode GEMV
-    17408x5120 at T = 1, 4, 16, 33, on the host cores."""
+    """The oracle (as it stands) timed on the host cores, once per (config, T):
+    the headline row-FP8 GEMV on the full 17408x5120 weight (`value`), and the
+    other configs on bounded row samples (stated per entry), as weight-bytes/s
+    (GB/s), tokens/s or ops/s.  Weight encoding and input generation are not
+    timed.  Elementwise numpy runs on one core, float64 matmuls on the BLAS
+    threads."""
     from oracle import method as M
     from quantized_weight_linear_amd import workloads as W
 
+    out = {}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    def gemv_entry(key, sec, wbytes, t, xy_bytes):
+        out[f"{key}_GBps"] = round((wbytes + xy_bytes) / sec / 1e9, 4)
+        out[f"{key}_weight_GBps"] = round(wbytes / sec / 1e9, 4)
+        out[f"{key}_tok_s"] = round(t / sec, 2)
+
+    # config 2 (the headline): full weight, T = 1, 4, 16, 33 (the weight's
+    # encode is setup: run on row bands in threads, not timed)
     n, k = W.FFN, W.HIDDEN
-    w = W.fp8row_weights_bf16(n, k)
-    wq, ws = M.encode_fp8row_bf16(w)
+    w2 = W.fp8row_weights_bf16(n, k)
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(min(16, len(os.sched_getaffinity(0)))) as ex:
+        parts = list(ex.map(lambda r0: M.encode_fp8row_bf16(w2[r0:r0 + 512]), range(0, n, 512)))
+    wq, ws = np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+    del w2, parts
     x33 = W.activations(33, k)
     total_bytes, total_s = 0, 0.0
     for t in (1, 4, 16, 33):
-        t0 = time.perf_counter()
-        M.gemv_fp8row(wq, ws, x33[:t])
-        total_s += time.perf_counter() - t0
+        sec = timed(lambda: M.gemv_fp8row(wq, ws, x33[:t]))
+        total_s += sec
         total_bytes += n * k + 2 * n + 2 * t * k + 2 * t * n
-    try:
-        import threadpoolctl
-        threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-    return {"value": round(total_bytes / total_s / 1e9, 3), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": "oracle decode GEMV (numpy float64) on the full row-FP8 17408x5120 weight, "
-                      "T = 1, 4, 16, 33 once each; the oracle's weight encode is not timed"}
+        gemv_entry(f"cfg2_fp8row_17408x5120_T{t}", sec, n * k + 2 * n, t, 2 * t * k + 2 * t * n)
+    del wq, ws
+    # config 1: MXFP8 256x512, T = 1
+    d1 = W.mxfp8_gemv()
+    out["cfg1_mxfp8_gemv_256x512_us"] = round(timed(lambda: M.gemv_qgroup("mxfp8", d1["words"], d1["e8m0"],
+                                                                            d1["x"])) * 1e6, 1)
+    # config 3: re-encode and down projection on 512 of the 5120 rows; the gate whole
+    d3 = W.block128_codes()
+    r3 = 512
+    c3, w3 = d3["codes"][:r3], d3["wsi"][:r3 // 128]
+    k3 = c3.shape[1]
+    res = {}
+    sec = timed(lambda: res.update(q=M.reencode_block128_to_row(c3, w3)))
+    out["cfg3_reencode_512x17408_GBps"] = round((2 * r3 * k3 + 4 * w3.size + 2 * r3) / sec / 1e9, 4)
+    q3, s3 = res["q"]
+    for t in (1, 33):
+        x = W.activations(t, k3, workload=3, tensor=3)
+        sec = timed(lambda: M.gemv_fp8row(q3, s3, x))
+        gemv_entry(f"cfg3_down_512x17408_T{t}", sec, r3 * k3 + 2 * r3, t, 2 * t * k3 + 2 * t * r3)
+    gate = W.gate_bf16()
+    for t in (1, 33):
+        x = W.activations(t, W.HIDDEN, workload=3, tensor=4)
+        sec = timed(lambda: M.gemv_qgroup("bf16", gate, None, x))
+        gemv_entry(f"cfg3_gate_96x5120_T{t}", sec, 2 * gate.size, t, 2 * t * W.HIDDEN + 2 * t * 96)
+    # config 4: Q4 group-64 / Q8 group-32 on 1024-row samples of both shapes
+    for name, gs, bpw in (("q4g64", 64, 0.5), ("q8g32", 32, 1.0)):
+        for (n4, k4) in ((W.FFN, W.HIDDEN), (W.HIDDEN, W.FFN)):
+            r4 = 1024
+            d4 = W.grouped(name, r4, k4)             # the first 1024 rows of the n4 x k4 matrix
+            c4, s4 = d4["codes"], d4["scales"]
+            wbytes = int(r4 * k4 * bpw) + 2 * r4 * (k4 // gs)
+            for t in (1, 8, 33):
+                x = W.activations(t, k4, workload=4, tensor=50)
+                sec = timed(lambda: M.gemv_qgroup(name, c4, s4, x))
+                gemv_entry(f"cfg4_{name}_{r4}of{n4}x{k4}_T{t}", sec, wbytes, t, 2 * t * k4 + 2 * t * r4)
+    # config 5: int8 quantization of the whole chunk; W8A8 and FP8 GEMMs on
+    # 1024 and 512 output columns of the chunk; the head at T = 1 on 4096 rows
+    c5 = 1024
+    d5 = W.w8a8_prefill(n=c5)                      # the whole chunk; the first 1024 weight rows
+    m5, k5 = d5["x"].shape
+    res = {}
+    sec = timed(lambda: res.update(q=M.quantize_act_int8_g64(d5["x"])))
+    out["cfg5_quant_int8_1792x5120_GBps"] = round((2 * m5 * k5 + m5 * k5 + 4 * m5 * (k5 // 64)) / sec / 1e9, 4)
+    qa, sa = res["q"]
+    sec = timed(lambda: M.gemm_w8a8_g64(qa, sa, d5["w"], d5["w_scale"]))
+    out["cfg5_w8a8_1792x1024x5120_GOPS"] = round(2 * m5 * c5 * k5 / sec / 1e9, 3)
+    wf = W.fp8row_weights_bf16(512, k5)
+    wfq, wfs = M.encode_fp8row_bf16(wf)
+    xf = W.activations(m5, k5, workload=5, tensor=6)
+    sec = timed(lambda: M.gemm_fp8row(xf, wfq, wfs))
+    out["cfg5_fp8_gemm_1792x512x5120_GFLOPS"] = round(2 * m5 * 512 * k5 / sec / 1e9, 3)
+    hw = W.head_weights_bf16(n=4096)               # the first 4096 rows of the head
+    hq, hs = M.encode_fp8row_bf16(hw)
+    xh = W.activations(1, k5, workload=5, tensor=4)
+    sec = timed(lambda: M.gemv_fp8row(hq, hs, xh))
+    gemv_entry("cfg5_head_4096of152064x5120_T1", sec, 4096 * k5 + 2 * 4096, 1, 2 * k5 + 2 * 4096)
+
+    line = {"value": round(total_bytes / total_s / 1e9, 3), "unit": "GB/s",
+            "cores": len(os.sched_getaffinity(0)), "blas_threads": _blas_threads(), "kind": "oracle",
+            "sample": "value: oracle decode GEMV (numpy float64) on the full row-FP8 17408x5120 weight, "
+                      "T = 1, 4, 16, 33 once each (encode not timed); other keys: per (config, T) on the "
+                      "row / column samples their names give"}
+    line.update(out)
+    return line
 
 
 def gemv_traffic(names):
@@ -532,7 +701,7 @@ def main():
             "data": "synthetic",
             "config": {"workload": "row-FP8 decode GEMV 17408x5120 (FFN up/gate), T=1,4,16,33, BF16 out; "
                                    "one step = every hot-path row once",
-                       "T": [1, 4, 16, 33], "N": 17408, "K": 5120}}
+                       "T": "1,4,16,33", "N": 17408, "K": 5120}}
     if head:
         byt = sum(r.work * len(r.ms) for r in head)
         sec = sum(sum(r.ms) * 1e-3 for r in head)
@@ -543,20 +712,41 @@ def main():
         if per_launch is not None:
             # whole-job HBM bytes per launch, averaged like `achieved`
             traffic = round(sum(per_launch[r.name] * len(r.ms) for r in head) / sum(len(r.ms) for r in head))
-        line["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                            "kernel": "gemv_mfma_kernel (one token block at T=1,4,16, three at T=33), "
-                                      "packed row-FP8 17408x5120",
-                            "bytes_per_launch": {r.name: r.work for r in head},
-                            "hbm_traffic_per_launch": per_launch,
-                            "us_per_launch": {r.name: results[r.name]["us"] for r in head}}
+        roof = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "gemv_mfma_kernel (one token block at T=1,4,16, three at T=33), packed row-FP8 17408x5120"}
+        for r in head:
+            roof[f"us_{r.name.split('_')[-1]}"] = results[r.name]["us"]
+            roof[f"bytes_{r.name.split('_')[-1]}"] = r.work
+            if per_launch is not None:
+                roof[f"traffic_{r.name.split('_')[-1]}"] = per_launch[r.name]
+        if "hbm_read_89MB" in results:
+            ceil = results["hbm_read_89MB"]["rate"]
+            roof["hbm_read_ceiling_89MB_GBps"] = ceil
+            roof["frac_of_read_ceiling"] = round(gbs / ceil, 4)
+        if "hbm_read_1GiB" in results:
+            roof["hbm_read_ceiling_1GiB_GBps"] = results["hbm_read_1GiB"]["rate"]
+        line["roofline"] = roof
+    # prefill GEMMs (flat, so record parsers keep every figure)
     pre = {}
-    for name in ("gemm_w8a8", "gemm_fp8"):
+    for name, key, peak_name in (("gemm_w8a8", "w8a8", "int8"), ("gemm_fp8", "fp8", "fp8"),
+                                 ("linear_q4g64_a8", "q4_a8_routed", "int8")):
         if name in results:
-            pre[name] = {"us": results[name]["us"], "rate": results[name]["rate"], "unit": results[name]["unit"],
-                         "frac_of_peak": results[name]["frac"]}
+            v = results[name]
+            pre[f"{key}_us"] = v["us"]
+            pre[f"{key}_{'TFLOPS' if name == 'gemm_fp8' else 'TOPS'}"] = v["rate"]
+            pre[f"{key}_frac_{peak_name}_peak"] = v["frac"]
+    if "gemm_fp8" in results:
+        pre["fp8_frac_bf16_peak"] = round(results["gemm_fp8"]["rate"] / (FP8_PEAK_TFLOPS / 2), 4)
     if pre:
+        pre.update({"M": 1792, "N": 17408, "K": 5120})
         line["prefill"] = pre
+    if "gemm_w8a8" in results:
+        v = results["gemm_w8a8"]
+        line["roofline_prefill"] = {"bound": "mfma", "achieved": v["rate"], "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                                    "frac": v["frac"], "us": v["us"],
+                                    "kernel": "gemm_kernel<W8A8> (v_mfma_i32_32x32x32_i8, FP32 per-group rescale), "
+                                              "M=1792 N=17408 K=5120"}
     cross = [t for t in range(1, 65) if f"head_T{t}" in results and f"head_q8g32_T{t}" in results]
     if cross:
         q8_faster = [t for t in cross if results[f"head_q8g32_T{t}"]["us"] < results[f"head_T{t}"]["us"]]
@@ -565,8 +755,23 @@ def main():
             "q8g32_faster_at_T": q8_faster,
             "fp8_us": [results[f"head_T{t}"]["us"] for t in cross],
             "q8g32_us": [results[f"head_q8g32_T{t}"]["us"] for t in cross]}
-    line["rows"] = {k: {"us": v["us"], "rate": v["rate"], "unit": v["unit"], "frac": v["frac"]}
-                    for k, v in results.items()}
+    a8 = {}
+    for name in ("q8g64", "q4g64"):
+        for shape in ("17408x5120", "5120x17408"):
+            for t in (1, 8, 33):
+                ka, kb = f"linear_a8d_{name}_{shape}_T{t}", (f"gemv_bf16act_{name}_{shape}_T{t}" if name == "q8g64"
+                                                             else f"gemv_{name}_{shape}_T{t}")
+                if ka in results and kb in results:
+                    a8[f"{name}_{shape}_T{t}_a8_us"] = results[ka]["us"]
+                    a8[f"{name}_{shape}_T{t}_bf16act_us"] = results[kb]["us"]
+    if a8:
+        line["a8_decode_vs_bf16act"] = a8
+    # every row: [us, rate, fraction of its peak]; decode rows also
+    # [weight GB/s, tokens/s] per layer shape
+    line["rows"] = {k: [v["us"], v["rate"], v["frac"]] for k, v in results.items()}
+    line["decode_per_shape"] = {r.name: [round(r.wbytes / (results[r.name]["us"] * 1e-6) / 1e9, 1),
+                                         round(r.tokens / (results[r.name]["us"] * 1e-6), 1)]
+                                for r in rows if r.wbytes is not None}
     line["timing"] = {"ms_per_step_gpu_events": round(gpu_step_ms, 3), "wall_s_timed_region": round(wall, 3),
                       "note": "timed region starts with a spin kernel that holds the stream while the host "
                               "enqueues all launches; per-launch times are HIP events on that stream"}

@@ -63,10 +63,21 @@ typedef enum {
     NQ_W_Q8G64_F16S = 2,  /* int8 codes [N][K], one FP16 scale per 64 elements [N][K/64] */
     NQ_W_MXFP8_G32 = 3,   /* four E4M3 codes per little-endian u32 word ([N][K/4]), one UE8M0
                              byte per 32 elements ([N][K/32]) worth 2^(b-127); b = 255 is NaN */
-    NQ_W_BF16 = 4         /* BF16 weights [N][K], no scales */
+    NQ_W_BF16 = 4,        /* BF16 weights [N][K], no scales */
+    NQ_W_Q3G64_F16S = 5,  /* 3-, 5- and 6-bit two's-complement codes as a dense little-endian bit stream */
+    NQ_W_Q5G64_F16S = 6,  /* along each row: element j at bits [b j, b j + b) of the row's K b / 8 bytes */
+    NQ_W_Q6G64_F16S = 7   /* (b = 4 would be the Q4 layout); one FP16 scale per 64 elements [N][K/64] */
 } nq_wfmt;
 
-typedef enum { NQ_ROUTE_BF16 = 0, NQ_ROUTE_A8 = 1 } nq_route_kind;
+typedef enum { NQ_ROUTE_BF16 = 0, NQ_ROUTE_A8 = 1, NQ_ROUTE_A8_DECODE = 2 } nq_route_kind;
+
+/* Flags of the routed calls (nq_route, nq_linear_*): which steps may run with
+ * int8 activations.  NQ_A8_PREFILL: steps of 129 tokens or more (the W8A8
+ * GEMM); NQ_A8_DECODE: steps of at most 128 tokens (the A8 decode GEMV, for
+ * the MLP projections of an engine that enables it).  1 keeps the meaning of
+ * the former boolean argument. */
+#define NQ_A8_PREFILL 1
+#define NQ_A8_DECODE 2
 
 /* Version of this interface (NQ_ABI_VERSION). */
 int nq_abi_version(void);
@@ -197,7 +208,10 @@ int64_t nq_gemv_workspace_bytes(int fmt, int64_t T, int64_t N, int64_t K);
  * lanes of a wavefront stored contiguously (lane 16 g + i holds row i of the
  * block, lane group g).  Pieces per row and chunk: FP8 / MXFP8 / Q8G64 four
  * of 16 B (64 columns each, lane group g at byte 16 g), Q4G64 four of 8 B,
- * Q8G32 eight of 8 B (32 columns, byte 8 g), BF16 eight of 16 B.  Every
+ * Q8G32 eight of 8 B (32 columns, byte 8 g), BF16 eight of 16 B.  Q3 / Q5 /
+ * Q6: per chunk and row block, each lane's 8 b bytes (the codes 64 q + 16 g +
+ * [0, 16) of its row for q = 0..3, the bit stream's bytes back to back) stored
+ * as 16-byte pieces (and an 8-byte tail for b = 3, 5), piece-major.  Every
  * load instruction of the GEMV reads a contiguous 512 B or 1 KiB, and the
  * grid, walking chunk by chunk, sweeps one contiguous window at a time.  The pages store weights in engine-specific tiled
  * layouts too ([NVFP4 card, "How it was created"]: the NVFP4 storage layout
@@ -227,10 +241,11 @@ nq_status nq_gemv_qgroup_packed(int fmt, const void* w_packed, const void* w_sca
  * Decode GEMV on grouped weights (see nq_wfmt for layouts), BF16 activations,
  * FP32 accumulation: y[t][n] = sum_g sc[n][g] * sum_{k in g} x[t][k] * q[n][k].
  * [NVFP4 card, "What is in the file"] (grouped Q4/Q5/Q6/Q8 with FP16 scales,
- * BF16 projections); [RTX5080 card, "Quantization profile"] (Q4 group-64 with
- * FP16 scales); [MXFP8 card, "How it was built"] (MXFP8).
+ * BF16 projections); [RTX5080 card, "Quantization profile"] (Q3/Q4/Q5
+ * group-64 with FP16 scales); [MXFP8 card, "How it was built"] (MXFP8).
  *   w_codes, w_scales  per nq_wfmt (w_scales is ignored and may be NULL for BF16)
- * Errors: K not a multiple of the group size -> NQ_ERR_SHAPE.
+ * Errors: K not a multiple of the group size -> NQ_ERR_SHAPE; for Q3/Q5/Q6
+ * also K % 256 != 0, or code bytes (rows padded to 16) of 2 GiB or more.
  */
 nq_status nq_gemv_qgroup(int fmt, const void* w_codes, const void* w_scales, const uint16_t* x,
                          int64_t T, int64_t N, int64_t K, int out_dt, void* y, void* workspace,
@@ -273,21 +288,52 @@ nq_status nq_gemm_fp8row(const uint16_t* x, const uint8_t* w, const uint16_t* w_
 
 /*
  * Route rule.  [int8 card, "What changes"]: a projection permitted to use
- * int8 activations takes that route only in steps of 129 tokens or more;
- * every other step keeps the BF16-activation route.  Host-only; returns an
- * nq_route_kind.
+ * int8 activations in prefill takes that route only in steps of 129 tokens
+ * or more (NQ_ROUTE_A8); decode and verify steps keep the BF16-activation
+ * route.  [FP8 card, "Start the server"]: a server variant also runs the MLP
+ * with int8 activations in decode; with NQ_A8_DECODE in the flags, steps of
+ * at most 128 tokens take the A8 decode GEMV (NQ_ROUTE_A8_DECODE).  The pages
+ * give no details of that variant; the arithmetic here is the W8A8 one
+ * (per-token-per-64 int8 activations, exact int32 group sums, FP32 rescale).
+ * Host-only; returns an nq_route_kind.
  */
-int nq_route(int64_t T, int allow_a8);
+int nq_route(int64_t T, int a8_flags);
 
 /*
- * The Q8 group-64 projection as an engine step runs it: routed by nq_route.
- * BF16 route: nq_gemv_qgroup(NQ_W_Q8G64_F16S, ...).  A8 route:
- * nq_quantize_act_int8_g64 into the caller-owned workspaces a_q_ws [T][K] and
- * a_scale_ws [T][K/64] (needed only when the A8 route is taken), then
- * nq_gemm_w8a8_g64.  `workspace` is the optional GEMV workspace.
+ * A8 decode GEMV: the W8A8 arithmetic of nq_gemm_w8a8_g64 at decode sizes
+ * (any T; tuned for T <= 64), streaming the weights once.
+ *   fmt      NQ_W_Q8G64_F16S (int8 codes [N][K]) or NQ_W_Q4G64_F16S (nibbles
+ *            [N][K/2], see nq_wfmt); row-major here, or packed by
+ *            nq_pack_weights(fmt, ...) for nq_gemv_a8_g64_packed
+ *   w_scale  [N][K/64] FP16 bits
+ *   a_q, a_scale   [T][K] int8 and [T][K/64] FP32 from nq_quantize_act_int8_g64
+ *   y        [T][N] FP32 or BF16 bits:
+ *            y[t][n] = sum_g P[t][n][g] * w_scale[n][g] * a_scale[t][g], each
+ *            P the exact int32 sum of a 64-channel group; the group terms are
+ *            summed in FP32 (a BF16 output is the RNE rounding of it)
+ *   workspace, workspace_bytes   optional, as for the BF16 GEMVs
+ *            (nq_gemv_a8_workspace_bytes; zero-filled once, left zero-filled)
+ * Errors: K % 256 != 0 -> NQ_ERR_SHAPE; another fmt -> NQ_ERR_FORMAT.
+ */
+int64_t nq_gemv_a8_workspace_bytes(int64_t T, int64_t N, int64_t K);
+nq_status nq_gemv_a8_g64(int fmt, const void* w_codes, const uint16_t* w_scale, const int8_t* a_q,
+                         const float* a_scale, int64_t T, int64_t N, int64_t K, int out_dt, void* y,
+                         void* workspace, int64_t workspace_bytes, void* stream);
+nq_status nq_gemv_a8_g64_packed(int fmt, const void* w_packed, const uint16_t* w_scale, const int8_t* a_q,
+                                const float* a_scale, int64_t T, int64_t N, int64_t K, int out_dt, void* y,
+                                void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * The Q8 group-64 projection as an engine step runs it: routed by
+ * nq_route(T, a8_flags).  BF16 route: nq_gemv_qgroup(NQ_W_Q8G64_F16S, ...).
+ * A8 routes: nq_quantize_act_int8_g64 into the caller-owned workspaces a_q_ws
+ * [T][K] and a_scale_ws [T][K/64] (needed only when an A8 route is taken),
+ * then nq_gemm_w8a8_g64 (prefill) or nq_gemv_a8_g64 (decode; K % 256 == 0).
+ * `workspace` is the optional GEMV workspace (size the larger of
+ * nq_gemv_workspace_bytes and nq_gemv_a8_workspace_bytes).
  */
 nq_status nq_linear_q8g64(const uint16_t* x, int64_t T, const int8_t* w_q, const uint16_t* w_scale,
-                          int64_t N, int64_t K, int allow_a8, int8_t* a_q_ws, float* a_scale_ws,
+                          int64_t N, int64_t K, int a8_flags, int8_t* a_q_ws, float* a_scale_ws,
                           int out_dt, void* y, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
@@ -301,19 +347,61 @@ nq_status nq_linear_q8g64(const uint16_t* x, int64_t T, const int8_t* w_q, const
 nq_status nq_unpack_q4_to_int8(const uint8_t* codes, int64_t N, int64_t K, int8_t* out, void* stream);
 
 /*
- * The Q4 group-64 projection as an engine step runs it: routed by nq_route.
- * [int8 card, "What changes"]: BF16 route nq_gemv_qgroup(NQ_W_Q4G64_F16S, ...);
- * A8 route: nq_quantize_act_int8_g64 into a_q_ws [T][K] and a_scale_ws
- * [T][K/64], the codes widened by nq_unpack_q4_to_int8 into w_i8_ws [N][K]
- * (caller-owned; a caller that keeps a widened copy can call
- * nq_gemm_w8a8_g64 directly), then nq_gemm_w8a8_g64 with the same FP16 scales.
- * The A8 workspaces are needed only when that route is taken; `workspace` is
- * the optional GEMV workspace.
+ * The Q4 group-64 projection as an engine step runs it: routed by
+ * nq_route(T, a8_flags).  [int8 card, "What changes"]: BF16 route
+ * nq_gemv_qgroup(NQ_W_Q4G64_F16S, ...); A8 prefill route:
+ * nq_quantize_act_int8_g64 into a_q_ws [T][K] and a_scale_ws [T][K/64], the
+ * codes widened by nq_unpack_q4_to_int8 into w_i8_ws [N][K] (caller-owned; a
+ * caller that keeps a widened copy can call nq_gemm_w8a8_g64 directly), then
+ * nq_gemm_w8a8_g64 with the same FP16 scales; A8 decode route: the same
+ * quantization, then nq_gemv_a8_g64 on the Q4 codes as stored (no widened
+ * copy; K % 256 == 0).  The A8 workspaces are needed only when their route is
+ * taken (w_i8_ws only for the prefill one); `workspace` is the optional GEMV
+ * workspace.
  */
 nq_status nq_linear_q4g64(const uint16_t* x, int64_t T, const uint8_t* w_codes, const uint16_t* w_scale,
-                          int64_t N, int64_t K, int allow_a8, int8_t* a_q_ws, float* a_scale_ws,
+                          int64_t N, int64_t K, int a8_flags, int8_t* a_q_ws, float* a_scale_ws,
                           int8_t* w_i8_ws, int out_dt, void* y, void* workspace, int64_t workspace_bytes,
                           void* stream);
+
+/*
+ * Measurement helper: a plain streaming read of `bytes` of device memory (a
+ * multiple of 16), nothing computed but a fold of the bytes into one word per
+ * workgroup written to sink [nq_stream_read_sink_words()].  It gives the HBM
+ * read rate that the weight-streaming GEMVs are compared against: [int8 card,
+ * "Files"] notes that decode is bandwidth bound.
+ * Errors: bytes % 16 != 0 -> NQ_ERR_SHAPE.
+ */
+int64_t nq_stream_read_sink_words(void);
+nq_status nq_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
+/*
+ * Q3 / Q5 / Q6 group-64 codes as int8 (the A8 routes' weights).  [int8 card,
+ * "What changes"]: in prefill the low-bit codes feed the int8 matrix units
+ * exactly.
+ *   fmt   NQ_W_Q3G64_F16S, NQ_W_Q5G64_F16S or NQ_W_Q6G64_F16S
+ *   codes [N][K b / 8] bytes (see nq_wfmt), 16-byte aligned
+ *   out   [N][K] int8, each code sign-extended
+ * Errors: K % 64 != 0 -> NQ_ERR_SHAPE; another fmt -> NQ_ERR_FORMAT.
+ */
+nq_status nq_unpack_qbits_to_int8(int fmt, const uint8_t* codes, int64_t N, int64_t K, int8_t* out,
+                                  void* stream);
+
+/*
+ * The Q3 / Q5 / Q6 group-64 projection as an engine step runs it, routed by
+ * nq_route(T, a8_flags) ([RTX5080 card, "Quantization profile"]; [int8 card,
+ * "What changes"]).  BF16 route: nq_gemv_qgroup(fmt, ...).  A8 routes:
+ * nq_quantize_act_int8_g64 into a_q_ws [T][K] and a_scale_ws [T][K/64], the
+ * codes widened by nq_unpack_qbits_to_int8 into w_i8_ws [N][K], then
+ * nq_gemm_w8a8_g64 (prefill) or the A8 decode GEMV on the widened codes
+ * (decode), both with the same FP16 scales.  The A8 workspaces are needed only
+ * when an A8 route is taken; `workspace` is the optional GEMV workspace.
+ * Errors: K % 256 != 0 -> NQ_ERR_SHAPE; another fmt -> NQ_ERR_FORMAT.
+ */
+nq_status nq_linear_qbits_g64(int fmt, const uint16_t* x, int64_t T, const uint8_t* w_codes,
+                              const uint16_t* w_scale, int64_t N, int64_t K, int a8_flags, int8_t* a_q_ws,
+                              float* a_scale_ws, int8_t* w_i8_ws, int out_dt, void* y, void* workspace,
+                              int64_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnq.so")
 
-SOURCES = ["nq_abi.cpp", "nq_convert.hip", "nq_gemv.hip", "nq_gemm.hip"]
+SOURCES = ["nq_abi.cpp", "nq_convert.hip", "nq_gemv.hip", "nq_gemv_fp8row.hip", "nq_gemv_mxfp8.hip",
+           "nq_gemv_bf16.hip", "nq_gemv_q8g64.hip", "nq_gemv_q4g64.hip", "nq_gemv_q8g32.hip", "nq_gemv_a8.hip",
+           "nq_gemv_qb.hip", "nq_gemm.hip",
+           "nq_probe.hip"]
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -40,7 +43,7 @@ def hipcc():
 # Per-source additions.  The GEMM and the GEMVs keep their MFMA results in
 # ordinary VGPRs, where the FP32 rescales read them directly (no copy out of
 # AGPRs per element; measured 5-12 % faster on the grouped GEMV formats).
-EXTRA = {"nq_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "nq_gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {name: ["-mllvm", "-amdgpu-mfma-vgpr-form"] for name in SOURCES if name.startswith(("nq_gemm", "nq_gemv"))}
 
 
 def _compile(src, verbose):

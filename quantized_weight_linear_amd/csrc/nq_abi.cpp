@@ -41,6 +41,9 @@ int group_of(int fmt) {
         case NQ_W_Q8G64_F16S: return 64;
         case NQ_W_MXFP8_G32: return 32;
         case NQ_W_BF16: return 1;
+        case NQ_W_Q3G64_F16S: return 64;
+        case NQ_W_Q5G64_F16S: return 64;
+        case NQ_W_Q6G64_F16S: return 64;
         default: return 0;
     }
 }
@@ -181,12 +184,21 @@ nq_status nq_quantize_act_fp8_row(const uint16_t* x, int64_t M, int64_t K, uint8
 
 int64_t nq_gemv_workspace_bytes(int fmt, int64_t T, int64_t N, int64_t K) {
     if (T < 0 || N < 0 || K < 0) return 0;
+    if (nq::qbits_of(fmt)) return nq::gemv_qbits_workspace_bytes(T, N, K);
     return nq::gemv_workspace_bytes(fmt, T, N, K);
 }
 
 }  // extern "C"
 
 namespace {
+
+// Q3 / Q5 / Q6: whole 256-column chunks and 32-bit buffer offsets for the
+// codes (rows padded to 16), activations and scales.
+bool qbits_shape_ok(int fmt, int64_t T, int64_t N, int64_t K) {
+    const int64_t b = nq::qbits_of(fmt);
+    return K % 256 == 0 && (N + 15) / 16 * 16 * (K * b / 8) < ((int64_t)1 << 31) &&
+           (T < 64 ? T : 64) * K * 2 < ((int64_t)1 << 31) && N * (K / 64) * 2 < ((int64_t)1 << 31);
+}
 
 // The packed layout needs whole 128-column chunks and 32-bit buffer offsets.
 bool packed_shape_ok(int64_t N, int64_t K) {
@@ -221,6 +233,7 @@ nq_status gemv_qgroup_impl(int fmt, const void* w_codes, const void* w_scales, c
     if (!out_ok(out_dt)) return NQ_ERR_FORMAT;
     if (T < 0 || N < 0 || K < 0 || workspace_bytes < 0 || K % gs != 0) return NQ_ERR_SHAPE;
     if (packed && !packed_shape_ok(N, K)) return NQ_ERR_SHAPE;
+    if (nq::qbits_of(fmt) && !qbits_shape_ok(fmt, T, N, K)) return NQ_ERR_SHAPE;
     NQ_TRY(need(w_codes, N * K));
     if (fmt != NQ_W_BF16) NQ_TRY(need(w_scales, N * K));
     NQ_TRY(need(x, T * K));
@@ -231,6 +244,10 @@ nq_status gemv_qgroup_impl(int fmt, const void* w_codes, const void* w_scales, c
     NQ_TRY(align_ok(y));
     NQ_TRY(align_ok(workspace));
     if (T == 0 || N == 0) return NQ_OK;
+    if (nq::qbits_of(fmt))
+        return from_hip(nq::launch_gemv_qbits(fmt, w_codes, reinterpret_cast<const uint16_t*>(w_scales), x, T, N, K,
+                                              out_dt == NQ_OUT_BF16, y, workspace, workspace ? workspace_bytes : 0,
+                                              as_stream(stream), packed));
     return from_hip(nq::launch_gemv(fmt, w_codes, fmt == NQ_W_BF16 ? nullptr : w_scales, x, T, N, K,
                                     out_dt == NQ_OUT_BF16, y, workspace, workspace ? workspace_bytes : 0,
                                     as_stream(stream), packed));
@@ -270,6 +287,7 @@ nq_status nq_gemv_qgroup_packed(int fmt, const void* w_packed, const void* w_sca
 
 int64_t nq_packed_weight_bytes(int fmt, int64_t N, int64_t K) {
     if (N < 0 || K < 0 || (fmt != -1 && group_of(fmt) == 0)) return 0;
+    if (nq::qbits_of(fmt)) return (N + 15) / 16 * 16 * (K * nq::qbits_of(fmt) / 8);
     return nq::packed_weight_bytes(internal_fmt(fmt), N, K);
 }
 
@@ -282,6 +300,10 @@ nq_status nq_pack_weights(int fmt, const void* w, int64_t N, int64_t K, void* w_
     NQ_TRY(align_ok(w));
     NQ_TRY(align_ok(w_packed));
     if (N == 0) return NQ_OK;
+    if (nq::qbits_of(fmt)) {
+        if (!qbits_shape_ok(fmt, 0, N, K)) return NQ_ERR_SHAPE;
+        return from_hip(nq::launch_pack_qbits(fmt, w, N, K, w_packed, as_stream(stream)));
+    }
     return from_hip(nq::launch_pack_weights(internal_fmt(fmt), w, N, K, w_packed, as_stream(stream)));
 }
 
@@ -329,19 +351,90 @@ nq_status nq_gemm_fp8row(const uint16_t* x, const uint8_t* w, const uint16_t* w_
     return from_hip(nq::launch_gemm_fp8(a_codes, a_scale, w, w_scale, M, N, K, out_dt == NQ_OUT_BF16, y, s));
 }
 
-int nq_route(int64_t T, int allow_a8) { return (allow_a8 && T >= 129) ? NQ_ROUTE_A8 : NQ_ROUTE_BF16; }
+}  // extern "C"
+
+namespace {
+
+nq_status gemv_a8_impl(int fmt, const void* w, const uint16_t* w_scale, const int8_t* a_q, const float* a_scale,
+                       int64_t T, int64_t N, int64_t K, int out_dt, void* y, void* workspace, int64_t workspace_bytes,
+                       void* stream, bool packed) {
+    if (fmt != NQ_W_Q8G64_F16S && fmt != NQ_W_Q4G64_F16S) return NQ_ERR_FORMAT;
+    if (!out_ok(out_dt)) return NQ_ERR_FORMAT;
+    if (T < 0 || N < 0 || K < 0 || workspace_bytes < 0 || K % 256 != 0) return NQ_ERR_SHAPE;
+    if (T * K >= ((int64_t)1 << 31) || N * (K / 64) * 2 >= ((int64_t)1 << 31)) return NQ_ERR_SHAPE;
+    if (packed && !packed_shape_ok(N, K)) return NQ_ERR_SHAPE;
+    NQ_TRY(need(w, N * K));
+    NQ_TRY(need(w_scale, N * K));
+    NQ_TRY(need(a_q, T * K));
+    NQ_TRY(need(a_scale, T * K));
+    NQ_TRY(need(y, T * N));
+    NQ_TRY(align_ok(w));
+    NQ_TRY(align_ok(w_scale));
+    NQ_TRY(align_ok(a_q));
+    NQ_TRY(align_ok(a_scale));
+    NQ_TRY(align_ok(y));
+    NQ_TRY(align_ok(workspace));
+    if (T == 0 || N == 0) return NQ_OK;
+    return from_hip(nq::launch_gemv_a8(fmt == NQ_W_Q8G64_F16S ? nq::W_Q8G64 : nq::W_Q4G64, w, w_scale, a_q, a_scale,
+                                       T, N, K, out_dt == NQ_OUT_BF16, y, workspace, workspace ? workspace_bytes : 0,
+                                       as_stream(stream), packed));
+}
+
+}  // namespace
+
+extern "C" {
+
+nq_status nq_gemv_a8_g64(int fmt, const void* w_codes, const uint16_t* w_scale, const int8_t* a_q,
+                         const float* a_scale, int64_t T, int64_t N, int64_t K, int out_dt, void* y, void* workspace,
+                         int64_t workspace_bytes, void* stream) {
+    return gemv_a8_impl(fmt, w_codes, w_scale, a_q, a_scale, T, N, K, out_dt, y, workspace, workspace_bytes, stream,
+                        false);
+}
+
+nq_status nq_gemv_a8_g64_packed(int fmt, const void* w_packed, const uint16_t* w_scale, const int8_t* a_q,
+                                const float* a_scale, int64_t T, int64_t N, int64_t K, int out_dt, void* y,
+                                void* workspace, int64_t workspace_bytes, void* stream) {
+    return gemv_a8_impl(fmt, w_packed, w_scale, a_q, a_scale, T, N, K, out_dt, y, workspace, workspace_bytes, stream,
+                        true);
+}
+
+int64_t nq_stream_read_sink_words(void) { return nq::stream_read_blocks(); }
+
+nq_status nq_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+    if (bytes < 0 || bytes % 16 != 0) return NQ_ERR_SHAPE;
+    NQ_TRY(need(src, bytes));
+    NQ_TRY(need(sink, bytes));
+    NQ_TRY(align_ok(src));
+    NQ_TRY(align_ok(sink));
+    if (bytes == 0) return NQ_OK;
+    return from_hip(nq::launch_stream_read(src, bytes, sink, as_stream(stream)));
+}
+
+int nq_route(int64_t T, int a8_flags) {
+    if ((a8_flags & NQ_A8_PREFILL) && T >= 129) return NQ_ROUTE_A8;
+    if ((a8_flags & NQ_A8_DECODE) && T <= 128) return NQ_ROUTE_A8_DECODE;
+    return NQ_ROUTE_BF16;
+}
+
+int64_t nq_gemv_a8_workspace_bytes(int64_t T, int64_t N, int64_t K) {
+    if (T < 0 || N < 0 || K < 0) return 0;
+    return nq::gemv_a8_workspace_bytes(T, N, K);
+}
 
 nq_status nq_linear_q8g64(const uint16_t* x, int64_t T, const int8_t* w_q, const uint16_t* w_scale, int64_t N,
                           int64_t K, int allow_a8, int8_t* a_q_ws, float* a_scale_ws, int out_dt, void* y,
                           void* workspace, int64_t workspace_bytes, void* stream) {
     if (T < 0 || N < 0 || K < 0 || K % 64 != 0 || workspace_bytes < 0) return NQ_ERR_SHAPE;
     if (!out_ok(out_dt)) return NQ_ERR_FORMAT;
-    const bool a8 = nq_route(T, allow_a8) == NQ_ROUTE_A8;
+    const int route = nq_route(T, allow_a8);
+    const bool a8 = route == NQ_ROUTE_A8;
+    const bool a8d = route == NQ_ROUTE_A8_DECODE;
+    if (a8d && K % 256 != 0) return NQ_ERR_SHAPE;
     NQ_TRY(need(x, T * K));
     NQ_TRY(need(w_q, N * K));
     NQ_TRY(need(w_scale, N * K));
     NQ_TRY(need(y, T * N));
-    if (a8) {
+    if (a8 || a8d) {
         NQ_TRY(need(a_q_ws, T * K));
         NQ_TRY(need(a_scale_ws, T * K));
         NQ_TRY(align_ok(a_q_ws));
@@ -354,11 +447,15 @@ nq_status nq_linear_q8g64(const uint16_t* x, int64_t T, const int8_t* w_q, const
     NQ_TRY(align_ok(workspace));
     if (T == 0 || N == 0) return NQ_OK;
     hipStream_t s = as_stream(stream);
-    if (!a8)
+    if (!a8 && !a8d)
         return from_hip(nq::launch_gemv(nq::W_Q8G64, w_q, w_scale, x, T, N, K, out_dt == NQ_OUT_BF16, y, workspace,
                                         workspace ? workspace_bytes : 0, s, false));
     hipError_t e = nq::launch_quantize_int8_g64(x, T, K, a_q_ws, a_scale_ws, s);
     if (e != hipSuccess) return NQ_ERR_HIP;
+    if (a8d)
+        return from_hip(nq::launch_gemv_a8(nq::W_Q8G64, w_q, w_scale, a_q_ws, a_scale_ws, T, N, K,
+                                           out_dt == NQ_OUT_BF16, y, workspace, workspace ? workspace_bytes : 0, s,
+                                           false));
     return from_hip(nq::launch_gemm_w8a8(a_q_ws, a_scale_ws, w_q, w_scale, T, N, K, out_dt == NQ_OUT_BF16, y,
                                          nullptr, s));
 }
@@ -368,12 +465,70 @@ nq_status nq_linear_q4g64(const uint16_t* x, int64_t T, const uint8_t* w_codes, 
                           void* y, void* workspace, int64_t workspace_bytes, void* stream) {
     if (T < 0 || N < 0 || K < 0 || K % 64 != 0 || workspace_bytes < 0) return NQ_ERR_SHAPE;
     if (!out_ok(out_dt)) return NQ_ERR_FORMAT;
-    const bool a8 = nq_route(T, allow_a8) == NQ_ROUTE_A8;
+    const int route = nq_route(T, allow_a8);
+    const bool a8 = route == NQ_ROUTE_A8;
+    const bool a8d = route == NQ_ROUTE_A8_DECODE;
+    if (a8d && K % 256 != 0) return NQ_ERR_SHAPE;
     NQ_TRY(need(x, T * K));
     NQ_TRY(need(w_codes, N * K));
     NQ_TRY(need(w_scale, N * K));
     NQ_TRY(need(y, T * N));
+    if (a8 || a8d) {
+        NQ_TRY(need(a_q_ws, T * K));
+        NQ_TRY(need(a_scale_ws, T * K));
+        NQ_TRY(align_ok(a_q_ws));
+        NQ_TRY(align_ok(a_scale_ws));
+    }
     if (a8) {
+        NQ_TRY(need(w_i8_ws, N * K));
+        NQ_TRY(align_ok(w_i8_ws));
+    }
+    NQ_TRY(align_ok(x));
+    NQ_TRY(align_ok(w_codes));
+    NQ_TRY(align_ok(w_scale));
+    NQ_TRY(align_ok(y));
+    NQ_TRY(align_ok(workspace));
+    if (T == 0 || N == 0) return NQ_OK;
+    hipStream_t s = as_stream(stream);
+    if (!a8 && !a8d)
+        return from_hip(nq::launch_gemv(nq::W_Q4G64, w_codes, w_scale, x, T, N, K, out_dt == NQ_OUT_BF16, y,
+                                        workspace, workspace ? workspace_bytes : 0, s, false));
+    hipError_t e = nq::launch_quantize_int8_g64(x, T, K, a_q_ws, a_scale_ws, s);
+    if (e != hipSuccess) return NQ_ERR_HIP;
+    if (a8d)
+        return from_hip(nq::launch_gemv_a8(nq::W_Q4G64, w_codes, w_scale, a_q_ws, a_scale_ws, T, N, K,
+                                           out_dt == NQ_OUT_BF16, y, workspace, workspace ? workspace_bytes : 0, s,
+                                           false));
+    e = nq::launch_unpack_q4_to_int8(w_codes, N, K, w_i8_ws, s);
+    if (e != hipSuccess) return NQ_ERR_HIP;
+    return from_hip(nq::launch_gemm_w8a8(a_q_ws, a_scale_ws, w_i8_ws, w_scale, T, N, K, out_dt == NQ_OUT_BF16, y,
+                                         nullptr, s));
+}
+
+nq_status nq_unpack_qbits_to_int8(int fmt, const uint8_t* codes, int64_t N, int64_t K, int8_t* out, void* stream) {
+    if (!nq::qbits_of(fmt)) return NQ_ERR_FORMAT;
+    if (N < 0 || K < 0 || K % 64 != 0) return NQ_ERR_SHAPE;
+    NQ_TRY(need(codes, N * K));
+    NQ_TRY(need(out, N * K));
+    NQ_TRY(align_ok(codes));
+    NQ_TRY(align_ok(out));
+    if (N == 0 || K == 0) return NQ_OK;
+    return from_hip(nq::launch_unpack_qbits_to_int8(fmt, codes, N, K, out, as_stream(stream)));
+}
+
+nq_status nq_linear_qbits_g64(int fmt, const uint16_t* x, int64_t T, const uint8_t* w_codes, const uint16_t* w_scale,
+                              int64_t N, int64_t K, int a8_flags, int8_t* a_q_ws, float* a_scale_ws, int8_t* w_i8_ws,
+                              int out_dt, void* y, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (!nq::qbits_of(fmt)) return NQ_ERR_FORMAT;
+    if (!out_ok(out_dt)) return NQ_ERR_FORMAT;
+    if (T < 0 || N < 0 || K < 0 || workspace_bytes < 0 || K % 256 != 0) return NQ_ERR_SHAPE;
+    if (!qbits_shape_ok(fmt, T, N, K)) return NQ_ERR_SHAPE;
+    const int route = nq_route(T, a8_flags);
+    NQ_TRY(need(x, T * K));
+    NQ_TRY(need(w_codes, N * K));
+    NQ_TRY(need(w_scale, N * K));
+    NQ_TRY(need(y, T * N));
+    if (route != NQ_ROUTE_BF16) {
         NQ_TRY(need(a_q_ws, T * K));
         NQ_TRY(need(a_scale_ws, T * K));
         NQ_TRY(need(w_i8_ws, N * K));
@@ -388,15 +543,18 @@ nq_status nq_linear_q4g64(const uint16_t* x, int64_t T, const uint8_t* w_codes, 
     NQ_TRY(align_ok(workspace));
     if (T == 0 || N == 0) return NQ_OK;
     hipStream_t s = as_stream(stream);
-    if (!a8)
-        return from_hip(nq::launch_gemv(nq::W_Q4G64, w_codes, w_scale, x, T, N, K, out_dt == NQ_OUT_BF16, y,
-                                        workspace, workspace ? workspace_bytes : 0, s, false));
+    const bool bf16 = out_dt == NQ_OUT_BF16;
+    if (route == NQ_ROUTE_BF16)
+        return from_hip(nq::launch_gemv_qbits(fmt, w_codes, w_scale, x, T, N, K, bf16, y, workspace,
+                                              workspace ? workspace_bytes : 0, s, false));
     hipError_t e = nq::launch_quantize_int8_g64(x, T, K, a_q_ws, a_scale_ws, s);
     if (e != hipSuccess) return NQ_ERR_HIP;
-    e = nq::launch_unpack_q4_to_int8(w_codes, N, K, w_i8_ws, s);
+    e = nq::launch_unpack_qbits_to_int8(fmt, w_codes, N, K, w_i8_ws, s);
     if (e != hipSuccess) return NQ_ERR_HIP;
-    return from_hip(nq::launch_gemm_w8a8(a_q_ws, a_scale_ws, w_i8_ws, w_scale, T, N, K, out_dt == NQ_OUT_BF16, y,
-                                         nullptr, s));
+    if (route == NQ_ROUTE_A8_DECODE)
+        return from_hip(nq::launch_gemv_a8(nq::W_Q8G64, w_i8_ws, w_scale, a_q_ws, a_scale_ws, T, N, K, bf16, y,
+                                           workspace, workspace ? workspace_bytes : 0, s, false));
+    return from_hip(nq::launch_gemm_w8a8(a_q_ws, a_scale_ws, w_i8_ws, w_scale, T, N, K, bf16, y, nullptr, s));
 }
 
 }  // extern "C"

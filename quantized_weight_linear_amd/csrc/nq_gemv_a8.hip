@@ -1,0 +1,266 @@
+// A8 decode GEMV: the W8A8 arithmetic at decode sizes (T <= 64 per pass).
+//   y[t][n] = sum_g P[t][n][g] * (ws[n][g] * as[t][g]),
+//   P[t][n][g] = sum_{k in g} aq[t][k] * wq[n][k]   (int32, exact),
+// with int8 activation codes aq and FP32 scales as from the per-token-per-64
+// quantizer, and Q8 group-64 (or Q4 group-64) weights with FP16 scales.
+//
+// One wave per 16-row block (a 64-thread workgroup): the wave owns its rows
+// over its K range outright, so nothing is shared through LDS and no barrier
+// runs.  A chunk is 256 columns = 4 groups of 64.  For group q of chunk c,
+// lane 16 g + i holds the 16 codes k = 256 c + 64 q + 16 g + [0, 16) of row i
+// (the A fragment of one v_mfma_i32_16x16x64_i8) and the same 16 activation
+// codes of token i of the token block (the B fragment): A and B use the same
+// lane -> k assignment, so each MFMA forms one group's exact dot products.
+// Q8 codes feed the MFMA as stored (no decode).  Q4 codes are widened to
+// bytes in registers as biased values u = q + 8 (0..15, two masks and two
+// byte permutes per 8 codes), and the bias is removed inside the matrix unit:
+// a first MFMA of a fragment of -8s against the activations starts the
+// accumulator at C - 8 sum(aq), so the second one ends at C + P exactly.
+// C is the bit pattern of 1.5 * 2^23 (0x4B400000): read as a float, the
+// int32 result is 12582912 + P exactly (|P| <= 64 * 127 * 127 < 2^22), and
+// the rescale is two FP32 FMAs per element and group:
+//     X = fma(D, ws, -12582912 ws)  (= P ws, rounded once),
+//     acc = fma(X, as, acc).
+// Weights stream from HBM into a register ring, 3 chunks deep (2 with three or
+// four token blocks); activation codes and scales come through buffer loads
+// whose out-of-range offsets read zero (tokens t >= T).  With a workspace the
+// K range is split over workgroups and the partial sums are exchanged as in
+// the BF16-activation GEMV (device-coherent stores and loads, a counter per
+// row block, the last arriver sums the splits in order: deterministic).
+#include "nq_wave_gemv.h"
+
+namespace nq {
+
+constexpr int A8_KC = WG_KC;
+constexpr unsigned A8_BUF_FLAGS = WG_BUF_FLAGS;
+
+template <int FMT>
+struct A8Piece {
+    static constexpr int PB = FMT == W_Q4G64 ? 8 : 16;                  // bytes per lane and group
+    static constexpr int64_t BLOCK_CHUNK = (int64_t)4 * 64 * PB;          // packed bytes per (chunk, row block)
+    using T = typename std::conditional<FMT == W_Q4G64, uint2, uint4>::type;
+};
+
+template <int NCB>
+constexpr int a8_depth() {
+    return NCB >= 3 ? 2 : 3;
+}
+
+template <int FMT, int NCB>
+struct A8Chunk {
+    typename A8Piece<FMT>::T w[4];      // group q's weight piece
+    uint4 x[4][NCB];                    // group q's activation codes, token block cb
+    uint4 as[NCB];                      // the token's activation scales of the chunk's 4 groups
+    uint2 ws[4];                        // row 4 lg + e: FP16 weight scales of the 4 groups
+};
+
+// 16 Q4 codes (row-major: two's complement nibbles, element 2j low in byte j;
+// packed: biased nibbles, code 2i at bits 4i and 2i + 1 at bits 16 + 4i of
+// each word) -> 16 bytes u = q + 8 in element order.
+template <bool PK>
+__device__ __forceinline__ v4i q4_to_biased_bytes(uint2 p) {
+    uint32_t d[2] = {p.x, p.y};
+    uint32_t o[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t u = PK ? d[h] : (d[h] ^ 0x88888888u);
+        const uint32_t m = u & 0x0F0F0F0Fu, n = (u >> 4) & 0x0F0F0F0Fu;
+        if (PK) {   // m = [u0 u4 u1 u5], n = [u2 u6 u3 u7]
+            o[2 * h] = __builtin_amdgcn_perm(n, m, 0x06040200u);
+            o[2 * h + 1] = __builtin_amdgcn_perm(n, m, 0x07050301u);
+        } else {    // m = [u0 u2 u4 u6], n = [u1 u3 u5 u7]
+            o[2 * h] = __builtin_amdgcn_perm(n, m, 0x05010400u);
+            o[2 * h + 1] = __builtin_amdgcn_perm(n, m, 0x07030602u);
+        }
+    }
+    return v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+}
+
+template <int FMT, int NCB, bool PK>
+__global__ __launch_bounds__(64) void gemv_a8_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ wsc,
+                                                     const int8_t* __restrict__ aq, const float* __restrict__ asc,
+                                                     int T, int N, int64_t K, int chunks_per_split, int splits,
+                                                     float* __restrict__ partial, unsigned* __restrict__ counters,
+                                                     int bf16_out, void* __restrict__ y) {
+    using P = A8Piece<FMT>;
+    constexpr int D = a8_depth<NCB>();
+    const int lane = threadIdx.x;
+    const int li = lane & 15, lg = lane >> 4;
+    const int rb = blockIdx.x;
+    const int split = blockIdx.y;
+    const int64_t nrb = ((int64_t)N + 15) / 16;
+    const int64_t G = K / 64;
+    const int64_t total_chunks = K / A8_KC;
+    const int64_t c_begin = (int64_t)split * chunks_per_split;
+    int nch = (int)(total_chunks - c_begin);
+    if (nch > chunks_per_split) nch = chunks_per_split;
+
+    // weights: the lane's row (row-major; rows past N clamped, never written)
+    // or its piece of the row block (packed)
+    int64_t row = (int64_t)rb * 16 + li;
+    if (row > N - 1) row = N - 1;
+    const uint8_t* wrow = PK ? w + (int64_t)rb * P::BLOCK_CHUNK + (int64_t)lane * P::PB
+                             : w + row * (FMT == W_Q4G64 ? K / 2 : K) + (int64_t)lg * P::PB;
+    const int64_t wcstride = PK ? nrb * P::BLOCK_CHUNK : A8_KC * P::PB / 16;
+    const int64_t wqstride = PK ? 64 * P::PB : 4 * P::PB;
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)aq, (short)0, (int)((int64_t)T * K), A8_BUF_FLAGS);
+    const __amdgpu_buffer_rsrc_t ar =
+        __builtin_amdgcn_make_buffer_rsrc((void*)asc, (short)0, (int)((int64_t)T * G * 4), A8_BUF_FLAGS);
+    const __amdgpu_buffer_rsrc_t sr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)wsc, (short)0, (int)((int64_t)N * G * 2), A8_BUF_FLAGS);
+    int xoff[NCB], aoff[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int t = cb * 16 + li;
+        xoff[cb] = (int)((int64_t)t * K + 16 * lg);
+        aoff[cb] = (int)((int64_t)t * G * 4);
+    }
+    int soff[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) soff[e] = (int)(((int64_t)rb * 16 + 4 * lg + e) * G * 2);
+
+    A8Chunk<FMT, NCB> ring[D];
+    auto load = [&](int slot, int64_t c) {
+        A8Chunk<FMT, NCB>& r = ring[slot];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            r.w[q] = *reinterpret_cast<const typename P::T*>(wrow + c * wcstride + q * wqstride);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+                r.x[q][cb] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[cb] + (int)(c * A8_KC) + 64 * q, 0, 0));
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+            r.as[cb] = __builtin_bit_cast(uint4,
+                                          __builtin_amdgcn_raw_buffer_load_b128(ar, aoff[cb] + (int)(c * 16), 0, 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            r.ws[e] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(sr, soff[e] + (int)(c * 8), 0, 0));
+    };
+
+    v4f acc[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+    const v4i bias = {0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000};
+    const v4i neg8 = {(int)0xF8F8F8F8u, (int)0xF8F8F8F8u, (int)0xF8F8F8F8u, (int)0xF8F8F8F8u};
+
+    auto compute = [&](int slot) {
+        const A8Chunk<FMT, NCB>& r = ring[slot];
+        float wsf[4][4], nb[4][4];     // [e][q]
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t s01 = r.ws[e].x, s23 = r.ws[e].y;
+            wsf[e][0] = f16_bits_to_f32(s01 & 0xFFFFu);
+            wsf[e][1] = f16_bits_to_f32(s01 >> 16);
+            wsf[e][2] = f16_bits_to_f32(s23 & 0xFFFFu);
+            wsf[e][3] = f16_bits_to_f32(s23 >> 16);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) nb[e][q] = -12582912.0f * wsf[e][q];   // exact: FP16 times 1.5 2^23
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            v4i a;
+            if constexpr (FMT == W_Q4G64) a = q4_to_biased_bytes<PK>(r.w[q]);
+            else a = __builtin_bit_cast(v4i, r.w[q]);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                const v4i b = __builtin_bit_cast(v4i, r.x[q][cb]);
+                v4i d;
+                if constexpr (FMT == W_Q4G64) {
+                    d = __builtin_amdgcn_mfma_i32_16x16x64_i8(neg8, b, bias, 0, 0, 0);
+                    d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, d, 0, 0, 0);
+                } else {
+                    d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, bias, 0, 0, 0);
+                }
+                const float sa = __uint_as_float(q == 0 ? r.as[cb].x : q == 1 ? r.as[cb].y : q == 2 ? r.as[cb].z
+                                                                                                  : r.as[cb].w);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x = fmaf(__int_as_float(d[e]), wsf[e][q], nb[e][q]);
+                    acc[cb][e] = fmaf(x, sa, acc[cb][e]);
+                }
+            }
+        }
+    };
+
+    if (nch > 0) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) load(d, c_begin + min(d, nch - 1));
+        int c = 0;
+        for (; c + D <= nch; c += D) {
+#pragma unroll
+            for (int u = 0; u < D; ++u) {
+                compute(u);
+                load(u, c_begin + min(c + u + D, nch - 1));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < D - 1; ++u)
+            if (c + u < nch) compute(u);
+    }
+
+    wave_finish<NCB>(acc, T, N, rb, split, splits, partial, counters, bf16_out, y);
+}
+
+// ---------------------------------------------------------------------------
+// Host side (plan: plan_wave).
+// ---------------------------------------------------------------------------
+int64_t gemv_a8_workspace_bytes(int64_t T, int64_t N, int64_t K) {
+    if (T <= 0 || N <= 0 || K <= 0 || K % A8_KC != 0) return 0;
+    return wave_workspace(plan_wave(N, K), T < 64 ? T : 64);
+}
+
+template <int FMT, int NCB, bool PK>
+static void launch_a8_ncb(const WavePlan& p, const void* w, const uint16_t* wsc, const int8_t* aq, const float* asc,
+                          int Tc, int64_t N, int64_t K, bool bf16_out, void* y, float* partial, unsigned* counters,
+                          hipStream_t stream) {
+    gemv_a8_kernel<FMT, NCB, PK><<<dim3((unsigned)p.rbs, (unsigned)p.splits), 64, 0, stream>>>(
+        reinterpret_cast<const uint8_t*>(w), wsc, aq, asc, Tc, (int)N, K, p.chunks_per_split, p.splits, partial,
+        counters, bf16_out ? 1 : 0, y);
+}
+
+template <int FMT, bool PK>
+static void launch_a8_fmt(const WavePlan& p, const void* w, const uint16_t* wsc, const int8_t* aq, const float* asc,
+                          int Tc, int64_t N, int64_t K, bool bf16_out, void* y, float* partial, unsigned* counters,
+                          hipStream_t stream) {
+    switch ((Tc + 15) / 16) {
+        case 1: launch_a8_ncb<FMT, 1, PK>(p, w, wsc, aq, asc, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+        case 2: launch_a8_ncb<FMT, 2, PK>(p, w, wsc, aq, asc, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+        case 3: launch_a8_ncb<FMT, 3, PK>(p, w, wsc, aq, asc, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+        default: launch_a8_ncb<FMT, 4, PK>(p, w, wsc, aq, asc, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+    }
+}
+
+hipError_t launch_gemv_a8(int fmt, const void* w, const uint16_t* w_scale, const int8_t* aq, const float* asc,
+                          int64_t T, int64_t N, int64_t K, bool bf16_out, void* y, void* workspace,
+                          int64_t workspace_bytes, hipStream_t stream, bool packed) {
+    if (T == 0 || N == 0) return hipSuccess;
+    if (K % A8_KC != 0 || (fmt != W_Q8G64 && fmt != W_Q4G64)) return hipErrorInvalidValue;
+    const int64_t G = K / 64;
+    const size_t ybytes = bf16_out ? 2 : 4;
+    for (int64_t t0 = 0; t0 < T; t0 += 64) {
+        const int Tc = (int)((T - t0) < 64 ? (T - t0) : 64);
+        float* partial;
+        unsigned* counters;
+        const WavePlan p = plan_wave_with(N, K, Tc, workspace, workspace_bytes, &partial, &counters);
+        const int8_t* aqc = aq + t0 * K;
+        const float* ac = asc + t0 * G;
+        void* yc = reinterpret_cast<char*>(y) + t0 * N * ybytes;
+        if (fmt == W_Q8G64) {
+            if (packed) launch_a8_fmt<W_Q8G64, true>(p, w, w_scale, aqc, ac, Tc, N, K, bf16_out, yc, partial, counters, stream);
+            else launch_a8_fmt<W_Q8G64, false>(p, w, w_scale, aqc, ac, Tc, N, K, bf16_out, yc, partial, counters, stream);
+        } else {
+            if (packed) launch_a8_fmt<W_Q4G64, true>(p, w, w_scale, aqc, ac, Tc, N, K, bf16_out, yc, partial, counters, stream);
+            else launch_a8_fmt<W_Q4G64, false>(p, w, w_scale, aqc, ac, Tc, N, K, bf16_out, yc, partial, counters, stream);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace nq

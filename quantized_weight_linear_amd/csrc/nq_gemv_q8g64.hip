@@ -1,0 +1,10 @@
+// Decode GEMV kernels instantiated for one weight format (W_Q8G64).
+#include "nq_gemv_kernels.h"
+
+namespace nq {
+
+NQ_GEMV_FMT_ENTRY(gemv_launch_q8g64) {
+    launch_fmt<W_Q8G64>(p, packed, w, scales, x, Tc, N, K, bf16_out, y, partial, counters, stream);
+}
+
+}  // namespace nq

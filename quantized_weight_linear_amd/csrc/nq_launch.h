@@ -7,7 +7,8 @@
 namespace nq {
 
 // Weight formats, same values as nq_wfmt plus the row-scaled FP8 format.
-enum WFmt { W_Q4G64 = 0, W_Q8G32 = 1, W_Q8G64 = 2, W_MXFP8 = 3, W_BF16 = 4, W_FP8ROW = 5 };
+enum WFmt { W_Q4G64 = 0, W_Q8G32 = 1, W_Q8G64 = 2, W_MXFP8 = 3, W_BF16 = 4, W_Q3G64 = 5, W_Q5G64 = 6, W_Q6G64 = 7,
+            W_FP8ROW = 8 };
 
 hipError_t launch_decode_mxfp8(const uint32_t* words, const uint8_t* e8, int64_t N, int64_t K, bool bf16_out,
                                void* out, hipStream_t stream);
@@ -35,6 +36,24 @@ hipError_t launch_gemv(int fmt, const void* w, const void* scales, const uint16_
 int64_t packed_weight_bytes(int fmt, int64_t N, int64_t K);
 hipError_t launch_pack_weights(int fmt, const void* src, int64_t N, int64_t K, void* dst, hipStream_t stream);
 
+// A8 decode GEMV (int8 activation codes and scales from launch_quantize_int8_g64,
+// Q8 or Q4 group-64 weights, row-major or packed as for launch_gemv).
+int64_t gemv_a8_workspace_bytes(int64_t T, int64_t N, int64_t K);
+hipError_t launch_gemv_a8(int fmt, const void* w, const uint16_t* w_scale, const int8_t* aq, const float* asc,
+                          int64_t T, int64_t N, int64_t K, bool bf16_out, void* y, void* workspace,
+                          int64_t workspace_bytes, hipStream_t stream, bool packed);
+
+// Q3 / Q5 / Q6 group-64 (dense little-endian bit streams): the BF16-activation
+// GEMV (row-major or packed), the packing, and the widening to int8.
+int qbits_of(int fmt);   // 3, 5, 6, or 0 for other formats
+int64_t gemv_qbits_workspace_bytes(int64_t T, int64_t N, int64_t K);
+hipError_t launch_gemv_qbits(int fmt, const void* w, const uint16_t* w_scale, const uint16_t* x, int64_t T, int64_t N,
+                             int64_t K, bool bf16_out, void* y, void* workspace, int64_t workspace_bytes,
+                             hipStream_t stream, bool packed);
+hipError_t launch_pack_qbits(int fmt, const void* src, int64_t N, int64_t K, void* dst, hipStream_t stream);
+hipError_t launch_unpack_qbits_to_int8(int fmt, const uint8_t* codes, int64_t N, int64_t K, int8_t* out,
+                                       hipStream_t stream);
+
 hipError_t launch_gemm_w8a8(const int8_t* a_q, const float* a_scale, const int8_t* w_q, const uint16_t* w_scale,
                             int64_t M, int64_t N, int64_t K, bool bf16_out, void* y, int32_t* group_sums,
                             hipStream_t stream);
@@ -42,5 +61,10 @@ hipError_t launch_gemm_fp8(const uint8_t* a_codes, const float* a_scale, const u
                            int64_t M, int64_t N, int64_t K, bool bf16_out, void* y, hipStream_t stream);
 
 int device_cu_count();
+
+// Plain streaming read of `bytes` (a multiple of 16) from src; one word per
+// workgroup (stream_read_blocks() of them) goes to sink.
+int stream_read_blocks();
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
 
 }  // namespace nq

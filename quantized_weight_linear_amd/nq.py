@@ -18,7 +18,9 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnq.so")
 NQ_OK, NQ_ERR_NULL, NQ_ERR_SHAPE, NQ_ERR_ALIGN, NQ_ERR_FORMAT, NQ_ERR_RANGE, NQ_ERR_HIP = range(7)
 NQ_OUT_F32, NQ_OUT_BF16 = 0, 1
 NQ_W_Q4G64_F16S, NQ_W_Q8G32_F16S, NQ_W_Q8G64_F16S, NQ_W_MXFP8_G32, NQ_W_BF16 = range(5)
-NQ_ROUTE_BF16, NQ_ROUTE_A8 = 0, 1
+NQ_W_Q3G64_F16S, NQ_W_Q5G64_F16S, NQ_W_Q6G64_F16S = 5, 6, 7
+NQ_ROUTE_BF16, NQ_ROUTE_A8, NQ_ROUTE_A8_DECODE = 0, 1, 2
+NQ_A8_PREFILL, NQ_A8_DECODE = 1, 2
 
 # every entry point the header declares: name -> (restype, argtypes)
 _P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
@@ -41,6 +43,13 @@ SIGNATURES = {
     "nq_pack_weights": (_I, [_I, _P, _I64, _I64, _P, _P]),
     "nq_gemv_fp8row_packed": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I64, _P]),
     "nq_gemv_qgroup_packed": (_I, [_I, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I64, _P]),
+    "nq_stream_read_sink_words": (_I64, []),
+    "nq_unpack_qbits_to_int8": (_I, [_I, _P, _I64, _I64, _P, _P]),
+    "nq_linear_qbits_g64": (_I, [_I, _P, _I64, _P, _P, _I64, _I64, _I, _P, _P, _P, _I, _P, _P, _I64, _P]),
+    "nq_gemv_a8_workspace_bytes": (_I64, [_I64, _I64, _I64]),
+    "nq_gemv_a8_g64": (_I, [_I, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I64, _P]),
+    "nq_gemv_a8_g64_packed": (_I, [_I, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I64, _P]),
+    "nq_stream_read": (_I, [_P, _I64, _P, _P]),
     "nq_linear_q8g64": (_I, [_P, _I64, _P, _P, _I64, _I64, _I, _P, _P, _I, _P, _P, _I64, _P]),
     "nq_unpack_q4_to_int8": (_I, [_P, _I64, _I64, _P, _P]),
     "nq_linear_q4g64": (_I, [_P, _I64, _P, _P, _I64, _I64, _I, _P, _P, _P, _I, _P, _P, _I64, _P]),
@@ -87,9 +96,11 @@ def _size(t, nbytes, what):
         raise ValueError(f"{what}: {have} bytes given, {int(nbytes)} needed")
 
 
-_CODE_BYTES = {NQ_W_Q4G64_F16S: 0.5, NQ_W_Q8G32_F16S: 1, NQ_W_Q8G64_F16S: 1, NQ_W_MXFP8_G32: 1, NQ_W_BF16: 2}
+_CODE_BYTES = {NQ_W_Q4G64_F16S: 0.5, NQ_W_Q8G32_F16S: 1, NQ_W_Q8G64_F16S: 1, NQ_W_MXFP8_G32: 1, NQ_W_BF16: 2,
+               NQ_W_Q3G64_F16S: 3 / 8, NQ_W_Q5G64_F16S: 5 / 8, NQ_W_Q6G64_F16S: 6 / 8}
 _SCALE_BYTES = {NQ_W_Q4G64_F16S: 2 / 64, NQ_W_Q8G32_F16S: 2 / 32, NQ_W_Q8G64_F16S: 2 / 64,
-                NQ_W_MXFP8_G32: 1 / 32, NQ_W_BF16: 0}
+                NQ_W_MXFP8_G32: 1 / 32, NQ_W_BF16: 0, NQ_W_Q3G64_F16S: 2 / 64, NQ_W_Q5G64_F16S: 2 / 64,
+                NQ_W_Q6G64_F16S: 2 / 64}
 
 
 def _stream(*tensors):
@@ -112,8 +123,15 @@ def nq_abi_version():
     return lib().nq_abi_version()
 
 
-def nq_route(T, allow_a8):
-    return lib().nq_route(T, 1 if allow_a8 else 0)
+def _a8_flags(a8):
+    """True / False (prefill A8 allowed or not) or an int of NQ_A8_* flags."""
+    if isinstance(a8, bool):
+        return NQ_A8_PREFILL if a8 else 0
+    return int(a8)
+
+
+def nq_route(T, a8):
+    return lib().nq_route(T, _a8_flags(a8))
 
 
 def nq_gemv_workspace_bytes(fmt, T, N, K):
@@ -208,10 +226,10 @@ def nq_gemm_fp8row(x, w, w_scale, M, N, K, a_codes, a_scale, y):
 def nq_linear_q8g64(x, T, w_q, w_scale, N, K, allow_a8, a_q_ws, a_scale_ws, y, workspace=None):
     _size(x, 2 * T * K, "x"); _size(w_q, N * K, "w_q"); _size(w_scale, 2 * N * (K // 64), "w_scale")
     _size(y, T * N * y.element_size(), "y")
-    if nq_route(T, allow_a8) == NQ_ROUTE_A8:
+    if nq_route(T, allow_a8) != NQ_ROUTE_BF16:
         _size(a_q_ws, T * K, "a_q_ws"); _size(a_scale_ws, 4 * T * (K // 64), "a_scale_ws")
     wp, wb = _ws(workspace)
-    _check(lib().nq_linear_q8g64(_ptr(x), T, _ptr(w_q), _ptr(w_scale), N, K, 1 if allow_a8 else 0,
+    _check(lib().nq_linear_q8g64(_ptr(x), T, _ptr(w_q), _ptr(w_scale), N, K, _a8_flags(allow_a8),
                                  _ptr(a_q_ws), _ptr(a_scale_ws), _out_dt(y), _ptr(y), wp, wb,
                                  _stream(x, w_q)), "nq_linear_q8g64")
 
@@ -224,13 +242,50 @@ def nq_unpack_q4_to_int8(codes, N, K, out):
 def nq_linear_q4g64(x, T, w_codes, w_scale, N, K, allow_a8, a_q_ws, a_scale_ws, w_i8_ws, y, workspace=None):
     _size(x, 2 * T * K, "x"); _size(w_codes, N * K // 2, "w_codes"); _size(w_scale, 2 * N * (K // 64), "w_scale")
     _size(y, T * N * y.element_size(), "y")
-    if nq_route(T, allow_a8) == NQ_ROUTE_A8:
+    route = nq_route(T, allow_a8)
+    if route != NQ_ROUTE_BF16:
         _size(a_q_ws, T * K, "a_q_ws"); _size(a_scale_ws, 4 * T * (K // 64), "a_scale_ws")
+    if route == NQ_ROUTE_A8:
         _size(w_i8_ws, N * K, "w_i8_ws")
     wp, wb = _ws(workspace)
-    _check(lib().nq_linear_q4g64(_ptr(x), T, _ptr(w_codes), _ptr(w_scale), N, K, 1 if allow_a8 else 0,
+    _check(lib().nq_linear_q4g64(_ptr(x), T, _ptr(w_codes), _ptr(w_scale), N, K, _a8_flags(allow_a8),
                                  _ptr(a_q_ws), _ptr(a_scale_ws), _ptr(w_i8_ws), _out_dt(y), _ptr(y), wp, wb,
                                  _stream(x, w_codes)), "nq_linear_q4g64")
+
+
+def nq_gemv_a8_workspace_bytes(T, N, K):
+    return lib().nq_gemv_a8_workspace_bytes(T, N, K)
+
+
+def alloc_gemv_a8_workspace(T, N, K, device):
+    """A zero-filled workspace big enough for nq_gemv_a8_* at (T, N, K), or None."""
+    n = nq_gemv_a8_workspace_bytes(T, N, K)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n > 0 else None
+
+
+def _gemv_a8(name, fmt, w, w_scale, a_q, a_scale, T, N, K, y, workspace, packed):
+    wbytes = nq_packed_weight_bytes(fmt, N, K) if packed else N * K * _CODE_BYTES.get(fmt, 1)
+    _size(w, wbytes, "w"); _size(w_scale, 2 * N * (K // 64), "w_scale")
+    _size(a_q, T * K, "a_q"); _size(a_scale, 4 * T * (K // 64), "a_scale"); _size(y, T * N * y.element_size(), "y")
+    wp, wb = _ws(workspace)
+    _check(getattr(lib(), name)(fmt, _ptr(w), _ptr(w_scale), _ptr(a_q), _ptr(a_scale), T, N, K, _out_dt(y), _ptr(y),
+                                wp, wb, _stream(w, a_q)), name)
+
+
+def nq_gemv_a8_g64(fmt, w_codes, w_scale, a_q, a_scale, T, N, K, y, workspace=None):
+    _gemv_a8("nq_gemv_a8_g64", fmt, w_codes, w_scale, a_q, a_scale, T, N, K, y, workspace, False)
+
+
+def nq_gemv_a8_g64_packed(fmt, w_packed, w_scale, a_q, a_scale, T, N, K, y, workspace=None):
+    _gemv_a8("nq_gemv_a8_g64_packed", fmt, w_packed, w_scale, a_q, a_scale, T, N, K, y, workspace, True)
+
+
+def nq_stream_read(src, sink):
+    """Read all of src (a device tensor, 16-byte multiple) once; sink is an
+    int32 device tensor of at least nq_stream_read_sink_words() elements."""
+    nbytes = src.numel() * src.element_size()
+    _size(sink, 4 * lib().nq_stream_read_sink_words(), "sink")
+    _check(lib().nq_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(src)), "nq_stream_read")
 
 
 NQ_FMT_FP8ROW = -1     # the format code the packing calls use for row-scaled FP8
@@ -263,3 +318,21 @@ def nq_gemv_qgroup_packed(fmt, w_packed, w_scales, x, T, N, K, y, workspace=None
     wp, wb = _ws(workspace)
     _check(lib().nq_gemv_qgroup_packed(fmt, _ptr(w_packed), _ptr(w_scales), _ptr(x), T, N, K, _out_dt(y),
                                        _ptr(y), wp, wb, _stream(w_packed, x)), "nq_gemv_qgroup_packed")
+
+
+def nq_unpack_qbits_to_int8(fmt, codes, N, K, out):
+    _size(codes, N * K * _CODE_BYTES[fmt], "codes"); _size(out, N * K, "out")
+    _check(lib().nq_unpack_qbits_to_int8(fmt, _ptr(codes), N, K, _ptr(out), _stream(codes, out)),
+           "nq_unpack_qbits_to_int8")
+
+
+def nq_linear_qbits_g64(fmt, x, T, w_codes, w_scale, N, K, a8, a_q_ws, a_scale_ws, w_i8_ws, y, workspace=None):
+    _size(x, 2 * T * K, "x"); _size(w_codes, N * K * _CODE_BYTES[fmt], "w_codes")
+    _size(w_scale, 2 * N * (K // 64), "w_scale"); _size(y, T * N * y.element_size(), "y")
+    if nq_route(T, a8) != NQ_ROUTE_BF16:
+        _size(a_q_ws, T * K, "a_q_ws"); _size(a_scale_ws, 4 * T * (K // 64), "a_scale_ws")
+        _size(w_i8_ws, N * K, "w_i8_ws")
+    wp, wb = _ws(workspace)
+    _check(lib().nq_linear_qbits_g64(fmt, _ptr(x), T, _ptr(w_codes), _ptr(w_scale), N, K, _a8_flags(a8),
+                                     _ptr(a_q_ws), _ptr(a_scale_ws), _ptr(w_i8_ws), _out_dt(y), _ptr(y), wp, wb,
+                                     _stream(x, w_codes)), "nq_linear_qbits_g64")

@@ -954,3 +954,297 @@ def test_linear_q4g64_prefill_full_size_sampled():
     qa, sa = M.quantize_act_int8_g64(x[rows])
     ref = M.gemm_w8a8_g64(qa, sa, M.unpack_q4(d["codes"][cols], k), d["scales"][cols])
     assert rel_fro(host(y, np.float32)[np.ix_(rows, cols)], ref) <= FP32_TOL
+
+
+# ---------------------------------------------------------------------------
+# A8 decode GEMV (int8 activations at decode sizes, W8A8 arithmetic)
+# ---------------------------------------------------------------------------
+
+A8_FMTS = [("q8g64", nq.NQ_W_Q8G64_F16S), ("q4g64", nq.NQ_W_Q4G64_F16S)]
+
+
+def _a8_weights(name, n, k, seed):
+    d = W.grouped(name, n, k, seed)
+    wq = d["codes"] if name == "q8g64" else M.unpack_q4(d["codes"], k).astype(np.int8)   # oracle's int codes
+    return d["codes"], wq, d["scales"]
+
+
+def _run_a8(fmt, codes_d, pk, ws_d, qa, sa, n, k, wmode, out="f32"):
+    t = qa.shape[0]
+    y = empty((t, n), np.float32 if out == "f32" else np.uint16)
+    wsp = nq.alloc_gemv_a8_workspace(t, n, k, DEV) if wmode else None
+    if pk is None:
+        nq.nq_gemv_a8_g64(fmt, codes_d, ws_d, dev(qa), dev(sa), t, n, k, y, wsp)
+    else:
+        nq.nq_gemv_a8_g64_packed(fmt, pk, ws_d, dev(qa), dev(sa), t, n, k, y, wsp)
+    got = host(y, np.float32 if out == "f32" else np.uint16)
+    assert _counters_zero(wsp, n)
+    return got
+
+
+@pytest.mark.parametrize("name,fmt", A8_FMTS)
+@pytest.mark.parametrize("n,k", [(1000, 1536), (200, 1280), (70, 256), (16448, 768), (33, 5120)])
+@pytest.mark.parametrize("t", [1, 8, 17, 33, 64, 65])
+def test_gemv_a8(name, fmt, n, k, t):
+    codes, wq, ws = _a8_weights(name, n, k, n + k + t)
+    x = W.bf16_normal(W.rng(140, t + k), (t, k), outlier_p=0.01)
+    qa, sa = M.quantize_act_int8_g64(x)
+    ref = M.gemm_w8a8_g64(qa, sa, wq, ws)
+    cd, sd = dev(codes), dev(ws)
+    pk = _pack_dev(fmt, cd, n, k)
+    outs = []
+    for p in (None, pk):
+        for wmode in (False, True):
+            g32 = _run_a8(fmt, cd, p, sd, qa, sa, n, k, wmode)
+            assert rel_fro(g32, ref) <= FP32_TOL, (p is None, wmode)
+            outs.append(g32)
+    g16 = _run_a8(fmt, cd, pk, sd, qa, sa, n, k, True, "bf16")
+    assert np.array_equal(g16, bf16_of_f32_bits(outs[3]))
+    assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))   # packed = row-major
+    assert np.array_equal(outs[1].view(np.uint32), outs[3].view(np.uint32))
+
+
+@pytest.mark.parametrize("name,fmt", A8_FMTS)
+def test_gemv_a8_group_sums_exact(name, fmt):
+    """One nonzero group per token and power-of-two scales: every output is
+    P * ws * as exactly, so the int32 group sums are checked bit for bit."""
+    n, k, t = 130, 1024, 20
+    codes, wq, _ = _a8_weights(name, n, k, 5)
+    g = W.rng(141, 0)
+    qa = W.int8_uniform(g, (t, k))
+    keep = g.integers(0, k // 64, t)
+    for i in range(t):
+        m = np.zeros(k, bool)
+        m[64 * keep[i]:64 * keep[i] + 64] = True
+        qa[i, ~m] = 0
+    sa = np.exp2(g.integers(-8, -2, (t, k // 64))).astype(np.float32).view(np.uint32)
+    ws = np.exp2(g.integers(-9, -5, (n, k // 64))).astype(np.float16).view(np.uint16)
+    cd, sd = dev(codes), dev(ws)
+    ref, sums = M.gemm_w8a8_g64(qa, sa, wq, ws, return_sums=True)
+    for p in (None, _pack_dev(fmt, cd, n, k)):
+        got = _run_a8(fmt, cd, p, sd, qa, sa, n, k, True)
+        assert np.array_equal(got.astype(np.float64), ref)
+    # the one nonzero group's sum, recovered exactly from the output
+    ti, ni = np.arange(t)[:, None], np.arange(n)[None, :]
+    denom = F.f16_decode(ws)[ni, keep[:, None]] * F.f32_decode(sa)[ti, keep[:, None]]
+    assert np.array_equal(ref / denom, sums[ti, ni, keep[:, None]].astype(np.float64))
+
+
+# The A8 decode rows bench.py times: 17408 x 5120 and 5120 x 17408, packed,
+# T = 1, 8, 33, every row against the oracle.
+@pytest.mark.slow
+@pytest.mark.parametrize("name,fmt", A8_FMTS)
+@pytest.mark.parametrize("n,k", [(W.FFN, W.HIDDEN), (W.HIDDEN, W.FFN)])
+def test_gemv_a8_full_size(name, fmt, n, k):
+    codes, wq, ws = _a8_weights(name, n, k, 0)
+    cd, sd = dev(codes), dev(ws)
+    pk = _pack_dev(fmt, cd, n, k)
+    x33 = W.activations(33, k, workload=4, tensor=50)
+    qa, sa = M.quantize_act_int8_g64(x33)
+    ref33 = M.gemm_w8a8_g64(qa, sa, wq, ws)
+    for t in (1, 8, 33):
+        g32 = _run_a8(fmt, cd, pk, sd, qa[:t], sa[:t], n, k, True)
+        assert rel_fro(g32, ref33[:t]) <= FP32_TOL, (name, t)
+        gr = _run_a8(fmt, cd, None, sd, qa[:t], sa[:t], n, k, True)
+        assert np.array_equal(g32.view(np.uint32), gr.view(np.uint32)), (name, t)
+
+
+@pytest.mark.parametrize("t", [1, 33, 128, 129])
+def test_linear_a8_decode_route(t):
+    """Routed Q8 and Q4 group-64 projections with the A8 decode flag (and the
+    prefill one): below 129 tokens the quantizer + A8 decode GEMV, from 129 on
+    the W8A8 GEMM; bit-identical to the direct calls."""
+    n, k = 200, 1280
+    flags = nq.NQ_A8_PREFILL | nq.NQ_A8_DECODE
+    assert nq.nq_route(t, flags) == (nq.NQ_ROUTE_A8 if t >= 129 else nq.NQ_ROUTE_A8_DECODE)
+    x = W.bf16_normal(W.rng(142, t), (t, k))
+    xd = dev(x)
+    aq, asc = empty((t, k), np.int8), empty((t, k // 64), np.float32)
+    for name, fmt in A8_FMTS:
+        codes, wq, ws = _a8_weights(name, n, k, t + 1)
+        cd, sd = dev(codes), dev(ws)
+        y = empty((t, n), np.float32)
+        wsp = nq.alloc_gemv_a8_workspace(t, n, k, DEV)
+        if name == "q8g64":
+            nq.nq_linear_q8g64(xd, t, cd, sd, n, k, flags, aq, asc, y, wsp)
+            ref = M.linear_w8g64(x, codes, ws, True, True)
+        else:
+            wi8 = empty((n, k), np.int8)
+            nq.nq_linear_q4g64(xd, t, cd, sd, n, k, flags, aq, asc, wi8, y, wsp)
+            ref = M.linear_q4g64(x, codes, ws, True, True)
+        got = host(y, np.float32)
+        assert rel_fro(got, ref) <= FP32_TOL, name
+        direct = empty((t, n), np.float32)
+        if t >= 129:
+            if name == "q8g64":
+                nq.nq_gemm_w8a8_g64(aq, asc, cd, sd, t, n, k, direct)
+            else:
+                nq.nq_gemm_w8a8_g64(aq, asc, wi8, sd, t, n, k, direct)
+        else:
+            nq.nq_gemv_a8_g64(fmt, cd, sd, aq, asc, t, n, k, direct, wsp)
+        assert np.array_equal(host(direct, np.uint32), got.view(np.uint32)), name
+
+
+# ---------------------------------------------------------------------------
+# Q3 / Q5 / Q6 group-64 (dense little-endian bit streams)
+# ---------------------------------------------------------------------------
+
+QB_FMTS = [("q3g64", nq.NQ_W_Q3G64_F16S, 3), ("q5g64", nq.NQ_W_Q5G64_F16S, 5), ("q6g64", nq.NQ_W_Q6G64_F16S, 6)]
+
+
+def _qb_gemv(fmt, cd, pk, sd, x, n, k, wmode, out="f32"):
+    t = x.shape[0]
+    y = empty((t, n), np.float32 if out == "f32" else np.uint16)
+    wsp = nq.alloc_gemv_workspace(fmt, t, n, k, DEV) if wmode else None
+    if pk is None:
+        nq.nq_gemv_qgroup(fmt, cd, sd, dev(x), t, n, k, y, wsp)
+    else:
+        nq.nq_gemv_qgroup_packed(fmt, pk, sd, dev(x), t, n, k, y, wsp)
+    got = host(y, np.float32 if out == "f32" else np.uint16)
+    assert _counters_zero(wsp, n)
+    return got
+
+
+@pytest.mark.parametrize("name,fmt,bits", QB_FMTS)
+@pytest.mark.parametrize("n,k", [(1000, 1536), (200, 1280), (70, 256), (16448, 768), (33, 5120)])
+@pytest.mark.parametrize("t", [1, 17, 33, 65])
+def test_gemv_qbits(name, fmt, bits, n, k, t):
+    d = W.grouped(name, n, k, seed=n + t)
+    x = W.bf16_normal(W.rng(150, t + k), (t, k))
+    ref = M.gemv_qgroup(name, d["codes"], d["scales"], x)
+    cd, sd = dev(d["codes"]), dev(d["scales"])
+    pk = _pack_dev(fmt, cd, n, k)
+    outs = []
+    for p in (None, pk):
+        for wmode in (False, True):
+            g = _qb_gemv(fmt, cd, p, sd, x, n, k, wmode)
+            assert rel_fro(g, ref) <= FP32_TOL, (p is None, wmode)
+            outs.append(g)
+    g16 = _qb_gemv(fmt, cd, pk, sd, x, n, k, True, "bf16")
+    assert np.array_equal(g16, bf16_of_f32_bits(outs[3]))
+    assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))      # packed = row-major
+    assert np.array_equal(outs[1].view(np.uint32), outs[3].view(np.uint32))
+
+
+@pytest.mark.parametrize("name,fmt,bits", QB_FMTS)
+def test_gemv_qbits_one_hot_is_exact(name, fmt, bits):
+    """One-hot activations give the decoded codes times their scales, exactly."""
+    n, k = 70, 512
+    d = W.grouped(name, n, k, seed=3)
+    cols = [0, 1, 15, 16, 63, 64, 200, 511]
+    x = np.zeros((len(cols), k), np.float32)
+    for i, c in enumerate(cols):
+        x[i, c] = 1.0
+    xb = W.to_bf16_bits(x)
+    cd, sd = dev(d["codes"]), dev(d["scales"])
+    ref = M.gemv_qgroup(name, d["codes"], d["scales"], xb)
+    for p in (None, _pack_dev(fmt, cd, n, k)):
+        assert np.array_equal(_qb_gemv(fmt, cd, p, sd, xb, n, k, True).astype(np.float64), ref)
+
+
+def _unpack_qbits_packed_reference(packed, bits, n, k):
+    """Invert the packed layout with numpy: per (chunk, row block), pieces of
+    16 bytes (and an 8-byte tail) lane after lane; a lane's 8 b bytes are the
+    2 b bytes of groups q = 0..3 of its row (lane 16 g + i: row i, codes
+    64 q + 16 g + [0, 16))."""
+    nrb, chunks, lb = -(-n // 16), k // 256, 8 * bits
+    out = np.zeros((nrb * 16, k * bits // 8), np.uint8)
+    blk = packed.reshape(chunks, nrb, 64 * lb)
+    np16 = lb // 16
+    for c in range(chunks):
+        for rb in range(nrb):
+            b = blk[c, rb]
+            lanes = np.zeros((64, lb), np.uint8)
+            for p in range(np16):
+                lanes[:, 16 * p:16 * p + 16] = b[1024 * p:1024 * p + 1024].reshape(64, 16)
+            if lb % 16:
+                lanes[:, 16 * np16:] = b[1024 * np16:1024 * np16 + 512].reshape(64, 8)
+            for lane in range(64):
+                i, g = lane & 15, lane >> 4
+                for q in range(4):
+                    off = bits * (32 * c + 8 * q + 2 * g)
+                    out[rb * 16 + i, off:off + 2 * bits] = lanes[lane, 2 * bits * q:2 * bits * (q + 1)]
+    return out[:n]
+
+
+@pytest.mark.parametrize("name,fmt,bits", QB_FMTS)
+@pytest.mark.parametrize("n,k", [(70, 512), (16, 256)])
+def test_pack_qbits_is_the_documented_permutation(name, fmt, bits, n, k):
+    src = W.rng(151, n + bits).integers(0, 256, (n, k * bits // 8), dtype=np.int16).astype(np.uint8)
+    pk = _pack_dev(fmt, dev(src), n, k)
+    assert pk.numel() == -(-n // 16) * 16 * k * bits // 8
+    assert np.array_equal(_unpack_qbits_packed_reference(host(pk, np.uint8), bits, n, k), src)
+
+
+@pytest.mark.parametrize("name,fmt,bits", QB_FMTS)
+@pytest.mark.parametrize("n,k", [(3, 64), (257, 1024), (130, 5120)])
+def test_unpack_qbits_to_int8(name, fmt, bits, n, k):
+    codes = W.grouped(name, n, k, seed=k)["codes"]
+    out = empty((n, k), np.int8)
+    nq.nq_unpack_qbits_to_int8(fmt, dev(codes), n, k, out)
+    assert np.array_equal(host(out, np.int8).astype(np.int64), M.unpack_qbits(codes, k, bits))
+
+
+@pytest.mark.parametrize("t", [1, 33, 129])
+@pytest.mark.parametrize("name,fmt,bits", QB_FMTS)
+def test_linear_qbits_route(name, fmt, bits, t):
+    """Routed Q3/Q5/Q6 projections: BF16 GEMV, A8 decode (flag) and A8 prefill
+    routes against the oracle, each bit-identical to its direct calls."""
+    n, k = 200, 1280
+    d = W.grouped(name, n, k, seed=t)
+    x = W.bf16_normal(W.rng(152, t), (t, k))
+    xd, cd, sd = dev(x), dev(d["codes"]), dev(d["scales"])
+    for flags, a8d in ((nq.NQ_A8_PREFILL, False), (nq.NQ_A8_PREFILL | nq.NQ_A8_DECODE, True)):
+        y = empty((t, n), np.float32)
+        aq, asc, wi8 = empty((t, k), np.int8), empty((t, k // 64), np.float32), empty((n, k), np.int8)
+        wsp = nq.alloc_gemv_workspace(fmt, t, n, k, DEV)
+        wsa = nq.alloc_gemv_a8_workspace(t, n, k, DEV)
+        ws_use = wsa if (a8d and t < 129) else wsp
+        nq.nq_linear_qbits_g64(fmt, xd, t, cd, sd, n, k, flags, aq, asc, wi8, y, ws_use)
+        got = host(y, np.float32)
+        assert rel_fro(got, M.linear_qbits_g64(name, x, d["codes"], d["scales"], True, a8d)) <= FP32_TOL, flags
+        direct = empty((t, n), np.float32)
+        if t >= 129:
+            assert np.array_equal(host(wi8, np.int8).astype(np.int64), M.unpack_qbits(d["codes"], k, bits))
+            nq.nq_gemm_w8a8_g64(aq, asc, wi8, sd, t, n, k, direct)
+        elif a8d:
+            nq.nq_gemv_a8_g64(nq.NQ_W_Q8G64_F16S, wi8, sd, aq, asc, t, n, k, direct, wsa)
+        else:
+            nq.nq_gemv_qgroup(fmt, cd, sd, xd, t, n, k, direct, wsp)
+        assert np.array_equal(host(direct, np.uint32), got.view(np.uint32)), flags
+
+
+# The Q5 / Q3 rows bench.py times: 17408 x 5120 and 5120 x 17408, packed, T =
+# 1, 8, 33, every row (the oracle runs in row bands).
+@pytest.mark.slow
+@pytest.mark.parametrize("name,fmt,bits", QB_FMTS[:2])
+@pytest.mark.parametrize("n,k", [(W.FFN, W.HIDDEN), (W.HIDDEN, W.FFN)])
+def test_gemv_qbits_full_size(name, fmt, bits, n, k):
+    d = W.grouped(name, n, k)
+    cd, sd = dev(d["codes"]), dev(d["scales"])
+    pk = _pack_dev(fmt, cd, n, k)
+    x33 = W.activations(33, k, workload=4, tensor=50)
+    parts = _banded(lambda a, b: M.gemv_qgroup(name, d["codes"][a:b], d["scales"][a:b], x33), n)
+    ref33 = np.concatenate(parts, axis=1)
+    for t in (1, 8, 33):
+        g32, g16, _ = _gemv_both_layouts(fmt, cd, pk, sd, x33[:t].copy(), n, k)
+        assert rel_fro(g32, ref33[:t]) <= FP32_TOL, (name, t)
+        assert rel_fro(F.bf16_decode(g16), ref33[:t]) <= BF16_TOL, (name, t)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,fmt,bits", QB_FMTS[:2])
+def test_linear_qbits_prefill_full_size_sampled(name, fmt, bits):
+    """Q5 / Q3 weights on the A8 route at the prefill chunk: 1792 x 17408 x 5120."""
+    m, n, k = W.PREFILL_CHUNK, W.FFN, W.HIDDEN
+    d = W.grouped(name, n, k)
+    x = W.w8a8_prefill(n=64)["x"]
+    y = empty((m, n), np.float32)
+    aq, asc, wi8 = empty((m, k), np.int8), empty((m, k // 64), np.float32), empty((n, k), np.int8)
+    nq.nq_linear_qbits_g64(fmt, dev(x), m, dev(d["codes"]), dev(d["scales"]), n, k, nq.NQ_A8_PREFILL, aq, asc, wi8, y)
+    rows = _sampled_rows(m, 14, count=24)
+    cols = _sampled_rows(n, 15, count=48)
+    assert np.array_equal(host(wi8, np.int8)[cols].astype(np.int64), M.unpack_qbits(d["codes"][cols], k, bits))
+    qa, sa = M.quantize_act_int8_g64(x[rows])
+    ref = M.gemm_w8a8_g64(qa, sa, M.unpack_qbits(d["codes"][cols], k, bits), d["scales"][cols])
+    assert rel_fro(host(y, np.float32)[np.ix_(rows, cols)], ref) <= FP32_TOL
