@@ -51,7 +51,8 @@ typedef enum {
     NQ_ERR_ALIGN = 3,   /* a pointer is not 16-byte aligned */
     NQ_ERR_FORMAT = 4,  /* an enum value is unknown */
     NQ_ERR_RANGE = 5,   /* a row range is empty or outside [0, N] */
-    NQ_ERR_HIP = 6      /* the HIP runtime reported an error when enqueuing */
+    NQ_ERR_HIP = 6,     /* the HIP runtime reported an error when enqueuing */
+    NQ_ERR_SCRATCH = 7  /* the call needs more scratch than the library's static array holds */
 } nq_status;
 
 typedef enum { NQ_OUT_F32 = 0, NQ_OUT_BF16 = 1 } nq_out;
@@ -236,6 +237,27 @@ nq_status nq_gemv_fp8row_packed(const uint8_t* w_packed, const uint16_t* w_scale
 nq_status nq_gemv_qgroup_packed(int fmt, const void* w_packed, const void* w_scales, const uint16_t* x,
                                 int64_t T, int64_t N, int64_t K, int out_dt, void* y, void* workspace,
                                 int64_t workspace_bytes, void* stream);
+
+/*
+ * nq_gemv_fp8row_packed without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The K-split / spread partials and
+ * counters go to a static device array of NQ_GEMV_STATIC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends; this call
+ * allocates nothing and calls no allocating routine.  Each call first clears
+ * the counters it uses with a small fill kernel on `stream` (no memset node),
+ * then runs the same kernels and plan as nq_gemv_fp8row_packed with a
+ * workspace: the results are bit-identical to that call's.  All calls on one
+ * GPU share its array, which keeps the last call's partials: calls that
+ * overlap on one GPU (different streams, or threads) race and must not be
+ * issued.
+ * Errors: as nq_gemv_fp8row_packed; NQ_ERR_SCRATCH when the call's plan needs
+ * more than NQ_GEMV_STATIC_SCRATCH_BYTES (nq_gemv_workspace_bytes(-1, T, N, K)
+ * tells in advance), checked before anything is enqueued.
+ */
+#define NQ_GEMV_STATIC_SCRATCH_BYTES (8 << 20)
+nq_status nq_gemv_fp8row_packed_noalloc(const uint8_t* w_packed, const uint16_t* w_scale, const uint16_t* x,
+                                        int64_t T, int64_t N, int64_t K, int out_dt, void* y, void* stream);
 
 /*
  * Decode GEMV on grouped weights (see nq_wfmt for layouts), BF16 activations,

@@ -82,6 +82,7 @@ const char* nq_status_string(int status) {
         case NQ_ERR_FORMAT: return "unknown format or output type";
         case NQ_ERR_RANGE: return "row range out of bounds";
         case NQ_ERR_HIP: return "HIP runtime error";
+        case NQ_ERR_SCRATCH: return "the call needs more scratch than the library's static array holds";
         default: return "unknown status";
     }
 }
@@ -283,6 +284,25 @@ nq_status nq_gemv_qgroup_packed(int fmt, const void* w_packed, const void* w_sca
                                 void* stream) {
     return gemv_qgroup_impl(fmt, w_packed, w_scales, x, T, N, K, out_dt, y, workspace, workspace_bytes, stream,
                             true);
+}
+
+nq_status nq_gemv_fp8row_packed_noalloc(const uint8_t* w_packed, const uint16_t* w_scale, const uint16_t* x,
+                                        int64_t T, int64_t N, int64_t K, int out_dt, void* y, void* stream) {
+    if (T < 0 || N < 0 || K < 0) return NQ_ERR_SHAPE;
+    if (!packed_shape_ok(N, K)) return NQ_ERR_SHAPE;
+    if (!out_ok(out_dt)) return NQ_ERR_FORMAT;
+    NQ_TRY(need(w_packed, N * K));
+    NQ_TRY(need(w_scale, N));
+    NQ_TRY(need(x, T * K));
+    NQ_TRY(need(y, T * N));
+    NQ_TRY(align_ok(w_packed));
+    NQ_TRY(align_ok(w_scale));
+    NQ_TRY(align_ok(x));
+    NQ_TRY(align_ok(y));
+    if (T == 0 || N == 0) return NQ_OK;
+    if (nq::gemv_workspace_bytes(nq::W_FP8ROW, T, N, K) > nq::GEMV_STATIC_SCRATCH_BYTES) return NQ_ERR_SCRATCH;
+    return from_hip(nq::launch_gemv_noalloc(nq::W_FP8ROW, w_packed, w_scale, x, T, N, K, out_dt == NQ_OUT_BF16, y,
+                                            as_stream(stream), true));
 }
 
 int64_t nq_packed_weight_bytes(int fmt, int64_t N, int64_t K) {

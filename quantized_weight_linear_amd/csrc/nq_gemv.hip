@@ -2,6 +2,8 @@
 // workgroups), the workspace size, the packed weight layout, and the entry
 // that runs a call in passes of at most 64 tokens.  The kernels are in
 // nq_gemv_kernels.h, instantiated per format in nq_gemv_<format>.hip.
+#include <mutex>
+
 #include "nq_gemv_kernels.h"
 
 namespace nq {
@@ -341,5 +343,60 @@ hipError_t launch_gemv(int fmt, const void* w, const void* scales, const uint16_
     return hipSuccess;
 }
 
+
+// ---------------------------------------------------------------------------
+// GEMV without a caller workspace, for callers that cannot allocate (graph
+// capture, tight serving loops): the K-split / spread partials and counters
+// live in a fixed device array of GEMV_STATIC_SCRATCH_BYTES, one per GPU,
+// held until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol): its device
+// address is looked up once per device with hipGetSymbolAddress and kept.
+// Every call clears the counters it will use with a fill kernel first (no
+// memset node, so the call can be captured in a graph); the partials need no
+// clearing.  Calls that overlap on one GPU share the array and race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[GEMV_STATIC_SCRATCH_BYTES];
+
+__global__ __launch_bounds__(256) void zero_words_kernel(unsigned* __restrict__ p, int n) {
+    for (int i = (int)(blockIdx.x * 256 + threadIdx.x); i < n; i += (int)(gridDim.x * 256)) p[i] = 0u;
+}
+
+static hipError_t scratch_address(void** out) {
+    static std::mutex mu;
+    static void* ptrs[64] = {nullptr};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> g(mu);
+    if (ptrs[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        ptrs[dev] = p;
+    }
+    *out = ptrs[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_gemv_noalloc(int fmt, const void* w, const void* scales, const uint16_t* x, int64_t T, int64_t N,
+                               int64_t K, bool bf16_out, void* y, hipStream_t stream, bool packed) {
+    if (T == 0 || N == 0) return hipSuccess;
+    const int64_t need = gemv_workspace_bytes(fmt, T, N, K);
+    if (need > GEMV_STATIC_SCRATCH_BYTES) return hipErrorInvalidValue;   // validated by the caller
+    void* ws = nullptr;
+    if (need > 0) {
+        hipError_t e = scratch_address(&ws);
+        if (e != hipSuccess) return e;
+        // the counters (one per row tile) lead the workspace and must start at zero
+        const int n = (int)((N + GV_ROWS - 1) / GV_ROWS);
+        zero_words_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(reinterpret_cast<unsigned*>(ws), n);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return launch_gemv(fmt, w, scales, x, T, N, K, bf16_out, y, ws, need > 0 ? GEMV_STATIC_SCRATCH_BYTES : 0, stream,
+                       packed);
+}
 
 }  // namespace nq

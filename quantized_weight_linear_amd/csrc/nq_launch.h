@@ -34,6 +34,12 @@ hipError_t launch_gemv(int fmt, const void* w, const void* scales, const uint16_
                        int64_t K, bool bf16_out, void* y, void* workspace, int64_t workspace_bytes,
                        hipStream_t stream, bool packed);
 int64_t packed_weight_bytes(int fmt, int64_t N, int64_t K);
+// launch_gemv with the library's own per-device scratch array instead of a
+// caller workspace (no allocation); the caller checks gemv_workspace_bytes
+// against GEMV_STATIC_SCRATCH_BYTES first.
+constexpr int64_t GEMV_STATIC_SCRATCH_BYTES = (int64_t)8 << 20;
+hipError_t launch_gemv_noalloc(int fmt, const void* w, const void* scales, const uint16_t* x, int64_t T, int64_t N,
+                               int64_t K, bool bf16_out, void* y, hipStream_t stream, bool packed);
 hipError_t launch_pack_weights(int fmt, const void* src, int64_t N, int64_t K, void* dst, hipStream_t stream);
 
 // A8 decode GEMV (int8 activation codes and scales from launch_quantize_int8_g64,

@@ -15,7 +15,8 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnq.so")
 
-NQ_OK, NQ_ERR_NULL, NQ_ERR_SHAPE, NQ_ERR_ALIGN, NQ_ERR_FORMAT, NQ_ERR_RANGE, NQ_ERR_HIP = range(7)
+NQ_OK, NQ_ERR_NULL, NQ_ERR_SHAPE, NQ_ERR_ALIGN, NQ_ERR_FORMAT, NQ_ERR_RANGE, NQ_ERR_HIP, NQ_ERR_SCRATCH = range(8)
+NQ_GEMV_STATIC_SCRATCH_BYTES = 8 << 20
 NQ_OUT_F32, NQ_OUT_BF16 = 0, 1
 NQ_W_Q4G64_F16S, NQ_W_Q8G32_F16S, NQ_W_Q8G64_F16S, NQ_W_MXFP8_G32, NQ_W_BF16 = range(5)
 NQ_W_Q3G64_F16S, NQ_W_Q5G64_F16S, NQ_W_Q6G64_F16S = 5, 6, 7
@@ -43,6 +44,7 @@ SIGNATURES = {
     "nq_pack_weights": (_I, [_I, _P, _I64, _I64, _P, _P]),
     "nq_gemv_fp8row_packed": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I64, _P]),
     "nq_gemv_qgroup_packed": (_I, [_I, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I64, _P]),
+    "nq_gemv_fp8row_packed_noalloc": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _P, _P]),
     "nq_stream_read_sink_words": (_I64, []),
     "nq_unpack_qbits_to_int8": (_I, [_I, _P, _I64, _I64, _P, _P]),
     "nq_linear_qbits_g64": (_I, [_I, _P, _I64, _P, _P, _I64, _I64, _I, _P, _P, _P, _I, _P, _P, _I64, _P]),
@@ -318,6 +320,13 @@ def nq_gemv_qgroup_packed(fmt, w_packed, w_scales, x, T, N, K, y, workspace=None
     wp, wb = _ws(workspace)
     _check(lib().nq_gemv_qgroup_packed(fmt, _ptr(w_packed), _ptr(w_scales), _ptr(x), T, N, K, _out_dt(y),
                                        _ptr(y), wp, wb, _stream(w_packed, x)), "nq_gemv_qgroup_packed")
+
+
+def nq_gemv_fp8row_packed_noalloc(w_packed, w_scale, x, T, N, K, y):
+    _size(w_packed, nq_packed_weight_bytes(NQ_FMT_FP8ROW, N, K), "w_packed")
+    _size(w_scale, 2 * N, "w_scale"); _size(x, 2 * T * K, "x"); _size(y, T * N * y.element_size(), "y")
+    _check(lib().nq_gemv_fp8row_packed_noalloc(_ptr(w_packed), _ptr(w_scale), _ptr(x), T, N, K, _out_dt(y), _ptr(y),
+                                               _stream(w_packed, x)), "nq_gemv_fp8row_packed_noalloc")
 
 
 def nq_unpack_qbits_to_int8(fmt, codes, N, K, out):
