@@ -8,13 +8,15 @@ order (prefill and conversions before decode, as in an engine step):
   gemm_fp8       per-token E4M3 quantization + FP8 GEMM, same shape
   q4_a8          Q4 group-64 weights on the A8 route, same shape: widening to
                  int8, and the routed projection (quantize + widen + GEMM)
+  q5g64_a8 / q3g64_a8   the same for Q5 / Q3 group-64 weights
   reencode       block-128 E4M3 -> per-row FP8, 5120x17408
   gemv_down      re-encoded 5120x17408, T = 1, 33; BF16 gate 96x5120, T = 1, 33
   decode_mxfp8   MXFP8 256x512 decode (FP32 out)            + MXFP8 GEMV T=1
   decode_mlx     MLX affine int8 17408x5120 -> BF16 (the draft layer's storage)
   head           row-FP8 152064x5120, T = 1..64
   head_q8        the same head as Q8 group-32, T = 1..64 (FP8-versus-Q8 crossover)
-  gemv_q4g64 / gemv_q8g32   at 17408x5120 and 5120x17408, T = 1, 8, 33
+  gemv_q4g64 / gemv_q8g32 / gemv_q5g64 / gemv_q3g64   at 17408x5120 and
+                 5120x17408, T = 1, 8, 33
   a8_decode      A8 decode GEMV (int8 activations) on Q8 / Q4 group-64 weights
                  at both shapes, T = 1, 8, 33: the kernel, the routed step
                  (quantize + GEMV), and the BF16-activation Q8 GEMV beside it
@@ -53,9 +55,9 @@ sys.path.insert(0, ROOT)
 # counters on `bench.py --calibrate-copy` (a 256 MiB copy reads FETCH_SIZE
 # 131083.5 KiB and writes WRITE_SIZE 262144 KiB: factors 1.99982 and 1.0).
 # Summaries: profiles/gemv_fp8row_17408x5120_hbm_traffic.md.  Valid only for
-# the GEMV source they were taken on (sha256 prefix of nq_gemv.hip).
+# the GEMV sources they were taken on (sha256 prefix over GEMV_SOURCES).
 GEMV_TRAFFIC = {
-    "source_sha256_16": "3a4533d275c4b80e",
+    "source_sha256_16": "3a4533d275c4b80e",  # taken before the GEMV source split
     "fetch_factor": 262144.0 / 131083.5,
     "write_factor": 1.0,
     "fetch_kib": {"gemv_fp8row_T1": 43815.7, "gemv_fp8row_T4": 44003.4, "gemv_fp8row_T16": 44771.9,
@@ -63,6 +65,8 @@ GEMV_TRAFFIC = {
     "write_kib": {"gemv_fp8row_T1": 79.5, "gemv_fp8row_T4": 301.5, "gemv_fp8row_T16": 1189.5,
                   "gemv_fp8row_T33": 2447.5},
 }
+
+GEMV_SOURCES = ("nq_launch.h", "nq_gemv_kernels.h", "nq_gemv.hip", "nq_gemv_fp8row.hip")
 
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
@@ -277,8 +281,9 @@ def rows_gate(nq, W):
 
 def rows_grouped(nq, W, name):
     torch = _torch()
-    fmt = {"q4g64": nq.NQ_W_Q4G64_F16S, "q8g32": nq.NQ_W_Q8G32_F16S}[name]
-    gs = 64 if name == "q4g64" else 32
+    fmt = {"q4g64": nq.NQ_W_Q4G64_F16S, "q8g32": nq.NQ_W_Q8G32_F16S, "q5g64": nq.NQ_W_Q5G64_F16S,
+           "q3g64": nq.NQ_W_Q3G64_F16S}[name]
+    gs = 32 if name == "q8g32" else 64
     rows = []
     for (n, k) in ((W.FFN, W.HIDDEN), (W.HIDDEN, W.FFN)):
         rows += _grouped_shape_rows(nq, W, name, fmt, gs, n, k, torch)
@@ -430,6 +435,25 @@ def rows_q4_a8(nq, W):
                 lambda: nq.nq_linear_q4g64(x, m, wc, ws, n, k, True, aq, asc, wi8, y))]
 
 
+def rows_qbits_a8(nq, W, name):
+    """Q5 / Q3 group-64 weights on the A8 route at the prefill chunk (1792 x
+    17408 x 5120): the codes widened to int8, and the routed projection
+    (quantize + widen + W8A8 GEMM)."""
+    torch = _torch()
+    fmt, bits = {"q5g64": (nq.NQ_W_Q5G64_F16S, 5), "q3g64": (nq.NQ_W_Q3G64_F16S, 3)}[name]
+    n, k, m = W.FFN, W.HIDDEN, W.PREFILL_CHUNK
+    d = W.grouped(name, n, k)
+    wc, ws = to_dev(d["codes"]), to_dev(d["scales"])
+    x = to_dev(W.w8a8_prefill(n=64)["x"])
+    aq, asc = empty((m, k), torch.int8), empty((m, k // 64), torch.float32)
+    wi8 = empty((n, k), torch.int8)
+    y = empty((m, n), torch.float32)
+    return [Row(f"unpack_{name}", f"unpack_{name}", "GB/s", n * k * bits // 8 + n * k,
+                lambda: nq.nq_unpack_qbits_to_int8(fmt, wc, n, k, wi8)),
+            Row(f"linear_{name}_a8", f"linear_{name}_a8", "TOPS", 2 * m * n * k,
+                lambda: nq.nq_linear_qbits_g64(fmt, x, m, wc, ws, n, k, nq.NQ_A8_PREFILL, aq, asc, wi8, y))]
+
+
 def _fp8_gemm_row(nq, W, m, n, k):
     torch = _torch()
     q, s = _encode_bf16_on_gpu(nq, W.fp8row_weights_bf16(n, k))
@@ -460,6 +484,9 @@ def build_rows(selected):
         rows += rows_prefill(nq, W, want("quant_int8"), want("gemm_w8a8"), want("gemm_fp8"))
     if want("q4_a8"):
         rows += rows_q4_a8(nq, W)
+    for name in ("q5g64", "q3g64"):
+        if want(f"{name}_a8"):
+            rows += rows_qbits_a8(nq, W, name)
     if want("reencode") or want("gemv_down"):
         rows += rows_reencode_and_down(nq, W, want("reencode"), want("gemv_down"))
     if want("decode_mxfp8"):
@@ -470,7 +497,7 @@ def build_rows(selected):
         rows += rows_head(nq, W)
     if want("head_q8"):
         rows += rows_head_q8(nq, W)
-    for name in ("q4g64", "q8g32"):
+    for name in ("q4g64", "q8g32", "q5g64", "q3g64"):
         if want(f"gemv_{name}"):
             rows += rows_grouped(nq, W, name)
     if want("a8_decode"):
@@ -598,9 +625,11 @@ def gemv_traffic(names):
     """Measured HBM bytes per launch of the headline GEMV, or None when the
     kernel source changed since the counters were taken."""
     import hashlib
-    src = os.path.join(ROOT, "quantized_weight_linear_amd", "csrc", "nq_gemv.hip")
-    with open(src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in GEMV_SOURCES:
+        with open(os.path.join(ROOT, "quantized_weight_linear_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    sha = h.hexdigest()[:16]
     t = GEMV_TRAFFIC
     if sha != t["source_sha256_16"] or any(n not in t["fetch_kib"] for n in names):
         return None
@@ -730,7 +759,9 @@ def main():
     # prefill GEMMs (flat, so record parsers keep every figure)
     pre = {}
     for name, key, peak_name in (("gemm_w8a8", "w8a8", "int8"), ("gemm_fp8", "fp8", "fp8"),
-                                 ("linear_q4g64_a8", "q4_a8_routed", "int8")):
+                                 ("linear_q4g64_a8", "q4_a8_routed", "int8"),
+                                 ("linear_q5g64_a8", "q5_a8_routed", "int8"),
+                                 ("linear_q3g64_a8", "q3_a8_routed", "int8")):
         if name in results:
             v = results[name]
             pre[f"{key}_us"] = v["us"]

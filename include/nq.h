@@ -392,7 +392,7 @@ nq_status nq_linear_q4g64(const uint16_t* x, int64_t T, const uint8_t* w_codes, 
  * workgroup written to sink [nq_stream_read_sink_words()].  It gives the HBM
  * read rate that the weight-streaming GEMVs are compared against: [int8 card,
  * "Files"] notes that decode is bandwidth bound.
- * Errors: bytes % 16 != 0 -> NQ_ERR_SHAPE.
+ * Errors: bytes % 16 != 0, or bytes of 2 GiB - 16 or more -> NQ_ERR_SHAPE.
  */
 int64_t nq_stream_read_sink_words(void);
 nq_status nq_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);

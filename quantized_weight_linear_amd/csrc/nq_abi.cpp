@@ -421,7 +421,7 @@ nq_status nq_gemv_a8_g64_packed(int fmt, const void* w_packed, const uint16_t* w
 int64_t nq_stream_read_sink_words(void) { return nq::stream_read_blocks(); }
 
 nq_status nq_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
-    if (bytes < 0 || bytes % 16 != 0) return NQ_ERR_SHAPE;
+    if (bytes < 0 || bytes % 16 != 0 || bytes >= ((int64_t)1 << 31) - 16) return NQ_ERR_SHAPE;
     NQ_TRY(need(src, bytes));
     NQ_TRY(need(sink, bytes));
     NQ_TRY(align_ok(src));

@@ -431,54 +431,104 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
 #pragma unroll
             for (int j = 0; j < TN; ++j) xb[j] = *reinterpret_cast<const v4u*>(&Sg.b[frag_off(wc0 + 32 * j, 2 * p)]);
         };
-        read_pair(0, ca, cb);
+        // the BF16 fragments of half hh (bytes [8 hh, 8 hh + 8) of each lane's 16 codes)
+        auto convert = [&](const v4u (&xa)[TM], const v4u (&xb)[TN], int hh, v8bf (&af)[TM], v8bf (&bf)[TN]) {
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            // The reads of pair p + 1 go out before pair p is converted and
-            // multiplied, so their latency hides behind this pair's MFMAs.
-            // The empty asm (a memory clobber, with pair p's codes passed
-            // through it) keeps the compiler from sinking those reads below
-            // the MFMAs.
-            v4u na[TM], nb[TN];
-            if (p + 1 < NP) read_pair(p + 1, na, nb);
-            if constexpr (TM == 2 && TN == 4)
-                asm volatile("" : "+v"(ca[0]), "+v"(ca[1]), "+v"(cb[0]), "+v"(cb[1]), "+v"(cb[2]), "+v"(cb[3]) :: "memory");
-            else if constexpr (TM == 2 && TN == 2)
-                asm volatile("" : "+v"(ca[0]), "+v"(ca[1]), "+v"(cb[0]), "+v"(cb[1]) :: "memory");
-            else
-                static_assert(TM == 2 && (TN == 2 || TN == 4), "operand list of the ordering asm");
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                v8bf af[TM], bf[TN];
-#pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    const uint32_t w0 = hh ? ca[i].z : ca[i].x, w1 = hh ? ca[i].w : ca[i].y;
-                    af[i] = __builtin_bit_cast(v8bf, make_uint4(e4m3x2_to_bf16x2<false>(w0, 1.0f),
-                                                                e4m3x2_to_bf16x2<true>(w0, 1.0f),
-                                                                e4m3x2_to_bf16x2<false>(w1, 1.0f),
-                                                                e4m3x2_to_bf16x2<true>(w1, 1.0f)));
-                }
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const uint32_t w0 = hh ? cb[j].z : cb[j].x, w1 = hh ? cb[j].w : cb[j].y;
-                    bf[j] = __builtin_bit_cast(v8bf, make_uint4(e4m3x2_to_bf16x2<false>(w0, 1.0f),
-                                                                e4m3x2_to_bf16x2<true>(w0, 1.0f),
-                                                                e4m3x2_to_bf16x2<false>(w1, 1.0f),
-                                                                e4m3x2_to_bf16x2<true>(w1, 1.0f)));
-                }
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+            for (int i = 0; i < TM; ++i) {
+                const uint32_t w0 = hh ? xa[i].z : xa[i].x, w1 = hh ? xa[i].w : xa[i].y;
+                af[i] = __builtin_bit_cast(v8bf, make_uint4(e4m3x2_to_bf16x2<false>(w0, 1.0f),
+                                                            e4m3x2_to_bf16x2<true>(w0, 1.0f),
+                                                            e4m3x2_to_bf16x2<false>(w1, 1.0f),
+                                                            e4m3x2_to_bf16x2<true>(w1, 1.0f)));
             }
-            __builtin_amdgcn_sched_barrier(0);   // pair p's MFMAs stay ahead of pair p + 1's wait
-            after_pair(p);
-            if (p + 1 < NP) {
 #pragma unroll
-                for (int i = 0; i < TM; ++i) ca[i] = na[i];
+            for (int j = 0; j < TN; ++j) {
+                const uint32_t w0 = hh ? xb[j].z : xb[j].x, w1 = hh ? xb[j].w : xb[j].y;
+                bf[j] = __builtin_bit_cast(v8bf, make_uint4(e4m3x2_to_bf16x2<false>(w0, 1.0f),
+                                                            e4m3x2_to_bf16x2<true>(w0, 1.0f),
+                                                            e4m3x2_to_bf16x2<false>(w1, 1.0f),
+                                                            e4m3x2_to_bf16x2<true>(w1, 1.0f)));
+            }
+        };
+        auto mfmas = [&](const v8bf (&af)[TM], const v8bf (&bf)[TN]) {
 #pragma unroll
-                for (int j = 0; j < TN; ++j) cb[j] = nb[j];
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        };
+        read_pair(0, ca, cb);
+        if constexpr (!KTAIL && TM == 2 && TN == 4) {
+            // Software-pipelined by half column pairs: the converts of the next
+            // half (of this pair, or the first half of the next pair, whose
+            // codes were read one pair ahead) are issued among the 8 MFMAs of
+            // the current half, 3 converts after each MFMA (sched_group_barrier),
+            // so the matrix unit is fed while the vector ALU converts.
+            v8bf af[2][TM], bf[2][TN];
+            convert(ca, cb, 0, af[0], bf[0]);
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                v4u na[TM], nb[TN];
+                if (p + 1 < NP) read_pair(p + 1, na, nb);
+                asm volatile("" : "+v"(ca[0]), "+v"(ca[1]), "+v"(cb[0]), "+v"(cb[1]), "+v"(cb[2]), "+v"(cb[3]) :: "memory");
+                // half 0 of pair p multiplied, half 1 converted
+                convert(ca, cb, 1, af[1], bf[1]);
+                mfmas(af[0], bf[0]);
+#pragma unroll
+                for (int g = 0; g < TM * TN; ++g) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);    // three VALU
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                // half 1 of pair p multiplied, half 0 of pair p + 1 converted
+                if (p + 1 < NP) convert(na, nb, 0, af[0], bf[0]);
+                mfmas(af[1], bf[1]);
+                if (p + 1 < NP) {
+#pragma unroll
+                    for (int g = 0; g < TM * TN; ++g) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);   // pair p's MFMAs stay ahead of pair p + 1's wait
+                after_pair(p);
+                if (p + 1 < NP) {
+#pragma unroll
+                    for (int i = 0; i < TM; ++i) ca[i] = na[i];
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) cb[j] = nb[j];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                // The reads of pair p + 1 go out before pair p is converted and
+                // multiplied, so their latency hides behind this pair's MFMAs.
+                // The empty asm (a memory clobber, with pair p's codes passed
+                // through it) keeps the compiler from sinking those reads below
+                // the MFMAs.
+                v4u na[TM], nb[TN];
+                if (p + 1 < NP) read_pair(p + 1, na, nb);
+                if constexpr (TM == 2 && TN == 4)
+                    asm volatile("" : "+v"(ca[0]), "+v"(ca[1]), "+v"(cb[0]), "+v"(cb[1]), "+v"(cb[2]), "+v"(cb[3]) :: "memory");
+                else if constexpr (TM == 2 && TN == 2)
+                    asm volatile("" : "+v"(ca[0]), "+v"(ca[1]), "+v"(cb[0]), "+v"(cb[1]) :: "memory");
+                else
+                    static_assert(TM == 2 && (TN == 2 || TN == 4), "operand list of the ordering asm");
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    v8bf af[TM], bf[TN];
+                    convert(ca, cb, hh, af, bf);
+                    mfmas(af, bf);
+                }
+                __builtin_amdgcn_sched_barrier(0);   // pair p's MFMAs stay ahead of pair p + 1's wait
+                after_pair(p);
+                if (p + 1 < NP) {
+#pragma unroll
+                    for (int i = 0; i < TM; ++i) ca[i] = na[i];
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) cb[j] = nb[j];
+                }
             }
         }
     };

@@ -211,7 +211,14 @@ __global__ __launch_bounds__(64) void gemv_a8_kernel(const uint8_t* __restrict__
 // ---------------------------------------------------------------------------
 int64_t gemv_a8_workspace_bytes(int64_t T, int64_t N, int64_t K) {
     if (T <= 0 || N <= 0 || K <= 0 || K % A8_KC != 0) return 0;
-    return wave_workspace(plan_wave(N, K), T < 64 ? T : 64);
+    int64_t need = 0;
+    for (int64_t tc = 1; tc <= (T < 64 ? T : 64); tc += 15) {     // the largest over the passes' plans
+        const int64_t w = wave_workspace(plan_wave(N, K, tc), tc);
+        if (w > need) need = w;
+    }
+    const int64_t tl = T < 64 ? T : 64;
+    const int64_t wl = wave_workspace(plan_wave(N, K, tl), tl);
+    return wl > need ? wl : need;
 }
 
 template <int FMT, int NCB, bool PK>

@@ -177,19 +177,17 @@ __device__ __forceinline__ uint32_t i4x2_to_bf16x2(uint32_t d, int sh) {
     return f32x2_to_bf16x2(a, b);
 }
 
-// With one token block, Q4 codes are multiplied in a biased form: the nibble
-// u = q + 8 (0..15) written into mantissa bits 3..6 of the BF16 1.0 is
-// exactly 1 + u / 16 = 1.5 + q / 16, so a group's MFMA sum D over the biased
-// weights gives the exact group sum as sum x q = 16 (D - 1.5 sum x) (sum x
-// from one more MFMA against a fragment of ones).  The packed layout stores u
-// with the two codes of a BF16 pair 16 bits apart (code 2i at bits 4i, code
-// 2i + 1 at bits 16 + 4i of each 32-bit word), so a pair costs one shift and
-// one and-or; the row-major layout (natural order, two's complement) builds
-// the same values with a few more operations.  With more token blocks the
-// decode is shared by their MFMAs while the sum of x and the correction are
-// per block, so there both layouts decode q itself (the same values, so
-// packed and row-major results stay identical).
+// Q4 codes are multiplied in a biased form: the nibble u = q + 8 (0..15)
+// written into mantissa bits 3..6 of the BF16 1.0 is exactly 1 + u / 16 =
+// 1.5 + q / 16, so a group's MFMA sum over the biased weights, started from
+// C = -1.5 sum x (chunk_mfma), is exactly sum x q / 16 up to FP32 rounding.
+// The packed layout stores u with the two codes of a BF16 pair 16 bits apart
+// (code 2i at bits 4i, code 2i + 1 at bits 16 + 4i of each 32-bit word), so a
+// pair costs one shift and one and-or; the row-major layout (natural order,
+// two's complement) builds the same values with a few more operations, so
+// packed and row-major results stay identical.
 constexpr uint32_t Q4_ONE = 0x3F803F80u;        // two BF16 1.0
+constexpr uint32_t Q4_NEG15 = 0xBFC0BFC0u;      // two BF16 -1.5
 constexpr uint32_t Q4_MANT = 0x00780078u;       // mantissa bits 3..6 of both halves
 // (t & mask) | one: with literal constants the compiler emits a separate and
 // + or (the VOP3 and-or takes no literal on this target); with the constants
@@ -197,7 +195,7 @@ constexpr uint32_t Q4_MANT = 0x00780078u;       // mantissa bits 3..6 of both ha
 // one v_and_or_b32.
 __device__ __forceinline__ uint32_t q4_packed_pair(uint32_t d, int i, uint32_t mask, uint32_t one) {
     const uint32_t t = i == 0 ? (d << 3) : (d >> (4 * i - 3));
-    return (t & mask) | (one & ~mask);
+    return (t & mask) | one;      // one v_and_or_b32 (mask uniform, one in a VGPR: see decode_afrag)
 }
 __device__ __forceinline__ uint32_t q4_natural_pair(uint32_t d, int i) {  // codes 2i, 2i + 1 of a row-major word
     const uint32_t b = ((d >> (8 * i)) ^ 0x88u) & 0xFFu;                  // u of both codes
@@ -233,7 +231,13 @@ __device__ __forceinline__ v8bf decode_afrag(const WChunk<FMT>& r, int rb, int l
         const uint2 q = r.p[rb];
         const uint32_t d0 = ls ? q.y : q.x;
         const uint32_t xq = d0 ^ 0x88888888u;
-        const uint32_t mask = __builtin_amdgcn_readfirstlane(Q4_MANT), one = __builtin_amdgcn_readfirstlane(Q4_ONE);
+        // The and-or takes at most one scalar operand on this target: the mask
+        // stays uniform, the constant 1.0 pair is moved to a vector register
+        // (a plain VALU move, consumed by VALU instructions only), so the
+        // compiler emits one v_and_or_b32 per pair instead of an and and an or.
+        const uint32_t mask = __builtin_amdgcn_readfirstlane(Q4_MANT);
+        uint32_t one;
+        asm("v_mov_b32 %0, %1" : "=v"(one) : "s"(__builtin_amdgcn_readfirstlane(Q4_ONE)));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             o[i] = BIAS ? (PK ? q4_packed_pair(d0, i, mask, one) : q4_natural_pair(d0, i))
@@ -277,47 +281,74 @@ __device__ __forceinline__ void chunk_mfma(const WChunk<FMT>& wc, const uint16_t
     } else {
         // GS == 64: the wave's two k-steps are one group; GS == 32: each k-step is one.
         constexpr int NGW = 64 / GS;                     // groups per wave and chunk
-        constexpr bool BIAS = FMT == W_Q4G64 && NCB == 1;   // biased Q4 weights: also sum x per group
-        v4f d[4][NCB];
-        v4f xsum[NCB];
+        if constexpr (FMT == W_Q4G64) {
+            // Biased Q4 weights (1.5 + q / 16, see decode_afrag), every token
+            // block: the bias is removed inside the matrix unit.  C = -1.5 sum x
+            // over the group comes from two MFMAs of a fragment of -1.5s
+            // against the activations (once per token block, shared by the
+            // row blocks), and each row block's chain starts from C, so it ends
+            // at sum x (1.5 + q / 16) - 1.5 sum x = sum x q / 16 (the factor 16
+            // is applied once per wave, q4_bias_finish).  The group scale is
+            // then one FMA per element.
+            v8bf b[2][NCB];
 #pragma unroll
-        for (int ls = 0; ls < 2; ++ls) {
-            const int col = kl + kstep_col<FMT>(2 * wv + ls, lg);
-            v8bf b[NCB];
+            for (int ls = 0; ls < 2; ++ls) {
+                const int col = kl + kstep_col<FMT>(2 * wv + ls, lg);
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) b[cb] = *reinterpret_cast<const v8bf*>(&xs[xrow[cb] + col]);
-            if constexpr (BIAS) {
-                const v8bf ones = __builtin_bit_cast(v8bf, make_uint4(Q4_ONE, Q4_ONE, Q4_ONE, Q4_ONE));
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb)
-                    xsum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        ones, b[cb], ls == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : xsum[cb], 0, 0, 0);
+                for (int cb = 0; cb < NCB; ++cb) b[ls][cb] = *reinterpret_cast<const v8bf*>(&xs[xrow[cb] + col]);
             }
+            const v8bf neg = __builtin_bit_cast(v8bf, make_uint4(Q4_NEG15, Q4_NEG15, Q4_NEG15, Q4_NEG15));
+            v4f c0[NCB];
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                c0[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg, b[0][cb], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                c0[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg, b[1][cb], c0[cb], 0, 0, 0);
+            }
+            const int gi = sgroup0 + wv;
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
-                const v8bf a = decode_afrag<FMT, PK, BIAS>(wc, rb, ls);
+                const v8bf a0 = decode_afrag<FMT, PK, true>(wc, rb, 0);
+                const v8bf a1 = decode_afrag<FMT, PK, true>(wc, rb, 1);
+                const uint2 s4 = *reinterpret_cast<const uint2*>(&scs[gi * GV_ROWS + 16 * rb + 4 * lg]);
+                const float sc[4] = {f16_bits_to_f32(s4.x & 0xFFFFu), f16_bits_to_f32(s4.x >> 16),
+                                     f16_bits_to_f32(s4.y & 0xFFFFu), f16_bits_to_f32(s4.y >> 16)};
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) {
-                    const v4f c0 = (NGW == 2 || ls == 0) ? v4f{0.f, 0.f, 0.f, 0.f} : d[rb][cb];
-                    d[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[cb], c0, 0, 0, 0);
+                    v4f d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b[0][cb], c0[cb], 0, 0, 0);
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b[1][cb], d, 0, 0, 0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[rb][cb][e] = fmaf(d[e], sc[e], acc[rb][cb][e]);
                 }
             }
-            if (NGW == 2 || ls == 1) {
-                const int gi = sgroup0 + (NGW == 2 ? 2 * wv + ls : wv);
+        } else {
+            v4f d[4][NCB];
+#pragma unroll
+            for (int ls = 0; ls < 2; ++ls) {
+                const int col = kl + kstep_col<FMT>(2 * wv + ls, lg);
+                v8bf b[NCB];
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) b[cb] = *reinterpret_cast<const v8bf*>(&xs[xrow[cb] + col]);
 #pragma unroll
                 for (int rb = 0; rb < 4; ++rb) {
-                    const uint2 s4 = *reinterpret_cast<const uint2*>(&scs[gi * GV_ROWS + 16 * rb + 4 * lg]);
-                    // biased Q4: sum x q = 16 (D - 1.5 sum x); the factor 16 is applied once
-                    // to the finished sums (q4_bias_finish: exact, a power of two)
-                    const float sc[4] = {f16_bits_to_f32(s4.x & 0xFFFFu), f16_bits_to_f32(s4.x >> 16),
-                                         f16_bits_to_f32(s4.y & 0xFFFFu), f16_bits_to_f32(s4.y >> 16)};
+                    const v8bf a = decode_afrag<FMT, PK, false>(wc, rb, ls);
 #pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb)
+                    for (int cb = 0; cb < NCB; ++cb) {
+                        const v4f c0 = (NGW == 2 || ls == 0) ? v4f{0.f, 0.f, 0.f, 0.f} : d[rb][cb];
+                        d[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[cb], c0, 0, 0, 0);
+                    }
+                }
+                if (NGW == 2 || ls == 1) {
+                    const int gi = sgroup0 + (NGW == 2 ? 2 * wv + ls : wv);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float v = BIAS ? fmaf(xsum[cb][e], -1.5f, d[rb][cb][e]) : d[rb][cb][e];
-                            acc[rb][cb][e] = fmaf(v, sc[e], acc[rb][cb][e]);
-                        }
+                    for (int rb = 0; rb < 4; ++rb) {
+                        const uint2 s4 = *reinterpret_cast<const uint2*>(&scs[gi * GV_ROWS + 16 * rb + 4 * lg]);
+                        const float sc[4] = {f16_bits_to_f32(s4.x & 0xFFFFu), f16_bits_to_f32(s4.x >> 16),
+                                             f16_bits_to_f32(s4.y & 0xFFFFu), f16_bits_to_f32(s4.y >> 16)};
+#pragma unroll
+                        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) acc[rb][cb][e] = fmaf(d[rb][cb][e], sc[e], acc[rb][cb][e]);
+                    }
                 }
             }
         }
@@ -327,9 +358,11 @@ __device__ __forceinline__ void chunk_mfma(const WChunk<FMT>& wc, const uint16_t
 // The factor 16 of the biased Q4 sums (see chunk_mfma), once per wave.
 template <int FMT, int NCB>
 __device__ __forceinline__ void q4_bias_finish(v4f (&acc)[4][NCB]) {
-    if constexpr (FMT == W_Q4G64 && NCB == 1)
+    if constexpr (FMT == W_Q4G64)
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) acc[rb][0] *= 16.0f;
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] *= 16.0f;
 }
 
 // Sum the four waves' partials of row block wv in wave order through LDS

@@ -105,14 +105,18 @@ __device__ __forceinline__ void wave_finish(v4f (&acc)[NCB], int T, int N, int r
 
 // Row blocks of 16; with fewer row blocks than the SIMDs (4 per CU), K is
 // split so that there are about as many workgroups as SIMDs, at least 4
-// chunks per split (only with a workspace).
+// chunks per split (only with a workspace).  More splits, for two or three
+// waves per SIMD, measured slower (17408 x 5120 A8 T = 1: 21.7 -> 25.9 us;
+// Q5 T = 8: 26.7 -> 31.3 us): the exchange and the repeated activation loads
+// cost more than the added overlap gains.
 struct WavePlan {
     int64_t rbs;
     int splits;
     int chunks_per_split;
 };
 
-inline WavePlan plan_wave(int64_t N, int64_t K) {
+inline WavePlan plan_wave(int64_t N, int64_t K, int64_t Tc) {
+    (void)Tc;
     WavePlan p{};
     p.rbs = (N + 15) / 16;
     const int64_t chunks = K / WG_KC;
@@ -140,7 +144,7 @@ inline int64_t wave_workspace(const WavePlan& p, int64_t Tc) {
 // counters and partials, or no split when the workspace is missing or small.
 inline WavePlan plan_wave_with(int64_t N, int64_t K, int64_t Tc, void* workspace, int64_t workspace_bytes,
                                float** partial, unsigned** counters) {
-    WavePlan p = plan_wave(N, K);
+    WavePlan p = plan_wave(N, K, Tc);
     *partial = nullptr;
     *counters = nullptr;
     if (p.splits > 1) {

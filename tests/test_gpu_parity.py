@@ -460,8 +460,11 @@ def _pack_dev(fmt, codes_d, n, k):
     return pk
 
 
-def _counters_zero(wsp, n):
-    return wsp is None or int(wsp.view(torch.int32)[:(n + 63) // 64].abs().sum().item()) == 0
+def _counters_zero(wsp, n, rows_per_counter=64):
+    """The workspace's counters (one per row tile, or per 16-row block for the
+    wave-per-row-block kernels) are back at zero."""
+    c = (n + rows_per_counter - 1) // rows_per_counter
+    return wsp is None or int(wsp.view(torch.int32)[:c].abs().sum().item()) == 0
 
 
 def _gemv_both_layouts(fmt, codes_d, pk, scales_d, x, n, k):
@@ -481,7 +484,8 @@ def _gemv_both_layouts(fmt, codes_d, pk, scales_d, x, n, k):
         nq.nq_gemv_qgroup_packed(fmt, pk, scales_d, xd, t, n, k, y32, wsp)
         nq.nq_gemv_qgroup(fmt, codes_d, scales_d, xd, t, n, k, yr, wsp)
     g32, g16, gr = host(y32, np.float32), host(y16, np.uint16), host(yr, np.float32)
-    assert _counters_zero(wsp, n)
+    wave_kernel = fmt in (nq.NQ_W_Q3G64_F16S, nq.NQ_W_Q5G64_F16S, nq.NQ_W_Q6G64_F16S)
+    assert _counters_zero(wsp, n, 16 if wave_kernel else 64)
     assert np.array_equal(g16, bf16_of_f32_bits(g32))          # BF16 = RNE of the same FP32 result
     assert np.array_equal(g32.view(np.uint32), gr.view(np.uint32))   # packed = row-major, bit for bit
     return g32, g16, gr
@@ -978,7 +982,7 @@ def _run_a8(fmt, codes_d, pk, ws_d, qa, sa, n, k, wmode, out="f32"):
     else:
         nq.nq_gemv_a8_g64_packed(fmt, pk, ws_d, dev(qa), dev(sa), t, n, k, y, wsp)
     got = host(y, np.float32 if out == "f32" else np.uint16)
-    assert _counters_zero(wsp, n)
+    assert _counters_zero(wsp, n, 16)
     return got
 
 
@@ -1101,7 +1105,7 @@ def _qb_gemv(fmt, cd, pk, sd, x, n, k, wmode, out="f32"):
     else:
         nq.nq_gemv_qgroup_packed(fmt, pk, sd, dev(x), t, n, k, y, wsp)
     got = host(y, np.float32 if out == "f32" else np.uint16)
-    assert _counters_zero(wsp, n)
+    assert _counters_zero(wsp, n, 16)
     return got
 
 
