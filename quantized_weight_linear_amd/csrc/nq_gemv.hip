@@ -91,7 +91,7 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     // direct kernel is as fast or faster (24576 x 5120: 24.5 against 26.7 us;
     // 17408 x 2048: 10.9 against 11.6 us at T = 1).
     const int64_t cus_n = (int64_t)device_cu_count();
-    const bool spread_one_round = fmt_group(fmt) == 0 && allow_spread && p.tiles > cus_n &&
+    const bool spread_one_round = (fmt_group(fmt) == 0 || Tc <= 16) && allow_spread && p.tiles > cus_n &&
                                   8 * (p.tiles - cus_n) <= cus_n && chunks >= 16;
     if (fmt_group(fmt) == 0 && Tc <= 16 && !spread_one_round) {
         // direct variant (no group scales, one token block): about one
@@ -129,16 +129,17 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     const bool grouped_leftover = fmt_group(fmt) != 0 && p.tiles > (int64_t)device_cu_count() &&
                                   p.tiles < 2 * (int64_t)device_cu_count() &&
                                   p.tiles % (int64_t)device_cu_count() != 0 && chunks >= 3 * (int64_t)min_chunks;
-    // Grouped formats with the tiles a multiple of the CUs (1-3 per CU): from
-    // 4 tokens on the streaming kernel with K split in two beats the resident
-    // kernel too (16384 x 5120 T = 4 / 8 / 12 / 16: Q8G32 25.3 / 26.1 / 31.5 /
-    // 31.9 -> 22.5 / 21.9 / 22.6 / 23.2 us, Q4 21.0 / 18.9 / 19.1 / 16.4 ->
-    // 16.5 / 16.2 / 16.7 / 17.2; 32768 x 5120 Q8G32 T = 8 / 16: 47.1 / 52.0 ->
-    // 39.8 / 41.7).
+    // Grouped formats with the tiles a multiple of the CUs (1-3 per CU): the
+    // streaming kernel beats the resident kernel at every T, without a K split
+    // below 4 tokens (16384 x 5120 T = 1: Q4 18.8 -> 14.3 us, Q8G32 25.4 ->
+    // 21.5) and with K split in two from 4 tokens on (T = 4 / 8 / 12 / 16:
+    // Q8G32 25.3 / 26.1 / 31.5 / 31.9 -> 22.5 / 21.9 / 22.6 / 23.2 us, Q4 21.0 /
+    // 18.9 / 19.1 / 16.4 -> 16.5 / 16.2 / 16.7 / 17.2; 32768 x 5120 Q8G32 T = 8
+    // / 16: 47.1 / 52.0 -> 39.8 / 41.7).
     const bool grouped_even = fmt_group(fmt) != 0 && p.tiles >= (int64_t)device_cu_count() &&
                               p.tiles % (int64_t)device_cu_count() == 0 && !many_tiles;
     const bool try_resident = Tc <= 16 && p.tiles >= (int64_t)device_cu_count() && !many_tiles && !spread_one_round &&
-                              !(grouped_leftover && Tc > 4) && !(grouped_even && Tc >= 4);
+                              !(grouped_leftover && Tc > 4) && !grouped_even;
     const int64_t sr = balanced_splits(p.tiles, chunks, smax);
     for (int64_t s = sr; try_resident && s <= 32 && s <= chunks; ++s) {
         const int64_t cps = (chunks + s - 1) / s;
@@ -172,7 +173,7 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     // (24576 x 5120 T = 8 / 33: Q8G32 35.9 / 46.8 against 33.0 / 42.1 us, Q4
     // 26.6 / 40.9 against 24.1 / 37.0).  Four or five splits are slower
     // again (the exchange).
-    if (grouped_leftover && Tc > 4) {
+    if (grouped_leftover && Tc > 4 && !spread_one_round) {
         const int64_t cus = (int64_t)device_cu_count();
         const int64_t w2 = (2 * p.tiles + cus - 1) / cus, w3 = (3 * p.tiles + cus - 1) / cus;
         s0 = 2 * w3 < 3 * w2 ? 3 : 2;
@@ -180,7 +181,7 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     const int64_t cps = (chunks + s0 - 1) / s0;
     p.chunks_per_split = (int)cps;
     p.splits = (int)((chunks + cps - 1) / cps);
-    if (fmt_group(fmt) == 0 && allow_spread) plan_spread(p, chunks);
+    if ((fmt_group(fmt) == 0 || spread_one_round) && allow_spread) plan_spread(p, chunks);
     return p;
 }
 

@@ -385,6 +385,32 @@ __device__ __forceinline__ void reduce_waves(v4f (&acc)[4][NCB], v4f (&fin)[NCB]
     }
 }
 
+// reduce_waves for sums held transposed, as MFMAs with the activations in the
+// A operand leave them (lane 16 g + i: tokens 4 g + e of row i): each value is
+// first written to its place in the usual layout (lane 16 g' + i': rows
+// 4 g' + e' of token i'), then the waves' sums are added alike.
+template <int NCB>
+__device__ __forceinline__ void reduce_waves_t(v4f (&acc)[4][NCB], v4f (&fin)[NCB], v4f* red, int wv, int lane) {
+    const int li = lane & 15, lg = lane >> 4;
+    float* rf = reinterpret_cast<float*>(red);
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                rf[(((wv * 4 + rb) * NCB + cb) * 64 + (li >> 2) * 16 + 4 * lg + e) * 4 + (li & 3)] = acc[rb][cb][e];
+    __syncthreads();
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        v4f s = red[((0 * 4 + wv) * NCB + cb) * 64 + lane];
+#pragma unroll
+        for (int w2 = 1; w2 < 4; ++w2) s += red[((w2 * 4 + wv) * NCB + cb) * 64 + lane];
+        fin[cb] = s;
+    }
+}
+
 // FP32 partials between workgroups: 16-byte buffer stores and loads with the
 // cache policy the compiler gives an agent-scope atomic access (sc1), so they
 // bypass the per-XCD L2, which is not coherent across XCDs.  Ordering comes
@@ -548,6 +574,7 @@ __device__ __forceinline__ void direct_spread(const uint8_t* __restrict__ w, con
                                               v4f* red, int* s_last) {
     using P = PieceFmt<FMT>;
     constexpr int D = 2;
+    constexpr int GS = group_size<FMT>();
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
@@ -579,6 +606,9 @@ __device__ __forceinline__ void direct_spread(const uint8_t* __restrict__ w, con
     };
     WChunk<FMT> wr[D];
     XFrag xr[D];
+    // formats with group scales: per row block, the scales of the lane's row
+    // for the wave's groups of the unit's chunk (GS = 64: one; GS = 32: two)
+    uint32_t sr[D][4];
     // (tile, chunk) of the next unit to load (stops at the last unit) and the
     // chunk of the next unit to compute
     int ld_t = tile0 + lt0, ld_c = (int)(u0 - (int64_t)lt0 * C), ld_i = 0;
@@ -609,13 +639,22 @@ __device__ __forceinline__ void direct_spread(const uint8_t* __restrict__ w, con
                 const int64_t rbg = rowb / 16 < nrb - 1 ? rowb / 16 : nrb - 1;   // blocks past N are clamped
                 pw = wlane + (rbg * P::BLOCK_CHUNK + (int64_t)c * cstride + q * (64 * P::PB));
             }
-            if constexpr (!PK || FMT == W_MXFP8) {
+            if constexpr (!PK || FMT == W_MXFP8 || GS != 0) {
                 const int64_t lim = (int64_t)N - 1 - rowb;                   // rows past N are clamped
                 const int lr = (int64_t)li < lim ? li : (int)lim;
                 row = rowb + lr;
             }
             if constexpr (!PK) pw = w + row * row_bytes<FMT>(K) + piece_offset<FMT>(c, q, lg);
             wr[slot].p[j] = *reinterpret_cast<const typename P::Piece*>(pw);
+            if constexpr (GS != 0) {
+                if (j % P::PW == 0) {
+                    // the wave's columns [64 wv, 64 wv + 64) of chunk c are group 4 c + wv
+                    // (GS = 64) or groups 8 c + 2 wv + {0, 1} (GS = 32)
+                    const uint16_t* s16 = reinterpret_cast<const uint16_t*>(scales) + row * (K / GS);
+                    if constexpr (GS == 64) sr[slot][rb] = s16[4 * c + wv];
+                    else sr[slot][rb] = *reinterpret_cast<const uint32_t*>(s16 + 8 * c + 2 * wv);
+                }
+            }
             if constexpr (FMT == W_MXFP8)
                 wr[slot].e8[j] = reinterpret_cast<const uint8_t*>(scales)[row * (K >> 5) +
                                                                           ((c * GV_KC + 64 * q + 16 * lg) >> 5)];
@@ -640,7 +679,8 @@ __device__ __forceinline__ void direct_spread(const uint8_t* __restrict__ w, con
     // segment k's sums: written directly or published as a partial; acc restarts
     auto close_segment = [&](int k) {
         v4f fin[NCB];
-        reduce_waves<NCB>(acc, fin, red, wv, lane);
+        if constexpr (GS != 0) reduce_waves_t<NCB>(acc, fin, red, wv, lane);
+        else reduce_waves<NCB>(acc, fin, red, wv, lane);
         const int tl = tile0 + lt0 + k;
         const int64_t n0 = (int64_t)tl * GV_ROWS + wv * 16 + 4 * lg;
         if (seg_full(k)) {
@@ -667,15 +707,46 @@ __device__ __forceinline__ void direct_spread(const uint8_t* __restrict__ w, con
         if (cp_c == 0 && cp_i > 0) close_segment(kseg++);   // this unit opens the next tile (uniform)
         ++cp_i;
         if (++cp_c == C) cp_c = 0;
-#pragma unroll
-        for (int ls = 0; ls < 2; ++ls) {
+        if constexpr (GS != 0) {
+            // Group scales: the MFMAs take the activations as A and the
+            // weights as B (both fragments hold the same k of their lane, so
+            // the group sums are the same), which leaves lane 16 g + i the
+            // sums of tokens 4 g + e of row i: one scale per row block and
+            // group.  Q4 codes are decoded exactly here (no bias).
+            constexpr int NGW = 64 / GS;
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
-                const v8bf a = decode_afrag<FMT>(wr[slot], rb, ls);
+                const float sc[2] = {f16_bits_to_f32(sr[slot][rb] & 0xFFFFu), f16_bits_to_f32(sr[slot][rb] >> 16)};
+                v4f d[NCB];
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb)
-                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        a, __builtin_bit_cast(v8bf, xr[slot].v[ls][cb]), acc[rb][cb], 0, 0, 0);
+                for (int ls = 0; ls < 2; ++ls) {
+                    const v8bf wf = decode_afrag<FMT, PK, false>(wr[slot], rb, ls);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) {
+                        const v4f c0 = (NGW == 2 || ls == 0) ? v4f{0.f, 0.f, 0.f, 0.f} : d[cb];
+                        d[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xr[slot].v[ls][cb]),
+                                                                        wf, c0, 0, 0, 0);
+                    }
+                    if (NGW == 2 || ls == 1) {
+                        const float g = sc[NGW == 2 ? ls : 0];
+#pragma unroll
+                        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) acc[rb][cb][e] = fmaf(d[cb][e], g, acc[rb][cb][e]);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int ls = 0; ls < 2; ++ls) {
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    const v8bf a = decode_afrag<FMT>(wr[slot], rb, ls);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+                        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            a, __builtin_bit_cast(v8bf, xr[slot].v[ls][cb]), acc[rb][cb], 0, 0, 0);
+                }
             }
         }
     };
@@ -757,15 +828,15 @@ __device__ __forceinline__ void direct_spread(const uint8_t* __restrict__ w, con
 // One barrier per chunk.
 // ---------------------------------------------------------------------------
 // Waves per SIMD the streaming kernel is compiled for: two for the formats
-// without group scales, so that a spread workgroup fits beside a whole-tile
-// one on every CU (see direct_spread), and for the grouped formats at three
-// token blocks (two K splits per tile then share a CU); one for the other
-// grouped cases, and for BF16 weights at four token blocks, which would spill
-// at that budget (a spread launch then runs its spread workgroups after the
-// whole tiles).
+// without group scales and for the grouped ones at one token block, so that a
+// spread workgroup fits beside a whole-tile one on every CU (see
+// direct_spread), and for the grouped formats at three token blocks (two K
+// splits per tile then share a CU); one for the grouped formats at two token
+// blocks and for BF16 weights at four, which would spill at that budget
+// (neither runs spread workgroups).
 template <int FMT, int NCB>
 constexpr int stream_min_waves() {
-    return (!(FMT == W_BF16 && NCB == 4) && (group_size<FMT>() == 0 || NCB == 3)) ? 2 : 1;
+    return (!(FMT == W_BF16 && NCB == 4) && (group_size<FMT>() == 0 || NCB == 1 || NCB == 3)) ? 2 : 1;
 }
 
 // With spread_wgs > 0 (formats without group scales, one split): workgroups
@@ -791,7 +862,7 @@ __global__ __launch_bounds__(256, (stream_min_waves<FMT, NCB>())) void gemv_mfma
     __shared__ __attribute__((aligned(16))) uint16_t scs[2][GS ? NG * GV_ROWS : 1];
     __shared__ int s_last;
     static_assert(sizeof(xs) >= 16384 * NCB, "reduction buffer");
-    if constexpr (GS == 0) {
+    if constexpr (GS == 0 || NCB == 1) {
         __shared__ int s_last_sp[SPREAD_MAXSEG];
         if ((int)blockIdx.x < spread_wgs) {
             const int tiles_all = (int)((N + GV_ROWS - 1) / GV_ROWS);

@@ -191,11 +191,17 @@ def test_gemv_plan_workspace(L):
     assert L.nq_gemv_workspace_bytes(-1, 33, 17408, 5120) == c272 + 16 * 11 * 33 * 64 * 4
     # 16384 rows: one whole tile per CU, nothing to exchange
     assert L.nq_gemv_workspace_bytes(-1, 1, 16384, 5120) == 0
-    # Q4 group-64, one token: resident kernel, K split in 5 (the split whose
-    # busiest CU has the fewest chunks: ceil(272 x 5 / 256) x 4 = 24)
-    assert L.nq_gemv_workspace_bytes(nq.NQ_W_Q4G64_F16S, 1, 17408, 5120) == c272 + 5 * 1 * 272 * 64 * 4
-    # Q8 group-32, 8 tokens, the same 16-tile leftover: streaming kernel, K in 3
-    assert L.nq_gemv_workspace_bytes(nq.NQ_W_Q8G32_F16S, 8, 17408, 5120) == c272 + 3 * 8 * 272 * 64 * 4
+    # The grouped formats at one token block take the same spread plan
+    # (Q4 group-64 at 1 token, Q8 group-32 at 8)
+    assert L.nq_gemv_workspace_bytes(nq.NQ_W_Q4G64_F16S, 1, 17408, 5120) == c272 + 16 * 11 * 1 * 64 * 4
+    assert L.nq_gemv_workspace_bytes(nq.NQ_W_Q8G32_F16S, 8, 17408, 5120) == c272 + 16 * 11 * 8 * 64 * 4
+    # ... and at 17 tokens (two token blocks) the streaming kernel with K in 3
+    assert L.nq_gemv_workspace_bytes(nq.NQ_W_Q8G32_F16S, 17, 17408, 5120) == c272 + 3 * 17 * 272 * 64 * 4
+    # Q4 group-64 at 16384 rows, one token: streaming kernel, whole tiles
+    assert L.nq_gemv_workspace_bytes(nq.NQ_W_Q4G64_F16S, 1, 16384, 5120) == 0
+    # 20480 rows (320 tiles, 64 leftover: too many to spread), 1 token: the
+    # resident kernel, K split in 4 (ceil(320 x 4 / 256) x 5 = 25 chunks at most)
+    assert L.nq_gemv_workspace_bytes(nq.NQ_W_Q4G64_F16S, 1, 20480, 5120) == 1280 + 4 * 1 * 320 * 64 * 4
     # row-FP8 5120 x 17408, 17 tokens (80 tiles, 68 chunks): streaming kernel
     # with the balanced split, 3 (ceil(80 x 3 / 256) x 23 = 23 chunks at most)
     assert L.nq_gemv_workspace_bytes(-1, 17, 5120, 17408) == 512 + 3 * 17 * 80 * 64 * 4

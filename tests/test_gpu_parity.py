@@ -593,6 +593,36 @@ def test_gemv_qgroup_two_split_leftover(name, fmt):
         assert rel_fro(g32, ref33[:t]) <= FP32_TOL, (name, t)
 
 
+# Grouped formats with a few row tiles past the CU count (257 tiles, and 258
+# with the last one ragged: 12 rows): whole tiles plus spread workgroups whose
+# units apply the group scales themselves; one token block (T <= 16).  The
+# workspace size shows the plan took that path.
+@pytest.mark.slow
+@pytest.mark.parametrize("name,fmt", GROUP_FMTS[:3])
+@pytest.mark.parametrize("n", [16448, 16460])
+def test_gemv_qgroup_spread(name, fmt, n):
+    k = 4096
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles, chunks = (n + 63) // 64, k // 256
+    r = tiles % cus
+    assert 0 < r and 8 * r <= cus
+    units = r * chunks
+    lmax = -(-units // min(units, cus))
+    e = -(-units // lmax)
+    maxslots = -(-chunks // (units // e)) + 1
+    d = W.grouped(name, n, k, seed=5)
+    cd, sd = dev(d["codes"]), dev(d["scales"])
+    pk = _pack_dev(fmt, cd, n, k)
+    x16 = W.activations(16, k, workload=4, tensor=52)
+    ref16 = M.gemv_qgroup(name, d["codes"], d["scales"], x16)
+    for t in (1, 5, 16):
+        assert nq.nq_gemv_workspace_bytes(fmt, t, n, k) == -(-tiles * 4 // 256) * 256 + r * maxslots * t * 64 * 4
+        g32, g16, _ = _gemv_both_layouts(fmt, cd, pk, sd, x16[:t].copy(), n, k)
+        assert rel_fro(g32, ref16[:t]) <= FP32_TOL, (name, t)
+        assert rel_fro(g32[:, (tiles - r) * 64:], ref16[:t, (tiles - r) * 64:]) <= FP32_TOL, (name, t)
+        assert rel_fro(F.bf16_decode(g16), ref16[:t]) <= BF16_TOL, (name, t)
+
+
 # The output head as bench.py times it (packed row-FP8, 2376 row tiles: 2304
 # whole, 72 spread), T = 1, 16, 33, 64; every row of the 72 spread tiles and a
 # sample; plus the row-major sweep.
