@@ -51,17 +51,18 @@ sys.path.insert(0, ROOT)
 
 # HBM traffic of the headline GEMV launches (packed row-FP8 17408x5120), from
 # `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` runs of
-# `bench.py --rows gemv_fp8row`, in KiB per dispatch, scaled by the same
+# `bench.py --rows gemv_fp8row,gemv_q4g64,gemv_q8g32`, in KiB per dispatch
+# (the headline rows' launches after the warm-up step), scaled by the same
 # counters on `bench.py --calibrate-copy` (a 256 MiB copy reads FETCH_SIZE
 # 131083.5 KiB and writes WRITE_SIZE 262144 KiB: factors 1.99982 and 1.0).
 # Summaries: profiles/gemv_fp8row_17408x5120_hbm_traffic.md.  Valid only for
 # the GEMV sources they were taken on (sha256 prefix over GEMV_SOURCES).
 GEMV_TRAFFIC = {
-    "source_sha256_16": "3a4533d275c4b80e",  # taken before the GEMV source split
+    "source_sha256_16": "f8ef0ac8e4f10098",
     "fetch_factor": 262144.0 / 131083.5,
     "write_factor": 1.0,
-    "fetch_kib": {"gemv_fp8row_T1": 43815.7, "gemv_fp8row_T4": 44003.4, "gemv_fp8row_T16": 44771.9,
-                  "gemv_fp8row_T33": 45902.2},
+    "fetch_kib": {"gemv_fp8row_T1": 43820.4, "gemv_fp8row_T4": 44011.0, "gemv_fp8row_T16": 44771.3,
+                  "gemv_fp8row_T33": 45905.7},
     "write_kib": {"gemv_fp8row_T1": 79.5, "gemv_fp8row_T4": 301.5, "gemv_fp8row_T16": 1189.5,
                   "gemv_fp8row_T33": 2447.5},
 }
