@@ -115,7 +115,8 @@ struct WSrc {
     const uint8_t* e8[4];    // MXFP8: the lane's row of scale bytes [K/32]
     int64_t cstride;         // packed: bytes from chunk c to chunk c + 1
     int q0;                  // first piece of this wave
-    int g;                   // lane group
+    int g;                   // lane group of the load (row-major: lane % 4, see rowmajor_to_frag)
+    int ge;                  // lane group of the fragment (MXFP8 scale bytes)
 };
 
 template <int FMT, bool PK>
@@ -126,17 +127,20 @@ __device__ __forceinline__ WSrc make_wsrc(const uint8_t* w, const void* scales, 
     const int64_t nrb = ((int64_t)N + 15) / 16;
     s.cstride = PK ? nrb * P::BLOCK_CHUNK : 0;
     s.q0 = P::PW * wv;
-    s.g = lane >> 4;
+    s.g = PK ? lane >> 4 : lane & 3;
+    s.ge = lane >> 4;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         int64_t row = row0 + 16 * r + (lane & 15);
         if (row > N - 1) row = N - 1;
+        int64_t rowc = row0 + 16 * r + (lane >> 2);     // row-major loads: four lanes per row
+        if (rowc > N - 1) rowc = N - 1;
         if (PK) {
             int64_t rb = (row0 >> 4) + r;
             if (rb > nrb - 1) rb = nrb - 1;
             s.base[r] = w + rb * P::BLOCK_CHUNK + (int64_t)lane * P::PB;
         } else {
-            s.base[r] = w + row * row_bytes<FMT>(K);
+            s.base[r] = w + rowc * row_bytes<FMT>(K);
         }
         s.e8[r] = reinterpret_cast<const uint8_t*>(scales) + row * (K >> 5);
     }
@@ -153,7 +157,33 @@ __device__ __forceinline__ void load_chunk(WChunk<FMT>& r, const WSrc& src, int6
         const uint8_t* p = PK ? src.base[rb] + c * src.cstride + q * (64 * P::PB)
                               : src.base[rb] + piece_offset<FMT>(c, q, src.g);
         r.p[j] = *reinterpret_cast<const typename P::Piece*>(p);
-        if constexpr (FMT == W_MXFP8) r.e8[j] = src.e8[rb][(c * GV_KC + 64 * q + 16 * src.g) >> 5];
+        if constexpr (FMT == W_MXFP8) r.e8[j] = src.e8[rb][(c * GV_KC + 64 * q + 16 * src.ge) >> 5];
+    }
+}
+
+// Row-major weights are loaded with four neighbouring lanes on one row (lane
+// l: row l / 4 of the row block, the piece's bytes of lane group l % 4), so
+// that each quad of lanes reads one contiguous run of its row; loaded in the
+// fragment's own order (lane 16 g + i on row i) every lane of a quad would
+// address another row, four times the memory requests per load.  The MFMA
+// fragment wants lane 16 g + i on row i: each word is fetched from lane 4 i + g
+// (ds_bpermute: a cross-lane move, no LDS memory).  Packed weights are stored
+// in fragment order already.
+template <int FMT, bool PK>
+__device__ __forceinline__ void rowmajor_to_frag(WChunk<FMT>& r) {
+    if constexpr (!PK) {
+        using P = PieceFmt<FMT>;
+        constexpr int WORDS = P::PB / 4;
+        const int lane = threadIdx.x & 63;
+        const int addr = 4 * (4 * (lane & 15) + (lane >> 4));
+#pragma unroll
+        for (int j = 0; j < 4 * P::PW; ++j) {
+            uint32_t v[WORDS];
+            __builtin_memcpy(v, &r.p[j], P::PB);
+#pragma unroll
+            for (int d = 0; d < WORDS; ++d) v[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v[d]);
+            __builtin_memcpy(&r.p[j], v, P::PB);
+        }
     }
 }
 
@@ -257,7 +287,8 @@ __device__ __forceinline__ v8bf decode_afrag(const WChunk<FMT>& r, int rb, int l
 
 // One chunk of one wave: xrow(cb) gives the LDS element index of the B
 // fragment row for token block cb (lane's token), kl the chunk's first column
-// in the LDS activation rows, scs / sbase the group scales of the chunk.
+// in the LDS activation rows, scs / sbase the group scales of the chunk.  The
+// weights are in fragment order (rowmajor_to_frag already applied).
 template <int FMT, int NCB, bool PK>
 __device__ __forceinline__ void chunk_mfma(const WChunk<FMT>& wc, const uint16_t* xs, const int (&xrow)[NCB], int kl,
                                            const uint16_t* scs, int sgroup0, int wv, int lg,
@@ -639,12 +670,17 @@ __device__ __forceinline__ void direct_spread(const uint8_t* __restrict__ w, con
                 const int64_t rbg = rowb / 16 < nrb - 1 ? rowb / 16 : nrb - 1;   // blocks past N are clamped
                 pw = wlane + (rbg * P::BLOCK_CHUNK + (int64_t)c * cstride + q * (64 * P::PB));
             }
-            if constexpr (!PK || FMT == W_MXFP8 || GS != 0) {
+            if constexpr (FMT == W_MXFP8 || GS != 0) {     // the lane's fragment row (scales)
                 const int64_t lim = (int64_t)N - 1 - rowb;                   // rows past N are clamped
                 const int lr = (int64_t)li < lim ? li : (int)lim;
                 row = rowb + lr;
             }
-            if constexpr (!PK) pw = w + row * row_bytes<FMT>(K) + piece_offset<FMT>(c, q, lg);
+            if constexpr (!PK) {
+                // four lanes per row (see rowmajor_to_frag)
+                const int64_t lim = (int64_t)N - 1 - rowb;
+                const int lc = (int64_t)(lane >> 2) < lim ? (lane >> 2) : (int)lim;
+                pw = w + (rowb + lc) * row_bytes<FMT>(K) + piece_offset<FMT>(c, q, lane & 3);
+            }
             wr[slot].p[j] = *reinterpret_cast<const typename P::Piece*>(pw);
             if constexpr (GS != 0) {
                 if (j % P::PW == 0) {
@@ -707,6 +743,7 @@ __device__ __forceinline__ void direct_spread(const uint8_t* __restrict__ w, con
         if (cp_c == 0 && cp_i > 0) close_segment(kseg++);   // this unit opens the next tile (uniform)
         ++cp_i;
         if (++cp_c == C) cp_c = 0;
+        rowmajor_to_frag<FMT, PK>(wr[slot]);
         if constexpr (GS != 0) {
             // Group scales: the MFMAs take the activations as A and the
             // weights as B (both fragments hold the same k of their lane, so
@@ -960,6 +997,7 @@ __global__ __launch_bounds__(256, (stream_min_waves<FMT, NCB>())) void gemv_mfma
     WChunk<FMT> ring[D];
     auto body = [&](int c, int u) {
         const int buf = c & 1;
+        rowmajor_to_frag<FMT, PK>(ring[u]);
         chunk_mfma<FMT, NCB, PK>(ring[u], xs[buf], xrow, 0, scs[buf], 0, wv, lg, acc);
         store_x((c + 1) & 1, (u + 1) % D);
         load_x(u, min(c + D, nch - 1));
@@ -1079,7 +1117,8 @@ __global__ __launch_bounds__(256) void gemv_resident_kernel(const uint8_t* __res
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) xrow[cb] = min(cb * 16 + li, T) * xpitch;
 
-    auto compute = [&](const WChunk<FMT>& wc, int c) {
+    auto compute = [&](WChunk<FMT>& wc, int c) {
+        rowmajor_to_frag<FMT, PK>(wc);
         chunk_mfma<FMT, NCB, PK>(wc, xs, xrow, c * GV_KC, scs, GS ? c * GV_KC / (GS ? GS : 1) : 0, wv, lg, acc);
     };
 
@@ -1195,6 +1234,7 @@ __global__ __launch_bounds__(256) void gemv_direct_kernel(const uint8_t* __restr
         for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = v4f{0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](int u) {
+        rowmajor_to_frag<FMT, PK>(wr[u]);
 #pragma unroll
         for (int ls = 0; ls < 2; ++ls) {
 #pragma unroll
