@@ -58,11 +58,11 @@ sys.path.insert(0, ROOT)
 # Summaries: profiles/gemv_fp8row_17408x5120_hbm_traffic.md.  Valid only for
 # the GEMV sources they were taken on (sha256 prefix over GEMV_SOURCES).
 GEMV_TRAFFIC = {
-    "source_sha256_16": "f8ef0ac8e4f10098",
+    "source_sha256_16": "fffa87d1b9da3d5e",
     "fetch_factor": 262144.0 / 131083.5,
     "write_factor": 1.0,
-    "fetch_kib": {"gemv_fp8row_T1": 43820.4, "gemv_fp8row_T4": 44011.0, "gemv_fp8row_T16": 44771.3,
-                  "gemv_fp8row_T33": 45905.7},
+    "fetch_kib": {"gemv_fp8row_T1": 43821.7, "gemv_fp8row_T4": 44011.5, "gemv_fp8row_T16": 44768.7,
+                  "gemv_fp8row_T33": 45913.2},
     "write_kib": {"gemv_fp8row_T1": 79.5, "gemv_fp8row_T4": 301.5, "gemv_fp8row_T16": 1189.5,
                   "gemv_fp8row_T33": 2447.5},
 }
