@@ -56,9 +56,9 @@ sys.path.insert(0, ROOT)
 # counters on `bench.py --calibrate-copy` (a 256 MiB copy reads FETCH_SIZE
 # 131083.5 KiB and writes WRITE_SIZE 262144 KiB: factors 1.99982 and 1.0).
 # Summaries: profiles/gemv_fp8row_17408x5120_hbm_traffic.md.  Valid only for
-# the GEMV sources they were taken on (sha256 prefix over GEMV_SOURCES).
+# the GEMV code they were taken on (gemv_source_hash over GEMV_SOURCES).
 GEMV_TRAFFIC = {
-    "source_sha256_16": "fffa87d1b9da3d5e",
+    "source_sha256_16": "3212ddf820bd1785",
     "fetch_factor": 262144.0 / 131083.5,
     "write_factor": 1.0,
     "fetch_kib": {"gemv_fp8row_T1": 43821.7, "gemv_fp8row_T4": 44011.5, "gemv_fp8row_T16": 44768.7,
@@ -622,15 +622,25 @@ def cpu_baseline():
     return line
 
 
+def gemv_source_hash():
+    """sha256 prefix of the GEMV sources' code: comments and whitespace are
+    dropped first, so that only a change of code invalidates the counters."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for name in GEMV_SOURCES:
+        with open(os.path.join(ROOT, "quantized_weight_linear_amd", "csrc", name)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
+    return h.hexdigest()[:16]
+
+
 def gemv_traffic(names):
     """Measured HBM bytes per launch of the headline GEMV, or None when the
     kernel source changed since the counters were taken."""
-    import hashlib
-    h = hashlib.sha256()
-    for name in GEMV_SOURCES:
-        with open(os.path.join(ROOT, "quantized_weight_linear_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    sha = h.hexdigest()[:16]
+    sha = gemv_source_hash()
     t = GEMV_TRAFFIC
     if sha != t["source_sha256_16"] or any(n not in t["fetch_kib"] for n in names):
         return None

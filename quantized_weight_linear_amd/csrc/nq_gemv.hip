@@ -89,7 +89,11 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     // 18.8 / 20.6; 16448 x 5120: T = 16 18.1 / 19.2); the resident kernel's K
     // split is slower than both.  With more leftover tiles or a shorter K the
     // direct kernel is as fast or faster (24576 x 5120: 24.5 against 26.7 us;
-    // 17408 x 2048: 10.9 against 11.6 us at T = 1).
+    // 17408 x 2048: 10.9 against 11.6 us at T = 1).  The grouped formats take
+    // the same path at one token block (their spread units load their own
+    // scales, see direct_spread): 17408 x 5120 Q4 T = 1 / 4 / 8 19.2 / 19.7 /
+    // 21.0 -> 15.4 / 15.6 / 16.0 us and Q8G32 27.3 / 29.5 / 29.9 -> 22.7 /
+    // 23.3 / 24.2 against the resident kernel or the streaming kernel's K split.
     const int64_t cus_n = (int64_t)device_cu_count();
     const bool spread_one_round = (fmt_group(fmt) == 0 || Tc <= 16) && allow_spread && p.tiles > cus_n &&
                                   8 * (p.tiles - cus_n) <= cus_n && chunks >= 16;
@@ -108,9 +112,10 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     // resident variant: from the split count that leaves the busiest CU the
     // fewest chunks, the smallest whose slice fits in LDS and whose FP32
     // partials stay within 12% of the weight bytes; only for one token block
-    // with the row tiles covering the CUs (17408 x 5120 T = 1, 5 splits: Q4
-    // 19.4 against 21.3 us for the streaming kernel without a split, Q8G32
-    // 26.8 / 30.7).  With fewer tiles than CUs the streaming kernel with the
+    // with the row tiles covering the CUs and more leftover tiles than the
+    // spread path takes (measured on 17408 x 5120 T = 1 before that shape went
+    // to the spread path, 5 splits: Q4 19.4 against 21.3 us for the streaming
+    // kernel without a split, Q8G32 26.8 / 30.7).  With fewer tiles than CUs the streaming kernel with the
     // balanced split is as fast or faster: the slice that fits in LDS forces
     // more splits than the balance needs (5120 x 17408: row-FP8 T = 17 32.9
     // -> 19.3 us, Q8G32 T = 8 36.8 -> 24.8, Q4 T = 1 21.7 -> 19.1; Q8G32
@@ -122,10 +127,11 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     // us for the resident kernel, whose split adds the partial exchange).
     const bool many_tiles = p.tiles >= 4 * (int64_t)device_cu_count();
     // Grouped formats between one and two tiles per CU, not a multiple of the
-    // CUs: from 5 tokens on the streaming kernel with K split in three (see
-    // below) beats the resident kernel (17408 x 5120 Q8G32 T = 8 / 16: 30.2 /
-    // 32.6 -> 28.6 / 30.3 us; Q4 level); below that the resident one wins (T = 1:
-    // Q4 19.5 against 21.2 us, Q8G32 26.9 / 28.1).
+    // CUs (and not taken by the spread path): from 5 tokens on the streaming
+    // kernel with K split in three (see below) beats the resident kernel
+    // (measured on 17408 x 5120 before the spread path: Q8G32 T = 8 / 16:
+    // 30.2 / 32.6 -> 28.6 / 30.3 us; Q4 level); below that the resident one
+    // wins (T = 1: Q4 19.5 against 21.2 us, Q8G32 26.9 / 28.1).
     const bool grouped_leftover = fmt_group(fmt) != 0 && p.tiles > (int64_t)device_cu_count() &&
                                   p.tiles < 2 * (int64_t)device_cu_count() &&
                                   p.tiles % (int64_t)device_cu_count() != 0 && chunks >= 3 * (int64_t)min_chunks;
