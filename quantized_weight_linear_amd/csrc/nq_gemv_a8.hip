@@ -46,10 +46,12 @@ constexpr int a8_depth() {
     return NCB >= 3 ? 2 : 3;
 }
 
-template <int FMT, int NCB>
+template <int FMT, int NCB, bool SH>
 struct A8Chunk {
     typename A8Piece<FMT>::T w[4];      // group q's weight piece
-    uint4 x[4][NCB];                    // group q's activation codes, token block cb
+    // SH: this thread's share of the chunk's activation codes (staged to LDS);
+    // otherwise the lane's B fragments [q * NCB + cb]
+    uint4 x[SH ? NCB : 4 * NCB];
     uint4 as[NCB];                      // the token's activation scales of the chunk's 4 groups
     uint2 ws[4];                        // row 4 lg + e: FP16 weight scales of the 4 groups
 };
@@ -76,19 +78,31 @@ __device__ __forceinline__ v4i q4_to_biased_bytes(uint2 p) {
     return v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
 }
 
-template <int FMT, int NCB, bool PK>
-__global__ __launch_bounds__(64) void gemv_a8_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ wsc,
+// SH: the workgroup's WG_WAVES waves (row blocks) share each chunk's
+// activation codes, staged in LDS (two or more token blocks: 17408x5120
+// Q8G64 T = 33 46.8 -> 40.9 us, 5120x17408 44.8 -> 34.9); otherwise each
+// 64-thread workgroup loads its own B fragments into registers, and the
+// single-wave workgroups spread evenly over the SIMDs (one token block:
+// 17408x5120 21.7 against 25.8 us with four row blocks per workgroup).
+template <int FMT, int NCB, bool PK, bool SH>
+__global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_a8_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ wsc,
                                                      const int8_t* __restrict__ aq, const float* __restrict__ asc,
                                                      int T, int N, int64_t K, int chunks_per_split, int splits,
                                                      float* __restrict__ partial, unsigned* __restrict__ counters,
                                                      int bf16_out, void* __restrict__ y) {
     using P = A8Piece<FMT>;
     constexpr int D = a8_depth<NCB>();
-    const int lane = threadIdx.x;
+    constexpr int TP = 16 * NCB;                 // token rows of the staged activation codes
+    constexpr int XPITCH = A8_KC + 16;           // bytes per LDS row: rows shift by 4 banks
+    __shared__ __attribute__((aligned(16))) uint8_t xs[2][SH ? TP * XPITCH : 16];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
     const int li = lane & 15, lg = lane >> 4;
-    const int rb = blockIdx.x;
-    const int split = blockIdx.y;
     const int64_t nrb = ((int64_t)N + 15) / 16;
+    const int rb_own = (SH ? WG_WAVES : 1) * (int)blockIdx.x + (tid >> 6);   // this wave's row block
+    const bool rb_valid = rb_own < nrb;
+    const int rb = rb_valid ? rb_own : (int)nrb - 1;           // past the last: loads clamped, nothing written
+    const int split = blockIdx.y;
     const int64_t G = K / 64;
     const int64_t total_chunks = K / A8_KC;
     const int64_t c_begin = (int64_t)split * chunks_per_split;
@@ -113,25 +127,37 @@ __global__ __launch_bounds__(64) void gemv_a8_kernel(const uint8_t* __restrict__
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         const int t = cb * 16 + li;
-        xoff[cb] = (int)((int64_t)t * K + 16 * lg);
+        xoff[cb] = (int)((int64_t)t * K + 16 * lg);        // !SH: the lane's B fragment row
         aoff[cb] = (int)((int64_t)t * G * 4);
     }
     int soff[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) soff[e] = (int)(((int64_t)rb * 16 + 4 * lg + e) * G * 2);
 
-    A8Chunk<FMT, NCB> ring[D];
+    A8Chunk<FMT, NCB, SH> ring[D];
     auto load = [&](int slot, int64_t c) {
-        A8Chunk<FMT, NCB>& r = ring[slot];
+        A8Chunk<FMT, NCB, SH>& r = ring[slot];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             r.w[q] = *reinterpret_cast<const typename P::T*>(wrow + c * wcstride + q * wqstride);
+        if constexpr (SH) {
+            // piece j of thread tid is row (tid + 256 j) / 16, 16 bytes
+            // (tid + 256 j) % 16 (rows >= T read zero)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+            for (int j = 0; j < NCB; ++j) {
+                const int idx = tid + 256 * j;
+                r.x[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       xr, (int)((int64_t)(idx >> 4) * K + c * A8_KC + 16 * (idx & 15)),
+                                                       0, 0));
+            }
+        } else {
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-                r.x[q][cb] = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[cb] + (int)(c * A8_KC) + 64 * q, 0, 0));
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    r.x[q * NCB + cb] = __builtin_bit_cast(
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[cb] + (int)(c * A8_KC) + 64 * q, 0, 0));
+        }
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
             r.as[cb] = __builtin_bit_cast(uint4,
@@ -147,8 +173,17 @@ __global__ __launch_bounds__(64) void gemv_a8_kernel(const uint8_t* __restrict__
     const v4i bias = {0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000};
     const v4i neg8 = {(int)0xF8F8F8F8u, (int)0xF8F8F8F8u, (int)0xF8F8F8F8u, (int)0xF8F8F8F8u};
 
-    auto compute = [&](int slot) {
-        const A8Chunk<FMT, NCB>& r = ring[slot];
+    auto store_x = [&](int buf, int slot) {
+        if constexpr (SH)
+#pragma unroll
+        for (int j = 0; j < NCB; ++j) {
+            const int idx = tid + 256 * j;
+            *reinterpret_cast<uint4*>(&xs[buf][(idx >> 4) * XPITCH + 16 * (idx & 15)]) = ring[slot].x[j];
+        }
+    };
+
+    auto compute = [&](int slot, const uint8_t* xb) {
+        const A8Chunk<FMT, NCB, SH>& r = ring[slot];
         float wsf[4][4], nb[4][4];     // [e][q]
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -167,7 +202,9 @@ __global__ __launch_bounds__(64) void gemv_a8_kernel(const uint8_t* __restrict__
             else a = __builtin_bit_cast(v4i, r.w[q]);
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
-                const v4i b = __builtin_bit_cast(v4i, r.x[q][cb]);
+                // B fragment: token cb * 16 + i, codes 64 q + 16 g .. + 16 of the chunk
+                const v4i b = SH ? *reinterpret_cast<const v4i*>(&xb[(cb * 16 + li) * XPITCH + 64 * q + 16 * lg])
+                                 : __builtin_bit_cast(v4i, r.x[q * NCB + cb]);
                 v4i d;
                 if constexpr (FMT == W_Q4G64) {
                     d = __builtin_amdgcn_mfma_i32_16x16x64_i8(neg8, b, bias, 0, 0, 0);
@@ -186,24 +223,40 @@ __global__ __launch_bounds__(64) void gemv_a8_kernel(const uint8_t* __restrict__
         }
     };
 
+    // One chunk c (ring slot u = c mod D): compute from LDS buffer c & 1,
+    // stage the activation codes of chunk c + 1, request chunk c + D into
+    // slot u (indices clamped to the last chunk, so the body has no branch),
+    // barrier.  The four waves (four row blocks) share the staged codes.
+    // Without SH: compute from the registers, refill the slot, no barrier.
+    auto body = [&](int c, int u) {
+        compute(u, xs[c & 1]);
+        if constexpr (SH) store_x((c + 1) & 1, (u + 1) % D);
+        load(u, c_begin + min(c + D, nch - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (SH) __syncthreads();
+    };
     if (nch > 0) {
 #pragma unroll
         for (int d = 0; d < D; ++d) load(d, c_begin + min(d, nch - 1));
+        if constexpr (SH) {
+            store_x(0, 0);
+            __syncthreads();
+        }
         int c = 0;
         for (; c + D <= nch; c += D) {
 #pragma unroll
-            for (int u = 0; u < D; ++u) {
-                compute(u);
-                load(u, c_begin + min(c + u + D, nch - 1));
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            for (int u = 0; u < D; ++u) body(c + u, u);
         }
 #pragma unroll
-        for (int u = 0; u < D - 1; ++u)
-            if (c + u < nch) compute(u);
+        for (int u = 0; u < D - 1; ++u) {
+            if (c + u < nch) {
+                if constexpr (SH) body(c + u, u);     // the next chunk's codes are staged here
+                else compute(u, xs[0]);
+            }
+        }
     }
 
-    wave_finish<NCB>(acc, T, N, rb, split, splits, partial, counters, bf16_out, y);
+    if (rb_valid) wave_finish<NCB>(acc, T, N, rb, split, splits, partial, counters, bf16_out, y);
 }
 
 // ---------------------------------------------------------------------------
@@ -225,7 +278,10 @@ template <int FMT, int NCB, bool PK>
 static void launch_a8_ncb(const WavePlan& p, const void* w, const uint16_t* wsc, const int8_t* aq, const float* asc,
                           int Tc, int64_t N, int64_t K, bool bf16_out, void* y, float* partial, unsigned* counters,
                           hipStream_t stream) {
-    gemv_a8_kernel<FMT, NCB, PK><<<dim3((unsigned)p.rbs, (unsigned)p.splits), 64, 0, stream>>>(
+    constexpr bool SH = NCB >= 2;
+    constexpr int NW = SH ? WG_WAVES : 1;
+    gemv_a8_kernel<FMT, NCB, PK, SH><<<dim3((unsigned)((p.rbs + NW - 1) / NW), (unsigned)p.splits), 64 * NW, 0,
+                                       stream>>>(
         reinterpret_cast<const uint8_t*>(w), wsc, aq, asc, Tc, (int)N, K, p.chunks_per_split, p.splits, partial,
         counters, bf16_out ? 1 : 0, y);
 }

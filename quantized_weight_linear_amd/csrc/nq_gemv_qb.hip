@@ -45,19 +45,34 @@ __device__ __forceinline__ int extract_code(const uint32_t (&w)[N], int pos) {
     return __builtin_amdgcn_sbfe((int)__builtin_amdgcn_alignbit(w[wi + 1], w[wi], r), 0, B);
 }
 
-template <int B, int NCB, bool PK>
-__global__ __launch_bounds__(64) void gemv_qbits_kernel(const uint8_t* __restrict__ w,
+// SH: the workgroup's WG_WAVES waves (row blocks) share each chunk's
+// activations, staged in LDS (two or more token blocks, where the activation
+// loads outweigh the weights: 17408x5120 Q5 T = 33 75.9 -> 44.4 us);
+// otherwise each 64-thread workgroup loads its own activation fragments into
+// registers, and the single-wave workgroups spread evenly over the SIMDs
+// (with four row blocks per workgroup, 1088 row blocks are 272 workgroups on
+// 256 CUs: T = 1 23.6 -> 28.6 us).
+template <int B, int NCB, bool PK, bool SH>
+__global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_qbits_kernel(const uint8_t* __restrict__ w,
                                                         const uint16_t* __restrict__ wsc,
                                                         const uint16_t* __restrict__ x, int T, int N, int64_t K,
                                                         int chunks_per_split, int splits,
                                                         float* __restrict__ partial, unsigned* __restrict__ counters,
                                                         int bf16_out, void* __restrict__ y) {
     using L = QbLayout<B>;
-    const int lane = threadIdx.x;
+    constexpr int TP = 16 * NCB;                 // token rows of the staged activations
+    constexpr int XPITCH = WG_KC + 8;            // bf16 per LDS row: rows shift by 4 banks
+    constexpr int XP = TP * (WG_KC / 8) / 256;   // 16-byte activation pieces per thread and chunk
+    constexpr int XR = SH ? XP : 8 * NCB;        // activation registers per ring slot
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][SH ? TP * XPITCH : 8];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
     const int li = lane & 15, lg = lane >> 4;
-    const int rb = blockIdx.x;
-    const int split = blockIdx.y;
     const int64_t nrb = ((int64_t)N + 15) / 16;
+    const int rb_own = (SH ? WG_WAVES : 1) * (int)blockIdx.x + (tid >> 6);   // this wave's row block
+    const bool rb_valid = rb_own < nrb;
+    const int rb = rb_valid ? rb_own : (int)nrb - 1;           // past the last: loads clamped, nothing written
+    const int split = blockIdx.y;
     const int64_t G = K / 64;
     const int64_t total_chunks = K / WG_KC;
     const int64_t c_begin = (int64_t)split * chunks_per_split;
@@ -77,7 +92,7 @@ __global__ __launch_bounds__(64) void gemv_qbits_kernel(const uint8_t* __restric
         __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)((int64_t)T * K * 2), WG_BUF_FLAGS);
     const __amdgpu_buffer_rsrc_t sr =
         __builtin_amdgcn_make_buffer_rsrc((void*)wsc, (short)0, (int)((int64_t)N * G * 2), WG_BUF_FLAGS);
-    int xoff[NCB];
+    int xoff[NCB];        // !SH: the lane's B fragment rows (token cb * 16 + i, columns 16 g ..)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) xoff[cb] = (int)(((int64_t)(cb * 16 + li) * K + 16 * lg) * 2);
     int soff[4];
@@ -86,10 +101,14 @@ __global__ __launch_bounds__(64) void gemv_qbits_kernel(const uint8_t* __restric
 
     struct Chunk {
         uint32_t wd[PK ? L::WORDS : 4 * L::GWORDS];
-        uint4 xa[4][2][NCB];
+        // SH: this thread's share of the chunk's activations, staged to LDS one
+        // chunk ahead; otherwise the lane's B fragments [(q * 2 + h) * NCB + cb]
+        uint4 xa[XR];
         uint2 ws[4];
     };
-    constexpr int D = NCB >= 3 ? 2 : 3;
+    // ring depth: two at three or more token blocks, and for Q6 in the shared
+    // form (its wider code windows would spill at three within two workgroups per CU)
+    constexpr int D = (NCB >= 3 || (SH && B == 6)) ? 2 : 3;
     Chunk ring[D];
     auto load = [&](int slot, int64_t c) {
         Chunk& r = ring[slot];
@@ -115,25 +134,44 @@ __global__ __launch_bounds__(64) void gemv_qbits_kernel(const uint8_t* __restric
                     r.wd[q * L::GWORDS + i] = __builtin_amdgcn_raw_buffer_load_b32(wr, off + 4 * i, 0, 0);
             }
         }
+        if constexpr (SH) {
+            // piece idx = tid + 256 j is row idx / 32, 16 bytes idx % 32 (rows >= T read zero)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+            for (int j = 0; j < XP; ++j) {
+                const int idx = tid + 256 * j;
+                const int t = idx >> 5, pc = idx & 31;
+                r.xa[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        xr, (int)(((int64_t)t * K + c * WG_KC + 8 * pc) * 2), 0, 0));
+            }
+        } else {
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb)
-                    r.xa[q][h][cb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                   xr, xoff[cb] + (int)(c * WG_KC * 2) + 128 * q + 16 * h,
-                                                                   0, 0));
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+                        r.xa[(q * 2 + h) * NCB + cb] = __builtin_bit_cast(
+                            uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[cb] + (int)(c * WG_KC * 2) + 128 * q + 16 * h,
+                                                                         0, 0));
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             r.ws[e] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(sr, soff[e] + (int)(c * 8), 0, 0));
+    };
+    auto store_x = [&](int buf, int slot) {
+        if constexpr (SH)
+#pragma unroll
+        for (int j = 0; j < XP; ++j) {
+            const int idx = tid + 256 * j;
+            *reinterpret_cast<uint4*>(&xs[buf][(idx >> 5) * XPITCH + 8 * (idx & 31)]) = ring[slot].xa[j];
+        }
     };
 
     v4f acc[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int slot) {
+    auto compute = [&](int slot, const uint16_t* xb) {
         const Chunk& r = ring[slot];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -169,9 +207,14 @@ __global__ __launch_bounds__(64) void gemv_qbits_kernel(const uint8_t* __restric
                 }
                 const v8bf af = __builtin_bit_cast(v8bf, make_uint4(o[0], o[1], o[2], o[3]));
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb)
-                    d[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(v8bf, r.xa[q][h][cb]),
-                                                                    h == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : d[cb], 0, 0, 0);
+                for (int cb = 0; cb < NCB; ++cb) {
+                    // B fragment: token cb * 16 + i, columns 64 q + 16 g + 8 h .. + 8 of the chunk
+                    const v8bf bx =
+                        SH ? *reinterpret_cast<const v8bf*>(&xb[(cb * 16 + li) * XPITCH + 64 * q + 16 * lg + 8 * h])
+                           : __builtin_bit_cast(v8bf, r.xa[(q * 2 + h) * NCB + cb]);
+                    d[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bx, h == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : d[cb],
+                                                                    0, 0, 0);
+                }
             }
             float sc[4];
 #pragma unroll
@@ -186,23 +229,40 @@ __global__ __launch_bounds__(64) void gemv_qbits_kernel(const uint8_t* __restric
         }
     };
 
+    // One chunk c (ring slot u = c mod D): compute from LDS buffer c & 1,
+    // stage the activations of chunk c + 1 (slot (u + 1) mod D), request the
+    // weights, scales and activations of chunk c + D into slot u (indices
+    // clamped to the last chunk, so the body has no branch), barrier.  The
+    // four waves of the workgroup (four row blocks) share the staged chunk.
+    // Without SH: compute from the registers, refill the slot, no barrier.
+    auto body = [&](int c, int u) {
+        compute(u, xs[c & 1]);
+        if constexpr (SH) store_x((c + 1) & 1, (u + 1) % D);
+        load(u, c_begin + min(c + D, nch - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (SH) __syncthreads();
+    };
     if (nch > 0) {
 #pragma unroll
         for (int d = 0; d < D; ++d) load(d, c_begin + min(d, nch - 1));
+        if constexpr (SH) {
+            store_x(0, 0);
+            __syncthreads();
+        }
         int c = 0;
         for (; c + D <= nch; c += D) {
 #pragma unroll
-            for (int u = 0; u < D; ++u) {
-                compute(u);
-                load(u, c_begin + min(c + u + D, nch - 1));
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            for (int u = 0; u < D; ++u) body(c + u, u);
         }
 #pragma unroll
-        for (int u = 0; u < D - 1; ++u)
-            if (c + u < nch) compute(u);
+        for (int u = 0; u < D - 1; ++u) {
+            if (c + u < nch) {
+                if constexpr (SH) body(c + u, u);     // the next chunk's activations are staged here
+                else compute(u, xs[0]);
+            }
+        }
     }
-    wave_finish<NCB>(acc, T, N, rb, split, splits, partial, counters, bf16_out, y);
+    if (rb_valid) wave_finish<NCB>(acc, T, N, rb, split, splits, partial, counters, bf16_out, y);
 }
 
 // Packed layout: thread per (chunk, row block, lane); the lane's 8 B bytes are
@@ -281,7 +341,10 @@ int64_t gemv_qbits_workspace_bytes(int64_t T, int64_t N, int64_t K) {
 template <int B, int NCB, bool PK>
 static void launch_qb_ncb(const WavePlan& p, const void* w, const uint16_t* wsc, const uint16_t* x, int Tc, int64_t N,
                           int64_t K, bool bf16_out, void* y, float* partial, unsigned* counters, hipStream_t stream) {
-    gemv_qbits_kernel<B, NCB, PK><<<dim3((unsigned)p.rbs, (unsigned)p.splits), 64, 0, stream>>>(
+    constexpr bool SH = NCB >= 2;
+    constexpr int NW = SH ? WG_WAVES : 1;
+    gemv_qbits_kernel<B, NCB, PK, SH><<<dim3((unsigned)((p.rbs + NW - 1) / NW), (unsigned)p.splits), 64 * NW, 0,
+                                        stream>>>(
         reinterpret_cast<const uint8_t*>(w), wsc, x, Tc, (int)N, K, p.chunks_per_split, p.splits, partial, counters,
         bf16_out ? 1 : 0, y);
 }

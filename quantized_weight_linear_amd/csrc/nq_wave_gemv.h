@@ -16,6 +16,7 @@
 namespace nq {
 
 constexpr int WG_KC = 256;                  // columns per chunk: 4 groups of 64
+constexpr int WG_WAVES = 4;                 // waves (row blocks) per workgroup, sharing each chunk's activations
 constexpr unsigned WG_BUF_FLAGS = 0x00020000u;
 constexpr int WG_CPOL_DEVICE = 16;          // sc1
 constexpr int64_t WG_OOB = 0x7FFFFFF0 / 4;  // an element index whose load reads zero
@@ -52,7 +53,7 @@ template <int NCB>
 __device__ __forceinline__ void wave_finish(v4f (&acc)[NCB], int T, int N, int rb, int split, int splits,
                                             float* __restrict__ partial, unsigned* __restrict__ counters,
                                             int bf16_out, void* __restrict__ y) {
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     const int li = lane & 15, lg = lane >> 4;
     const int64_t n0 = (int64_t)rb * 16 + 4 * lg;
     if (splits == 1) {
