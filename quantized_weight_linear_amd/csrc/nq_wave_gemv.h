@@ -1,6 +1,8 @@
 // Shared parts of the wave-per-row-block GEMVs (the A8 decode GEMV and the
-// Q3 / Q5 / Q6 GEMV): one 64-thread workgroup owns 16 weight rows over its K
-// range, so a wave's sums need no cross-wave reduction.  Output layout of a
+// Q3 / Q5 / Q6 GEMV): one wave owns 16 weight rows over its K range, so a
+// wave's sums need no cross-wave reduction.  At one token block each wave is
+// a workgroup of its own; with more, WG_WAVES waves (consecutive row blocks)
+// form a workgroup and share each chunk's activations through LDS.  Output layout of a
 // 16x16 MFMA result: lane 16 g + i holds rows 4 g + e (e = 0..3) of token i of
 // the token block.  With a K split the partial sums go to a workspace
 // [splits][T][rows padded to 16] through device-coherent stores (the cache
