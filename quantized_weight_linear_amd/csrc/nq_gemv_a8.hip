@@ -4,9 +4,11 @@
 // with int8 activation codes aq and FP32 scales as from the per-token-per-64
 // quantizer, and Q8 group-64 (or Q4 group-64) weights with FP16 scales.
 //
-// One wave per 16-row block (a 64-thread workgroup): the wave owns its rows
-// over its K range outright, so nothing is shared through LDS and no barrier
-// runs.  A chunk is 256 columns = 4 groups of 64.  For group q of chunk c,
+// One wave per 16-row block: the wave owns its rows over its K range
+// outright (no cross-wave sum).  At one token block each wave is a 64-thread
+// workgroup of its own and no barrier runs; from two token blocks on, four
+// waves share each chunk's activation codes through LDS (one barrier per
+// chunk).  A chunk is 256 columns = 4 groups of 64.  For group q of chunk c,
 // lane 16 g + i holds the 16 codes k = 256 c + 64 q + 16 g + [0, 16) of row i
 // (the A fragment of one v_mfma_i32_16x16x64_i8) and the same 16 activation
 // codes of token i of the token block (the B fragment): A and B use the same
@@ -23,7 +25,8 @@
 //     acc = fma(X, as, acc).
 // Weights stream from HBM into a register ring, 3 chunks deep (2 with three or
 // four token blocks); activation codes and scales come through buffer loads
-// whose out-of-range offsets read zero (tokens t >= T).  With a workspace the
+// whose out-of-range offsets read zero (tokens t >= T).  Row-major weights
+// are loaded four lanes to a row and moved into fragment order by ds_bpermute.  With a workspace the
 // K range is split over workgroups and the partial sums are exchanged as in
 // the BF16-activation GEMV (device-coherent stores and loads, a counter per
 // row block, the last arriver sums the splits in order: deterministic).
@@ -109,12 +112,15 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_a8_k
     int nch = (int)(total_chunks - c_begin);
     if (nch > chunks_per_split) nch = chunks_per_split;
 
-    // weights: the lane's row (row-major; rows past N clamped, never written)
-    // or its piece of the row block (packed)
-    int64_t row = (int64_t)rb * 16 + li;
-    if (row > N - 1) row = N - 1;
+    // weights: the lane's piece of the row block (packed), or (row-major) a
+    // row with four neighbouring lanes on it, lane l on row l / 4 of the
+    // block at lane group l % 4, so that each quad reads one contiguous run;
+    // the pieces are moved into fragment order (lane 16 g + i on row i) by
+    // ds_bpermute before use.  Rows past N are clamped (never written).
+    int64_t rowc = (int64_t)rb * 16 + (lane >> 2);
+    if (rowc > N - 1) rowc = N - 1;
     const uint8_t* wrow = PK ? w + (int64_t)rb * P::BLOCK_CHUNK + (int64_t)lane * P::PB
-                             : w + row * (FMT == W_Q4G64 ? K / 2 : K) + (int64_t)lg * P::PB;
+                             : w + rowc * (FMT == W_Q4G64 ? K / 2 : K) + (int64_t)(lane & 3) * P::PB;
     const int64_t wcstride = PK ? nrb * P::BLOCK_CHUNK : A8_KC * P::PB / 16;
     const int64_t wqstride = PK ? 64 * P::PB : 4 * P::PB;
     const __amdgpu_buffer_rsrc_t xr =
@@ -183,7 +189,18 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_a8_k
     };
 
     auto compute = [&](int slot, const uint8_t* xb) {
-        const A8Chunk<FMT, NCB, SH>& r = ring[slot];
+        A8Chunk<FMT, NCB, SH>& r = ring[slot];
+        if constexpr (!PK) {
+            const int addr = 4 * (4 * li + lg);       // fragment lane 16 g + i takes lane 4 i + g's words
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t v[P::PB / 4];
+                __builtin_memcpy(v, &r.w[q], P::PB);
+#pragma unroll
+                for (int d = 0; d < P::PB / 4; ++d) v[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v[d]);
+                __builtin_memcpy(&r.w[q], v, P::PB);
+            }
+        }
         float wsf[4][4], nb[4][4];     // [e][q]
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
