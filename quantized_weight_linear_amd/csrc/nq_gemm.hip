@@ -593,6 +593,45 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the empty tail loads
 
+    // Output.  A tile inside the matrix (every tile of the prefill shapes)
+    // writes without per-element bounds checks, each output type in a loop of
+    // its own: checked per element, every store had become a branch of its own
+    // (64 per wave and tile).
+    auto value = [&](int i, int j, int e, int ml, int nl) {
+        float v = acc[i][j][e];
+        if constexpr (!W8A8) v = (v * s_rs[ml]) * s_rs[BM + nl];
+        return v;
+    };
+    if (m0 + BM <= M && n0 + BN <= N) {
+        if (bf16_out) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int nl = wc0 + 32 * j + (lane & 31);
+                    uint16_t* yc = reinterpret_cast<uint16_t*>(y) + (int64_t)m0 * N + n0 + nl;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int ml = wr0 + 32 * i + d_row(lane, e);
+                        yc[(int64_t)ml * N] = (uint16_t)f32_to_bf16_rne(value(i, j, e, ml, nl));
+                    }
+                }
+        } else {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int nl = wc0 + 32 * j + (lane & 31);
+                    float* yc = reinterpret_cast<float*>(y) + (int64_t)m0 * N + n0 + nl;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int ml = wr0 + 32 * i + d_row(lane, e);
+                        yc[(int64_t)ml * N] = value(i, j, e, ml, nl);
+                    }
+                }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -600,15 +639,12 @@ __global__ __launch_bounds__(64 * GemmCfg<W8A8>::NW) void gemm_kernel(
             const int nl = wc0 + 32 * j + (lane & 31);
             const int n = n0 + nl;
             if (n >= N) continue;
-            float sw = 1.0f;
-            if constexpr (!W8A8) sw = s_rs[BM + nl];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int ml = wr0 + 32 * i + d_row(lane, e);
                 const int m = m0 + ml;
                 if (m >= M) continue;
-                float v = acc[i][j][e];
-                if constexpr (!W8A8) v = (v * s_rs[ml]) * sw;
+                const float v = value(i, j, e, ml, nl);
                 if (bf16_out) reinterpret_cast<uint16_t*>(y)[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v);
                 else reinterpret_cast<float*>(y)[(int64_t)m * N + n] = v;
             }
