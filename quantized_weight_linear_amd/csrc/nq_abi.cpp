@@ -193,12 +193,20 @@ int64_t nq_gemv_workspace_bytes(int fmt, int64_t T, int64_t N, int64_t K) {
 
 namespace {
 
+// Token rows a pass of the decode kernels addresses: a pass takes at most 64
+// tokens, padded to whole blocks of 16 (the padding rows read as zero through
+// out-of-range buffer offsets, which must not wrap around 32 bits).
+static int64_t padded_pass_rows(int64_t T) {
+    const int64_t t = T < 64 ? T : 64;
+    return (t + 15) / 16 * 16;
+}
+
 // Q3 / Q5 / Q6: whole 256-column chunks and 32-bit buffer offsets for the
 // codes (rows padded to 16), activations and scales.
 bool qbits_shape_ok(int fmt, int64_t T, int64_t N, int64_t K) {
     const int64_t b = nq::qbits_of(fmt);
     return K % 256 == 0 && (N + 15) / 16 * 16 * (K * b / 8) < ((int64_t)1 << 31) &&
-           (T < 64 ? T : 64) * K * 2 < ((int64_t)1 << 31) && N * (K / 64) * 2 < ((int64_t)1 << 31);
+           padded_pass_rows(T) * K * 2 < ((int64_t)1 << 31) && N * (K / 64) * 2 < ((int64_t)1 << 31);
 }
 
 // The packed layout needs whole 128-column chunks and 32-bit buffer offsets.
@@ -381,7 +389,9 @@ nq_status gemv_a8_impl(int fmt, const void* w, const uint16_t* w_scale, const in
     if (fmt != NQ_W_Q8G64_F16S && fmt != NQ_W_Q4G64_F16S) return NQ_ERR_FORMAT;
     if (!out_ok(out_dt)) return NQ_ERR_FORMAT;
     if (T < 0 || N < 0 || K < 0 || workspace_bytes < 0 || K % 256 != 0) return NQ_ERR_SHAPE;
-    if (T * K >= ((int64_t)1 << 31) || N * (K / 64) * 2 >= ((int64_t)1 << 31)) return NQ_ERR_SHAPE;
+    if (T * K >= ((int64_t)1 << 31) || padded_pass_rows(T) * K >= ((int64_t)1 << 31) ||
+        N * (K / 64) * 2 >= ((int64_t)1 << 31))
+        return NQ_ERR_SHAPE;
     if (packed && !packed_shape_ok(N, K)) return NQ_ERR_SHAPE;
     NQ_TRY(need(w, N * K));
     NQ_TRY(need(w_scale, N * K));

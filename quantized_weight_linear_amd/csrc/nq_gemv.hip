@@ -68,8 +68,9 @@ static int64_t balanced_splits(int64_t tiles, int64_t chunks, int64_t smax) {
 
 static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_spread = true) {
     GemvPlan p{};
-    // buffer offsets are 32-bit: the activation block must stay below 2 GiB
-    p.mfma = (K > 0) && (K % GV_KC == 0) && (Tc * K * 2 < ((int64_t)1 << 31)) &&
+    // buffer offsets are 32-bit: the activation rows a pass addresses (padded
+    // to whole token blocks; the padding reads zero) must stay below 2 GiB
+    p.mfma = (K > 0) && (K % GV_KC == 0) && ((Tc + 15) / 16 * 16 * K * 2 < ((int64_t)1 << 31)) &&
              (N * (K / 32) * 2 < ((int64_t)1 << 31));
     p.kc = GV_KC;
     p.tiles = (N + GV_ROWS - 1) / GV_ROWS;

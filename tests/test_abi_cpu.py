@@ -123,6 +123,16 @@ def test_gemv_validation(L):
     assert q(nq.NQ_W_BF16, A, None, A, 0, 8, 64, 0, A, None, 0, None) == nq.NQ_OK    # BF16 needs no scales
 
 
+# A pass addresses its tokens padded to whole blocks of 16 (the padding reads
+# zero through out-of-range 32-bit buffer offsets): 17 tokens of 2^25 columns
+# fit in 2 GiB, their 32 padded rows do not, so the call is refused.
+def test_padded_token_rows_bound_the_shape(L):
+    k = 1 << 25
+    assert L.nq_gemv_qgroup(nq.NQ_W_Q5G64_F16S, A, A, A, 17, 1, k, 0, A, None, 0, None) == nq.NQ_ERR_SHAPE
+    assert L.nq_gemv_a8_g64(nq.NQ_W_Q8G64_F16S, A, A, A, A, 17, 1, 2 * k, 0, A, None, 0, None) == nq.NQ_ERR_SHAPE
+    assert L.nq_gemv_a8_g64(nq.NQ_W_Q8G64_F16S, A, A, A, A, 17, 1, 2 * k + 256, 0, A, None, 0, None) == nq.NQ_ERR_SHAPE
+
+
 def test_gemm_validation(L):
     w = L.nq_gemm_w8a8_g64
     assert w(A, A, A, A, 4, 8, 96, 0, A, None, None) == nq.NQ_ERR_SHAPE
