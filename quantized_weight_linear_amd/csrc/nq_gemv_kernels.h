@@ -351,6 +351,43 @@ __device__ __forceinline__ void chunk_mfma(const WChunk<FMT>& wc, const uint16_t
                     for (int e = 0; e < 4; ++e) acc[rb][cb][e] = fmaf(d[e], sc[e], acc[rb][cb][e]);
                 }
             }
+        } else if constexpr (NGW == 1) {
+            // GS == 64: row blocks in two pairs, the pair's chains interleaved;
+            // 2 NCB group sums are live at a time (not 4 NCB), which keeps the
+            // four-token-block build within 256 registers (two waves per SIMD).
+            v8bf b[2][NCB];
+#pragma unroll
+            for (int ls = 0; ls < 2; ++ls) {
+                const int col = kl + kstep_col<FMT>(2 * wv + ls, lg);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) b[ls][cb] = *reinterpret_cast<const v8bf*>(&xs[xrow[cb] + col]);
+            }
+            const int gi = sgroup0 + wv;
+#pragma unroll
+            for (int rp = 0; rp < 2; ++rp) {
+                v4f d[2][NCB];
+#pragma unroll
+                for (int ls = 0; ls < 2; ++ls)
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) {
+                        const v8bf a = decode_afrag<FMT, PK, false>(wc, 2 * rp + r, ls);
+#pragma unroll
+                        for (int cb = 0; cb < NCB; ++cb)
+                            d[r][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                a, b[ls][cb], ls == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : d[r][cb], 0, 0, 0);
+                    }
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const int rb = 2 * rp + r;
+                    const uint2 s4 = *reinterpret_cast<const uint2*>(&scs[gi * GV_ROWS + 16 * rb + 4 * lg]);
+                    const float sc[4] = {f16_bits_to_f32(s4.x & 0xFFFFu), f16_bits_to_f32(s4.x >> 16),
+                                         f16_bits_to_f32(s4.y & 0xFFFFu), f16_bits_to_f32(s4.y >> 16)};
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[rb][cb][e] = fmaf(d[r][cb][e], sc[e], acc[rb][cb][e]);
+                }
+            }
         } else {
             v4f d[4][NCB];
 #pragma unroll
@@ -864,19 +901,20 @@ __device__ __forceinline__ void direct_spread(const uint8_t* __restrict__ w, con
 // before the next weights so that waiting for them never waits for weights.
 // One barrier per chunk.
 // ---------------------------------------------------------------------------
-// Waves per SIMD the streaming kernel is compiled for: two for the formats
-// without group scales and for the grouped ones at one token block, so that a
-// spread workgroup fits beside a whole-tile one on every CU (see
-// direct_spread), and for the grouped formats at three token blocks (two K
-// splits per tile then share a CU); one for the grouped formats at two token
-// blocks and for BF16 weights at four, which would spill at that budget
-// (neither runs spread workgroups).
+// Waves per SIMD the streaming kernel is compiled for: two, so that a spread
+// workgroup fits beside a whole-tile one on every CU (see direct_spread) and
+// two K splits of a tile share a CU, except at four token blocks for BF16
+// weights, which would spill at that budget, and for the grouped formats,
+// which run no spread workgroups there and fit in 256 registers without the
+// bound.  At two token blocks the two-wave budget measured faster for the
+// grouped formats too (5120 x 17408, T = 17: Q4 23.4 -> 22.7 us packed,
+// Q8 group-32 row-major 35.2 -> 33.0 us).
 template <int FMT, int NCB>
 constexpr int stream_min_waves() {
-    return (!(FMT == W_BF16 && NCB == 4) && (group_size<FMT>() == 0 || NCB == 1 || NCB == 3)) ? 2 : 1;
+    return (NCB < 4 || (FMT != W_BF16 && group_size<FMT>() == 0)) ? 2 : 1;
 }
 
-// With spread_wgs > 0 (formats without group scales, one split): workgroups
+// With spread_wgs > 0 (one split; the grouped formats at one token block only): workgroups
 // [0, spread_wgs) share the tiles [main_tiles, tiles) unit by unit
 // (direct_spread) and the main_tiles after them take one whole tile each as
 // below.  The spread workgroups come first so that they are dispatched first:
