@@ -11,11 +11,11 @@
 // 4 groups of 64.  For group q of chunk c, lane 16 g + i takes the 16 codes k
 // = 256 c + 64 q + 16 g + [0, 16) of row i: 2 b bytes of the row, starting on
 // a byte boundary (b (32 c + 8 q + 2 g) bytes into the row).  The lane moves
-// them into a window whose bit 0 is the first code's bit 0, extracts every
-// code with a signed bit-field extract (positions known at compile time),
-// converts it to FP32 and packs pairs to BF16 (exact for |q| <= 32), and runs
-// two 16x16x32 BF16 MFMAs against the matching activations (rows t >= T read
-// zero); the group's FP32 sum is then scaled by its FP16 scale.
+// them into a window whose bit 0 is the first code's bit 0, decodes each pair
+// of codes to a biased BF16 pair (qb_pair; positions known at compile time),
+// and runs two 16x16x32 BF16 MFMAs against the matching activations (rows
+// t >= T read zero) after the two that remove the bias; the group's FP32 sum
+// is then scaled by its FP16 scale.
 //   Row-major: the 2 b bytes are loaded as 32-bit words from the 4-byte
 //   boundary at or below them (for odd b and odd g they start 2 bytes past
 //   it) and shifted down.  Packed: per (chunk, row block) the 64 lanes' 8 b
@@ -43,6 +43,44 @@ __device__ __forceinline__ int extract_code(const uint32_t (&w)[N], int pos) {
     const int wi = pos >> 5, r = pos & 31;
     if (r + B <= 32) return __builtin_amdgcn_sbfe((int)w[wi], r, B);
     return __builtin_amdgcn_sbfe((int)__builtin_amdgcn_alignbit(w[wi + 1], w[wi], r), 0, B);
+}
+
+// Biased decode.  With every code's top bit flipped, the B-bit field holds
+// u = q + 2^(B-1) in [0, 2^B); placed in mantissa bits [7 - B, 7) of BF16 1.0
+// it is the BF16 value 1 + u / 2^B = 1.5 + q / 2^B, exactly.  The MFMA chain
+// of a group starts at -1.5 * sum x (two MFMAs of a fragment of -1.5s
+// against the activations), so it ends at sum x q / 2^B, scaled by 2^B once
+// per wave.  Two codes take one unsigned extract of their 2 B adjacent bits,
+// one multiply that lays the field down twice (at bit 7 - B and 16 bits
+// higher, carry-free for B <= 5; two shifted ORs for B = 6) and one and-or,
+// instead of two signed extracts, two integer converts and a pack.
+constexpr uint32_t QB_ONE = 0x3F803F80u;     // two BF16 1.0
+constexpr uint32_t QB_NEG15 = 0xBFC0BFC0u;   // two BF16 -1.5
+
+// Word i of the top-bit flip of the 16 B-bit fields of a group window.
+template <int B>
+constexpr uint32_t qb_flip_word(int i) {
+    uint32_t m = 0;
+    for (int j = 0; j < 16; ++j) {
+        const int bit = B * j + B - 1 - 32 * i;
+        if (bit >= 0 && bit < 32) m |= 1u << bit;
+    }
+    return m;
+}
+
+// The BF16 pair (1.5 + q_j / 2^B, 1.5 + q_{j+1} / 2^B) of codes j, j + 1 of a
+// flipped window (pos = B j); mask and one as in decode_afrag's Q4 pairs
+// (the mask uniform, the 1.0 pair in a vector register, so that the last
+// step is a single and-or).
+template <int B, int N>
+__device__ __forceinline__ uint32_t qb_pair(const uint32_t (&w)[N], int pos, uint32_t mask, uint32_t one) {
+    const int wi = pos >> 5, r = pos & 31;
+    const uint32_t t = (r + 2 * B <= 32) ? __builtin_amdgcn_ubfe(w[wi], r, 2 * B)
+                                         : __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(w[wi + 1], w[wi], r), 0, 2 * B);
+    uint32_t a;
+    if constexpr (B <= 5) a = __umul24(t, (1u << (7 - B)) | (1u << (23 - 2 * B)));
+    else a = (t << (7 - B)) | (t << (23 - 2 * B));
+    return (a & mask) | one;
 }
 
 // SH: the workgroup's WG_WAVES waves (row blocks) share each chunk's
@@ -171,6 +209,9 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_qbit
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    const uint32_t mask = __builtin_amdgcn_readfirstlane(((1u << B) - 1u) * 0x00010001u << (7 - B));
+    uint32_t one;
+    asm("v_mov_b32 %0, %1" : "=v"(one) : "s"(__builtin_amdgcn_readfirstlane(QB_ONE)));
     auto compute = [&](int slot, const uint16_t* xb) {
         const Chunk& r = ring[slot];
 #pragma unroll
@@ -194,27 +235,32 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_qbit
                     gw[i] = __builtin_amdgcn_alignbit(hi, lo, rm_shift);
                 }
             }
+#pragma unroll
+            for (int i = 0; i < L::GWORDS; ++i) gw[i] ^= qb_flip_word<B>(i);
+            // B fragments: token cb * 16 + i, columns 64 q + 16 g + 8 h .. + 8 of the chunk
+            v8bf bx[2][NCB];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    bx[h][cb] = SH ? *reinterpret_cast<const v8bf*>(&xb[(cb * 16 + li) * XPITCH + 64 * q + 16 * lg + 8 * h])
+                                   : __builtin_bit_cast(v8bf, r.xa[(q * 2 + h) * NCB + cb]);
+            const v8bf neg = __builtin_bit_cast(v8bf, make_uint4(QB_NEG15, QB_NEG15, QB_NEG15, QB_NEG15));
             v4f d[NCB];
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                d[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg, bx[0][cb], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                d[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg, bx[1][cb], d[cb], 0, 0, 0);
+            }
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 uint32_t o[4];
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const int j = 8 * h + 2 * p;
-                    const float a = (float)extract_code<B>(gw, B * j);
-                    const float b = (float)extract_code<B>(gw, B * (j + 1));
-                    o[p] = f32x2_to_bf16x2(a, b);
-                }
+                for (int p = 0; p < 4; ++p) o[p] = qb_pair<B>(gw, B * (8 * h + 2 * p), mask, one);
                 const v8bf af = __builtin_bit_cast(v8bf, make_uint4(o[0], o[1], o[2], o[3]));
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-                    // B fragment: token cb * 16 + i, columns 64 q + 16 g + 8 h .. + 8 of the chunk
-                    const v8bf bx =
-                        SH ? *reinterpret_cast<const v8bf*>(&xb[(cb * 16 + li) * XPITCH + 64 * q + 16 * lg + 8 * h])
-                           : __builtin_bit_cast(v8bf, r.xa[(q * 2 + h) * NCB + cb]);
-                    d[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bx, h == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : d[cb],
-                                                                    0, 0, 0);
-                }
+                for (int cb = 0; cb < NCB; ++cb)
+                    d[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bx[h][cb], d[cb], 0, 0, 0);
             }
             float sc[4];
 #pragma unroll
@@ -262,6 +308,8 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_qbit
             }
         }
     }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[cb] *= (float)(1 << B);   // the biased sums' factor 2^B
     if (rb_valid) wave_finish<NCB>(acc, T, N, rb, split, splits, partial, counters, bf16_out, y);
 }
 
