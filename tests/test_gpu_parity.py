@@ -412,6 +412,22 @@ def test_gemv_qgroup(name, fmt, n, k, t):
         _check_float_out(y32, y16, ref)
 
 
+# Four token blocks on 272 row tiles (17408 rows), the shape where the group
+# formats' four-token-block streaming build has to fit two waves per SIMD
+# (Q8 group-64: its row blocks in pairs), packed and row-major, every row.
+@pytest.mark.parametrize("name,fmt", GROUP_FMTS[:3])
+@pytest.mark.parametrize("t", [49, 64])
+def test_gemv_qgroup_four_token_blocks_many_tiles(name, fmt, t):
+    n, k = W.FFN, 1280
+    codes, scales = _grouped_inputs(name, n, k, 31 * t + 7)
+    x = W.bf16_normal(W.rng(100, 3 * t + k), (t, k))
+    ref = M.gemv_qgroup(name, codes, scales, x)
+    cd, sd = dev(codes), dev(scales)
+    pk = _pack_dev(fmt, cd, n, k)
+    g32, g16, _ = _gemv_both_layouts(fmt, cd, pk, sd, x, n, k)
+    _check_float_out(g32, g16, ref)
+
+
 def test_gemv_mxfp8_config1():
     d = W.mxfp8_gemv()
     n, k = d["words"].shape[0], d["words"].shape[1] * 4
