@@ -412,6 +412,25 @@ def test_gemv_qgroup(name, fmt, n, k, t):
         _check_float_out(y32, y16, ref)
 
 
+@pytest.mark.parametrize("t", [1, 8, 40])
+def test_gemv_q4_every_code_large_offset(t):
+    """Q4: every code value at every position, activations 30 + N(0, 1): the
+    biased decode's worst case (group sums of x far above those of x q)."""
+    n, k = 64, 1024
+    q = (np.arange(n)[:, None] * 7 + np.arange(k)[None, :]) % 16 - 8
+    u = (q & 15).astype(np.uint8)
+    codes = (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+    assert np.array_equal(M.unpack_q4(codes, k), q)
+    scales = W.grouped("q4g64", n, k, seed=12)["scales"]
+    x = W.to_bf16_bits((30.0 + W.rng(152, t).standard_normal((t, k))).astype(np.float32))
+    ref = M.gemv_qgroup("q4g64", codes, scales, x)
+    fmt = nq.NQ_W_Q4G64_F16S
+    cd, sd = dev(codes), dev(scales)
+    pk = _pack_dev(fmt, cd, n, k)
+    g32, g16, _ = _gemv_both_layouts(fmt, cd, pk, sd, x, n, k)
+    _check_float_out(g32, g16, ref)
+
+
 # Four token blocks on 272 row tiles (17408 rows), the shape where the group
 # formats' four-token-block streaming build has to fit two waves per SIMD
 # (Q8 group-64: its row blocks in pairs), packed and row-major, every row.
@@ -1174,6 +1193,29 @@ def test_gemv_qbits(name, fmt, bits, n, k, t):
     assert np.array_equal(g16, bf16_of_f32_bits(outs[3]))
     assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))      # packed = row-major
     assert np.array_equal(outs[1].view(np.uint32), outs[3].view(np.uint32))
+
+
+@pytest.mark.parametrize("name,fmt,bits", QB_FMTS)
+@pytest.mark.parametrize("t", [8, 40])
+def test_gemv_qbits_every_code_large_offset(name, fmt, bits, t):
+    """Every code value at every position of a group, against activations
+    with a large common offset (30 + N(0, 1)): group sums of x dwarf those of
+    x q, the hardest case for sums taken on codes shifted by 2^(b-1)."""
+    n, k = 64, 1024
+    q = (np.arange(n)[:, None] * 7 + np.arange(k)[None, :]) % (1 << bits) - (1 << (bits - 1))
+    u = (q & ((1 << bits) - 1)).astype(np.uint8)
+    stream = ((u[:, :, None] >> np.arange(bits, dtype=np.uint8)) & 1).reshape(n, k * bits)
+    codes = np.packbits(stream, axis=1, bitorder="little")
+    assert np.array_equal(M.unpack_qbits(codes, k, bits), q)     # the stream holds the intended codes
+    scales = W.grouped(name, n, k, seed=11)["scales"]
+    x32 = 30.0 + W.rng(151, t).standard_normal((t, k))
+    x = W.to_bf16_bits(x32.astype(np.float32))
+    ref = M.gemv_qgroup(name, codes, scales, x)
+    cd, sd = dev(codes), dev(scales)
+    pk = _pack_dev(fmt, cd, n, k)
+    for p in (None, pk):
+        g = _qb_gemv(fmt, cd, p, sd, x, n, k, True)
+        assert rel_fro(g, ref) <= FP32_TOL, p is None
 
 
 @pytest.mark.parametrize("name,fmt,bits", QB_FMTS)
