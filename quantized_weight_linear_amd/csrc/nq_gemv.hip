@@ -188,7 +188,18 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     const int64_t cps = (chunks + s0 - 1) / s0;
     p.chunks_per_split = (int)cps;
     p.splits = (int)((chunks + cps - 1) / cps);
-    if ((fmt_group(fmt) == 0 || spread_one_round) && allow_spread) plan_spread(p, chunks);
+    // One-byte formats without group scales on at least 4 tiles per CU, from
+    // three token blocks on: two row tiles per workgroup share one activation
+    // stage, in place of the spread workgroups (152064 x 5120 row-FP8 packed,
+    // T = 33 / 48 / 64: 168.7 / 185.7 / 206.7 -> 142.7 / 155.0 / 177.1 us;
+    // row-major 198.9 / 207.2 / 233.9 -> 176.7 / 182.1 / 201.4; 65536 x 5120
+    // packed 66.5 / 72.2 / 80.6 -> 61.5 / 64.8 / 74.9).  At two token blocks
+    // it measured level (138.7 -> 135.8 us on the head, 56.9 -> 58.8 on 65536
+    // rows), and for BF16 weights, whose activation bytes weigh half as much
+    // against the weights', packed level or slower (65536 x 5120 T = 33 110.5
+    // -> 116.0 us).
+    p.two_tiles = (fmt == W_FP8ROW || fmt == W_MXFP8) && many_tiles && p.splits == 1 && Tc > 32;
+    if ((fmt_group(fmt) == 0 || spread_one_round) && allow_spread && !p.two_tiles) plan_spread(p, chunks);
     return p;
 }
 

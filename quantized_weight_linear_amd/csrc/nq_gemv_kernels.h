@@ -453,6 +453,30 @@ __device__ __forceinline__ void reduce_waves(v4f (&acc)[4][NCB], v4f (&fin)[NCB]
     }
 }
 
+// reduce_waves for the waves with `mine` set: the barriers are the whole
+// workgroup's, the writes and sums only theirs.
+template <int NCB>
+__device__ __forceinline__ void reduce_waves_half(v4f (&acc)[4][NCB], v4f (&fin)[NCB], v4f* red, int wv, int lane,
+                                                  bool mine) {
+    __syncthreads();
+    if (mine) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) red[((wv * 4 + rb) * NCB + cb) * 64 + lane] = acc[rb][cb];
+    }
+    __syncthreads();
+    if (mine) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            v4f s = red[((0 * 4 + wv) * NCB + cb) * 64 + lane];
+#pragma unroll
+            for (int w2 = 1; w2 < 4; ++w2) s += red[((w2 * 4 + wv) * NCB + cb) * 64 + lane];
+            fin[cb] = s;
+        }
+    }
+}
+
 // reduce_waves for sums held transposed, as MFMAs with the activations in the
 // A operand leave them (lane 16 g + i: tokens 4 g + e of row i): each value is
 // first written to its place in the usual layout (lane 16 g' + i': rows
@@ -914,21 +938,36 @@ constexpr int stream_min_waves() {
     return (NCB < 4 || (FMT != W_BF16 && group_size<FMT>() == 0)) ? 2 : 1;
 }
 
+// The builds with two row tiles per workgroup (the one-byte formats without
+// group scales, three or four token blocks; eight waves on a CU's four SIMDs
+// fit the two-wave register budget there).
+template <int FMT, int NCB>
+constexpr bool two_tile_format() {
+    return (FMT == W_FP8ROW || FMT == W_MXFP8) && NCB >= 3 && stream_min_waves<FMT, NCB>() == 2;
+}
+
 // With spread_wgs > 0 (one split; the grouped formats at one token block only): workgroups
 // [0, spread_wgs) share the tiles [main_tiles, tiles) unit by unit
 // (direct_spread) and the main_tiles after them take one whole tile each as
 // below.  The spread workgroups come first so that they are dispatched first:
 // their partial exchange then ends well inside the whole tiles' time.
-template <int FMT, int NCB, bool PK>
-__global__ __launch_bounds__(256, (stream_min_waves<FMT, NCB>())) void gemv_mfma_kernel(
+//
+// TH = 2 (formats without group scales, one K split, no spread workgroups,
+// many tiles per CU): eight waves take two neighbouring row tiles, waves
+// 4 h + q tile h and column quarter q, and share one activation stage, which
+// halves the activation bytes staged per weight byte.
+template <int FMT, int NCB, bool PK, int TH = 1>
+__global__ __launch_bounds__(256 * TH, (TH == 1 ? stream_min_waves<FMT, NCB>() : 2)) void gemv_mfma_kernel(
     const uint8_t* __restrict__ w, const void* __restrict__ scales, const uint16_t* __restrict__ x, int T, int N,
     int64_t K, int chunks_per_split, int splits, float* __restrict__ partial, unsigned* __restrict__ counters,
     int bf16_out, void* __restrict__ y, int main_tiles, int spread_wgs, int maxslots) {
     constexpr int TP = 16 * NCB;
     constexpr int XPITCH = GV_KC + 8;                 // bf16 per LDS row: rows shift by 4 banks
     constexpr int XPR = GV_KC / 8;                    // 16-byte activation pieces per row and chunk
-    constexpr int XP = TP * XPR / 256;                // ... per thread
+    constexpr int NT = 256 * TH;                      // threads
+    constexpr int XP = TP * XPR / NT;                 // ... per thread
     constexpr int GS = group_size<FMT>();
+    static_assert(TH == 1 || GS == 0, "two tiles per workgroup: formats without group scales");
     constexpr int NG = GS ? GV_KC / (GS ? GS : 1) : 1;   // scale groups per chunk
     constexpr int SP = GS ? (NG * GV_ROWS + 255) / 256 : 1;
     constexpr int D = depth<FMT, NCB>();
@@ -937,7 +976,7 @@ __global__ __launch_bounds__(256, (stream_min_waves<FMT, NCB>())) void gemv_mfma
     __shared__ __attribute__((aligned(16))) uint16_t scs[2][GS ? NG * GV_ROWS : 1];
     __shared__ int s_last;
     static_assert(sizeof(xs) >= 16384 * NCB, "reduction buffer");
-    if constexpr (GS == 0 || NCB == 1) {
+    if constexpr ((GS == 0 || NCB == 1) && TH == 1) {
         __shared__ int s_last_sp[SPREAD_MAXSEG];
         if ((int)blockIdx.x < spread_wgs) {
             const int tiles_all = (int)((N + GV_ROWS - 1) / GV_ROWS);
@@ -950,10 +989,11 @@ __global__ __launch_bounds__(256, (stream_min_waves<FMT, NCB>())) void gemv_mfma
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wv = tid >> 6;
+    const int wv = TH == 1 ? tid >> 6 : (tid >> 6) & 3;   // the wave's column quarter of a chunk
+    const int half = TH == 1 ? 0 : tid >> 8;              // the wave's row tile of the TH
     const int li = lane & 15;
     const int lg = lane >> 4;
-    const int tile = (int)blockIdx.x - spread_wgs;   // spread workgroups come first
+    const int tile = ((int)blockIdx.x - spread_wgs) * TH + half;   // spread workgroups come first
     // A whole tile's waves issue ahead of a spread workgroup's on the same CU
     // (these are younger, and equal priority favours the oldest wave): the
     // spread work then fills the cycles the tile leaves idle.
@@ -986,7 +1026,7 @@ __global__ __launch_bounds__(256, (stream_min_waves<FMT, NCB>())) void gemv_mfma
         const int64_t kc0 = k_begin + (int64_t)c * GV_KC;
 #pragma unroll
         for (int j = 0; j < XP; ++j) {
-            const int idx = tid + 256 * j;
+            const int idx = tid + NT * j;
             const int t = idx / XPR, pc = idx % XPR;
             const int off = (int)(((int64_t)t * K + kc0 + 8 * pc) * 2);
             xreg[slot][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, off, 0, 0));
@@ -1005,7 +1045,7 @@ __global__ __launch_bounds__(256, (stream_min_waves<FMT, NCB>())) void gemv_mfma
     auto store_x = [&](int buf, int slot) {
 #pragma unroll
         for (int j = 0; j < XP; ++j) {
-            const int idx = tid + 256 * j;
+            const int idx = tid + NT * j;
             const int t = idx / XPR, pc = idx % XPR;
             *reinterpret_cast<uint4*>(&xs[buf][t * XPITCH + 8 * pc]) = xreg[slot][j];
         }
@@ -1064,7 +1104,19 @@ __global__ __launch_bounds__(256, (stream_min_waves<FMT, NCB>())) void gemv_mfma
 
     v4f fin[NCB];
     q4_bias_finish<FMT, NCB>(acc);
-    reduce_waves<NCB>(acc, fin, reinterpret_cast<v4f*>(&xs[0][0]), wv, lane);
+    if constexpr (TH == 1) {
+        reduce_waves<NCB>(acc, fin, reinterpret_cast<v4f*>(&xs[0][0]), wv, lane);
+    } else {
+        // the two tiles' sums in turn through the one buffer
+#pragma unroll
+        for (int h = 0; h < TH; ++h) {
+            v4f fh[NCB];
+            reduce_waves_half<NCB>(acc, fh, reinterpret_cast<v4f*>(&xs[0][0]), wv, lane, half == h);
+            if (half == h)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) fin[cb] = fh[cb];
+        }
+    }
     finish_tile<FMT, NCB>(fin, scales, T, N, row0, wv, lane, tile, split, splits, partial, counters, bf16_out, y,
                           &s_last);
 }
@@ -1384,6 +1436,7 @@ struct GemvPlan {
     int splits;
     int chunks_per_split;
     int64_t lds_bytes;       // dynamic LDS of the resident kernel
+    bool two_tiles;          // streaming kernel with two row tiles per workgroup (TH = 2)
 };
 
 constexpr int64_t RESIDENT_LDS_MAX = 64 << 10;
@@ -1402,17 +1455,25 @@ static void launch_mfma(const GemvPlan& p, const void* w, const void* scales, co
             return;
         }
     }
-    if (p.resident)
+    if (p.resident) {
         gemv_resident_kernel<FMT, NCB, PK><<<grid, 256, (size_t)p.lds_bytes, stream>>>(
             reinterpret_cast<const uint8_t*>(w), scales, x, Tc, (int)N, K, p.chunks_per_split, p.splits, partial,
             counters, bf16_out ? 1 : 0, y);
-    else {
-        const dim3 g = p.spread_wgs > 0 ? dim3((unsigned)(p.main_tiles + p.spread_wgs)) : grid;
-        gemv_mfma_kernel<FMT, NCB, PK><<<g, 256, 0, stream>>>(reinterpret_cast<const uint8_t*>(w), scales, x, Tc,
-                                                                  (int)N, K, p.chunks_per_split, p.splits, partial,
-                                                                  counters, bf16_out ? 1 : 0, y, (int)p.main_tiles,
-                                                                  p.spread_wgs, p.maxslots);
+        return;
     }
+    if constexpr (two_tile_format<FMT, NCB>()) {
+        if (p.two_tiles) {
+            gemv_mfma_kernel<FMT, NCB, PK, 2><<<dim3((unsigned)((p.tiles + 1) / 2)), 512, 0, stream>>>(
+                reinterpret_cast<const uint8_t*>(w), scales, x, Tc, (int)N, K, p.chunks_per_split, 1, partial,
+                counters, bf16_out ? 1 : 0, y, 0, 0, 0);
+            return;
+        }
+    }
+    const dim3 g = p.spread_wgs > 0 ? dim3((unsigned)(p.main_tiles + p.spread_wgs)) : grid;
+    gemv_mfma_kernel<FMT, NCB, PK><<<g, 256, 0, stream>>>(reinterpret_cast<const uint8_t*>(w), scales, x, Tc, (int)N,
+                                                          K, p.chunks_per_split, p.splits, partial, counters,
+                                                          bf16_out ? 1 : 0, y, (int)p.main_tiles, p.spread_wgs,
+                                                          p.maxslots);
 }
 
 template <int FMT, bool PK>

@@ -447,6 +447,30 @@ def test_gemv_qgroup_four_token_blocks_many_tiles(name, fmt, t):
     _check_float_out(g32, g16, ref)
 
 
+# Formats without group scales on at least four row tiles per CU, more than
+# one token block: the streaming kernel's two-tile workgroups (eight waves,
+# one activation stage for both tiles).  1025 tiles: the last workgroup's
+# second tile lies wholly past the matrix (its reads clamp to the last row,
+# its writes are dropped).  Packed and row-major, every row.
+@pytest.mark.parametrize("name,fmt", [("fp8row", -1)] + GROUP_FMTS[3:])
+@pytest.mark.parametrize("t", [17, 40, 64])
+def test_gemv_two_tile_workgroups(name, fmt, t):
+    n, k = 1025 * 64 - 5, 512
+    if fmt == -1:
+        w = W.bf16_normal(W.rng(96, 31 * t), (n, k), std=0.02)
+        codes, scales = M.encode_fp8row_bf16(w)
+    else:
+        codes, scales = _grouped_inputs(name, n, k, 41 * t + 3)
+    x = W.bf16_normal(W.rng(100, 5 * t + k), (t, k))
+    ref = (M.gemv_fp8row(codes, scales, x) if fmt == -1 else M.gemv_qgroup(name, codes, scales, x))
+    cd = dev(codes)
+    sd = dev(scales) if scales is not None else None
+    pk = _pack_dev(fmt, cd, n, k)
+    g32, g16, _ = _gemv_both_layouts(fmt, cd, pk, sd, x, n, k)
+    _check_float_out(g32, g16, ref)
+    assert rel_fro(g32[:, -64:], ref[:, -64:]) <= FP32_TOL
+
+
 def test_gemv_mxfp8_config1():
     d = W.mxfp8_gemv()
     n, k = d["words"].shape[0], d["words"].shape[1] * 4
