@@ -188,17 +188,19 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     const int64_t cps = (chunks + s0 - 1) / s0;
     p.chunks_per_split = (int)cps;
     p.splits = (int)((chunks + cps - 1) / cps);
-    // One-byte formats without group scales on at least 4 tiles per CU, from
-    // three token blocks on: two row tiles per workgroup share one activation
-    // stage, in place of the spread workgroups (152064 x 5120 row-FP8 packed,
-    // T = 33 / 48 / 64: 168.7 / 185.7 / 206.7 -> 142.7 / 155.0 / 177.1 us;
-    // row-major 198.9 / 207.2 / 233.9 -> 176.7 / 182.1 / 201.4; 65536 x 5120
-    // packed 66.5 / 72.2 / 80.6 -> 61.5 / 64.8 / 74.9).  At two token blocks
-    // it measured level (138.7 -> 135.8 us on the head, 56.9 -> 58.8 on 65536
-    // rows), and for BF16 weights, whose activation bytes weigh half as much
-    // against the weights', packed level or slower (65536 x 5120 T = 33 110.5
-    // -> 116.0 us).
-    p.two_tiles = (fmt == W_FP8ROW || fmt == W_MXFP8) && many_tiles && p.splits == 1 && Tc > 32;
+    // One-byte formats without group scales on at least 4 tiles per CU, above
+    // one token block: two row tiles per workgroup share one activation stage,
+    // in place of the spread workgroups (152064 x 5120 row-FP8 packed, T = 17
+    // / 24 / 32 / 33 / 48 / 64: 138.7 / 149.3 / 161.1 / 168.7 / 185.7 / 206.7 ->
+    // 134.8 / 139.0 / 143.4 / 142.7 / 155.0 / 177.1 us; row-major T = 32 / 64
+    // 185.9 / 233.9 -> 170.2 / 201.4; 65536 x 5120 packed T = 32 / 64 67.5 /
+    // 80.6 -> 60.9 / 74.9; MXFP8 packed T = 17 / 64 198.2 / 269 -> 187.2 /
+    // 238).  The plan is the same for both weight layouts, so that their results
+    // agree bit for bit; row-major MXFP8 loses at two token blocks (head T = 17
+    // / 24: 215.2 / 222.4 -> 225.9 / 229.9 us).  Not for BF16 weights, whose
+    // activation bytes weigh half as much against the weights' (packed 65536 x
+    // 5120 T = 33 110.5 -> 116.0 us).
+    p.two_tiles = (fmt == W_FP8ROW || fmt == W_MXFP8) && many_tiles && p.splits == 1 && Tc > 16;
     if ((fmt_group(fmt) == 0 || spread_one_round) && allow_spread && !p.two_tiles) plan_spread(p, chunks);
     return p;
 }

@@ -453,7 +453,7 @@ def test_gemv_qgroup_four_token_blocks_many_tiles(name, fmt, t):
 # second tile lies wholly past the matrix (its reads clamp to the last row,
 # its writes are dropped).  Packed and row-major, every row.
 @pytest.mark.parametrize("name,fmt", [("fp8row", -1)] + GROUP_FMTS[3:])
-@pytest.mark.parametrize("t", [17, 40, 64])
+@pytest.mark.parametrize("t", [17, 32, 40, 64])
 def test_gemv_two_tile_workgroups(name, fmt, t):
     n, k = 1025 * 64 - 5, 512
     if fmt == -1:
