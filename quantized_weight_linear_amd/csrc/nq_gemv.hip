@@ -98,7 +98,24 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     const int64_t cus_n = (int64_t)device_cu_count();
     const bool spread_one_round = (fmt_group(fmt) == 0 || Tc <= 16) && allow_spread && p.tiles > cus_n &&
                                   8 * (p.tiles - cus_n) <= cus_n && chunks >= 16;
-    if (fmt_group(fmt) == 0 && Tc <= 16 && !spread_one_round) {
+    // One-byte formats without group scales on at least 4 tiles per CU: two
+    // row tiles per workgroup share one activation stage (gemv_mfma_kernel
+    // with TH = 2), in place of the spread workgroups, from 5 tokens on for
+    // row-FP8 and 8 for MXFP8 (below that the direct kernel is as fast, and
+    // MXFP8 packed at T = 5 faster: 171.0 against 178.6 us on the head).
+    // Measured, 152064 x 5120 row-FP8 packed, T = 8 / 12 / 16 / 17 / 24 / 32 /
+    // 33 / 48 / 64: 129.6 / 134.6 / 141.7 / 138.7 / 149.3 / 161.1 / 168.7 /
+    // 185.7 / 206.7 -> 130.1 / 132.4 / 133.6 / 134.8 / 139.0 / 143.4 / 142.7 /
+    // 155.0 / 177.1 us; row-major T = 5 / 16 / 32 / 64 158.7 / 185.2 / 185.9 /
+    // 233.9 -> 147.3 / 153.9 / 170.2 / 201.4; 65536 x 5120 packed T = 16 / 32
+    // / 64 61.4 / 67.5 / 80.6 -> 57.0 / 60.9 / 74.9; MXFP8 packed T = 16 / 32 /
+    // 64 198.7 / 217.1 / 269 -> 186.3 / 197.6 / 238.  The plan is the same for
+    // both weight layouts, so that their results agree bit for bit; row-major
+    // MXFP8 loses at T = 17 / 24 (215.2 / 222.4 -> 225.9 / 229.9 us).  Not for
+    // BF16 weights, whose activation bytes weigh half as much against the
+    // weights' (packed 65536 x 5120 T = 33 110.5 -> 116.0 us).
+    const bool two_tiles = ((fmt == W_FP8ROW && Tc > 4) || (fmt == W_MXFP8 && Tc >= 8)) && p.tiles >= 4 * cus_n;
+    if (fmt_group(fmt) == 0 && Tc <= 16 && !spread_one_round && !two_tiles) {
         // direct variant (no group scales, one token block): about one
         // workgroup per CU (measured: more per CU only slow it down); with
         // fewer tiles than CUs, K split so that the busiest CU has the fewest chunks
@@ -188,19 +205,7 @@ static GemvPlan plan_gemv(int fmt, int64_t Tc, int64_t N, int64_t K, bool allow_
     const int64_t cps = (chunks + s0 - 1) / s0;
     p.chunks_per_split = (int)cps;
     p.splits = (int)((chunks + cps - 1) / cps);
-    // One-byte formats without group scales on at least 4 tiles per CU, above
-    // one token block: two row tiles per workgroup share one activation stage,
-    // in place of the spread workgroups (152064 x 5120 row-FP8 packed, T = 17
-    // / 24 / 32 / 33 / 48 / 64: 138.7 / 149.3 / 161.1 / 168.7 / 185.7 / 206.7 ->
-    // 134.8 / 139.0 / 143.4 / 142.7 / 155.0 / 177.1 us; row-major T = 32 / 64
-    // 185.9 / 233.9 -> 170.2 / 201.4; 65536 x 5120 packed T = 32 / 64 67.5 /
-    // 80.6 -> 60.9 / 74.9; MXFP8 packed T = 17 / 64 198.2 / 269 -> 187.2 /
-    // 238).  The plan is the same for both weight layouts, so that their results
-    // agree bit for bit; row-major MXFP8 loses at two token blocks (head T = 17
-    // / 24: 215.2 / 222.4 -> 225.9 / 229.9 us).  Not for BF16 weights, whose
-    // activation bytes weigh half as much against the weights' (packed 65536 x
-    // 5120 T = 33 110.5 -> 116.0 us).
-    p.two_tiles = (fmt == W_FP8ROW || fmt == W_MXFP8) && many_tiles && p.splits == 1 && Tc > 16;
+    p.two_tiles = two_tiles && p.splits == 1;
     if ((fmt_group(fmt) == 0 || spread_one_round) && allow_spread && !p.two_tiles) plan_spread(p, chunks);
     return p;
 }

@@ -939,11 +939,11 @@ constexpr int stream_min_waves() {
 }
 
 // The builds with two row tiles per workgroup (the one-byte formats without
-// group scales, above one token block; eight waves on a CU's four SIMDs fit
-// the two-wave register budget there).
+// group scales; eight waves on a CU's four SIMDs fit the two-wave register
+// budget there).
 template <int FMT, int NCB>
 constexpr bool two_tile_format() {
-    return (FMT == W_FP8ROW || FMT == W_MXFP8) && NCB >= 2 && stream_min_waves<FMT, NCB>() == 2;
+    return (FMT == W_FP8ROW || FMT == W_MXFP8) && stream_min_waves<FMT, NCB>() == 2;
 }
 
 // With spread_wgs > 0 (one split; the grouped formats at one token block only): workgroups

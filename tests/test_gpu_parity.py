@@ -447,13 +447,14 @@ def test_gemv_qgroup_four_token_blocks_many_tiles(name, fmt, t):
     _check_float_out(g32, g16, ref)
 
 
-# Formats without group scales on at least four row tiles per CU, more than
-# one token block: the streaming kernel's two-tile workgroups (eight waves,
-# one activation stage for both tiles).  1025 tiles: the last workgroup's
+# One-byte formats without group scales on at least four row tiles per CU,
+# from 5 (row-FP8) or 8 (MXFP8) tokens on: the streaming kernel's two-tile
+# workgroups (eight waves, one activation stage for both tiles); below that
+# the direct kernel.  1025 tiles: the last workgroup's
 # second tile lies wholly past the matrix (its reads clamp to the last row,
 # its writes are dropped).  Packed and row-major, every row.
 @pytest.mark.parametrize("name,fmt", [("fp8row", -1)] + GROUP_FMTS[3:])
-@pytest.mark.parametrize("t", [17, 32, 40, 64])
+@pytest.mark.parametrize("t", [4, 5, 8, 16, 17, 32, 40, 64])
 def test_gemv_two_tile_workgroups(name, fmt, t):
     n, k = 1025 * 64 - 5, 512
     if fmt == -1:
