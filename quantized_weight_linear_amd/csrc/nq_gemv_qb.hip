@@ -86,11 +86,18 @@ __device__ __forceinline__ uint32_t qb_pair(const uint32_t (&w)[N], int pos, uin
 // SH: the workgroup's WG_WAVES waves (row blocks) share each chunk's
 // activations, staged in LDS (two or more token blocks, where the activation
 // loads outweigh the weights: 17408x5120 Q5 T = 33 75.9 -> 44.4 us);
-// otherwise each 64-thread workgroup loads its own activation fragments into
-// registers, and the single-wave workgroups spread evenly over the SIMDs
-// (with four row blocks per workgroup, 1088 row blocks are 272 workgroups on
-// 256 CUs: T = 1 23.6 -> 28.6 us).
-template <int B, int NCB, bool PK, bool SH>
+// otherwise each 64-thread workgroup works alone, and the single-wave
+// workgroups spread evenly over the SIMDs (with four row blocks per
+// workgroup, 1088 row blocks are 272 workgroups on 256 CUs: T = 1 23.6 ->
+// 28.6 us).  A single wave either loads its B fragments straight into
+// registers (XS = 0: 8 loads of 16 bytes per lane and chunk, every lane's
+// token row, rows t >= T read as zero), or (XS > 0, few tokens) loads only
+// the first 2 XS token rows of the chunk, XS contiguous 1 KiB loads, and
+// stages them in its own LDS rows, where the fragment reads of the lanes
+// past those rows hit one zero row.  The zero-reading loads of absent token
+// rows cost as much address work as real ones: at T <= 8 they were most of
+// a wave's memory instructions.
+template <int B, int NCB, bool PK, bool SH, int XS = 0>
 __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_qbits_kernel(const uint8_t* __restrict__ w,
                                                         const uint16_t* __restrict__ wsc,
                                                         const uint16_t* __restrict__ x, int T, int N, int64_t K,
@@ -101,8 +108,11 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_qbit
     constexpr int TP = 16 * NCB;                 // token rows of the staged activations
     constexpr int XPITCH = WG_KC + 8;            // bf16 per LDS row: rows shift by 4 banks
     constexpr int XP = TP * (WG_KC / 8) / 256;   // 16-byte activation pieces per thread and chunk
-    constexpr int XR = SH ? XP : 8 * NCB;        // activation registers per ring slot
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][SH ? TP * XPITCH : 8];
+    constexpr bool CS = !SH && XS > 0;           // the wave stages its own first 2 XS token rows
+    static_assert(!CS || NCB == 1, "compact staging: one token block");
+    constexpr int SROWS = 2 * XS;                // CS: token rows staged; row SROWS stays zero
+    constexpr int XR = SH ? XP : (CS ? XS : 8 * NCB);   // activation registers per ring slot
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][SH ? TP * XPITCH : (CS ? (SROWS + 1) * XPITCH : 8)];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int li = lane & 15, lg = lane >> 4;
@@ -172,11 +182,11 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_qbit
                     r.wd[q * L::GWORDS + i] = __builtin_amdgcn_raw_buffer_load_b32(wr, off + 4 * i, 0, 0);
             }
         }
-        if constexpr (SH) {
-            // piece idx = tid + 256 j is row idx / 32, 16 bytes idx % 32 (rows >= T read zero)
+        if constexpr (SH || CS) {
+            // piece idx = tid + 256 j (CS: lane + 64 j) is row idx / 32, 16 bytes idx % 32 (rows >= T read zero)
 #pragma unroll
-            for (int j = 0; j < XP; ++j) {
-                const int idx = tid + 256 * j;
+            for (int j = 0; j < XR; ++j) {
+                const int idx = tid + (SH ? 256 : 64) * j;
                 const int t = idx >> 5, pc = idx & 31;
                 r.xa[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                         xr, (int)(((int64_t)t * K + c * WG_KC + 8 * pc) * 2), 0, 0));
@@ -197,10 +207,10 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_qbit
             r.ws[e] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(sr, soff[e] + (int)(c * 8), 0, 0));
     };
     auto store_x = [&](int buf, int slot) {
-        if constexpr (SH)
+        if constexpr (SH || CS)
 #pragma unroll
-        for (int j = 0; j < XP; ++j) {
-            const int idx = tid + 256 * j;
+        for (int j = 0; j < XR; ++j) {
+            const int idx = tid + (SH ? 256 : 64) * j;
             *reinterpret_cast<uint4*>(&xs[buf][(idx >> 5) * XPITCH + 8 * (idx & 31)]) = ring[slot].xa[j];
         }
     };
@@ -208,6 +218,14 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_qbit
     v4f acc[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+    // CS: the zero row of both buffers (columns [0, 256): lanes 0..31 buffer 0,
+    // 32..63 buffer 1), and the lane's fragment row (its token, or the zero row).
+    // One wave: its LDS accesses take effect in program order, no barrier.
+    int xrow1 = 0;
+    if constexpr (CS) {
+        *reinterpret_cast<uint4*>(&xs[lane >> 5][SROWS * XPITCH + 8 * (lane & 31)]) = make_uint4(0u, 0u, 0u, 0u);
+        xrow1 = (li < SROWS ? li : SROWS) * XPITCH;
+    }
 
     const uint32_t mask = __builtin_amdgcn_readfirstlane(((1u << B) - 1u) * 0x00010001u << (7 - B));
     uint32_t one;
@@ -243,8 +261,9 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_qbit
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb)
-                    bx[h][cb] = SH ? *reinterpret_cast<const v8bf*>(&xb[(cb * 16 + li) * XPITCH + 64 * q + 16 * lg + 8 * h])
-                                   : __builtin_bit_cast(v8bf, r.xa[(q * 2 + h) * NCB + cb]);
+                    bx[h][cb] = SH   ? *reinterpret_cast<const v8bf*>(&xb[(cb * 16 + li) * XPITCH + 64 * q + 16 * lg + 8 * h])
+                                : CS ? *reinterpret_cast<const v8bf*>(&xb[xrow1 + 64 * q + 16 * lg + 8 * h])
+                                     : __builtin_bit_cast(v8bf, r.xa[(q * 2 + h) * NCB + cb]);
             const v8bf neg = __builtin_bit_cast(v8bf, make_uint4(QB_NEG15, QB_NEG15, QB_NEG15, QB_NEG15));
             v4f d[NCB];
 #pragma unroll
@@ -280,10 +299,11 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_qbit
     // weights, scales and activations of chunk c + D into slot u (indices
     // clamped to the last chunk, so the body has no branch), barrier.  The
     // four waves of the workgroup (four row blocks) share the staged chunk.
-    // Without SH: compute from the registers, refill the slot, no barrier.
+    // CS: the same staging within one wave, no barrier.  Otherwise: compute
+    // from the registers, refill the slot, no barrier.
     auto body = [&](int c, int u) {
         compute(u, xs[c & 1]);
-        if constexpr (SH) store_x((c + 1) & 1, (u + 1) % D);
+        if constexpr (SH || CS) store_x((c + 1) & 1, (u + 1) % D);
         load(u, c_begin + min(c + D, nch - 1));
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (SH) __syncthreads();
@@ -291,10 +311,8 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_qbit
     if (nch > 0) {
 #pragma unroll
         for (int d = 0; d < D; ++d) load(d, c_begin + min(d, nch - 1));
-        if constexpr (SH) {
-            store_x(0, 0);
-            __syncthreads();
-        }
+        if constexpr (SH || CS) store_x(0, 0);
+        if constexpr (SH) __syncthreads();
         int c = 0;
         for (; c + D <= nch; c += D) {
 #pragma unroll
@@ -303,7 +321,7 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_qbit
 #pragma unroll
         for (int u = 0; u < D - 1; ++u) {
             if (c + u < nch) {
-                if constexpr (SH) body(c + u, u);     // the next chunk's activations are staged here
+                if constexpr (SH || CS) body(c + u, u);     // the next chunk's activations are staged here
                 else compute(u, xs[0]);
             }
         }
@@ -386,13 +404,13 @@ int64_t gemv_qbits_workspace_bytes(int64_t T, int64_t N, int64_t K) {
     return wl > need ? wl : need;
 }
 
-template <int B, int NCB, bool PK>
+template <int B, int NCB, bool PK, int XS = 0>
 static void launch_qb_ncb(const WavePlan& p, const void* w, const uint16_t* wsc, const uint16_t* x, int Tc, int64_t N,
                           int64_t K, bool bf16_out, void* y, float* partial, unsigned* counters, hipStream_t stream) {
     constexpr bool SH = NCB >= 2;
     constexpr int NW = SH ? WG_WAVES : 1;
-    gemv_qbits_kernel<B, NCB, PK, SH><<<dim3((unsigned)((p.rbs + NW - 1) / NW), (unsigned)p.splits), 64 * NW, 0,
-                                        stream>>>(
+    gemv_qbits_kernel<B, NCB, PK, SH, XS><<<dim3((unsigned)((p.rbs + NW - 1) / NW), (unsigned)p.splits), 64 * NW, 0,
+                                            stream>>>(
         reinterpret_cast<const uint8_t*>(w), wsc, x, Tc, (int)N, K, p.chunks_per_split, p.splits, partial, counters,
         bf16_out ? 1 : 0, y);
 }
@@ -400,10 +418,14 @@ static void launch_qb_ncb(const WavePlan& p, const void* w, const uint16_t* wsc,
 template <int B, bool PK>
 static void launch_qb(const WavePlan& p, const void* w, const uint16_t* wsc, const uint16_t* x, int Tc, int64_t N,
                       int64_t K, bool bf16_out, void* y, float* partial, unsigned* counters, hipStream_t stream) {
-    switch ((Tc + 15) / 16) {
-        case 1: launch_qb_ncb<B, 1, PK>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
-        case 2: launch_qb_ncb<B, 2, PK>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
-        case 3: launch_qb_ncb<B, 3, PK>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+    // one token block: the wave stages its first 2, 4 or 8 token rows itself (T <= 8)
+    switch (Tc <= 2 ? 1 : Tc <= 4 ? 2 : Tc <= 8 ? 4 : (Tc + 15) / 16 + 8) {
+        case 1: launch_qb_ncb<B, 1, PK, 1>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+        case 2: launch_qb_ncb<B, 1, PK, 2>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+        case 4: launch_qb_ncb<B, 1, PK, 4>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+        case 9: launch_qb_ncb<B, 1, PK>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+        case 10: launch_qb_ncb<B, 2, PK>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+        case 11: launch_qb_ncb<B, 3, PK>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
         default: launch_qb_ncb<B, 4, PK>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
     }
 }
