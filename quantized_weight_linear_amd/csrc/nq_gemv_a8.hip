@@ -49,12 +49,13 @@ constexpr int a8_depth() {
     return NCB >= 3 ? 2 : 3;
 }
 
-template <int FMT, int NCB, bool SH>
+template <int FMT, int NCB, bool SH, int XS = 0>
 struct A8Chunk {
     typename A8Piece<FMT>::T w[4];      // group q's weight piece
     // SH: this thread's share of the chunk's activation codes (staged to LDS);
-    // otherwise the lane's B fragments [q * NCB + cb]
-    uint4 x[SH ? NCB : 4 * NCB];
+    // XS > 0: the wave's own share of its first 4 XS token rows (staged to
+    // its LDS rows); otherwise the lane's B fragments [q * NCB + cb]
+    uint4 x[SH ? NCB : (XS > 0 ? XS : 4 * NCB)];
     uint4 as[NCB];                      // the token's activation scales of the chunk's 4 groups
     uint2 ws[4];                        // row 4 lg + e: FP16 weight scales of the 4 groups
 };
@@ -84,10 +85,16 @@ __device__ __forceinline__ v4i q4_to_biased_bytes(uint2 p) {
 // SH: the workgroup's WG_WAVES waves (row blocks) share each chunk's
 // activation codes, staged in LDS (two or more token blocks: 17408x5120
 // Q8G64 T = 33 46.8 -> 40.9 us, 5120x17408 44.8 -> 34.9); otherwise each
-// 64-thread workgroup loads its own B fragments into registers, and the
-// single-wave workgroups spread evenly over the SIMDs (one token block:
-// 17408x5120 21.7 against 25.8 us with four row blocks per workgroup).
-template <int FMT, int NCB, bool PK, bool SH>
+// 64-thread workgroup works alone, and the single-wave workgroups spread
+// evenly over the SIMDs (one token block: 17408x5120 21.7 against 25.8 us
+// with four row blocks per workgroup).  A single wave either loads its B
+// fragments straight into registers (XS = 0: 4 loads of 16 bytes per lane
+// and chunk, rows t >= T read as zero) or (XS > 0, few tokens) loads only the
+// first 4 XS token rows of the chunk, XS contiguous 1 KiB loads, and stages
+// them in its own LDS rows; the fragment reads of the lanes past those rows
+// hit one zero row (zero-reading loads of absent rows cost as much address
+// work as real ones).
+template <int FMT, int NCB, bool PK, bool SH, int XS = 0>
 __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_a8_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ wsc,
                                                      const int8_t* __restrict__ aq, const float* __restrict__ asc,
                                                      int T, int N, int64_t K, int chunks_per_split, int splits,
@@ -97,7 +104,10 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_a8_k
     constexpr int D = a8_depth<NCB>();
     constexpr int TP = 16 * NCB;                 // token rows of the staged activation codes
     constexpr int XPITCH = A8_KC + 16;           // bytes per LDS row: rows shift by 4 banks
-    __shared__ __attribute__((aligned(16))) uint8_t xs[2][SH ? TP * XPITCH : 16];
+    constexpr bool CS = !SH && XS > 0;           // the wave stages its own first 4 XS token rows
+    static_assert(!CS || NCB == 1, "compact staging: one token block");
+    constexpr int SROWS = 4 * XS;                // CS: token rows staged; row SROWS stays zero
+    __shared__ __attribute__((aligned(16))) uint8_t xs[2][SH ? TP * XPITCH : (CS ? (SROWS + 1) * XPITCH : 16)];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int li = lane & 15, lg = lane >> 4;
@@ -140,18 +150,18 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_a8_k
 #pragma unroll
     for (int e = 0; e < 4; ++e) soff[e] = (int)(((int64_t)rb * 16 + 4 * lg + e) * G * 2);
 
-    A8Chunk<FMT, NCB, SH> ring[D];
+    A8Chunk<FMT, NCB, SH, XS> ring[D];
     auto load = [&](int slot, int64_t c) {
-        A8Chunk<FMT, NCB, SH>& r = ring[slot];
+        A8Chunk<FMT, NCB, SH, XS>& r = ring[slot];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             r.w[q] = *reinterpret_cast<const typename P::T*>(wrow + c * wcstride + q * wqstride);
-        if constexpr (SH) {
+        if constexpr (SH || CS) {
             // piece j of thread tid is row (tid + 256 j) / 16, 16 bytes
-            // (tid + 256 j) % 16 (rows >= T read zero)
+            // (tid + 256 j) % 16 (CS: lane + 64 j; rows >= T read zero)
 #pragma unroll
-            for (int j = 0; j < NCB; ++j) {
-                const int idx = tid + 256 * j;
+            for (int j = 0; j < (SH ? NCB : XS); ++j) {
+                const int idx = tid + (SH ? 256 : 64) * j;
                 r.x[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                        xr, (int)((int64_t)(idx >> 4) * K + c * A8_KC + 16 * (idx & 15)),
                                                        0, 0));
@@ -180,16 +190,26 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_a8_k
     const v4i neg8 = {(int)0xF8F8F8F8u, (int)0xF8F8F8F8u, (int)0xF8F8F8F8u, (int)0xF8F8F8F8u};
 
     auto store_x = [&](int buf, int slot) {
-        if constexpr (SH)
+        if constexpr (SH || CS)
 #pragma unroll
-        for (int j = 0; j < NCB; ++j) {
-            const int idx = tid + 256 * j;
+        for (int j = 0; j < (SH ? NCB : XS); ++j) {
+            const int idx = tid + (SH ? 256 : 64) * j;
             *reinterpret_cast<uint4*>(&xs[buf][(idx >> 4) * XPITCH + 16 * (idx & 15)]) = ring[slot].x[j];
         }
     };
 
+    // CS: the zero row of both buffers (lanes 0..15 buffer 0, 16..31 buffer
+    // 1) and the lane's fragment row (its token, or the zero row).  One wave:
+    // its LDS accesses take effect in program order, no barrier.
+    int xrow1 = 0;
+    if constexpr (CS) {
+        if (lane < 32)
+            *reinterpret_cast<uint4*>(&xs[lane >> 4][SROWS * XPITCH + 16 * (lane & 15)]) = make_uint4(0u, 0u, 0u, 0u);
+        xrow1 = (li < SROWS ? li : SROWS) * XPITCH;
+    }
+
     auto compute = [&](int slot, const uint8_t* xb) {
-        A8Chunk<FMT, NCB, SH>& r = ring[slot];
+        A8Chunk<FMT, NCB, SH, XS>& r = ring[slot];
         if constexpr (!PK) {
             const int addr = 4 * (4 * li + lg);       // fragment lane 16 g + i takes lane 4 i + g's words
 #pragma unroll
@@ -220,8 +240,9 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_a8_k
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
                 // B fragment: token cb * 16 + i, codes 64 q + 16 g .. + 16 of the chunk
-                const v4i b = SH ? *reinterpret_cast<const v4i*>(&xb[(cb * 16 + li) * XPITCH + 64 * q + 16 * lg])
-                                 : __builtin_bit_cast(v4i, r.x[q * NCB + cb]);
+                const v4i b = SH   ? *reinterpret_cast<const v4i*>(&xb[(cb * 16 + li) * XPITCH + 64 * q + 16 * lg])
+                              : CS ? *reinterpret_cast<const v4i*>(&xb[xrow1 + 64 * q + 16 * lg])
+                                   : __builtin_bit_cast(v4i, r.x[q * NCB + cb]);
                 v4i d;
                 if constexpr (FMT == W_Q4G64) {
                     d = __builtin_amdgcn_mfma_i32_16x16x64_i8(neg8, b, bias, 0, 0, 0);
@@ -244,10 +265,11 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_a8_k
     // stage the activation codes of chunk c + 1, request chunk c + D into
     // slot u (indices clamped to the last chunk, so the body has no branch),
     // barrier.  The four waves (four row blocks) share the staged codes.
-    // Without SH: compute from the registers, refill the slot, no barrier.
+    // CS: the same staging within one wave, no barrier.  Otherwise: compute
+    // from the registers, refill the slot, no barrier.
     auto body = [&](int c, int u) {
         compute(u, xs[c & 1]);
-        if constexpr (SH) store_x((c + 1) & 1, (u + 1) % D);
+        if constexpr (SH || CS) store_x((c + 1) & 1, (u + 1) % D);
         load(u, c_begin + min(c + D, nch - 1));
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (SH) __syncthreads();
@@ -255,10 +277,8 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_a8_k
     if (nch > 0) {
 #pragma unroll
         for (int d = 0; d < D; ++d) load(d, c_begin + min(d, nch - 1));
-        if constexpr (SH) {
-            store_x(0, 0);
-            __syncthreads();
-        }
+        if constexpr (SH || CS) store_x(0, 0);
+        if constexpr (SH) __syncthreads();
         int c = 0;
         for (; c + D <= nch; c += D) {
 #pragma unroll
@@ -267,7 +287,7 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_a8_k
 #pragma unroll
         for (int u = 0; u < D - 1; ++u) {
             if (c + u < nch) {
-                if constexpr (SH) body(c + u, u);     // the next chunk's codes are staged here
+                if constexpr (SH || CS) body(c + u, u);     // the next chunk's codes are staged here
                 else compute(u, xs[0]);
             }
         }
@@ -291,14 +311,14 @@ int64_t gemv_a8_workspace_bytes(int64_t T, int64_t N, int64_t K) {
     return wl > need ? wl : need;
 }
 
-template <int FMT, int NCB, bool PK>
+template <int FMT, int NCB, bool PK, int XS = 0>
 static void launch_a8_ncb(const WavePlan& p, const void* w, const uint16_t* wsc, const int8_t* aq, const float* asc,
                           int Tc, int64_t N, int64_t K, bool bf16_out, void* y, float* partial, unsigned* counters,
                           hipStream_t stream) {
     constexpr bool SH = NCB >= 2;
     constexpr int NW = SH ? WG_WAVES : 1;
-    gemv_a8_kernel<FMT, NCB, PK, SH><<<dim3((unsigned)((p.rbs + NW - 1) / NW), (unsigned)p.splits), 64 * NW, 0,
-                                       stream>>>(
+    gemv_a8_kernel<FMT, NCB, PK, SH, XS><<<dim3((unsigned)((p.rbs + NW - 1) / NW), (unsigned)p.splits), 64 * NW, 0,
+                                           stream>>>(
         reinterpret_cast<const uint8_t*>(w), wsc, aq, asc, Tc, (int)N, K, p.chunks_per_split, p.splits, partial,
         counters, bf16_out ? 1 : 0, y);
 }
@@ -307,10 +327,13 @@ template <int FMT, bool PK>
 static void launch_a8_fmt(const WavePlan& p, const void* w, const uint16_t* wsc, const int8_t* aq, const float* asc,
                           int Tc, int64_t N, int64_t K, bool bf16_out, void* y, float* partial, unsigned* counters,
                           hipStream_t stream) {
-    switch ((Tc + 15) / 16) {
-        case 1: launch_a8_ncb<FMT, 1, PK>(p, w, wsc, aq, asc, Tc, N, K, bf16_out, y, partial, counters, stream); break;
-        case 2: launch_a8_ncb<FMT, 2, PK>(p, w, wsc, aq, asc, Tc, N, K, bf16_out, y, partial, counters, stream); break;
-        case 3: launch_a8_ncb<FMT, 3, PK>(p, w, wsc, aq, asc, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+    // one token block: the wave stages its first 4 or 8 token rows itself (T <= 8)
+    switch (Tc <= 4 ? 1 : Tc <= 8 ? 2 : (Tc + 15) / 16 + 8) {
+        case 1: launch_a8_ncb<FMT, 1, PK, 1>(p, w, wsc, aq, asc, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+        case 2: launch_a8_ncb<FMT, 1, PK, 2>(p, w, wsc, aq, asc, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+        case 9: launch_a8_ncb<FMT, 1, PK>(p, w, wsc, aq, asc, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+        case 10: launch_a8_ncb<FMT, 2, PK>(p, w, wsc, aq, asc, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+        case 11: launch_a8_ncb<FMT, 3, PK>(p, w, wsc, aq, asc, Tc, N, K, bf16_out, y, partial, counters, stream); break;
         default: launch_a8_ncb<FMT, 4, PK>(p, w, wsc, aq, asc, Tc, N, K, bf16_out, y, partial, counters, stream); break;
     }
 }
