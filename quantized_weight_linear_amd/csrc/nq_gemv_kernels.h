@@ -956,7 +956,17 @@ constexpr bool two_tile_format() {
 // many tiles per CU): eight waves take two neighbouring row tiles, waves
 // 4 h + q tile h and column quarter q, and share one activation stage, which
 // halves the activation bytes staged per weight byte.
-template <int FMT, int NCB, bool PK, int TH = 1>
+//
+// XSKIP (TH = 1, one token block, T <= 8): the second 8-row round of the
+// activation staging holds no token, so it is not loaded; the B fragment
+// rows of the lanes past the staged rows read one zero row instead (row 8 of
+// each buffer, cleared once).  Loads of absent token rows read zero through
+// the buffer bounds but cost the address unit as much as real ones
+// (17408x5120 Q8G32 T = 1 / 8: 23.2 / 24.4 -> 21.6 / 22.5 us, 5120x17408
+// 25.0 / 25.5 -> 22.2 / 22.5; row-FP8 T = 1 / 4 17.8 / 17.6 -> 17.4 / 17.3).
+// Skipping the last round at three token blocks (T = 33..40) did not help
+// row-FP8 and cost the grouped formats 1-4 %, so it is used at one block only.
+template <int FMT, int NCB, bool PK, int TH = 1, bool XSKIP = false>
 __global__ __launch_bounds__(256 * TH, (TH == 1 ? stream_min_waves<FMT, NCB>() : 2)) void gemv_mfma_kernel(
     const uint8_t* __restrict__ w, const void* __restrict__ scales, const uint16_t* __restrict__ x, int T, int N,
     int64_t K, int chunks_per_split, int splits, float* __restrict__ partial, unsigned* __restrict__ counters,
@@ -966,6 +976,9 @@ __global__ __launch_bounds__(256 * TH, (TH == 1 ? stream_min_waves<FMT, NCB>() :
     constexpr int XPR = GV_KC / 8;                    // 16-byte activation pieces per row and chunk
     constexpr int NT = 256 * TH;                      // threads
     constexpr int XP = TP * XPR / NT;                 // ... per thread
+    static_assert(!XSKIP || (TH == 1 && NCB == 1), "skipped staging round: one tile, one token block");
+    constexpr int XPS = XSKIP ? XP - 1 : XP;          // staging rounds loaded
+    constexpr int ZROW = XPS * NT / XPR;              // XSKIP: the zero row (first row not staged)
     constexpr int GS = group_size<FMT>();
     static_assert(TH == 1 || GS == 0, "two tiles per workgroup: formats without group scales");
     constexpr int NG = GS ? GV_KC / (GS ? GS : 1) : 1;   // scale groups per chunk
@@ -1025,7 +1038,7 @@ __global__ __launch_bounds__(256 * TH, (TH == 1 ? stream_min_waves<FMT, NCB>() :
     auto load_x = [&](int slot, int c) {
         const int64_t kc0 = k_begin + (int64_t)c * GV_KC;
 #pragma unroll
-        for (int j = 0; j < XP; ++j) {
+        for (int j = 0; j < XPS; ++j) {
             const int idx = tid + NT * j;
             const int t = idx / XPR, pc = idx % XPR;
             const int off = (int)(((int64_t)t * K + kc0 + 8 * pc) * 2);
@@ -1044,7 +1057,7 @@ __global__ __launch_bounds__(256 * TH, (TH == 1 ? stream_min_waves<FMT, NCB>() :
     };
     auto store_x = [&](int buf, int slot) {
 #pragma unroll
-        for (int j = 0; j < XP; ++j) {
+        for (int j = 0; j < XPS; ++j) {
             const int idx = tid + NT * j;
             const int t = idx / XPR, pc = idx % XPR;
             *reinterpret_cast<uint4*>(&xs[buf][t * XPITCH + 8 * pc]) = xreg[slot][j];
@@ -1066,7 +1079,11 @@ __global__ __launch_bounds__(256 * TH, (TH == 1 ? stream_min_waves<FMT, NCB>() :
         for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = v4f{0.f, 0.f, 0.f, 0.f};
     int xrow[NCB];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) xrow[cb] = (cb * 16 + li) * XPITCH;
+    for (int cb = 0; cb < NCB; ++cb) xrow[cb] = (XSKIP && cb * 16 + li > ZROW ? ZROW : cb * 16 + li) * XPITCH;
+    if constexpr (XSKIP) {     // the zero row of both buffers (threads 0..63), before the first barrier
+        if (tid < 64)
+            *reinterpret_cast<uint4*>(&xs[tid >> 5][ZROW * XPITCH + 8 * (tid & 31)]) = make_uint4(0u, 0u, 0u, 0u);
+    }
 
     // One chunk c (c = u mod D): compute from ring slot u and LDS buffer c & 1,
     // stage the activations of chunk c + 1 (register slot (u + 1) mod D),
@@ -1470,10 +1487,14 @@ static void launch_mfma(const GemvPlan& p, const void* w, const void* scales, co
         }
     }
     const dim3 g = p.spread_wgs > 0 ? dim3((unsigned)(p.main_tiles + p.spread_wgs)) : grid;
-    gemv_mfma_kernel<FMT, NCB, PK><<<g, 256, 0, stream>>>(reinterpret_cast<const uint8_t*>(w), scales, x, Tc, (int)N,
-                                                          K, p.chunks_per_split, p.splits, partial, counters,
-                                                          bf16_out ? 1 : 0, y, (int)p.main_tiles, p.spread_wgs,
-                                                          p.maxslots);
+    if (NCB == 1 && Tc <= 8)      // no token in the second 8-row staging round
+        gemv_mfma_kernel<FMT, 1, PK, 1, true><<<g, 256, 0, stream>>>(
+            reinterpret_cast<const uint8_t*>(w), scales, x, Tc, (int)N, K, p.chunks_per_split, p.splits, partial,
+            counters, bf16_out ? 1 : 0, y, (int)p.main_tiles, p.spread_wgs, p.maxslots);
+    else
+        gemv_mfma_kernel<FMT, NCB, PK><<<g, 256, 0, stream>>>(
+            reinterpret_cast<const uint8_t*>(w), scales, x, Tc, (int)N, K, p.chunks_per_split, p.splits, partial,
+            counters, bf16_out ? 1 : 0, y, (int)p.main_tiles, p.spread_wgs, p.maxslots);
 }
 
 template <int FMT, bool PK>
