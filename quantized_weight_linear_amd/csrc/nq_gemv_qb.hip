@@ -110,8 +110,10 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_qbit
     constexpr int XP = TP * (WG_KC / 8) / 256;   // 16-byte activation pieces per thread and chunk
     constexpr bool CS = !SH && XS > 0;           // the wave stages its own first 2 XS token rows
     static_assert(!CS || NCB == 1, "compact staging: one token block");
-    constexpr int SROWS = 2 * XS;                // CS: token rows staged; row SROWS stays zero
-    constexpr int XR = SH ? XP : (CS ? XS : 8 * NCB);   // activation registers per ring slot
+    constexpr bool SK = SH && XS > 0;            // SH: only the first XS 8-row staging rounds hold tokens
+    static_assert(!SK || XS < XP, "skipped staging rounds");
+    constexpr int SROWS = CS ? 2 * XS : 8 * XS;  // CS / SK: token rows staged; row SROWS stays zero
+    constexpr int XR = SH ? (SK ? XS : XP) : (CS ? XS : 8 * NCB);   // activation registers per ring slot
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][SH ? TP * XPITCH : (CS ? (SROWS + 1) * XPITCH : 8)];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -226,6 +228,11 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_qbit
         *reinterpret_cast<uint4*>(&xs[lane >> 5][SROWS * XPITCH + 8 * (lane & 31)]) = make_uint4(0u, 0u, 0u, 0u);
         xrow1 = (li < SROWS ? li : SROWS) * XPITCH;
     }
+    // SK: the zero row of both buffers (threads 0..63), before the first barrier
+    if constexpr (SK) {
+        if (tid < 64)
+            *reinterpret_cast<uint4*>(&xs[tid >> 5][SROWS * XPITCH + 8 * (tid & 31)]) = make_uint4(0u, 0u, 0u, 0u);
+    }
 
     const uint32_t mask = __builtin_amdgcn_readfirstlane(((1u << B) - 1u) * 0x00010001u << (7 - B));
     uint32_t one;
@@ -261,7 +268,7 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_qbit
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb)
-                    bx[h][cb] = SH   ? *reinterpret_cast<const v8bf*>(&xb[(cb * 16 + li) * XPITCH + 64 * q + 16 * lg + 8 * h])
+                    bx[h][cb] = SH   ? *reinterpret_cast<const v8bf*>(&xb[(SK && cb * 16 + li > SROWS ? SROWS : cb * 16 + li) * XPITCH + 64 * q + 16 * lg + 8 * h])
                                 : CS ? *reinterpret_cast<const v8bf*>(&xb[xrow1 + 64 * q + 16 * lg + 8 * h])
                                      : __builtin_bit_cast(v8bf, r.xa[(q * 2 + h) * NCB + cb]);
             const v8bf neg = __builtin_bit_cast(v8bf, make_uint4(QB_NEG15, QB_NEG15, QB_NEG15, QB_NEG15));
@@ -424,9 +431,19 @@ static void launch_qb(const WavePlan& p, const void* w, const uint16_t* wsc, con
         case 2: launch_qb_ncb<B, 1, PK, 2>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
         case 4: launch_qb_ncb<B, 1, PK, 4>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
         case 9: launch_qb_ncb<B, 1, PK>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
-        case 10: launch_qb_ncb<B, 2, PK>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
-        case 11: launch_qb_ncb<B, 3, PK>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
-        default: launch_qb_ncb<B, 4, PK>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream); break;
+        // two or more token blocks: the last 8-row staging round is skipped when it holds no token
+        case 10:
+            if (Tc <= 24) launch_qb_ncb<B, 2, PK, 3>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream);
+            else launch_qb_ncb<B, 2, PK>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream);
+            break;
+        case 11:
+            if (Tc <= 40) launch_qb_ncb<B, 3, PK, 5>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream);
+            else launch_qb_ncb<B, 3, PK>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream);
+            break;
+        default:
+            if (Tc <= 56) launch_qb_ncb<B, 4, PK, 7>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream);
+            else launch_qb_ncb<B, 4, PK>(p, w, wsc, x, Tc, N, K, bf16_out, y, partial, counters, stream);
+            break;
     }
 }
 

@@ -1202,7 +1202,7 @@ def _qb_gemv(fmt, cd, pk, sd, x, n, k, wmode, out="f32"):
 
 @pytest.mark.parametrize("name,fmt,bits", QB_FMTS)
 @pytest.mark.parametrize("n,k", [(1000, 1536), (200, 1280), (70, 256), (16448, 768), (33, 5120)])
-@pytest.mark.parametrize("t", [1, 2, 3, 4, 6, 8, 9, 16, 17, 33, 65])
+@pytest.mark.parametrize("t", [1, 2, 3, 4, 6, 8, 9, 16, 17, 24, 25, 33, 40, 41, 56, 65])
 def test_gemv_qbits(name, fmt, bits, n, k, t):
     d = W.grouped(name, n, k, seed=n + t)
     x = W.bf16_normal(W.rng(150, t + k), (t, k))
