@@ -155,7 +155,11 @@ __global__ __launch_bounds__(SH ? 64 * WG_WAVES : 64, SH ? 2 : 1) void gemv_a8_k
         A8Chunk<FMT, NCB, SH, XS>& r = ring[slot];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            r.w[q] = *reinterpret_cast<const typename P::T*>(wrow + c * wcstride + q * wqstride);
+            // packed: non-temporal (1-7 % faster at T = 1, 8 in the same run, level
+            // at 33); row-major rows are read in quarters of a line by four waves,
+            // which non-temporal loads made 12-55 % slower
+            if constexpr (PK) ld_nt(r.w[q], wrow + c * wcstride + q * wqstride);
+            else r.w[q] = *reinterpret_cast<const typename P::T*>(wrow + c * wcstride + q * wqstride);
         if constexpr (SH || CS) {
             // piece j of thread tid is row (tid + 256 j) / 16, 16 bytes
             // (tid + 256 j) % 16 (CS: lane + 64 j; rows >= T read zero)

@@ -147,7 +147,9 @@ __device__ __forceinline__ WSrc make_wsrc(const uint8_t* w, const void* scales, 
     return s;
 }
 
-template <int FMT, bool PK>
+// NT (packed only): non-temporal loads, for the kernels and weight sizes where
+// they measured faster (see launch_mfma).
+template <int FMT, bool PK, bool NT = false>
 __device__ __forceinline__ void load_chunk(WChunk<FMT>& r, const WSrc& src, int64_t c) {
     using P = PieceFmt<FMT>;
 #pragma unroll
@@ -156,7 +158,8 @@ __device__ __forceinline__ void load_chunk(WChunk<FMT>& r, const WSrc& src, int6
         const int q = src.q0 + j % P::PW;
         const uint8_t* p = PK ? src.base[rb] + c * src.cstride + q * (64 * P::PB)
                               : src.base[rb] + piece_offset<FMT>(c, q, src.g);
-        r.p[j] = *reinterpret_cast<const typename P::Piece*>(p);
+        if constexpr (PK && NT) ld_nt(r.p[j], p);
+        else r.p[j] = *reinterpret_cast<const typename P::Piece*>(p);
         if constexpr (FMT == W_MXFP8) r.e8[j] = src.e8[rb][(c * GV_KC + 64 * q + 16 * src.ge) >> 5];
     }
 }
@@ -658,7 +661,7 @@ constexpr int SPREAD_MAXSEG = 3;
 // The spread workgroup whose range holds leftover unit v.
 __device__ __forceinline__ int spread_owner(int64_t v, int64_t U, int E) { return (int)(((v + 1) * E - 1) / U); }
 
-template <int FMT, int NCB, bool PK>
+template <int FMT, int NCB, bool PK, bool NT = false>
 __device__ __forceinline__ void direct_spread(const uint8_t* __restrict__ w, const void* __restrict__ scales,
                                               const uint16_t* __restrict__ x, int T, int N, int64_t K, int tile0,
                                               int R, int e, int E, int maxslots, float* __restrict__ partial,
@@ -742,7 +745,8 @@ __device__ __forceinline__ void direct_spread(const uint8_t* __restrict__ w, con
                 const int lc = (int64_t)(lane >> 2) < lim ? (lane >> 2) : (int)lim;
                 pw = w + (rowb + lc) * row_bytes<FMT>(K) + piece_offset<FMT>(c, q, lane & 3);
             }
-            wr[slot].p[j] = *reinterpret_cast<const typename P::Piece*>(pw);
+            if constexpr (PK && NT) ld_nt(wr[slot].p[j], pw);
+            else wr[slot].p[j] = *reinterpret_cast<const typename P::Piece*>(pw);
             if constexpr (GS != 0) {
                 if (j % P::PW == 0) {
                     // the wave's columns [64 wv, 64 wv + 64) of chunk c are group 4 c + wv
@@ -957,6 +961,8 @@ constexpr bool two_tile_format() {
 // 4 h + q tile h and column quarter q, and share one activation stage, which
 // halves the activation bytes staged per weight byte.
 //
+// WNT: non-temporal weight loads (packed weights; see launch_mfma).
+//
 // XSKIP (TH = 1, one token block, T <= 8): the second 8-row round of the
 // activation staging holds no token, so it is not loaded; the B fragment
 // rows of the lanes past the staged rows read one zero row instead (row 8 of
@@ -966,7 +972,7 @@ constexpr bool two_tile_format() {
 // 25.0 / 25.5 -> 22.2 / 22.5; row-FP8 T = 1 / 4 17.8 / 17.6 -> 17.4 / 17.3).
 // Skipping the last round at three token blocks (T = 33..40) did not help
 // row-FP8 and cost the grouped formats 1-4 %, so it is used at one block only.
-template <int FMT, int NCB, bool PK, int TH = 1, bool XSKIP = false>
+template <int FMT, int NCB, bool PK, int TH = 1, bool XSKIP = false, bool WNT = false>
 __global__ __launch_bounds__(256 * TH, (TH == 1 ? stream_min_waves<FMT, NCB>() : 2)) void gemv_mfma_kernel(
     const uint8_t* __restrict__ w, const void* __restrict__ scales, const uint16_t* __restrict__ x, int T, int N,
     int64_t K, int chunks_per_split, int splits, float* __restrict__ partial, unsigned* __restrict__ counters,
@@ -993,7 +999,7 @@ __global__ __launch_bounds__(256 * TH, (TH == 1 ? stream_min_waves<FMT, NCB>() :
         __shared__ int s_last_sp[SPREAD_MAXSEG];
         if ((int)blockIdx.x < spread_wgs) {
             const int tiles_all = (int)((N + GV_ROWS - 1) / GV_ROWS);
-            direct_spread<FMT, NCB, PK>(w, scales, x, T, N, K, main_tiles, tiles_all - main_tiles,
+            direct_spread<FMT, NCB, PK, WNT>(w, scales, x, T, N, K, main_tiles, tiles_all - main_tiles,
                                         (int)blockIdx.x, spread_wgs, maxslots, partial, counters,
                                         bf16_out, y, reinterpret_cast<v4f*>(&xs[0][0]), s_last_sp);
             return;
@@ -1096,7 +1102,7 @@ __global__ __launch_bounds__(256 * TH, (TH == 1 ? stream_min_waves<FMT, NCB>() :
         chunk_mfma<FMT, NCB, PK>(ring[u], xs[buf], xrow, 0, scs[buf], 0, wv, lg, acc);
         store_x((c + 1) & 1, (u + 1) % D);
         load_x(u, min(c + D, nch - 1));
-        load_chunk<FMT, PK>(ring[u], src, c_begin + min(c + D, nch - 1));
+        load_chunk<FMT, PK, WNT>(ring[u], src, c_begin + min(c + D, nch - 1));
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
     };
@@ -1105,7 +1111,7 @@ __global__ __launch_bounds__(256 * TH, (TH == 1 ? stream_min_waves<FMT, NCB>() :
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             load_x(d, min(d, nch - 1));
-            load_chunk<FMT, PK>(ring[d], src, c_begin + min(d, nch - 1));
+            load_chunk<FMT, PK, WNT>(ring[d], src, c_begin + min(d, nch - 1));
         }
         store_x(0, 0);
         __syncthreads();
@@ -1273,7 +1279,7 @@ constexpr int depth_direct() {
 // one tile more and the launch takes nearly twice as long; the spread
 // workgroups (a few units each, resident beside the whole-tile ones) even the
 // CUs out, and their partial exchange ends long before the whole tiles do.
-template <int FMT, int NCB, bool PK>
+template <int FMT, int NCB, bool PK, bool NT = false>
 __global__ __launch_bounds__(256) void gemv_direct_kernel(const uint8_t* __restrict__ w,
                                                           const void* __restrict__ scales,
                                                           const uint16_t* __restrict__ x, int T, int N, int64_t K,
@@ -1289,7 +1295,7 @@ __global__ __launch_bounds__(256) void gemv_direct_kernel(const uint8_t* __restr
     __shared__ int s_last_sp[SPREAD_MAXSEG];
     if ((int)blockIdx.x < spread_wgs) {
         const int tiles_all = (int)((N + GV_ROWS - 1) / GV_ROWS);
-        direct_spread<FMT, NCB, PK>(w, scales, x, T, N, K, main_tiles, tiles_all - main_tiles,
+        direct_spread<FMT, NCB, PK, NT>(w, scales, x, T, N, K, main_tiles, tiles_all - main_tiles,
                                     (int)blockIdx.x, spread_wgs, maxslots, partial, counters, bf16_out,
                                     y, red, s_last_sp);
         return;
@@ -1331,7 +1337,7 @@ __global__ __launch_bounds__(256) void gemv_direct_kernel(const uint8_t* __restr
             for (int cb = 0; cb < NCB; ++cb)
                 xr[u].v[ls][cb] = __builtin_bit_cast(
                     uint4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, xoff[ls][cb] + (int)(c * GV_KC * 2), 0, 0));
-        load_chunk<FMT, PK>(wr[u], src, c);
+        load_chunk<FMT, PK, NT>(wr[u], src, c);
     };
 
     v4f acc[4][NCB];
@@ -1463,12 +1469,27 @@ static void launch_mfma(const GemvPlan& p, const void* w, const void* scales, co
                         int64_t K, bool bf16_out, void* y, float* partial, unsigned* counters,
                         hipStream_t stream) {
     dim3 grid((unsigned)p.tiles, (unsigned)p.splits);
+    // Non-temporal weight loads (packed weights of 32 MiB or more; the direct
+    // kernel, and the two-tile kernel up to two token blocks).  Measured against
+    // plain loads: row-FP8 152064x5120 T = 1 / 4 / 8 / 16 / 32 129.2 / 128.7 /
+    // 130.6 / 132.0 / 141.2 -> 114.2 / 112.5 / 118.3 / 120.3 / 132.3 us,
+    // 5120x17408 T = 1 18.1 -> 17.2; slower: the two-tile kernel at T = 48 / 64
+    // (+2 / +4 %), the one-tile streaming kernel (17408x5120 row-FP8 T = 16
+    // +5 %, Q8G32 T = 1 +6 %), small matrices that the last-level cache keeps
+    // between launches (96x5120 BF16 +15 %), and row-major weights, whose rows
+    // four waves read in quarters of a line (+7..24 %).
+    const bool nt = PK && (int64_t)N * (FMT == W_BF16 ? 2 * K : K) >= ((int64_t)32 << 20);
     if constexpr (group_size<FMT>() == 0) {
         if (p.direct) {
             const dim3 g = p.spread_wgs > 0 ? dim3((unsigned)(p.main_tiles + p.spread_wgs)) : grid;
-            gemv_direct_kernel<FMT, NCB, PK><<<g, 256, 0, stream>>>(
-                reinterpret_cast<const uint8_t*>(w), scales, x, Tc, (int)N, K, p.chunks_per_split, p.splits, partial,
-                counters, bf16_out ? 1 : 0, y, (int)p.main_tiles, p.spread_wgs, p.maxslots);
+            if (nt)
+                gemv_direct_kernel<FMT, NCB, PK, true><<<g, 256, 0, stream>>>(
+                    reinterpret_cast<const uint8_t*>(w), scales, x, Tc, (int)N, K, p.chunks_per_split, p.splits,
+                    partial, counters, bf16_out ? 1 : 0, y, (int)p.main_tiles, p.spread_wgs, p.maxslots);
+            else
+                gemv_direct_kernel<FMT, NCB, PK><<<g, 256, 0, stream>>>(
+                    reinterpret_cast<const uint8_t*>(w), scales, x, Tc, (int)N, K, p.chunks_per_split, p.splits,
+                    partial, counters, bf16_out ? 1 : 0, y, (int)p.main_tiles, p.spread_wgs, p.maxslots);
             return;
         }
     }
@@ -1480,9 +1501,14 @@ static void launch_mfma(const GemvPlan& p, const void* w, const void* scales, co
     }
     if constexpr (two_tile_format<FMT, NCB>()) {
         if (p.two_tiles) {
-            gemv_mfma_kernel<FMT, NCB, PK, 2><<<dim3((unsigned)((p.tiles + 1) / 2)), 512, 0, stream>>>(
-                reinterpret_cast<const uint8_t*>(w), scales, x, Tc, (int)N, K, p.chunks_per_split, 1, partial,
-                counters, bf16_out ? 1 : 0, y, 0, 0, 0);
+            if (nt && NCB <= 2)
+                gemv_mfma_kernel<FMT, NCB, PK, 2, false, true><<<dim3((unsigned)((p.tiles + 1) / 2)), 512, 0, stream>>>(
+                    reinterpret_cast<const uint8_t*>(w), scales, x, Tc, (int)N, K, p.chunks_per_split, 1, partial,
+                    counters, bf16_out ? 1 : 0, y, 0, 0, 0);
+            else
+                gemv_mfma_kernel<FMT, NCB, PK, 2><<<dim3((unsigned)((p.tiles + 1) / 2)), 512, 0, stream>>>(
+                    reinterpret_cast<const uint8_t*>(w), scales, x, Tc, (int)N, K, p.chunks_per_split, 1, partial,
+                    counters, bf16_out ? 1 : 0, y, 0, 0, 0);
             return;
         }
     }
