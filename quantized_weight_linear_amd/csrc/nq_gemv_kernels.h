@@ -1470,12 +1470,14 @@ static void launch_mfma(const GemvPlan& p, const void* w, const void* scales, co
                         hipStream_t stream) {
     dim3 grid((unsigned)p.tiles, (unsigned)p.splits);
     // Non-temporal weight loads (packed weights of 32 MiB or more; the direct
-    // kernel, and the two-tile kernel up to two token blocks).  Measured against
+    // kernel, the two-tile kernel up to two token blocks, and the one-tile
+    // streaming kernel on many tiles at one token block).  Measured against
     // plain loads: row-FP8 152064x5120 T = 1 / 4 / 8 / 16 / 32 129.2 / 128.7 /
     // 130.6 / 132.0 / 141.2 -> 114.2 / 112.5 / 118.3 / 120.3 / 132.3 us,
     // 5120x17408 T = 1 18.1 -> 17.2; slower: the two-tile kernel at T = 48 / 64
-    // (+2 / +4 %), the one-tile streaming kernel (17408x5120 row-FP8 T = 16
-    // +5 %, Q8G32 T = 1 +6 %), small matrices that the last-level cache keeps
+    // (+2 / +4 %), the one-tile streaming kernel with one tile per CU and
+    // spread workgroups (17408x5120 row-FP8 T = 16 +5 %, Q8G32 T = 1 +6 %),
+    // small matrices that the last-level cache keeps
     // between launches (96x5120 BF16 +15 %), and row-major weights, whose rows
     // four waves read in quarters of a line (+7..24 %).
     const bool nt = PK && (int64_t)N * (FMT == W_BF16 ? 2 * K : K) >= ((int64_t)32 << 20);
@@ -1513,8 +1515,20 @@ static void launch_mfma(const GemvPlan& p, const void* w, const void* scales, co
         }
     }
     const dim3 g = p.spread_wgs > 0 ? dim3((unsigned)(p.main_tiles + p.spread_wgs)) : grid;
-    if (NCB == 1 && Tc <= 8)      // no token in the second 8-row staging round
+    // the one-tile streaming kernel takes non-temporal loads on many tiles per
+    // CU at one token block only (152064x5120 Q8G32 T = 1 / 8 / 16 140.8 /
+    // 155.0 / 168.1 -> 132.6 / 146.9 / 162.7 us; level to +2 % from 17 tokens on)
+    const bool snt = nt && NCB == 1 && p.tiles >= 4 * (int64_t)device_cu_count();
+    if (NCB == 1 && Tc <= 8 && snt)
+        gemv_mfma_kernel<FMT, 1, PK, 1, true, true><<<g, 256, 0, stream>>>(
+            reinterpret_cast<const uint8_t*>(w), scales, x, Tc, (int)N, K, p.chunks_per_split, p.splits, partial,
+            counters, bf16_out ? 1 : 0, y, (int)p.main_tiles, p.spread_wgs, p.maxslots);
+    else if (NCB == 1 && Tc <= 8)      // no token in the second 8-row staging round
         gemv_mfma_kernel<FMT, 1, PK, 1, true><<<g, 256, 0, stream>>>(
+            reinterpret_cast<const uint8_t*>(w), scales, x, Tc, (int)N, K, p.chunks_per_split, p.splits, partial,
+            counters, bf16_out ? 1 : 0, y, (int)p.main_tiles, p.spread_wgs, p.maxslots);
+    else if (snt)
+        gemv_mfma_kernel<FMT, 1, PK, 1, false, true><<<g, 256, 0, stream>>>(
             reinterpret_cast<const uint8_t*>(w), scales, x, Tc, (int)N, K, p.chunks_per_split, p.splits, partial,
             counters, bf16_out ? 1 : 0, y, (int)p.main_tiles, p.spread_wgs, p.maxslots);
     else
