@@ -1039,8 +1039,18 @@ __global__ __launch_bounds__(256 * TH, (TH == 1 ? stream_min_waves<FMT, NCB>() :
     // chunks ahead, in the same order as the chunk's weights, and stored to
     // LDS one chunk ahead of use: waiting for them then never waits for more
     // than the weights the current chunk needs anyway.
+    // WSC (group-64 formats in the XSKIP build): the chunk's group scales come
+    // from one 8-byte load per row by wave 0 instead of one 2-byte load per
+    // scale by every thread (four load instructions per chunk down to one;
+    // two comparisons on different boxes, T = 1 / 8: Q4G64 17408x5120 14.8 /
+    // 15.6 -> 14.0 / 15.5 us and 14.5 / 15.4 -> 14.3 / 15.6, 5120x17408 16.3 /
+    // 16.8 -> 15.3 / 15.7 and 16.1 / 16.7 -> 15.7 / 16.2, Q8G64 -2..3 %; in the
+    // other builds the branch made the compiler spill, 2-5x slower with the
+    // 16-byte form for group-32 scales).
+    constexpr bool WSC = GS == 64 && XSKIP;
     uint4 xreg[D][XP];
-    uint32_t sreg[D][SP];
+    uint32_t sreg[D][WSC ? 2 : SP];
+    const int wv_s = __builtin_amdgcn_readfirstlane(tid >> 6);
     auto load_x = [&](int slot, int c) {
         const int64_t kc0 = k_begin + (int64_t)c * GV_KC;
 #pragma unroll
@@ -1050,7 +1060,17 @@ __global__ __launch_bounds__(256 * TH, (TH == 1 ? stream_min_waves<FMT, NCB>() :
             const int off = (int)(((int64_t)t * K + kc0 + 8 * pc) * 2);
             xreg[slot][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, off, 0, 0));
         }
-        if constexpr (GS != 0) {
+        if constexpr (WSC) {
+            // wave 0 only: lane r loads row row0 + r's four scales of the
+            // chunk (contiguous 8 bytes) in one load; rows >= N read as zero
+            if (wv_s == 0) {
+                const int64_t row = row0 + lane;
+                const int off = (int)((row * (K / GS) + kc0 / GS) * 2);
+                const v2u v = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(srsrc, off, 0, 0));
+                sreg[slot][0] = v[0];
+                sreg[slot][1] = v[1];
+            }
+        } else if constexpr (GS != 0) {
 #pragma unroll
             for (int j = 0; j < SP; ++j) {
                 const int idx = tid + 256 * j;          // idx = row * NG + group
@@ -1068,7 +1088,13 @@ __global__ __launch_bounds__(256 * TH, (TH == 1 ? stream_min_waves<FMT, NCB>() :
             const int t = idx / XPR, pc = idx % XPR;
             *reinterpret_cast<uint4*>(&xs[buf][t * XPITCH + 8 * pc]) = xreg[slot][j];
         }
-        if constexpr (GS != 0) {
+        if constexpr (WSC) {
+            if (wv_s == 0) {
+#pragma unroll
+                for (int g = 0; g < NG; ++g)
+                    scs[buf][g * GV_ROWS + lane] = (uint16_t)(sreg[slot][g >> 1] >> (16 * (g & 1)));
+            }
+        } else if constexpr (GS != 0) {
 #pragma unroll
             for (int j = 0; j < SP; ++j) {
                 const int idx = tid + 256 * j;
