@@ -58,11 +58,11 @@ sys.path.insert(0, ROOT)
 # Summaries: profiles/gemv_fp8row_17408x5120_hbm_traffic.md.  Valid only for
 # the GEMV code they were taken on (gemv_source_hash over GEMV_SOURCES).
 GEMV_TRAFFIC = {
-    "source_sha256_16": "7731e9539417f47b",
+    "source_sha256_16": "b606c2413e711ba0",
     "fetch_factor": 262144.0 / 131083.5,
     "write_factor": 1.0,
-    "fetch_kib": {"gemv_fp8row_T1": 43819.9, "gemv_fp8row_T4": 44009.1, "gemv_fp8row_T16": 44767.7,
-                  "gemv_fp8row_T33": 45920.3},
+    "fetch_kib": {"gemv_fp8row_T1": 43819.3, "gemv_fp8row_T4": 44009.3, "gemv_fp8row_T16": 44768.8,
+                  "gemv_fp8row_T33": 45918.0},
     "write_kib": {"gemv_fp8row_T1": 79.5, "gemv_fp8row_T4": 301.5, "gemv_fp8row_T16": 1189.5,
                   "gemv_fp8row_T33": 2447.5},
 }
