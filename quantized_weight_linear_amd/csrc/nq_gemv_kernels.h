@@ -1042,7 +1042,7 @@ __global__ __launch_bounds__(256 * TH, (TH == 1 ? stream_min_waves<FMT, NCB>() :
     // WSC (group-64 formats in the XSKIP build): the chunk's group scales come
     // from one 8-byte load per row by wave 0 instead of one 2-byte load per
     // scale by every thread (four load instructions per chunk down to one;
-    // two comparisons on different boxes, T = 1 / 8: Q4G64 17408x5120 14.8 /
+    // two comparisons in separate runs, T = 1 / 8: Q4G64 17408x5120 14.8 /
     // 15.6 -> 14.0 / 15.5 us and 14.5 / 15.4 -> 14.3 / 15.6, 5120x17408 16.3 /
     // 16.8 -> 15.3 / 15.7 and 16.1 / 16.7 -> 15.7 / 16.2, Q8G64 -2..3 %; in the
     // other builds the branch made the compiler spill, 2-5x slower with the
