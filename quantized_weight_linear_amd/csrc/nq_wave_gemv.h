@@ -107,24 +107,27 @@ __device__ __forceinline__ void wave_finish(v4f (&acc)[NCB], int T, int N, int r
 }
 
 // Row blocks of 16; with fewer row blocks than the SIMDs (4 per CU), K is
-// split so that there are about as many workgroups as SIMDs, at least 4
-// chunks per split (only with a workspace).  More splits, for two or three
-// waves per SIMD, measured slower (17408 x 5120 A8 T = 1: 21.7 -> 25.9 us;
-// Q5 T = 8: 26.7 -> 31.3 us): the exchange and the repeated activation loads
-// cost more than the added overlap gains.
+// split so that there are about as many waves as SIMDs, at least 4 chunks per
+// split (only with a workspace).  Twice as many waves (two per SIMD, K split
+// twice as often) where that measured faster: two or more token blocks with
+// fewer row blocks than SIMDs (5120 x 17408 T = 33: Q3 / Q5 -8 %, A8 Q8G64 /
+// Q4G64 -9 / -15 %), and the Q3 / Q5 / Q6 kernel at T <= 2 (17408 x 5120 and
+// 5120 x 17408 T = 1: -6..10 %).  Elsewhere two waves per SIMD were slower
+// (T = 8: Q3 / Q5 +3..11 %; the A8 kernel at one token block +5..16 %).
 struct WavePlan {
     int64_t rbs;
     int splits;
     int chunks_per_split;
 };
 
-inline WavePlan plan_wave(int64_t N, int64_t K, int64_t Tc) {
-    (void)Tc;
+inline WavePlan plan_wave(int64_t N, int64_t K, int64_t Tc, bool qbits) {
     WavePlan p{};
     p.rbs = (N + 15) / 16;
     const int64_t chunks = K / WG_KC;
     const int64_t simds = 4 * (int64_t)device_cu_count();
-    int64_t s = p.rbs >= simds ? 1 : (simds + p.rbs / 2) / p.rbs;
+    const bool two_per_simd = (qbits && Tc <= 2) || (Tc > 16 && p.rbs < simds);
+    const int64_t waves = (two_per_simd ? 2 : 1) * simds;
+    int64_t s = p.rbs >= waves ? 1 : (waves + p.rbs / 2) / p.rbs;
     int64_t smax = chunks / 4;
     if (smax < 1) smax = 1;
     if (s > smax) s = smax;
@@ -145,9 +148,9 @@ inline int64_t wave_workspace(const WavePlan& p, int64_t Tc) {
 
 // The plan for one pass of Tc tokens, given the caller's workspace: the
 // counters and partials, or no split when the workspace is missing or small.
-inline WavePlan plan_wave_with(int64_t N, int64_t K, int64_t Tc, void* workspace, int64_t workspace_bytes,
-                               float** partial, unsigned** counters) {
-    WavePlan p = plan_wave(N, K, Tc);
+inline WavePlan plan_wave_with(int64_t N, int64_t K, int64_t Tc, bool qbits, void* workspace,
+                               int64_t workspace_bytes, float** partial, unsigned** counters) {
+    WavePlan p = plan_wave(N, K, Tc, qbits);
     *partial = nullptr;
     *counters = nullptr;
     if (p.splits > 1) {
