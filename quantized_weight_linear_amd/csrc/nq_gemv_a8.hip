@@ -307,12 +307,17 @@ int64_t gemv_a8_workspace_bytes(int64_t T, int64_t N, int64_t K) {
     if (T <= 0 || N <= 0 || K <= 0 || K % A8_KC != 0) return 0;
     int64_t need = 0;
     for (int64_t tc = 1; tc <= (T < 64 ? T : 64); tc += 15) {     // the largest over the passes' plans
-        const int64_t w = wave_workspace(plan_wave(N, K, tc, false), tc);
+        const int64_t w = wave_workspace(plan_wave(N, K, tc, 0), tc);
         if (w > need) need = w;
     }
     const int64_t tl = T < 64 ? T : 64;
-    const int64_t wl = wave_workspace(plan_wave(N, K, tl, false), tl);
-    return wl > need ? wl : need;
+    const int64_t wl = wave_workspace(plan_wave(N, K, tl, 0), tl);
+    if (wl > need) need = wl;
+    if (T > 64 && T % 64) {                                       // the remainder pass
+        const int64_t wr = wave_workspace(plan_wave(N, K, T % 64, 0), T % 64);
+        if (wr > need) need = wr;
+    }
+    return need;
 }
 
 template <int FMT, int NCB, bool PK, int XS = 0>
@@ -353,7 +358,7 @@ hipError_t launch_gemv_a8(int fmt, const void* w, const uint16_t* w_scale, const
         const int Tc = (int)((T - t0) < 64 ? (T - t0) : 64);
         float* partial;
         unsigned* counters;
-        const WavePlan p = plan_wave_with(N, K, Tc, false, workspace, workspace_bytes, &partial, &counters);
+        const WavePlan p = plan_wave_with(N, K, Tc, 0, workspace, workspace_bytes, &partial, &counters);
         const int8_t* aqc = aq + t0 * K;
         const float* ac = asc + t0 * G;
         void* yc = reinterpret_cast<char*>(y) + t0 * N * ybytes;

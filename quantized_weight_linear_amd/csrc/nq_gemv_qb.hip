@@ -403,12 +403,17 @@ int64_t gemv_qbits_workspace_bytes(int64_t T, int64_t N, int64_t K) {
     if (T <= 0 || N <= 0 || K <= 0 || K % WG_KC != 0) return 0;
     int64_t need = 0;
     for (int64_t tc = 1; tc <= (T < 64 ? T : 64); tc += 15) {     // the largest over the passes' plans
-        const int64_t w = wave_workspace(plan_wave(N, K, tc, true), tc);
+        const int64_t w = wave_workspace(plan_wave(N, K, tc, 3), tc);   // Q3's plan: the most splits
         if (w > need) need = w;
     }
     const int64_t tl = T < 64 ? T : 64;
-    const int64_t wl = wave_workspace(plan_wave(N, K, tl, true), tl);
-    return wl > need ? wl : need;
+    const int64_t wl = wave_workspace(plan_wave(N, K, tl, 3), tl);
+    if (wl > need) need = wl;
+    if (T > 64 && T % 64) {                                       // the remainder pass
+        const int64_t wr = wave_workspace(plan_wave(N, K, T % 64, 3), T % 64);
+        if (wr > need) need = wr;
+    }
+    return need;
 }
 
 template <int B, int NCB, bool PK, int XS = 0>
@@ -458,7 +463,7 @@ hipError_t launch_gemv_qbits(int fmt, const void* w, const uint16_t* w_scale, co
         const int Tc = (int)((T - t0) < 64 ? (T - t0) : 64);
         float* partial;
         unsigned* counters;
-        const WavePlan p = plan_wave_with(N, K, Tc, true, workspace, workspace_bytes, &partial, &counters);
+        const WavePlan p = plan_wave_with(N, K, Tc, b, workspace, workspace_bytes, &partial, &counters);
         const uint16_t* xc = x + t0 * K;
         void* yc = reinterpret_cast<char*>(y) + t0 * N * ybytes;
 #define NQ_QB_CASE(BITS)                                                                                         \

@@ -112,20 +112,22 @@ __device__ __forceinline__ void wave_finish(v4f (&acc)[NCB], int T, int N, int r
 // twice as often) where that measured faster: two or more token blocks with
 // fewer row blocks than SIMDs (5120 x 17408 T = 33: Q3 / Q5 -8 %, A8 Q8G64 /
 // Q4G64 -9 / -15 %), and the Q3 / Q5 / Q6 kernel at T <= 2 (17408 x 5120 and
-// 5120 x 17408 T = 1: -6..10 %).  Elsewhere two waves per SIMD were slower
-// (T = 8: Q3 / Q5 +3..11 %; the A8 kernel at one token block +5..16 %).
+// 5120 x 17408 T = 1: -6..10 %), for Q3 up to T = 4 (T = 3, 4: -6..9 %; Q5
+// +5..7 %).  Elsewhere two waves per SIMD were slower (T = 6, 8: Q3 / Q5
+// +1..11 %; the A8 kernel at one token block +5..16 %).  qbits: the code
+// width of the Q3 / Q5 / Q6 kernel, 0 for the A8 kernel.
 struct WavePlan {
     int64_t rbs;
     int splits;
     int chunks_per_split;
 };
 
-inline WavePlan plan_wave(int64_t N, int64_t K, int64_t Tc, bool qbits) {
+inline WavePlan plan_wave(int64_t N, int64_t K, int64_t Tc, int qbits) {
     WavePlan p{};
     p.rbs = (N + 15) / 16;
     const int64_t chunks = K / WG_KC;
     const int64_t simds = 4 * (int64_t)device_cu_count();
-    const bool two_per_simd = (qbits && Tc <= 2) || (Tc > 16 && p.rbs < simds);
+    const bool two_per_simd = (qbits && Tc <= (qbits == 3 ? 4 : 2)) || (Tc > 16 && p.rbs < simds);
     const int64_t waves = (two_per_simd ? 2 : 1) * simds;
     int64_t s = p.rbs >= waves ? 1 : (waves + p.rbs / 2) / p.rbs;
     int64_t smax = chunks / 4;
@@ -148,7 +150,7 @@ inline int64_t wave_workspace(const WavePlan& p, int64_t Tc) {
 
 // The plan for one pass of Tc tokens, given the caller's workspace: the
 // counters and partials, or no split when the workspace is missing or small.
-inline WavePlan plan_wave_with(int64_t N, int64_t K, int64_t Tc, bool qbits, void* workspace,
+inline WavePlan plan_wave_with(int64_t N, int64_t K, int64_t Tc, int qbits, void* workspace,
                                int64_t workspace_bytes, float** partial, unsigned** counters) {
     WavePlan p = plan_wave(N, K, Tc, qbits);
     *partial = nullptr;
